@@ -1,0 +1,303 @@
+"""Checks that pin the fp64 oracle to things other than itself.
+
+Each check returns ``None`` when it holds and a short message when it does not,
+so that the same checks serve the plain pin tests (``test_oracle_pins.py``) and
+the planted-mistake tests (``test_oracle_mutants.py``), which replace one piece
+of the oracle with a plausible wrong version and require some check to fail.
+
+What each check compares against:
+* ``bruteforce``     -- 40-digit ``decimal`` scalar loops (no NumPy) on tiny inputs,
+                        with GQA handled by ``np.repeat`` of the KV heads (MHA form);
+* ``closed_forms``   -- one token (output = its value, LSE = its score) and two
+                        tokens (logistic weights, ``logaddexp``), via SciPy/NumPy;
+* ``mean_probe``     -- all-zero query: exact rational mean of integer values, LSE = ln L;
+* ``shift``          -- adding a constant c to every score leaves the output and
+                        moves the LSE by c (built with an extra key dimension);
+* ``sdpa``           -- the paged decode step equals the last row of full causal
+                        attention over the contiguous sequence (PyTorch SDPA, fp64,
+                        ``enable_gqa``), contiguous K/V rebuilt from the generator's
+                        own record of which token sits in which slot;
+* ``gather``         -- the oracle's gather equals that record, bit for bit;
+* ``slots``          -- the oracle's slot for each new token equals the generator's;
+* ``merge``          -- S interleaved shards merged equal the unsharded result, for
+                        two partition sizes, and merging is associative.
+"""
+from __future__ import annotations
+
+from decimal import Decimal, getcontext
+
+import numpy as np
+
+from oracle import paged_attention as pa
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+# ----------------------------------------------------------------------------------
+def bruteforce_attention(q, K, V, scale):
+    """Scalar, 40-digit decimal softmax attention in MHA form: ``K``/``V`` are
+    ``[L][Hq][d]`` (one KV row per query head).  Returns lists of Decimals."""
+    getcontext().prec = 40
+    hq, dk = len(q), len(q[0])
+    L = len(K)
+    dv = len(V[0][0])
+    sc = Decimal(float(scale))
+    out, lses = [], []
+    for h in range(hq):
+        e = []
+        for t in range(L):
+            s = Decimal(0)
+            for d in range(dk):
+                s += Decimal(float(q[h][d])) * Decimal(float(K[t][h][d]))
+            e.append((sc * s).exp())
+        den = sum(e, Decimal(0))
+        row = []
+        for j in range(dv):
+            num = Decimal(0)
+            for t in range(L):
+                num += e[t] * Decimal(float(V[t][h][j]))
+            row.append(num / den)
+        out.append(row)
+        lses.append(den.ln())
+    return out, lses
+
+
+def check_bruteforce(seeds=range(6)):
+    for seed in seeds:
+        r = _rng(seed)
+        hkv = int(r.integers(1, 3))
+        g = int(r.integers(1, 3))
+        hq = hkv * g
+        L = int(r.integers(1, 9))
+        dk = int(r.integers(1, 5))
+        dv = int(r.integers(1, 5))
+        q = r.standard_normal((hq, dk)).astype(np.float32)
+        K = r.standard_normal((L, hkv, dk)).astype(np.float32)
+        V = r.standard_normal((L, hkv, dv)).astype(np.float32)
+        scale = float(np.float32(r.uniform(0.2, 1.5)))
+        o, lse = pa.attention(q, K, V, scale)
+        Kx = np.repeat(K.astype(np.float64), g, axis=1)
+        Vx = np.repeat(V.astype(np.float64), g, axis=1)
+        ob, lb = bruteforce_attention(q.astype(np.float64), Kx, Vx, scale)
+        ob = np.array([[float(x) for x in row] for row in ob])
+        lb = np.array([float(x) for x in lb])
+        if np.max(np.abs(o - ob)) > 1e-13 or np.max(np.abs(lse - lb)) > 1e-13:
+            return f"bruteforce seed {seed}: |do|={np.max(np.abs(o - ob)):.3g} |dlse|={np.max(np.abs(lse - lb)):.3g}"
+    return None
+
+
+def check_closed_forms():
+    from scipy.special import expit
+
+    r = _rng(11)
+    for dk, dv in ((3, 2), (8, 5)):
+        q = r.standard_normal((2, dk))
+        K = r.standard_normal((2, 1, dk))
+        V = r.standard_normal((2, 1, dv))
+        scale = 0.7
+        # one token
+        o, lse = pa.attention(q, K[:1], V[:1], scale)
+        s0 = scale * np.array([np.dot(q[h], K[0, 0]) for h in range(2)])
+        if not (np.array_equal(o, np.repeat(V[0], 2, axis=0)) and np.allclose(lse, s0, rtol=0, atol=1e-14)):
+            return "single token: output must be its value and lse its score"
+        # two tokens
+        o, lse = pa.attention(q, K, V, scale)
+        for h in range(2):
+            a = scale * np.dot(q[h], K[0, 0])
+            b = scale * np.dot(q[h], K[1, 0])
+            want = expit(a - b) * V[0, 0] + expit(b - a) * V[1, 0]
+            if np.max(np.abs(o[h] - want)) > 1e-14 or abs(lse[h] - np.logaddexp(a, b)) > 1e-14:
+                return "two tokens: logistic weights / logaddexp mismatch"
+    return None
+
+
+def check_mean_probe():
+    from fractions import Fraction
+
+    r = _rng(12)
+    for L in (1, 5, 37):
+        hkv, g, dk, dv = 2, 3, 4, 6
+        q = np.zeros((hkv * g, dk))
+        K = r.standard_normal((L, hkv, dk))
+        V = r.integers(-8, 9, (L, hkv, dv)).astype(np.float64)
+        o, lse = pa.attention(q, K, V, 1.0)
+        for h in range(hkv * g):
+            kvh = np.repeat(np.arange(hkv), g)[h]
+            for j in range(dv):
+                exact = Fraction(int(V[:, kvh, j].sum()), L)
+                if abs(o[h, j] - float(exact)) > 1e-14:
+                    return f"mean probe L={L}: output is not the mean of V"
+        if np.max(np.abs(lse - np.log(L))) > 1e-14:
+            return f"mean probe L={L}: lse is not ln L"
+    return None
+
+
+def check_shift():
+    r = _rng(13)
+    L, hkv, g, dk, dv = 23, 2, 2, 5, 3
+    q = r.standard_normal((hkv * g, dk))
+    K = r.standard_normal((L, hkv, dk))
+    V = r.standard_normal((L, hkv, dv))
+    scale = 0.6
+    o0, l0 = pa.attention(q, K, V, scale)
+    for c in (3.25, -40.0):
+        q1 = np.concatenate([q, np.full((hkv * g, 1), c / scale)], axis=1)
+        K1 = np.concatenate([K, np.ones((L, hkv, 1))], axis=2)
+        o1, l1 = pa.attention(q1, K1, V, scale)
+        if np.max(np.abs(o1 - o0)) > 1e-12 or np.max(np.abs(l1 - (l0 + c))) > 1e-12:
+            return f"shift by {c}: output must not move and lse must move by c"
+    return None
+
+
+# ----------------------------------------------------------------------------------
+# paged path, using the input generator's own record of the layout
+# ----------------------------------------------------------------------------------
+def small_workloads():
+    import workloads as wl
+
+    return [
+        wl.small("mha_f32", [1, 7, 30], 3, 3, 8, 8, 4, wl.F32, seed=21),
+        wl.small("gqa_bf16", [5, 33, 17], 4, 2, 16, 16, 8, wl.BF16, partition_tokens=8, seed=22),
+        wl.small("dcp_i1", [1, 3, 41, 64], 4, 2, 8, 8, 4, wl.BF16, n_shards=4, interleave=1,
+                 partition_tokens=4, seed=23),
+        wl.small("dcp_i3", [2, 29, 50], 2, 1, 8, 8, 4, wl.F32, n_shards=3, interleave=3,
+                 partition_tokens=8, seed=24),
+        wl.small("latent", [17, 70, 70, 131], 8, 1, 24, 16, 8, wl.BF16, latent=True,
+                 prefix_group=2, prefix_tokens=16, partition_tokens=16, seed=25),
+    ]
+
+
+def tensors_np(w, fill="normal"):
+    import torch
+    import workloads as wl
+
+    t = wl.make_tensors(w, "cpu", fill=fill)
+
+    def conv(x):
+        if x is None:
+            return None
+        if x.dtype == torch.bfloat16:
+            return x.contiguous().view(torch.int16).numpy().view(np.uint16)
+        return x.contiguous().numpy()
+
+    return {k: conv(v) for k, v in t.items()}
+
+
+def contiguous_from_generator(w, T, b):
+    """Global-order K/V rows of sequence ``b`` rebuilt from the generator's
+    token-id record (every slot of every block in the sequence's table row that
+    holds one of its tokens), with the appended token taken from ``k_new``/``v_new``."""
+    L = int(w.context_lens[b])
+    kc, vc = T["k_cache"], T["v_cache"]
+    hkv, dk, dv = w.n_kv_heads, w.dk, w.dv
+    K = np.empty((L, hkv, dk), kc.dtype)
+    V = np.empty((L, hkv, dv), kc.dtype)
+    seen = np.zeros(L, bool)
+    for r in range(w.n_shards):
+        for phys in w.block_table[b, r]:
+            if phys < 0:
+                continue
+            for o in range(w.block_size):
+                i = w.token_id[phys, o]
+                if i < 0 or i >= L or not w.live[phys, o]:
+                    continue
+                K[i] = kc[phys, :, o, :]
+                V[i] = kc[phys, :, o, :dv] if vc is None else vc[phys, :, :, o]
+                seen[i] = True
+    K[L - 1] = T["k_new"][b]
+    V[L - 1] = T["k_new"][b][:, :dv] if T["v_new"] is None else T["v_new"][b]
+    seen[L - 1] = True
+    assert seen.all()
+    return K, V
+
+
+def run_oracle_step(w, T, partition_tokens=None):
+    Tp = partition_tokens or w.partition_tokens or 16
+    pmax = pa.max_partitions(int(w.context_lens.max()), w.n_shards, w.interleave, Tp)
+    return pa.decode_step(T["q"], T["k_new"], T["v_new"], T["k_cache"], T["v_cache"],
+                          w.block_table, w.context_lens, w.n_shards, w.interleave, w.block_size,
+                          Tp, pmax, w.scale_f32, w.dv)
+
+
+def check_sdpa():
+    import torch
+    import torch.nn.functional as F
+
+    for w in small_workloads():
+        T = tensors_np(w)
+        res = run_oracle_step(w, T)
+        for b in range(w.n_seqs):
+            K, V = contiguous_from_generator(w, T, b)
+            L = K.shape[0]
+            r = _rng(100 + b)
+            Q = r.standard_normal((L, w.n_q_heads, w.dk))
+            Q[L - 1] = pa.widen(T["q"][b])
+            qt = torch.from_numpy(Q).permute(1, 0, 2)[None]
+            kt = torch.from_numpy(pa.widen(K)).permute(1, 0, 2)[None]
+            vt = torch.from_numpy(pa.widen(V)).permute(1, 0, 2)[None]
+            ref = F.scaled_dot_product_attention(qt, kt, vt, is_causal=True, scale=w.scale_f32,
+                                                 enable_gqa=True)[0, :, L - 1, :].numpy()
+            err = np.max(np.abs(res["o"][b] - ref))
+            if not err <= 1e-12:
+                return f"sdpa {w.name} seq {b}: |do|={err:.3g}"
+    return None
+
+
+def check_gather():
+    for w in small_workloads():
+        T = tensors_np(w)
+        res = run_oracle_step(w, T)
+        for b in range(w.n_seqs):
+            K, V = contiguous_from_generator(w, T, b)
+            Kg, Vg = pa.gather_sequence(res["k_cache"], res["v_cache"], w.block_table[b],
+                                        int(w.context_lens[b]), w.n_shards, w.interleave,
+                                        w.block_size, w.dv)
+            if not (np.array_equal(K.view(np.uint8), Kg.view(np.uint8))
+                    and np.array_equal(V.view(np.uint8), Vg.view(np.uint8))):
+                return f"gather {w.name} seq {b}: bits differ from the generator's layout"
+    return None
+
+
+def check_slots():
+    for w in small_workloads():
+        s = pa.slot_mapping(w.block_table, w.context_lens, w.n_shards, w.interleave, w.block_size)
+        if not np.array_equal(s, w.new_slot):
+            return f"slots {w.name}: {s} vs generator {w.new_slot}"
+    return None
+
+
+def check_merge():
+    import workloads as wl
+
+    for I in (1, 5):
+        w = wl.small("m", [1, 6, 77], 4, 2, 8, 8, 4, wl.F32, n_shards=4, interleave=I, seed=31)
+        T = tensors_np(w)
+        res = run_oracle_step(w, T, partition_tokens=4)
+        res2 = run_oracle_step(w, T, partition_tokens=64)
+        for b in range(w.n_seqs):
+            K, V = contiguous_from_generator(w, T, b)
+            o, lse = pa.attention(T["q"][b], K, V, w.scale_f32)
+            for rr in (res, res2):
+                if np.max(np.abs(rr["o"][b] - o)) > 1e-12 or np.max(np.abs(rr["lse"][b] - lse)) > 1e-12:
+                    return f"merge I={I} seq {b}: shards merged != unsharded"
+            # associativity: merge per shard, then merge the shard results
+            po, pl = res["part_o"][b], res["part_lse"][b]
+            per = [pa.merge_lse(po[r], pl[r]) for r in range(w.n_shards)]
+            o2, l2 = pa.merge_lse(np.stack([x[0] for x in per]), np.stack([x[1] for x in per]))
+            if np.max(np.abs(o2 - o)) > 1e-12 or np.max(np.abs(l2 - lse)) > 1e-12:
+                return f"merge I={I} seq {b}: not associative"
+    return None
+
+
+ALL_CHECKS = {
+    "bruteforce": check_bruteforce,
+    "closed_forms": check_closed_forms,
+    "mean_probe": check_mean_probe,
+    "shift": check_shift,
+    "sdpa": check_sdpa,
+    "gather": check_gather,
+    "slots": check_slots,
+    "merge": check_merge,
+}

@@ -1,0 +1,276 @@
+"""Seeded synthetic inputs for paged decode attention.
+
+This module builds the INPUTS of one decode step -- context lengths, block
+tables over a shuffled shared pool, K/V cache contents, queries and the new
+tokens' K/V -- and nothing else.  It holds none of the attention arithmetic
+(no scores, softmax, merge or expected values).  Tests, ``bench.py`` and the
+smoke check feed the same tensors to the HIP library and to the fp64 oracle.
+
+Like the scheduler of a serving system, it decides where each token's K/V
+lives: a sequence's tokens are dealt to ``n_shards`` shards ``interleave`` at
+a time (token i on shard (i // interleave) % n_shards), each shard keeps its
+tokens in global order, and each shard's tokens fill blocks taken from the
+pool one after another.  Unused blocks, the unused tail slots of last blocks
+and the slot of the token the step appends are NaN-poisoned, so a kernel that
+reads a value it should not read produces NaN instead of a silently plausible
+number.
+
+The five workloads are the configurations the north star of the build names:
+``tiny`` (1 sequence, fp32), ``batch`` (continuous-batching step, 64 ragged
+sequences), ``long`` (8 sequences with log-normal lengths around 142K),
+``dcp`` (one 200K sequence split into 4 interleaved shards) and ``latent``
+(128 query heads on one 576-wide latent head, shared 2,048-token prefixes).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+BF16 = "bf16"
+F32 = "f32"
+
+
+@dataclass
+class Workload:
+    name: str
+    n_q_heads: int
+    n_kv_heads: int
+    dk: int
+    dv: int
+    block_size: int
+    dtype: str
+    context_lens: np.ndarray            # int32 [N], includes the appended token
+    n_shards: int = 1
+    interleave: int = 1
+    partition_tokens: int = 0           # 0 -> chosen by the library binding
+    scale: float = 0.0                  # 0 -> 1/sqrt(dk), rounded to fp32
+    latent: bool = False                # V is the first dv entries of each K row
+    prefix_group: int = 1               # sequences per shared-prefix group
+    prefix_tokens: int = 0              # shared prefix length (multiple of block_size)
+    spare_frac: float = 0.10            # extra never-used blocks in the pool
+    n_blocks: int = 0                   # physical pool size (0 -> computed)
+    seed: int = 0
+    # filled by plan():
+    block_table: np.ndarray = field(default=None, repr=False)
+    live: np.ndarray = field(default=None, repr=False)       # bool [NB][bs]: holds a stored token
+    token_id: np.ndarray = field(default=None, repr=False)   # int64 [NB][bs]: global id, -1 unused
+    new_slot: np.ndarray = field(default=None, repr=False)   # int64 [N]: slot of the appended token
+
+    @property
+    def n_seqs(self) -> int:
+        return int(len(self.context_lens))
+
+    @property
+    def group(self) -> int:
+        return self.n_q_heads // self.n_kv_heads
+
+    @property
+    def elem_bytes(self) -> int:
+        return 4 if self.dtype == F32 else 2
+
+    @property
+    def scale_f32(self) -> float:
+        s = self.scale if self.scale else 1.0 / np.sqrt(self.dk)
+        return float(np.float32(s))
+
+    @property
+    def max_blocks_per_shard(self) -> int:
+        return int(self.block_table.shape[2])
+
+    def kv_bytes_per_token(self) -> int:
+        """Bytes of K and V read per token per step (V counted once when it is
+        part of the K row)."""
+        per_head = self.dk if self.latent else self.dk + self.dv
+        return self.n_kv_heads * per_head * self.elem_bytes
+
+
+def _split_counts(L: int, n_shards: int, interleave: int) -> np.ndarray:
+    """How many of tokens 0..L-1 each shard receives when they are dealt
+    ``interleave`` at a time."""
+    ids = np.arange(L, dtype=np.int64)
+    return np.bincount((ids // interleave) % n_shards, minlength=n_shards)
+
+
+def plan(w: Workload) -> Workload:
+    """Lay the workload's tokens out in a shuffled physical pool."""
+    rng = np.random.default_rng([w.seed, 1])
+    N, S, I, bs = w.n_seqs, w.n_shards, w.interleave, w.block_size
+    counts = [_split_counts(int(L), S, I) for L in w.context_lens]
+    nblk = [[-(-int(c) // bs) for c in cs] for cs in counts]
+    maxblk = max(max(r) for r in nblk)
+    shared_blocks = w.prefix_tokens // bs
+    if w.prefix_tokens:
+        # the shared prefix is whole blocks and every sequence appends after it,
+        # so no step writes into a shared block
+        assert S == 1 and w.prefix_tokens % bs == 0
+        assert int(np.min(w.context_lens)) > w.prefix_tokens
+    need = sum(sum(r) for r in nblk)
+    if shared_blocks:
+        n_groups = -(-N // w.prefix_group)
+        need -= (N - n_groups) * shared_blocks
+    nb = w.n_blocks or int(np.ceil(need * (1.0 + w.spare_frac))) + 1
+    assert nb >= need
+    w.n_blocks = nb
+    order = iter(rng.permutation(nb).tolist())
+
+    bt = np.full((N, S, maxblk), -1, dtype=np.int32)
+    live = np.zeros((nb, bs), dtype=bool)
+    tok = np.full((nb, bs), -1, dtype=np.int64)
+    new_slot = np.empty(N, dtype=np.int64)
+    prefix_of_group: dict = {}
+    for b in range(N):
+        L = int(w.context_lens[b])
+        for r in range(S):
+            for j in range(nblk[b][r]):
+                if shared_blocks and j < shared_blocks:
+                    key = (b // w.prefix_group, j)
+                    if key not in prefix_of_group:
+                        prefix_of_group[key] = next(order)
+                    bt[b, r, j] = prefix_of_group[key]
+                else:
+                    bt[b, r, j] = next(order)
+        # global ids of each shard's tokens, in order, into their slots
+        ids = np.arange(L, dtype=np.int64)
+        shard = (ids // I) % S
+        for r in range(S):
+            mine = ids[shard == r]
+            loc = np.arange(mine.size)
+            phys = bt[b, r, loc // bs].astype(np.int64)
+            live[phys, loc % bs] = True
+            tok[phys, loc % bs] = mine
+        r_new = ((L - 1) // I) % S
+        loc_new = int(counts[b][r_new]) - 1
+        phys_new = int(bt[b, r_new, loc_new // bs])
+        new_slot[b] = phys_new * bs + loc_new % bs
+    # the appended token's slot holds nothing until kv_append writes it
+    for s in new_slot:
+        live[s // bs, s % bs] = False
+    w.block_table, w.live, w.token_id, w.new_slot = bt, live, tok, new_slot
+    return w
+
+
+# --------------------------------------------------------------------------------------
+# the five workloads
+# --------------------------------------------------------------------------------------
+def tiny(context_len: int = 67, seed: int = 1) -> Workload:
+    """1 sequence, 4 query heads on 1 KV head, head 64, fp32, 4-token blocks,
+    context 67 (new token included), 17 logical blocks in a 64-block pool."""
+    w = Workload("tiny", 4, 1, 64, 64, 4, F32, np.array([context_len], np.int32), n_blocks=64,
+                 scale=0.125, seed=seed)
+    return plan(w)
+
+
+def batch(seed: int = 2) -> Workload:
+    """Continuous-batching step: 64 sequences of prompt U[8,32] + generated U[16,96]
+    tokens, 32 query / 8 KV heads, head 128, bf16, 16-token blocks."""
+    rng = np.random.default_rng(seed)
+    prompt = rng.integers(8, 33, 64)
+    gen = rng.integers(16, 97, 64)
+    return plan(Workload("batch", 32, 8, 128, 128, 16, BF16, (prompt + gen).astype(np.int32),
+                         seed=seed))
+
+
+def long_lengths(seed: int = 2, n: int = 8) -> np.ndarray:
+    rng = np.random.default_rng(seed)
+    L = np.clip(np.rint(rng.lognormal(np.log(142000.0), 0.5, n)), 16384, 200000)
+    return L.astype(np.int32)
+
+
+def long(seed: int = 2, partition_tokens: int = 4096) -> Workload:
+    """Long-context decode: 8 sequences, log-normal lengths (median 142,000,
+    sigma 0.5, clipped to [16,384, 200,000]), 32/8 heads, head 128, bf16,
+    16-token blocks, 4,096-token split-KV partitions."""
+    return plan(Workload("long", 32, 8, 128, 128, 16, BF16, long_lengths(seed),
+                         partition_tokens=partition_tokens, seed=seed))
+
+
+def dcp(interleave: int = 1, n_shards: int = 4, context_len: int = 200000, seed: int = 4,
+        partition_tokens: int = 0) -> Workload:
+    """One 200,000-token sequence, 64/8 heads, head 128, bf16, 16-token blocks,
+    split into ``n_shards`` interleaved shards."""
+    return plan(Workload(f"dcp_S{n_shards}_I{interleave}", 64, 8, 128, 128, 16, BF16,
+                         np.array([context_len], np.int32), n_shards=n_shards,
+                         interleave=interleave, partition_tokens=partition_tokens, seed=seed))
+
+
+def latent(seed: int = 5, n_seqs: int = 32, lo: int = 4096, hi: int = 65536) -> Workload:
+    """Latent (MLA-style) cache: 32 sequences, 128 query heads on 1 KV head, key
+    width 576 with the value the first 512 entries, context U[4,096, 65,536],
+    bf16, 64-token blocks; groups of 4 sequences share a 2,048-token prefix."""
+    rng = np.random.default_rng(seed)
+    L = rng.integers(lo, hi + 1, n_seqs).astype(np.int32)
+    return plan(Workload("latent", 128, 1, 576, 512, 64, BF16, L, latent=True, prefix_group=4,
+                         prefix_tokens=2048, seed=seed))
+
+
+def small(name: str, lens, hq: int, hkv: int, dk: int, dv: int, bs: int, dtype: str,
+          n_shards: int = 1, interleave: int = 1, partition_tokens: int = 0, latent: bool = False,
+          seed: int = 0, prefix_group: int = 1, prefix_tokens: int = 0, scale: float = 0.0) -> Workload:
+    """Any small shape, for parity sweeps."""
+    return plan(Workload(name, hq, hkv, dk, dv, bs, dtype, np.asarray(lens, np.int32),
+                         n_shards=n_shards, interleave=interleave,
+                         partition_tokens=partition_tokens, latent=latent, seed=seed,
+                         prefix_group=prefix_group, prefix_tokens=prefix_tokens, scale=scale))
+
+
+# --------------------------------------------------------------------------------------
+# tensors
+# --------------------------------------------------------------------------------------
+def make_tensors(w: Workload, device="cpu", fill: str = "normal", seed: int | None = None):
+    """Torch tensors of the workload on ``device``.
+
+    ``fill="normal"``: q, K, V and the new tokens' K/V are N(0,1) drawn in fp32
+    and rounded to the workload's element type (round-to-nearest-even for bf16).
+    ``fill="mean_probe"``: q = 0 (every score is 0) and the value of token t in
+    dimension j is (31 t + j) mod 16, exactly representable in bf16, so the
+    attention output is exactly the mean of the values.
+
+    Returns a dict with ``q [N][Hq][dk]``, ``k_new [N][Hkv][dk]``,
+    ``v_new [N][Hkv][dv]`` (None for latent), ``k_cache [NB][Hkv][bs][dk]``,
+    ``v_cache [NB][Hkv][dv][bs]`` (None for latent), ``block_table``,
+    ``context_lens`` and ``slot_mapping`` (int64, where the generator put the new
+    tokens; the library computes its own).
+    """
+    import torch
+
+    dt = torch.float32 if w.dtype == F32 else torch.bfloat16
+    dev = torch.device(device)
+    g = torch.Generator(device=dev)
+    g.manual_seed(int(w.seed if seed is None else seed) * 1000003 + 7)
+    N, Hq, Hkv, dk, dv, bs, NB = w.n_seqs, w.n_q_heads, w.n_kv_heads, w.dk, w.dv, w.block_size, w.n_blocks
+
+    def randn(*shape):
+        return torch.randn(*shape, generator=g, device=dev, dtype=torch.float32).to(dt)
+
+    live = torch.from_numpy(w.live).to(dev)
+    k_cache = randn(NB, Hkv, bs, dk)
+    v_cache = None if w.latent else randn(NB, Hkv, dv, bs)
+    q = randn(N, Hq, dk)
+    k_new = randn(N, Hkv, dk)
+    v_new = None if w.latent else randn(N, Hkv, dv)
+    if fill == "mean_probe":
+        q.zero_()
+        tid = torch.from_numpy(w.token_id).to(dev)                    # [NB][bs]
+        j = torch.arange(dv, device=dev)
+        val = ((31 * tid[:, :, None] + j[None, None, :]) % 16).to(dt)  # [NB][bs][dv]
+        if w.latent:
+            k_cache[..., :dv] = val[:, None, :, :].expand(NB, Hkv, bs, dv)
+        else:
+            v_cache.copy_(val.transpose(1, 2)[:, None, :, :].expand(NB, Hkv, dv, bs))
+        Lm1 = torch.from_numpy(w.context_lens.astype(np.int64) - 1).to(dev)
+        newv = ((31 * Lm1[:, None] + j[None, :]) % 16).to(dt)         # [N][dv]
+        if w.latent:
+            k_new[..., :dv] = newv[:, None, :]
+        else:
+            v_new.copy_(newv[:, None, :].expand(N, Hkv, dv))
+    elif fill != "normal":
+        raise ValueError(fill)
+    nan = float("nan")
+    k_cache.masked_fill_(~live[:, None, :, None], nan)
+    if v_cache is not None:
+        v_cache.masked_fill_(~live[:, None, None, :], nan)
+    return dict(q=q, k_new=k_new, v_new=v_new, k_cache=k_cache, v_cache=v_cache,
+                block_table=torch.from_numpy(w.block_table).to(dev),
+                context_lens=torch.from_numpy(w.context_lens.astype(np.int32)).to(dev),
+                slot_mapping=torch.from_numpy(w.new_slot).to(dev))
