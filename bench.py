@@ -1,0 +1,256 @@
+"""Benchmark of one decode step of paged attention on one MI355X.
+
+A step is the whole hot path on one stream: slot routing of the new tokens,
+kv append, the partitioned attention (pa_decode) and the LSE merge.  Inputs are
+seeded synthetic tensors already resident in HBM.  Prints ONE JSON line.
+
+  python bench.py [--steps K] [--warmup W] [--config long|dcp1|dcp16|batch|latent|tiny]
+                  [--no-cpu-baseline] [--secondary]
+
+The default workload is the long-context step (8 sequences, log-normal lengths
+around 142K tokens), the configuration the HBM-roofline target is stated for.
+``value`` is KV-read GB/s over the whole step (algorithmic bytes: every stored
+K and V element of every sequence read once per step).  ``roofline`` prices the
+decode kernel alone: the same algorithmic bytes over its average launch time,
+measured with HIP events around each launch inside the timed region.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0     # MI355X HBM3E, published
+MFMA_BF16_TFLOPS = 2500.0  # MI355X dense bf16, published
+
+
+def make_workload(name):
+    import workloads as wl
+
+    return {
+        "long": lambda: wl.long(),
+        "dcp1": lambda: wl.dcp(interleave=1, partition_tokens=1024),
+        "dcp16": lambda: wl.dcp(interleave=16, partition_tokens=1024),
+        "batch": lambda: wl.batch(),
+        "latent": lambda: wl.latent(),
+        "tiny": lambda: wl.tiny(),
+    }[name]()
+
+
+DESCRIBE = {
+    "long": "long-context decode: 8 seqs, L log-normal (median 142K, sigma 0.5, clip [16384, 200000]), "
+            "32 q / 8 kv heads, d 128, bf16, block 16, split-KV partitions of 4096 tokens",
+    "dcp1": "DCP emulation: 1 seq of 200000 tokens, 64 q / 8 kv heads, d 128, bf16, block 16, "
+            "S=4 interleaved shards, I=1, partitions of 1024 local tokens",
+    "dcp16": "DCP emulation: 1 seq of 200000 tokens, 64 q / 8 kv heads, d 128, bf16, block 16, "
+             "S=4 interleaved shards, I=16, partitions of 1024 local tokens",
+    "batch": "continuous-batching step: 64 seqs, L = U[8,32] + U[16,96], 32 q / 8 kv heads, d 128, "
+             "bf16, block 16",
+    "latent": "latent (MLA-style) cache: 32 seqs, L U[4096, 65536], 128 q heads on 1 kv head, "
+              "key 576 / value 512 (view), bf16, block 64, 2048-token prefixes shared by 4",
+    "tiny": "1 seq, L 67, 4 q / 1 kv head, d 64, fp32, block 4",
+}
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "decode_attention_paged_kv_amd", "csrc")
+    for fn in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, fn), "rb") as f:
+            h.update(fn.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(config, launches_bytes):
+    """HBM bytes per decode launch from the committed rocprofv3 counter summary,
+    if it was taken of the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"decode_{config}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def time_gpu(w, T, step, steps, warmup):
+    import torch
+
+    args = (T["q"], T["k_new"], T["v_new"], T["k_cache"], T["v_cache"], T["block_table"],
+            T["context_lens"])
+    nb = T["k_cache"].shape[0]
+    for _ in range(warmup):
+        step(*args)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record()
+    for i in range(steps):
+        step.route(T["block_table"], T["context_lens"], nb)
+        step.append(T["k_new"], T["v_new"], T["k_cache"], T["v_cache"])
+        ev[i][0].record()
+        step.attend(T["q"], T["k_cache"], T["v_cache"], T["block_table"], T["context_lens"])
+        ev[i][1].record()
+        step.merge()
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t0.elapsed_time(t1)
+    dec = sorted(a.elapsed_time(b) for a, b in ev)
+    return dict(total_ms=total_ms, wall_s=wall, decode_ms_mean=sum(dec) / len(dec),
+                decode_ms_median=dec[len(dec) // 2], decode_ms_min=dec[0])
+
+
+def cpu_baseline(w, T, budget_s=12.0):
+    """The fp64 oracle (as it stands) on a bounded sample of the same workload:
+    whole sequences, in order, until ``budget_s`` of CPU time is spent."""
+    import numpy as np
+    import torch
+
+    from oracle import paged_attention as pa
+
+    def host(x):
+        if x is None:
+            return None
+        x = x.detach().cpu().contiguous()
+        return x.view(torch.int16).numpy().view(np.uint16) if x.dtype == torch.bfloat16 else x.numpy()
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:
+        cores = 1
+    done_tokens, elapsed, seqs = 0, 0.0, []
+    for b in range(w.n_seqs):
+        ids = np.unique(w.block_table[b][w.block_table[b] >= 0])
+        remap = np.full(w.n_blocks, -1, np.int64)
+        remap[ids] = np.arange(ids.size)
+        bt = np.where(w.block_table[b:b + 1] >= 0, remap[np.maximum(w.block_table[b:b + 1], 0)], -1).astype(np.int32)
+        idx = torch.from_numpy(ids).to(T["k_cache"].device)
+        kc = host(T["k_cache"].index_select(0, idx))
+        vc = None if T["v_cache"] is None else host(T["v_cache"].index_select(0, idx))
+        Tp = w.partition_tokens or 4096
+        pmax = pa.max_partitions(int(w.context_lens[b]), w.n_shards, w.interleave, Tp)
+        t = time.perf_counter()
+        pa.decode_step(host(T["q"][b:b + 1]), host(T["k_new"][b:b + 1]),
+                       None if T["v_new"] is None else host(T["v_new"][b:b + 1]), kc, vc, bt,
+                       w.context_lens[b:b + 1], w.n_shards, w.interleave, w.block_size, Tp,
+                       max(pmax, 1), w.scale_f32, w.dv)
+        elapsed += time.perf_counter() - t
+        done_tokens += int(w.context_lens[b])
+        seqs.append(b)
+        if elapsed >= budget_s:
+            break
+    gbs = done_tokens * w.kv_bytes_per_token() / elapsed / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": int(cores), "kind": "oracle",
+            "seq_steps_per_s": round(len(seqs) / elapsed, 4),
+            "sample": f"sequences {seqs} of the same workload ({done_tokens} tokens, full decode "
+                      f"step in the fp64 NumPy oracle), {elapsed:.2f} s"}
+
+
+def run_config(name, steps, warmup, with_cpu):
+    import numpy as np
+    import torch
+
+    import decode_attention_paged_kv_amd as P
+    import workloads as wl
+
+    w = make_workload(name)
+    dev = torch.device("cuda", 0)
+    T = wl.make_tensors(w, dev)
+    step = P.DecodeStep(w.n_seqs, w.n_q_heads, w.n_kv_heads, w.dk, w.dv, w.block_size,
+                        int(w.context_lens.max()), w.n_shards, w.interleave,
+                        w.partition_tokens, w.scale_f32, device=dev)
+    cpu = cpu_baseline(w, T) if with_cpu else None
+    t = time_gpu(w, T, step, steps, warmup)
+    assert int(step.err_flag.item()) == 0, "device error flag set"
+    assert torch.isfinite(step.out).all(), "non-finite output"
+    kv_bytes = int(np.sum(w.context_lens.astype(np.int64))) * w.kv_bytes_per_token()
+    ms = t["total_ms"] / steps
+    dec_ms = t["decode_ms_mean"]
+    achieved = kv_bytes / (dec_ms * 1e-3) / 1e9
+    res = dict(w=w, step=step, kv_bytes=kv_bytes, ms_per_step=ms, decode_ms=dec_ms,
+               value=kv_bytes / (ms * 1e-3) / 1e9, seq_steps=w.n_seqs / (ms * 1e-3),
+               achieved=achieved, timing=t, cpu=cpu)
+    if w.latent:
+        flops = int(np.sum(w.context_lens.astype(np.int64))) * w.n_q_heads * 2 * (w.dk + w.dv)
+        res["tflops"] = flops / (dec_ms * 1e-3) / 1e12
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="long", choices=sorted(DESCRIBE))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--secondary", action="store_true",
+                    help="also time the other workloads (reported under 'secondary')")
+    a = ap.parse_args()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only (DCP shards are emulated as "
+              "partitions on a single device); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    r = run_config(a.config, a.steps, a.warmup, not a.no_cpu_baseline)
+    w = r["w"]
+    traffic = measured_traffic(a.config, r["kv_bytes"])
+    line = {
+        "metric": "paged decode-attention KV-read GB/s (and % of MI355X HBM peak; seq-steps/s)",
+        "value": round(r["value"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(r["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if w.dtype == "f32" else "bf16",
+        "data": "synthetic (seeded N(0,1) K/V/q in a shuffled block pool)",
+        "config": {"workload": DESCRIBE[a.config], "name": a.config, "n_seqs": w.n_seqs,
+                   "context_tokens": int(w.context_lens.sum()), "max_context": int(w.context_lens.max()),
+                   "partition_tokens": r["step"].partition_tokens,
+                   "kv_bytes_per_step": r["kv_bytes"]},
+        "hbm_frac": round(r["value"] / HBM_PEAK_GBS, 4),
+        "seq_steps_per_s": round(r["seq_steps"], 2),
+        "decode_ms": round(r["decode_ms"], 5),
+        "roofline": {"bound": "hbm", "achieved": round(r["achieved"], 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(r["achieved"] / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel": "pa_decode",
+                     "algorithmic_bytes_per_launch": r["kv_bytes"]},
+        "cpu_baseline": r["cpu"],
+    }
+    if "tflops" in r:
+        line["roofline"]["mfma_tflops"] = round(r["tflops"], 2)
+        line["roofline"]["mfma_frac"] = round(r["tflops"] / MFMA_BF16_TFLOPS, 4)
+    if a.secondary:
+        sec = {}
+        for name in ("dcp1", "dcp16", "batch", "latent", "tiny"):
+            if name == a.config:
+                continue
+            s = run_config(name, a.steps, a.warmup, False)
+            sec[name] = {"kv_GBs_step": round(s["value"], 2), "kv_GBs_decode": round(s["achieved"], 2),
+                         "hbm_frac_decode": round(s["achieved"] / HBM_PEAK_GBS, 4),
+                         "ms_per_step": round(s["ms_per_step"], 5), "decode_ms": round(s["decode_ms"], 5),
+                         "seq_steps_per_s": round(s["seq_steps"], 2)}
+            if "tflops" in s:
+                sec[name]["mfma_tflops"] = round(s["tflops"], 2)
+            del s
+        line["secondary"] = sec
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,12 @@
+"""Paged decode attention for AMD MI355X (gfx950): the Python face of libpagedattn.so.
+
+``pa_*`` functions mirror the C ABI in ``include/pa.h`` one to one (see ``_lib``).
+``DecodeStep`` strings the four calls of one decode step together on one stream:
+slot routing, kv append, the partitioned attention and the LSE merge.
+"""
+from ._lib import (  # noqa: F401
+    ERR_BLOCK_ID, ERR_CAPACITY, ERR_SLOT, LIB_PATH, PA_BF16, PA_F32, PaError, lib,
+    pa_decode, pa_default_partition_tokens, pa_gather_kv, pa_kv_append, pa_max_partitions,
+    pa_merge_lse, pa_shard_length, pa_slot_mapping,
+)
+from .step import DecodeStep  # noqa: F401

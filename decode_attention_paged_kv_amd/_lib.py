@@ -1,0 +1,197 @@
+"""ctypes binding of libpagedattn.so (declared in include/pa.h).
+
+Argument marshalling only: each function takes torch tensors that already live
+on the GPU, checks their element type, shape and contiguity, passes raw device
+pointers and the current HIP stream to the C entry point of the same name, and
+raises ``PaError`` on a nonzero status.  All computation happens in the HIP
+kernels.  There is no fallback: if the library is missing, importing this
+module fails.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.environ.get("PAGEDATTN_LIB", os.path.join(_HERE, "libpagedattn.so"))
+
+PA_F32, PA_BF16 = 0, 1
+ERR_BLOCK_ID, ERR_CAPACITY, ERR_SLOT = 1, 2, 4
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it first with __graft_entry__.build() "
+                      "(hipcc --offload-arch=gfx950)")
+lib = ctypes.CDLL(LIB_PATH)
+
+_i32, _i64, _f32, _p = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p
+_SIGS = {
+    "pa_slot_mapping": [_p, _p, _i32, _i32, _i32, _i32, _i32, _i64, _p, _p, _p],
+    "pa_kv_append": [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i64, _i32, _p, _p],
+    "pa_decode": [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i64, _i32, _i32, _i32,
+                  _i32, _i32, _f32, _i32, _p, _p, _p, _p],
+    "pa_merge_lse": [_p, _p, _i32, _i32, _i32, _i32, _p, _i32, _p, _p],
+    "pa_gather_kv": [_p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i64, _i32, _i32, _i32,
+                     _i32, _p, _p, _p, _p],
+    "pa_shard_length": [_i32, _i32, _i32, _i32],
+    "pa_max_partitions": [_i32, _i32, _i32, _i32],
+    "pa_default_partition_tokens": [_i32, _i32, _i32, _i32, _i32, _i32],
+    "pa_last_error": [],
+}
+for _name, _args in _SIGS.items():
+    _fn = getattr(lib, _name)
+    _fn.argtypes = _args
+    _fn.restype = ctypes.c_char_p if _name == "pa_last_error" else ctypes.c_int32
+
+
+class PaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"status {status}: {msg}")
+        self.status = status
+
+
+def _check(status: int):
+    if status != 0:
+        raise PaError(status, lib.pa_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _dtype_code(t):
+    if t.dtype == torch.float32:
+        return PA_F32
+    if t.dtype == torch.bfloat16:
+        return PA_BF16
+    raise TypeError(f"unsupported element type {t.dtype}")
+
+
+def _need(t, dtype=None, dims=None, name="tensor"):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if dims is not None and t.dim() != dims:
+        raise ValueError(f"{name} must have {dims} dims, got {tuple(t.shape)}")
+
+
+# ------------------------------------------------------------------ host helpers
+def pa_shard_length(context_len: int, n_shards: int, interleave: int, shard: int) -> int:
+    return int(lib.pa_shard_length(context_len, n_shards, interleave, shard))
+
+
+def pa_max_partitions(max_context_len: int, n_shards: int, interleave: int, partition_tokens: int) -> int:
+    return int(lib.pa_max_partitions(max_context_len, n_shards, interleave, partition_tokens))
+
+
+def pa_default_partition_tokens(n_seqs, n_kv_heads, max_context_len, n_shards, interleave, block_size) -> int:
+    return int(lib.pa_default_partition_tokens(n_seqs, n_kv_heads, max_context_len, n_shards,
+                                               interleave, block_size))
+
+
+# ------------------------------------------------------------------ entry points
+def pa_slot_mapping(block_table, context_lens, n_shards, interleave, block_size, n_blocks,
+                    slot_mapping, err_flag=None):
+    _need(block_table, torch.int32, 3, "block_table")
+    _need(context_lens, torch.int32, 1, "context_lens")
+    _need(slot_mapping, torch.int64, 1, "slot_mapping")
+    _need(err_flag, torch.int32, None, "err_flag")
+    n = context_lens.shape[0]
+    if block_table.shape[0] != n or block_table.shape[1] != n_shards or slot_mapping.shape[0] != n:
+        raise ValueError("block_table / context_lens / slot_mapping shapes disagree")
+    _check(lib.pa_slot_mapping(_ptr(block_table), _ptr(context_lens), n, n_shards, interleave,
+                               block_size, block_table.shape[2], n_blocks, _ptr(slot_mapping),
+                               _ptr(err_flag), _stream(block_table)))
+
+
+def pa_kv_append(k_new, v_new, k_cache, v_cache, slot_mapping, err_flag=None):
+    _need(k_new, None, 3, "k_new")
+    _need(k_cache, k_new.dtype, 4, "k_cache")
+    _need(v_new, k_new.dtype, 3, "v_new")
+    _need(v_cache, k_new.dtype, 4, "v_cache")
+    _need(slot_mapping, torch.int64, 1, "slot_mapping")
+    _need(err_flag, torch.int32, None, "err_flag")
+    n, hkv, dk = k_new.shape
+    nb, hkv2, bs, dk2 = k_cache.shape
+    dv = 0 if v_new is None else v_new.shape[2]
+    if hkv2 != hkv or dk2 != dk or slot_mapping.shape[0] != n:
+        raise ValueError("k_new / k_cache / slot_mapping shapes disagree")
+    if v_cache is not None and tuple(v_cache.shape) != (nb, hkv, dv, bs):
+        raise ValueError("v_cache must be [n_blocks][n_kv_heads][dv][block_size]")
+    _check(lib.pa_kv_append(_ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+                            _ptr(slot_mapping), n, hkv, dk, dv, bs, nb, _dtype_code(k_new),
+                            _ptr(err_flag), _stream(k_cache)))
+
+
+def pa_decode(q, k_cache, v_cache, block_table, context_lens, n_shards, interleave,
+              partition_tokens, max_partitions, scale, part_out, part_lse, dv=None, err_flag=None):
+    _need(q, None, 3, "q")
+    _need(k_cache, q.dtype, 4, "k_cache")
+    _need(v_cache, q.dtype, 4, "v_cache")
+    _need(block_table, torch.int32, 3, "block_table")
+    _need(context_lens, torch.int32, 1, "context_lens")
+    _need(part_out, torch.float32, 5, "part_out")
+    _need(part_lse, torch.float32, 4, "part_lse")
+    _need(err_flag, torch.int32, None, "err_flag")
+    n, hq, dk = q.shape
+    nb, hkv, bs, dk2 = k_cache.shape
+    if dv is None:
+        dv = v_cache.shape[2] if v_cache is not None else dk
+    if dk2 != dk:
+        raise ValueError("q and k_cache head sizes differ")
+    if v_cache is not None and tuple(v_cache.shape) != (nb, hkv, dv, bs):
+        raise ValueError("v_cache must be [n_blocks][n_kv_heads][dv][block_size]")
+    if tuple(part_out.shape) != (n, n_shards, max_partitions, hq, dv):
+        raise ValueError(f"part_out must be {(n, n_shards, max_partitions, hq, dv)}")
+    if tuple(part_lse.shape) != (n, n_shards, max_partitions, hq):
+        raise ValueError(f"part_lse must be {(n, n_shards, max_partitions, hq)}")
+    if block_table.shape[0] != n or block_table.shape[1] != n_shards or context_lens.shape[0] != n:
+        raise ValueError("block_table / context_lens shapes disagree with q")
+    _check(lib.pa_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                         _ptr(context_lens), n, hq, hkv, dk, dv, bs, nb, block_table.shape[2],
+                         n_shards, interleave, partition_tokens, max_partitions, float(scale),
+                         _dtype_code(q), _ptr(part_out), _ptr(part_lse), _ptr(err_flag),
+                         _stream(q)))
+
+
+def pa_merge_lse(part_out, part_lse, out, lse=None):
+    """``part_out [N][P...][Hq][dv]`` (any number of part axes), ``out [N][Hq][dv]``."""
+    _need(part_out, torch.float32, None, "part_out")
+    _need(part_lse, torch.float32, None, "part_lse")
+    _need(out, None, 3, "out")
+    _need(lse, torch.float32, 2, "lse")
+    n, hq, dv = out.shape
+    n_parts = part_lse.numel() // max(n * hq, 1)
+    if part_lse.numel() != n * n_parts * hq or part_out.numel() != n * n_parts * hq * dv:
+        raise ValueError("part_out / part_lse / out sizes disagree")
+    _check(lib.pa_merge_lse(_ptr(part_out), _ptr(part_lse), n, n_parts, hq, dv, _ptr(out),
+                            _dtype_code(out), _ptr(lse), _stream(out)))
+
+
+def pa_gather_kv(k_cache, v_cache, block_table, seq, shard, context_len, n_shards, interleave,
+                 k_out, v_out, err_flag=None):
+    _need(k_cache, None, 4, "k_cache")
+    _need(v_cache, k_cache.dtype, 4, "v_cache")
+    _need(block_table, torch.int32, 3, "block_table")
+    _need(k_out, k_cache.dtype, 3, "k_out")
+    _need(v_out, k_cache.dtype, 3, "v_out")
+    _need(err_flag, torch.int32, None, "err_flag")
+    nb, hkv, bs, dk = k_cache.shape
+    dv = v_out.shape[2]
+    L_r = pa_shard_length(context_len, n_shards, interleave, shard)
+    if k_out.shape[0] < L_r or v_out.shape[0] < L_r:
+        raise ValueError(f"k_out/v_out need {L_r} rows")
+    _check(lib.pa_gather_kv(_ptr(k_cache), _ptr(v_cache), _ptr(block_table), seq, shard,
+                            context_len, hkv, dk, dv, bs, nb, block_table.shape[2], n_shards,
+                            interleave, _dtype_code(k_cache), _ptr(k_out), _ptr(v_out),
+                            _ptr(err_flag), _stream(k_cache)))

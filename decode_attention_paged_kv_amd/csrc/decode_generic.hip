@@ -1,0 +1,168 @@
+// decode_generic.hip -- paged decode attention for any supported shape (VALU, fp32 math).
+//
+// One workgroup computes one (partition, sequence x shard, KV head, chunk of up to 16
+// query heads of that KV head's group).  It walks the partition's local tokens in tiles
+// of 32: scores of the tile (scale * q.k), an online-softmax update of the running max m,
+// sum l and output accumulator, then the weighted values.  At the end it writes
+// o = acc / l and lse = m + ln l for the partition (DCP page, soroban.highreso.jp,
+// "Why long-context LLMs get slow ...": local attention returns output and LSE, and the
+// LSEs of online softmax are what the merge reweights with).  Keys and values are read
+// through the block table (PagedAttention page, ai-compass.weeybrid.co.jp, block-table
+// section).
+//
+// This kernel covers every shape and element type the ABI accepts (including fp32 and
+// tiny head sizes); the MFMA kernels take the large bf16 shapes.
+#include <math.h>
+
+#include "pa_common.h"
+#include "pa_launch.h"
+
+namespace pa {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kHeads = 16;  // query heads per workgroup
+constexpr int kTile = 32;   // tokens per tile
+constexpr int kAcc = kHeads * 512 / kThreads;
+
+template <int DT>
+__global__ __launch_bounds__(kThreads) void decode_generic_kernel(DecodeArgs a) {
+  using E = Elem<DT>;
+  using raw = typename E::raw;
+  const raw* q = static_cast<const raw*>(a.q);
+  const raw* kc = static_cast<const raw*>(a.k_cache);
+  const raw* vc = static_cast<const raw*>(a.v_cache);
+
+  const int p = blockIdx.x;
+  const int b = blockIdx.y / a.n_shards;
+  const int r = blockIdx.y % a.n_shards;
+  const int g = a.hq / a.hkv;
+  const int chunks = (g + kHeads - 1) / kHeads;
+  const int kvh = blockIdx.z / chunks;
+  const int chunk = blockIdx.z % chunks;
+  const int h0 = kvh * g + chunk * kHeads;
+  const int nh = min(kHeads, g - chunk * kHeads);
+  const int tid = threadIdx.x;
+  const int dk = a.dk, dv = a.dv, bs = a.bs;
+
+  const int L = a.context_lens[b];
+  const int Lr = L > 0 ? shard_len(L, a.n_shards, a.interleave, r) : 0;
+  const int T = a.part_tokens;
+  if (p == 0 && tid == 0 && (Lr + T - 1) / T > a.max_parts) raise_flag(a.flag, kErrCapacity);
+  const int t_begin = p * T;
+  const int t_end = min(t_begin + T, Lr);
+
+  const int64_t out_row = ((int64_t(b) * a.n_shards + r) * a.max_parts + p) * a.hq;
+  if (t_begin >= t_end) {  // empty partition
+    for (int i = tid; i < nh * dv; i += kThreads)
+      a.part_out[(out_row + h0 + i / dv) * dv + i % dv] = 0.f;
+    if (tid < nh) a.part_lse[out_row + h0 + tid] = -INFINITY;
+    return;
+  }
+
+  __shared__ float q_s[kHeads * kMaxHeadDim];
+  __shared__ float s_s[kHeads][kTile];
+  __shared__ float m_s[kHeads], l_s[kHeads], alpha_s[kHeads];
+  __shared__ int64_t kbase_s[kTile], vbase_s[kTile];
+  __shared__ int ok_s[kTile];
+
+  for (int i = tid; i < nh * dk; i += kThreads)
+    q_s[i] = E::load(q, (int64_t(b) * a.hq + h0 + i / dk) * dk + i % dk);
+  if (tid < kHeads) {
+    m_s[tid] = -INFINITY;
+    l_s[tid] = 0.f;
+  }
+  float acc[kAcc];
+#pragma unroll
+  for (int k = 0; k < kAcc; ++k) acc[k] = 0.f;
+
+  const int32_t* row = a.block_table + (int64_t(b) * a.n_shards + r) * a.max_blocks;
+  for (int t0 = t_begin; t0 < t_end; t0 += kTile) {
+    const int n_t = min(kTile, t_end - t0);
+    if (tid < kTile) {
+      int ok = 0;
+      int64_t kb = 0, vb = 0;
+      if (tid < n_t) {
+        const int t = t0 + tid;
+        const int64_t phys = table_block(row, t / bs, a.max_blocks, a.n_blocks, a.flag);
+        if (phys >= 0) {
+          ok = 1;
+          const int off = t % bs;
+          kb = ((phys * a.hkv + kvh) * bs + off) * dk;
+          vb = vc ? (phys * a.hkv + kvh) * int64_t(dv) * bs + off : kb;
+        }
+      }
+      ok_s[tid] = ok;
+      kbase_s[tid] = kb;
+      vbase_s[tid] = vb;
+    }
+    __syncthreads();
+    // scores
+    for (int idx = tid; idx < kHeads * kTile; idx += kThreads) {
+      const int hh = idx / kTile, tt = idx % kTile;
+      float s = -INFINITY;
+      if (hh < nh && tt < n_t && ok_s[tt]) {
+        const int64_t kb = kbase_s[tt];
+        float dot = 0.f;
+        for (int d = 0; d < dk; ++d) dot = fmaf(q_s[hh * dk + d], E::load(kc, kb + d), dot);
+        s = dot * a.scale;
+      }
+      s_s[hh][tt] = s;
+    }
+    __syncthreads();
+    // online softmax update, one thread per head
+    if (tid < nh) {
+      float mt = m_s[tid];
+      for (int tt = 0; tt < n_t; ++tt) mt = fmaxf(mt, s_s[tid][tt]);
+      const float alpha = (mt == -INFINITY) ? 1.f : expf(m_s[tid] - mt);
+      float sum = 0.f;
+      for (int tt = 0; tt < kTile; ++tt) {
+        const float e = (tt < n_t && s_s[tid][tt] != -INFINITY) ? expf(s_s[tid][tt] - mt) : 0.f;
+        s_s[tid][tt] = e;
+        sum += e;
+      }
+      l_s[tid] = l_s[tid] * alpha + sum;
+      m_s[tid] = mt;
+      alpha_s[tid] = alpha;
+    }
+    __syncthreads();
+    // weighted values
+#pragma unroll
+    for (int k = 0; k < kAcc; ++k) {
+      const int idx = tid + k * kThreads;
+      const int hh = idx / dv, d = idx % dv;
+      if (hh < nh) {
+        float v = acc[k] * alpha_s[hh];
+        for (int tt = 0; tt < n_t; ++tt) {
+          if (!ok_s[tt]) continue;
+          const float x = vc ? E::load(vc, vbase_s[tt] + int64_t(d) * bs) : E::load(kc, vbase_s[tt] + d);
+          v = fmaf(s_s[hh][tt], x, v);
+        }
+        acc[k] = v;
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int k = 0; k < kAcc; ++k) {
+    const int idx = tid + k * kThreads;
+    const int hh = idx / dv, d = idx % dv;
+    if (hh < nh) a.part_out[(out_row + h0 + hh) * dv + d] = acc[k] / l_s[hh];
+  }
+  if (tid < nh) a.part_lse[out_row + h0 + tid] = m_s[tid] + logf(l_s[tid]);
+}
+
+}  // namespace
+
+hipError_t launch_decode_generic(const DecodeArgs& a, hipStream_t st) {
+  const int g = a.hq / a.hkv;
+  const int chunks = (g + kHeads - 1) / kHeads;
+  const dim3 grid(a.max_parts, a.n_seqs * a.n_shards, a.hkv * chunks);
+  if (a.dtype == kF32)
+    hipLaunchKernelGGL(decode_generic_kernel<kF32>, grid, dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL(decode_generic_kernel<kBF16>, grid, dim3(kThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace pa

@@ -1,0 +1,10 @@
+// dispatch.cpp -- decode kernel selection.
+#include "pa_dispatch.h"
+
+namespace pa {
+
+hipError_t dispatch_decode(const DecodeArgs& a, hipStream_t st) {
+  return launch_decode_generic(a, st);
+}
+
+}  // namespace pa

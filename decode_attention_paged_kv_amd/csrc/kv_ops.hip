@@ -1,0 +1,128 @@
+// kv_ops.hip -- slot routing, kv append and the block-table gather.
+//
+// kv append: a decode step stores the new token's key and value rows before the
+// attention reads them (qiita.com/systemdesignsimple "KV cache and continuous
+// batching", section "What does the KV cache hold?").  The copy is of raw bits, so it
+// is exact for any element type.
+// Slot routing and gather: placement by the DCP interleave rule and block-table
+// lookup, as in pa_common.h.
+#include "pa_common.h"
+#include "pa_launch.h"
+
+namespace pa {
+namespace {
+
+__global__ void slot_mapping_kernel(const int32_t* __restrict__ bt, const int32_t* __restrict__ lens,
+                                    int n_seqs, int S, int I, int bs, int max_blocks,
+                                    int64_t n_blocks, int64_t* __restrict__ slots, int* flag) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= n_seqs) return;
+  const int L = lens[b];
+  int64_t slot = -1;
+  if (L > 0) {
+    const int i = L - 1;
+    const int r = shard_of(i, S, I);
+    const int t = local_index(i, S, I);
+    const int32_t* row = bt + (int64_t(b) * S + r) * max_blocks;
+    const int64_t phys = table_block(row, t / bs, max_blocks, n_blocks, flag);
+    if (phys >= 0) slot = phys * bs + t % bs;
+  }
+  slots[b] = slot;
+}
+
+template <typename RAW>
+__global__ void kv_append_kernel(const RAW* __restrict__ k_new, const RAW* __restrict__ v_new,
+                                 RAW* __restrict__ k_cache, RAW* __restrict__ v_cache,
+                                 const int64_t* __restrict__ slots, int hkv, int dk, int dv, int bs,
+                                 int64_t n_blocks, int* flag) {
+  const int n = blockIdx.x;
+  const int h = blockIdx.y;
+  const int64_t slot = slots[n];
+  if (slot < 0) return;
+  if (slot >= n_blocks * bs) {
+    if (threadIdx.x == 0) raise_flag(flag, kErrSlot);
+    return;
+  }
+  const int64_t blk = slot / bs;
+  const int off = int(slot % bs);
+  const RAW* ks = k_new + (int64_t(n) * hkv + h) * dk;
+  RAW* kd = k_cache + ((blk * hkv + h) * bs + off) * dk;
+  for (int e = threadIdx.x; e < dk; e += blockDim.x) kd[e] = ks[e];
+  if (v_cache != nullptr) {
+    const RAW* vs = v_new + (int64_t(n) * hkv + h) * dv;
+    RAW* vd = v_cache + (blk * hkv + h) * int64_t(dv) * bs + off;
+    for (int d = threadIdx.x; d < dv; d += blockDim.x) vd[int64_t(d) * bs] = vs[d];
+  }
+}
+
+template <typename RAW>
+__global__ void gather_kernel(const RAW* __restrict__ k_cache, const RAW* __restrict__ v_cache,
+                              const int32_t* __restrict__ row, int hkv, int dk, int dv, int bs,
+                              int64_t n_blocks, int max_blocks, RAW* __restrict__ k_out,
+                              RAW* __restrict__ v_out, int* flag) {
+  const int t = blockIdx.x;
+  const int h = blockIdx.y;
+  __shared__ int64_t phys_s;
+  if (threadIdx.x == 0) phys_s = table_block(row, t / bs, max_blocks, n_blocks, flag);
+  __syncthreads();
+  const int64_t phys = phys_s;
+  if (phys < 0) return;
+  const int off = t % bs;
+  const RAW* ks = k_cache + ((phys * hkv + h) * bs + off) * dk;
+  RAW* kd = k_out + (int64_t(t) * hkv + h) * dk;
+  for (int e = threadIdx.x; e < dk; e += blockDim.x) kd[e] = ks[e];
+  RAW* vd = v_out + (int64_t(t) * hkv + h) * dv;
+  if (v_cache != nullptr) {
+    const RAW* vs = v_cache + (phys * hkv + h) * int64_t(dv) * bs + off;
+    for (int d = threadIdx.x; d < dv; d += blockDim.x) vd[d] = vs[int64_t(d) * bs];
+  } else {
+    for (int d = threadIdx.x; d < dv; d += blockDim.x) vd[d] = ks[d];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_slot_mapping(const int32_t* bt, const int32_t* lens, int n_seqs, int S, int I,
+                               int bs, int max_blocks, int64_t n_blocks, int64_t* slots, int* flag,
+                               hipStream_t st) {
+  const int threads = 256;
+  const int blocks = (n_seqs + threads - 1) / threads;
+  hipLaunchKernelGGL(slot_mapping_kernel, dim3(blocks), dim3(threads), 0, st, bt, lens, n_seqs, S,
+                     I, bs, max_blocks, n_blocks, slots, flag);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                            const int64_t* slots, int n_tokens, int hkv, int dk, int dv, int bs,
+                            int64_t n_blocks, int dtype, int* flag, hipStream_t st) {
+  const dim3 grid(n_tokens, hkv);
+  if (dtype == kF32) {
+    hipLaunchKernelGGL(kv_append_kernel<uint32_t>, grid, dim3(64), 0, st,
+                       (const uint32_t*)k_new, (const uint32_t*)v_new, (uint32_t*)k_cache,
+                       (uint32_t*)v_cache, slots, hkv, dk, dv, bs, n_blocks, flag);
+  } else {
+    hipLaunchKernelGGL(kv_append_kernel<uint16_t>, grid, dim3(64), 0, st,
+                       (const uint16_t*)k_new, (const uint16_t*)v_new, (uint16_t*)k_cache,
+                       (uint16_t*)v_cache, slots, hkv, dk, dv, bs, n_blocks, flag);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gather(const void* k_cache, const void* v_cache, const int32_t* bt_row,
+                         int L_r, int hkv, int dk, int dv, int bs, int64_t n_blocks,
+                         int max_blocks, int dtype, void* k_out, void* v_out, int* flag,
+                         hipStream_t st) {
+  const dim3 grid(L_r, hkv);
+  if (dtype == kF32) {
+    hipLaunchKernelGGL(gather_kernel<uint32_t>, grid, dim3(64), 0, st, (const uint32_t*)k_cache,
+                       (const uint32_t*)v_cache, bt_row, hkv, dk, dv, bs, n_blocks, max_blocks,
+                       (uint32_t*)k_out, (uint32_t*)v_out, flag);
+  } else {
+    hipLaunchKernelGGL(gather_kernel<uint16_t>, grid, dim3(64), 0, st, (const uint16_t*)k_cache,
+                       (const uint16_t*)v_cache, bt_row, hkv, dk, dv, bs, n_blocks, max_blocks,
+                       (uint16_t*)k_out, (uint16_t*)v_out, flag);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace pa

@@ -1,0 +1,210 @@
+// pa_api.cpp -- the C ABI declared in include/pa.h: argument validation, launch
+// configuration and dispatch.  Nothing is launched when validation fails.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "../../include/pa.h"
+#include "pa_common.h"
+#include "pa_launch.h"
+#include "pa_dispatch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return PA_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool valid_dtype(int32_t dt) { return dt == PA_F32 || dt == PA_BF16; }
+
+#define REQUIRE(cond, code, ...) \
+  do {                           \
+    if (!(cond)) return fail(code, __VA_ARGS__); \
+  } while (0)
+
+int check_placement(int32_t n_shards, int32_t interleave, int32_t block_size) {
+  REQUIRE(n_shards >= 1 && n_shards <= 65535, PA_ERR_SHAPE, "n_shards=%d must be in [1, 65535]", n_shards);
+  REQUIRE(interleave >= 1, PA_ERR_SHAPE, "interleave=%d must be >= 1", interleave);
+  REQUIRE(int64_t(n_shards) * interleave <= (int64_t(1) << 30), PA_ERR_SHAPE,
+          "n_shards*interleave=%lld too large", (long long)n_shards * interleave);
+  REQUIRE(block_size >= 1 && block_size <= PA_MAX_BLOCK_SIZE, PA_ERR_UNSUPPORTED,
+          "block_size=%d must be in [1, %d]", block_size, PA_MAX_BLOCK_SIZE);
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_last_error(void) { return g_last_error.c_str(); }
+
+int32_t pa_shard_length(int32_t context_len, int32_t n_shards, int32_t interleave, int32_t shard) {
+  if (context_len < 0 || n_shards < 1 || interleave < 1 || shard < 0 || shard >= n_shards) return -1;
+  if (int64_t(n_shards) * interleave > (int64_t(1) << 30)) return -1;
+  return pa::shard_len(context_len, n_shards, interleave, shard);
+}
+
+int32_t pa_max_partitions(int32_t max_context_len, int32_t n_shards, int32_t interleave,
+                          int32_t partition_tokens) {
+  if (partition_tokens < 1) return -1;
+  const int32_t longest = pa_shard_length(max_context_len, n_shards, interleave, 0);
+  if (longest < 0) return -1;
+  return (longest + partition_tokens - 1) / partition_tokens;
+}
+
+int32_t pa_default_partition_tokens(int32_t n_seqs, int32_t n_kv_heads, int32_t max_context_len,
+                                    int32_t n_shards, int32_t interleave, int32_t block_size) {
+  if (n_seqs < 1 || n_kv_heads < 1 || block_size < 1 || block_size > PA_MAX_BLOCK_SIZE) return -1;
+  const int32_t longest = pa_shard_length(max_context_len, n_shards, interleave, 0);
+  if (longest < 0) return -1;
+  // Enough units for several workgroups per compute unit, partitions no longer
+  // than 4,096 tokens and no shorter than 256 tokens (or one block).
+  const int64_t want_units = 4 * 256;
+  const int64_t rows = int64_t(n_seqs) * n_shards * n_kv_heads;
+  int32_t T = 4096;
+  while (T > 256 && rows * ((longest + T - 1) / T) < want_units) T /= 2;
+  T = ((T + block_size - 1) / block_size) * block_size;
+  return T;
+}
+
+int pa_slot_mapping(const int32_t* block_table, const int32_t* context_lens, int32_t n_seqs,
+                    int32_t n_shards, int32_t interleave, int32_t block_size,
+                    int32_t max_blocks_per_shard, int64_t n_blocks, int64_t* slot_mapping,
+                    int32_t* err_flag, void* stream) {
+  REQUIRE(block_table && context_lens && slot_mapping, PA_ERR_NULL,
+          "pa_slot_mapping: block_table, context_lens and slot_mapping must be non-NULL");
+  REQUIRE(n_seqs >= 0, PA_ERR_SHAPE, "n_seqs=%d must be >= 0", n_seqs);
+  if (int rc = check_placement(n_shards, interleave, block_size)) return rc;
+  REQUIRE(max_blocks_per_shard >= 1 && n_blocks >= 1, PA_ERR_SHAPE,
+          "max_blocks_per_shard=%d and n_blocks=%lld must be >= 1", max_blocks_per_shard,
+          (long long)n_blocks);
+  if (n_seqs == 0) return ok();
+  return hip_status(pa::launch_slot_mapping(block_table, context_lens, n_seqs, n_shards, interleave,
+                                            block_size, max_blocks_per_shard, n_blocks,
+                                            slot_mapping, err_flag, (hipStream_t)stream),
+                    "pa_slot_mapping launch");
+}
+
+int pa_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                 const int64_t* slot_mapping, int32_t n_tokens, int32_t n_kv_heads, int32_t dk,
+                 int32_t dv, int32_t block_size, int64_t n_blocks, int32_t dtype,
+                 int32_t* err_flag, void* stream) {
+  REQUIRE(k_new && k_cache && slot_mapping, PA_ERR_NULL,
+          "pa_kv_append: k_new, k_cache and slot_mapping must be non-NULL");
+  REQUIRE((v_new == nullptr) == (v_cache == nullptr), PA_ERR_NULL,
+          "pa_kv_append: v_new and v_cache must both be NULL (latent cache) or both non-NULL");
+  REQUIRE(valid_dtype(dtype), PA_ERR_UNSUPPORTED, "dtype=%d is not PA_F32 or PA_BF16", dtype);
+  REQUIRE(n_tokens >= 0, PA_ERR_SHAPE, "n_tokens=%d must be >= 0", n_tokens);
+  REQUIRE(n_kv_heads >= 1 && n_kv_heads <= 65535, PA_ERR_SHAPE, "n_kv_heads=%d out of range", n_kv_heads);
+  REQUIRE(dk >= 1 && dk <= PA_MAX_HEAD_DIM, PA_ERR_UNSUPPORTED, "dk=%d must be in [1, %d]", dk, PA_MAX_HEAD_DIM);
+  REQUIRE(v_cache == nullptr || (dv >= 1 && dv <= PA_MAX_HEAD_DIM), PA_ERR_UNSUPPORTED,
+          "dv=%d must be in [1, %d]", dv, PA_MAX_HEAD_DIM);
+  REQUIRE(block_size >= 1 && block_size <= PA_MAX_BLOCK_SIZE, PA_ERR_UNSUPPORTED,
+          "block_size=%d must be in [1, %d]", block_size, PA_MAX_BLOCK_SIZE);
+  REQUIRE(n_blocks >= 1, PA_ERR_SHAPE, "n_blocks=%lld must be >= 1", (long long)n_blocks);
+  if (n_tokens == 0) return ok();
+  return hip_status(pa::launch_kv_append(k_new, v_new, k_cache, v_cache, slot_mapping, n_tokens,
+                                         n_kv_heads, dk, dv, block_size, n_blocks, dtype, err_flag,
+                                         (hipStream_t)stream),
+                    "pa_kv_append launch");
+}
+
+int pa_decode(const void* q, const void* k_cache, const void* v_cache,
+              const int32_t* block_table, const int32_t* context_lens, int32_t n_seqs,
+              int32_t n_q_heads, int32_t n_kv_heads, int32_t dk, int32_t dv, int32_t block_size,
+              int64_t n_blocks, int32_t max_blocks_per_shard, int32_t n_shards, int32_t interleave,
+              int32_t partition_tokens, int32_t max_partitions, float scale, int32_t dtype,
+              float* part_out, float* part_lse, int32_t* err_flag, void* stream) {
+  REQUIRE(q && k_cache && block_table && context_lens && part_out && part_lse, PA_ERR_NULL,
+          "pa_decode: q, k_cache, block_table, context_lens, part_out and part_lse must be non-NULL");
+  REQUIRE(valid_dtype(dtype), PA_ERR_UNSUPPORTED, "dtype=%d is not PA_F32 or PA_BF16", dtype);
+  REQUIRE(n_seqs >= 0, PA_ERR_SHAPE, "n_seqs=%d must be >= 0", n_seqs);
+  REQUIRE(n_q_heads >= 1 && n_kv_heads >= 1 && n_q_heads % n_kv_heads == 0, PA_ERR_SHAPE,
+          "n_q_heads=%d must be a positive multiple of n_kv_heads=%d", n_q_heads, n_kv_heads);
+  REQUIRE(dk >= 1 && dk <= PA_MAX_HEAD_DIM, PA_ERR_UNSUPPORTED, "dk=%d must be in [1, %d]", dk, PA_MAX_HEAD_DIM);
+  REQUIRE(dv >= 1 && dv <= 512, PA_ERR_UNSUPPORTED, "dv=%d must be in [1, 512]", dv);
+  REQUIRE(v_cache != nullptr || dv <= dk, PA_ERR_SHAPE,
+          "latent cache (v_cache NULL) needs dv=%d <= dk=%d", dv, dk);
+  if (int rc = check_placement(n_shards, interleave, block_size)) return rc;
+  REQUIRE(max_blocks_per_shard >= 1 && n_blocks >= 1, PA_ERR_SHAPE,
+          "max_blocks_per_shard=%d and n_blocks=%lld must be >= 1", max_blocks_per_shard,
+          (long long)n_blocks);
+  REQUIRE(partition_tokens >= 1 && partition_tokens % block_size == 0, PA_ERR_SHAPE,
+          "partition_tokens=%d must be a positive multiple of block_size=%d", partition_tokens,
+          block_size);
+  REQUIRE(max_partitions >= 1, PA_ERR_BUFFER, "max_partitions=%d must be >= 1", max_partitions);
+  REQUIRE(int64_t(n_seqs) * n_shards <= 65535, PA_ERR_SHAPE,
+          "n_seqs*n_shards=%lld exceeds 65535", (long long)n_seqs * n_shards);
+  REQUIRE(n_kv_heads * ((n_q_heads / n_kv_heads + 15) / 16) <= 65535, PA_ERR_SHAPE,
+          "too many heads");
+  if (n_seqs == 0) return ok();
+  pa::DecodeArgs a{q,        k_cache,         v_cache,    block_table, context_lens, n_seqs,
+                   n_q_heads, n_kv_heads,     dk,         dv,          block_size,   n_blocks,
+                   max_blocks_per_shard, n_shards, interleave, partition_tokens, max_partitions,
+                   scale,    dtype,           part_out,   part_lse,    err_flag};
+  return hip_status(pa::dispatch_decode(a, (hipStream_t)stream), "pa_decode launch");
+}
+
+int pa_merge_lse(const float* part_out, const float* part_lse, int32_t n_seqs, int32_t n_parts,
+                 int32_t n_q_heads, int32_t dv, void* out, int32_t out_dtype, float* lse,
+                 void* stream) {
+  REQUIRE(part_out && part_lse && out, PA_ERR_NULL,
+          "pa_merge_lse: part_out, part_lse and out must be non-NULL");
+  REQUIRE(valid_dtype(out_dtype), PA_ERR_UNSUPPORTED, "out_dtype=%d is not PA_F32 or PA_BF16", out_dtype);
+  REQUIRE(n_seqs >= 0 && n_parts >= 1 && n_q_heads >= 1, PA_ERR_SHAPE,
+          "n_seqs=%d, n_parts=%d, n_q_heads=%d out of range", n_seqs, n_parts, n_q_heads);
+  REQUIRE(dv >= 1 && dv <= 512, PA_ERR_UNSUPPORTED, "dv=%d must be in [1, 512]", dv);
+  REQUIRE(int64_t(n_seqs) * n_q_heads <= 0x7fffffff, PA_ERR_SHAPE, "n_seqs*n_q_heads too large");
+  if (n_seqs == 0) return ok();
+  return hip_status(pa::launch_merge(part_out, part_lse, n_seqs, n_parts, n_q_heads, dv, out,
+                                     out_dtype, lse, (hipStream_t)stream),
+                    "pa_merge_lse launch");
+}
+
+int pa_gather_kv(const void* k_cache, const void* v_cache, const int32_t* block_table,
+                 int32_t seq, int32_t shard, int32_t context_len, int32_t n_kv_heads, int32_t dk,
+                 int32_t dv, int32_t block_size, int64_t n_blocks, int32_t max_blocks_per_shard,
+                 int32_t n_shards, int32_t interleave, int32_t dtype, void* k_out, void* v_out,
+                 int32_t* err_flag, void* stream) {
+  REQUIRE(k_cache && block_table && k_out && v_out, PA_ERR_NULL,
+          "pa_gather_kv: k_cache, block_table, k_out and v_out must be non-NULL");
+  REQUIRE(valid_dtype(dtype), PA_ERR_UNSUPPORTED, "dtype=%d is not PA_F32 or PA_BF16", dtype);
+  if (int rc = check_placement(n_shards, interleave, block_size)) return rc;
+  REQUIRE(seq >= 0 && shard >= 0 && shard < n_shards && context_len >= 0, PA_ERR_SHAPE,
+          "seq=%d, shard=%d (n_shards=%d), context_len=%d out of range", seq, shard, n_shards,
+          context_len);
+  REQUIRE(n_kv_heads >= 1 && n_kv_heads <= 65535, PA_ERR_SHAPE, "n_kv_heads=%d out of range", n_kv_heads);
+  REQUIRE(dk >= 1 && dk <= PA_MAX_HEAD_DIM && dv >= 1 && dv <= PA_MAX_HEAD_DIM, PA_ERR_UNSUPPORTED,
+          "dk=%d, dv=%d must be in [1, %d]", dk, dv, PA_MAX_HEAD_DIM);
+  REQUIRE(v_cache != nullptr || dv <= dk, PA_ERR_SHAPE, "latent cache needs dv <= dk");
+  REQUIRE(max_blocks_per_shard >= 1 && n_blocks >= 1, PA_ERR_SHAPE,
+          "max_blocks_per_shard and n_blocks must be >= 1");
+  const int L_r = pa::shard_len(context_len, n_shards, interleave, shard);
+  if (L_r == 0) return ok();
+  const int32_t* row = block_table + (int64_t(seq) * n_shards + shard) * max_blocks_per_shard;
+  return hip_status(pa::launch_gather(k_cache, v_cache, row, L_r, n_kv_heads, dk, dv, block_size,
+                                      n_blocks, max_blocks_per_shard, dtype, k_out, v_out,
+                                      err_flag, (hipStream_t)stream),
+                    "pa_gather_kv launch");
+}
+
+}  // extern "C"

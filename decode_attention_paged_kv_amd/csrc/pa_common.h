@@ -1,0 +1,88 @@
+// pa_common.h -- device/host helpers shared by the paged decode-attention kernels.
+//
+// Token placement follows the DCP page (soroban.highreso.jp, "Why long-context LLMs
+// get slow: distributing the KV cache with Decode Context Parallelism", DCP mechanism
+// section): token i goes to shard (i / I) % S, dealt I tokens at a time.  A shard keeps
+// its tokens in global order.  Closed forms used here:
+//   local index of token i       : (i / (I*S)) * I + i % I
+//   tokens on shard r of length L: c*I + clamp(L - c*I*S - r*I, 0, I),  c = L / (I*S)
+// Block addressing follows the PagedAttention page (ai-compass.weeybrid.co.jp, "What is
+// PagedAttention?", block-table section): local token t of a shard is in the physical
+// block listed at entry t / block_size of that shard's table row, at offset
+// t % block_size.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+enum : int { kF32 = 0, kBF16 = 1 };
+
+constexpr int kMaxHeadDim = 576;
+constexpr int kMaxBlockSize = 256;
+
+// ---------------------------------------------------------------- placement math
+__host__ __device__ inline int shard_len(int L, int S, int I, int r) {
+  const int round = I * S;
+  const int c = L / round;
+  int extra = L - c * round - r * I;
+  extra = extra < 0 ? 0 : (extra > I ? I : extra);
+  return c * I + extra;
+}
+
+__host__ __device__ inline int shard_of(int i, int S, int I) { return (i / I) % S; }
+
+__host__ __device__ inline int local_index(int i, int S, int I) {
+  return (i / (I * S)) * I + i % I;
+}
+
+// ---------------------------------------------------------------- error flag
+// Device-detected data errors.  Stored with an ordinary vector atomic.
+enum : int { kErrBlockId = 1, kErrCapacity = 2, kErrSlot = 4 };
+
+__device__ inline void raise_flag(int* flag, int bits) {
+  if (flag) atomicOr(flag, bits);
+}
+
+// Physical block of logical entry j of a table row, or -1 (and the flag raised) when
+// the entry lies outside the row or holds an id outside [0, n_blocks).
+__device__ inline int64_t table_block(const int32_t* row, int j, int max_blocks, int64_t n_blocks,
+                                      int* flag) {
+  if (j < 0 || j >= max_blocks) {
+    raise_flag(flag, kErrCapacity);
+    return -1;
+  }
+  const int64_t phys = row[j];
+  if (phys < 0 || phys >= n_blocks) {
+    raise_flag(flag, kErrBlockId);
+    return -1;
+  }
+  return phys;
+}
+
+// ---------------------------------------------------------------- element types
+__device__ inline float bf16_bits_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+
+// fp32 -> bf16, round to nearest even; NaN stays a quiet NaN of the same sign.
+__device__ inline uint16_t f32_to_bf16_bits(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40u);
+  const uint32_t rounded = u + 0x7fffu + ((u >> 16) & 1u);
+  return uint16_t(rounded >> 16);
+}
+
+template <int DT>
+struct Elem;
+template <>
+struct Elem<kF32> {
+  using raw = uint32_t;
+  static __device__ inline float load(const raw* p, int64_t i) { return __uint_as_float(p[i]); }
+};
+template <>
+struct Elem<kBF16> {
+  using raw = uint16_t;
+  static __device__ inline float load(const raw* p, int64_t i) { return bf16_bits_to_f32(p[i]); }
+};
+
+}  // namespace pa

@@ -1,0 +1,40 @@
+// pa_launch.h -- host-side launchers of the kernels (internal to the library).
+// The C ABI in pa_api.cpp validates arguments and then calls these.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+struct DecodeArgs {
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;  // NULL: value = first dv entries of the key row
+  const int32_t* block_table;
+  const int32_t* context_lens;
+  int n_seqs, hq, hkv, dk, dv, bs;
+  int64_t n_blocks;
+  int max_blocks, n_shards, interleave, part_tokens, max_parts;
+  float scale;
+  int dtype;
+  float* part_out;
+  float* part_lse;
+  int* flag;
+};
+
+hipError_t launch_slot_mapping(const int32_t* bt, const int32_t* lens, int n_seqs, int S, int I,
+                               int bs, int max_blocks, int64_t n_blocks, int64_t* slots, int* flag,
+                               hipStream_t st);
+hipError_t launch_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                            const int64_t* slots, int n_tokens, int hkv, int dk, int dv, int bs,
+                            int64_t n_blocks, int dtype, int* flag, hipStream_t st);
+hipError_t launch_gather(const void* k_cache, const void* v_cache, const int32_t* bt_row,
+                         int L_r, int hkv, int dk, int dv, int bs, int64_t n_blocks,
+                         int max_blocks, int dtype, void* k_out, void* v_out, int* flag,
+                         hipStream_t st);
+hipError_t launch_decode_generic(const DecodeArgs& a, hipStream_t st);
+hipError_t launch_merge(const float* part_out, const float* part_lse, int n_seqs, int n_parts,
+                        int hq, int dv, void* out, int out_dtype, float* lse, hipStream_t st);
+
+}  // namespace pa

@@ -1,0 +1,57 @@
+"""One decode step on one stream: slot routing, kv append, attention, LSE merge.
+
+``DecodeStep`` owns the step's output and scratch tensors (allocated once, with
+torch, for a maximum context length) and issues the four library calls.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib as L
+
+
+class DecodeStep:
+    def __init__(self, n_seqs, n_q_heads, n_kv_heads, dk, dv, block_size, max_context_len,
+                 n_shards=1, interleave=1, partition_tokens=0, scale=None, device="cuda",
+                 out_dtype=torch.float32):
+        self.n_seqs, self.hq, self.hkv, self.dk, self.dv = n_seqs, n_q_heads, n_kv_heads, dk, dv
+        self.block_size, self.n_shards, self.interleave = block_size, n_shards, interleave
+        if not partition_tokens:
+            partition_tokens = L.pa_default_partition_tokens(n_seqs, n_kv_heads, max_context_len,
+                                                             n_shards, interleave, block_size)
+        self.partition_tokens = partition_tokens
+        self.max_partitions = max(1, L.pa_max_partitions(max_context_len, n_shards, interleave,
+                                                         partition_tokens))
+        self.scale = float(torch.tensor(scale if scale is not None else dk ** -0.5,
+                                        dtype=torch.float32))
+        dev = torch.device(device)
+        P = self.max_partitions
+        self.slot_mapping = torch.empty(n_seqs, dtype=torch.int64, device=dev)
+        self.part_out = torch.empty(n_seqs, n_shards, P, n_q_heads, dv, dtype=torch.float32, device=dev)
+        self.part_lse = torch.empty(n_seqs, n_shards, P, n_q_heads, dtype=torch.float32, device=dev)
+        self.out = torch.empty(n_seqs, n_q_heads, dv, dtype=out_dtype, device=dev)
+        self.lse = torch.empty(n_seqs, n_q_heads, dtype=torch.float32, device=dev)
+        self.err_flag = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def route(self, block_table, context_lens, n_blocks):
+        L.pa_slot_mapping(block_table, context_lens, self.n_shards, self.interleave,
+                          self.block_size, n_blocks, self.slot_mapping, self.err_flag)
+
+    def append(self, k_new, v_new, k_cache, v_cache):
+        L.pa_kv_append(k_new, v_new, k_cache, v_cache, self.slot_mapping, self.err_flag)
+
+    def attend(self, q, k_cache, v_cache, block_table, context_lens):
+        L.pa_decode(q, k_cache, v_cache, block_table, context_lens, self.n_shards, self.interleave,
+                    self.partition_tokens, self.max_partitions, self.scale, self.part_out,
+                    self.part_lse, dv=self.dv, err_flag=self.err_flag)
+
+    def merge(self):
+        L.pa_merge_lse(self.part_out, self.part_lse, self.out, self.lse)
+
+    def __call__(self, q, k_new, v_new, k_cache, v_cache, block_table, context_lens):
+        """The whole step; returns ``(out, lse)`` (views of this object's buffers)."""
+        self.route(block_table, context_lens, k_cache.shape[0])
+        self.append(k_new, v_new, k_cache, v_cache)
+        self.attend(q, k_cache, v_cache, block_table, context_lens)
+        self.merge()
+        return self.out, self.lse

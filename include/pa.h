@@ -1,0 +1,189 @@
+/*
+ * pa.h -- C ABI of one decode step of attention over a block-table-paged KV cache,
+ * for AMD Instinct MI355X (gfx950).  Library: libpagedattn.so.
+ *
+ * Pages the operations follow (cited per entry point below):
+ *  [KVB] qiita.com/systemdesignsimple/items/76d9c4d7ac4a80e2deff, "KV cache and
+ *        continuous batching": a decode step stores the new token's key/value and
+ *        then attends over every stored token (section "What does the KV cache
+ *        hold?"); bytes per token (section "How KV-cache memory limits concurrency").
+ *  [PA]  ai-compass.weeybrid.co.jp/algorizm/paged-attention/, "What is
+ *        PagedAttention?": fixed-size blocks, a per-request block table from logical
+ *        to physical blocks, attention reads KV through the table (section "A block
+ *        table separates logical order from physical placement").
+ *  [DCP] soroban.highreso.jp/article/techblog-engineer-choubunllm, "Why long-context
+ *        LLMs get slow: distributing the KV cache with Decode Context Parallelism":
+ *        tokens dealt to S shards `interleave` at a time; each shard attends over its
+ *        own tokens and returns an output plus its softmax LSE; the partial outputs
+ *        are reweighted with the LSEs and summed (DCP mechanism section); the decode
+ *        backend must return the LSE (DCP configuration section).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every pointer argument is a DEVICE pointer owned by the caller, unless stated.
+ *    The library allocates no device memory and keeps no pointer after returning.
+ *  - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL = the null
+ *    stream) and runs asynchronously; no call synchronises.
+ *  - Return value: PA_OK (0) or a negative pa_status.  On an error detected on the
+ *    host (null pointer, bad shape, unsupported combination, buffer too small)
+ *    NOTHING is launched; pa_last_error() returns a message (per calling thread).
+ *  - Data-dependent errors (a block id outside [0, n_blocks), a context longer than
+ *    the block table holds, a slot outside the pool) are detected on the device:
+ *    the offending token or block is skipped and, if `err_flag` is non-NULL, a
+ *    nonzero value is stored in *err_flag (never cleared by the library).
+ *  - Element types: PA_F32 (IEEE binary32) or PA_BF16 (bfloat16).  q, K and V of one
+ *    call share one type.  Partial outputs and LSEs are always float32.
+ *
+ * Layout of the paged cache (one layer)
+ * -------------------------------------
+ *  k_cache  [n_blocks][n_kv_heads][block_size][dk]   a token's key row is contiguous
+ *  v_cache  [n_blocks][n_kv_heads][dv][block_size]   token index fastest
+ *  Latent (MLA-style) cache: v_cache == NULL; the value of a token is the first dv
+ *  entries of its key row (dv <= dk), read from k_cache.
+ *  slot = physical_block * block_size + offset_in_block.
+ *
+ * Sharding (DCP emulated on one GPU)
+ * ----------------------------------
+ *  Global token i (0-based) of a sequence lives on shard (i / interleave) % n_shards;
+ *  each shard keeps its tokens in global order, so token i has local index
+ *  (i / (interleave*n_shards))*interleave + i % interleave, and shard r of a length-L
+ *  sequence holds  L_r = c*interleave + clamp(L - c*interleave*n_shards - r*interleave,
+ *  0, interleave)  tokens with c = L / (interleave*n_shards).
+ *  block_table  int32 [n_seqs][n_shards][max_blocks_per_shard]: row [b][r] lists the
+ *  physical blocks of shard r of sequence b in logical order (entry j holds local
+ *  tokens j*block_size .. j*block_size+block_size-1).  Unused entries are ignored.
+ *  n_shards = 1 is the ordinary unsharded cache.
+ *
+ * context_lens  int32 [n_seqs]: tokens of each sequence INCLUDING the token this
+ *  step appends, which sits at global position context_lens[b]-1.  0 = no tokens.
+ */
+#ifndef PAGEDATTN_PA_H
+#define PAGEDATTN_PA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_NULL = -1,         /* a required pointer is NULL                          */
+  PA_ERR_SHAPE = -2,        /* a size is out of range or sizes are inconsistent   */
+  PA_ERR_UNSUPPORTED = -3,  /* valid but not implemented (dtype, head size, ...)  */
+  PA_ERR_BUFFER = -4,       /* a caller buffer is too small for the request       */
+  PA_ERR_HIP = -5           /* the HIP runtime reported an error on launch        */
+} pa_status;
+
+typedef enum pa_dtype { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
+
+/* Largest supported sizes. */
+#define PA_MAX_HEAD_DIM 576
+#define PA_MAX_BLOCK_SIZE 256
+
+/*
+ * pa_slot_mapping -- cache slot of each sequence's new token ([DCP]: a token made
+ * during decode is placed by the same interleave rule; [PA]: the current block is
+ * filled while it has room, so the token goes to local offset (local index mod
+ * block_size) of the block the table lists for it).
+ *   block_table, context_lens : as above.
+ *   slot_mapping (out)        : int64 [n_seqs]; slot of token context_lens[b]-1, or
+ *                               -1 when context_lens[b] <= 0 or its block id is invalid
+ *                               (then *err_flag is set).
+ */
+int pa_slot_mapping(const int32_t* block_table, const int32_t* context_lens, int32_t n_seqs,
+                    int32_t n_shards, int32_t interleave, int32_t block_size,
+                    int32_t max_blocks_per_shard, int64_t n_blocks, int64_t* slot_mapping,
+                    int32_t* err_flag, void* stream);
+
+/*
+ * pa_kv_append -- store each new token's key and value into its slot, bit for bit
+ * ([KVB], "What does the KV cache hold?").
+ *   k_new  [n_tokens][n_kv_heads][dk];  v_new [n_tokens][n_kv_heads][dv] (NULL for the
+ *   latent cache, where v_cache must be NULL too).
+ *   slot_mapping int64 [n_tokens]: slot < 0 is padding and is skipped; a slot at or
+ *   beyond n_blocks*block_size is skipped and sets *err_flag.  Two tokens with the
+ *   same slot: the stored row is one of them, unspecified which.
+ */
+int pa_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                 const int64_t* slot_mapping, int32_t n_tokens, int32_t n_kv_heads, int32_t dk,
+                 int32_t dv, int32_t block_size, int64_t n_blocks, int32_t dtype,
+                 int32_t* err_flag, void* stream);
+
+/*
+ * pa_decode -- attention of one query token per sequence over its paged K/V, split
+ * into shards and partitions, each emitting an output and its LSE ([PA]: attention
+ * follows the block table; [DCP]: local attention per shard returning output + LSE).
+ *   q          [n_seqs][n_q_heads][dk]; query head h reads KV head h / (n_q_heads/n_kv_heads).
+ *   partition_tokens T (> 0, a multiple of block_size): shard r of sequence b is cut
+ *              into partitions of T consecutive LOCAL tokens; partition p covers local
+ *              tokens [p*T, min((p+1)*T, L_r)).
+ *   max_partitions Pmax: partition slots per shard in the outputs; must be at least
+ *              pa_max_partitions(max context, n_shards, interleave, T) for the lengths
+ *              passed (a longer context sets *err_flag and its excess is dropped).
+ *   scale      multiplies q.k before the softmax.
+ *   part_out   float32 [n_seqs][n_shards][Pmax][n_q_heads][dv]: softmax-weighted mean
+ *              of the partition's values; 0 for an empty partition.
+ *   part_lse   float32 [n_seqs][n_shards][Pmax][n_q_heads]: natural log of the sum of
+ *              exp(scale*q.k) over the partition; -inf for an empty partition.
+ *   Unsupported: dk or dv outside [1, PA_MAX_HEAD_DIM], dv > 512, block_size outside
+ *   [1, PA_MAX_BLOCK_SIZE], n_q_heads not a multiple of n_kv_heads.
+ */
+int pa_decode(const void* q, const void* k_cache, const void* v_cache,
+              const int32_t* block_table, const int32_t* context_lens, int32_t n_seqs,
+              int32_t n_q_heads, int32_t n_kv_heads, int32_t dk, int32_t dv, int32_t block_size,
+              int64_t n_blocks, int32_t max_blocks_per_shard, int32_t n_shards, int32_t interleave,
+              int32_t partition_tokens, int32_t max_partitions, float scale, int32_t dtype,
+              float* part_out, float* part_lse, int32_t* err_flag, void* stream);
+
+/*
+ * pa_merge_lse -- combine the partials of each (sequence, head) into the attention
+ * over all its tokens ([DCP], DCP mechanism section: gather the LSEs, reweight each
+ * partial output, sum).  With lse = log(sum_p exp(lse_p)), part p has weight
+ * exp(lse_p - lse); parts with lse_p = -inf have weight 0; if every part is empty the
+ * output is 0 and lse is -inf.
+ *   part_out float32 [n_seqs][n_parts][n_q_heads][dv], part_lse float32
+ *   [n_seqs][n_parts][n_q_heads] (pa_decode's outputs with n_parts = n_shards*Pmax).
+ *   out      [n_seqs][n_q_heads][dv] of out_dtype (PA_F32, or PA_BF16 rounded to nearest
+ *            even);  lse float32 [n_seqs][n_q_heads], may be NULL.
+ */
+int pa_merge_lse(const float* part_out, const float* part_lse, int32_t n_seqs, int32_t n_parts,
+                 int32_t n_q_heads, int32_t dv, void* out, int32_t out_dtype, float* lse,
+                 void* stream);
+
+/*
+ * pa_gather_kv -- copy the K/V rows of shard `shard` of sequence `seq` into contiguous
+ * arrays in local token order, through the same block-table address generation
+ * pa_decode uses ([PA], block-table section).  For checking the paged addressing.
+ *   context_len: L of sequence `seq` (host value, the same as its context_lens entry).
+ *   k_out [L_r][n_kv_heads][dk], v_out [L_r][n_kv_heads][dv] (v_out from the first dv
+ *   entries of the key rows when v_cache is NULL); L_r = pa_shard_length(L, ...).
+ *   Rows whose block id is invalid are left unwritten and set *err_flag.
+ */
+int pa_gather_kv(const void* k_cache, const void* v_cache, const int32_t* block_table,
+                 int32_t seq, int32_t shard, int32_t context_len, int32_t n_kv_heads, int32_t dk,
+                 int32_t dv, int32_t block_size, int64_t n_blocks, int32_t max_blocks_per_shard,
+                 int32_t n_shards, int32_t interleave, int32_t dtype, void* k_out, void* v_out,
+                 int32_t* err_flag, void* stream);
+
+/* Host helpers (no device work).  Return -1 on invalid arguments. */
+int32_t pa_shard_length(int32_t context_len, int32_t n_shards, int32_t interleave, int32_t shard);
+int32_t pa_max_partitions(int32_t max_context_len, int32_t n_shards, int32_t interleave,
+                          int32_t partition_tokens);
+
+/*
+ * pa_default_partition_tokens -- a partition size (a multiple of block_size) that
+ * cuts the work of a step into enough (sequence, shard, partition, KV head) units to
+ * keep all 256 compute units of an MI355X busy, preferring long partitions (fewer
+ * partials to merge).  A heuristic of this library, not something the pages define.
+ */
+int32_t pa_default_partition_tokens(int32_t n_seqs, int32_t n_kv_heads, int32_t max_context_len,
+                                    int32_t n_shards, int32_t interleave, int32_t block_size);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* pa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PAGEDATTN_PA_H */

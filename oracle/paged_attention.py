@@ -119,9 +119,13 @@ def slot_mapping(block_table: np.ndarray, context_lens: np.ndarray, n_shards: in
     """Cache slot (``physical_block * block_size + offset``) of each sequence's new
     token, the one at global position ``L - 1`` ([KVB], "What does the KV cache
     hold?": the step stores the new token's key and value; [PA]: the current
-    block is filled while it has room; [DCP]: new tokens follow the placement rule)."""
+    block is filled while it has room; [DCP]: new tokens follow the placement rule).
+    A sequence with no tokens gets -1 ("no slot")."""
     out = np.empty(len(context_lens), dtype=np.int64)
     for b, L in enumerate(np.asarray(context_lens)):
+        if L <= 0:                      # no token, nothing to place
+            out[b] = -1
+            continue
         _, _, phys, off = token_home(block_table[b], int(L) - 1, n_shards, interleave, block_size)
         out[b] = phys * block_size + off
     return out

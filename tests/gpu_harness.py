@@ -1,0 +1,197 @@
+"""Run a workload through the HIP library and through the fp64 oracle, and
+compare them.  Used by the ``gpu``-marked tests and by ``__graft_entry__.smoke``.
+
+Tolerances (the benchmark spec, stated per input type):
+* fp32 inputs: output max-abs 1e-5, LSE max-abs 1e-5;
+* bf16 inputs: output max-abs 5e-3, LSE max-abs 1e-3;
+plus a relative L2 bound on the whole output, ||o - o*|| / ||o*||, because at
+long context the outputs are themselves only ~5e-3 in size (so max-abs 5e-3
+alone would accept a zero output).  The relative bound comes from the kernels'
+arithmetic: fp32 accumulation of exactly-widened inputs with the softmax
+weights kept to >= 16 significant bits gives ~1e-6; the bound is 1e-4.  Kernels
+that round the weights to bf16 once (8 significant bits, relative error <= 2^-9
+per weight, ~2e-3 in L2 on random data) are held to 4e-3 (``rel_l2`` argument).
+kv append, slot routing and the gather are compared bit for bit.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import workloads as wl
+from oracle import paged_attention as pa
+
+TOL = {wl.F32: dict(out=1e-5, lse=1e-5), wl.BF16: dict(out=5e-3, lse=1e-3)}
+REL_L2 = 1e-4
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def to_np(t):
+    if t is None:
+        return None
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def bits_equal(a, b) -> bool:
+    return a.shape == b.shape and np.array_equal(np.ascontiguousarray(a).view(np.uint8),
+                                                 np.ascontiguousarray(b).view(np.uint8))
+
+
+def run_library(w, T, partition_tokens=None, out_dtype=torch.float32):
+    """One full step through the library on the current stream.  ``T`` holds GPU
+    tensors from ``workloads.make_tensors`` (the caches are updated in place)."""
+    import decode_attention_paged_kv_amd as P
+
+    Tp = partition_tokens or w.partition_tokens or 0
+    step = P.DecodeStep(w.n_seqs, w.n_q_heads, w.n_kv_heads, w.dk, w.dv, w.block_size,
+                        int(w.context_lens.max()), w.n_shards, w.interleave, Tp, w.scale_f32,
+                        device=T["q"].device, out_dtype=out_dtype)
+    out, lse = step(T["q"], T["k_new"], T["v_new"], T["k_cache"], T["v_cache"],
+                    T["block_table"], T["context_lens"])
+    torch.cuda.synchronize()
+    return step
+
+
+def compare_outputs(name, dtype, o, lse, o_ref, lse_ref, rel_l2=REL_L2, out_tol=None):
+    """Raise AssertionError with a message if the library's output misses the oracle's."""
+    tol = TOL[dtype]
+    out_tol = tol["out"] if out_tol is None else out_tol
+    o = np.asarray(o, np.float64)
+    lse = np.asarray(lse, np.float64)
+    assert not np.isnan(o).any(), f"{name}: NaN in output"
+    empty = ~np.isfinite(lse_ref)
+    assert np.array_equal(np.isfinite(lse), ~empty), f"{name}: empty/nonempty pattern differs"
+    assert np.all(lse[empty] == -np.inf) and np.all(o[empty] == 0), f"{name}: empty rows not (0, -inf)"
+    d_o = np.max(np.abs(o - o_ref)) if o.size else 0.0
+    d_l = np.max(np.abs(lse[~empty] - lse_ref[~empty])) if (~empty).any() else 0.0
+    nrm = np.linalg.norm(o_ref)
+    rel = np.linalg.norm(o - o_ref) / nrm if nrm > 0 else 0.0
+    say(f"  {name}: max|do|={d_o:.3g} (tol {out_tol}) max|dlse|={d_l:.3g} (tol {tol['lse']}) "
+        f"rel_l2={rel:.3g} (tol {rel_l2})")
+    assert d_o <= out_tol, f"{name}: output max-abs {d_o:.3g} > {out_tol}"
+    assert d_l <= tol["lse"], f"{name}: lse max-abs {d_l:.3g} > {tol['lse']}"
+    assert rel <= rel_l2, f"{name}: output relative L2 {rel:.3g} > {rel_l2}"
+
+
+def check_small(w, partition_tokens=None, fill="normal", rel_l2=REL_L2, seed=None):
+    """Whole-workload parity: routing, append (whole pool, bitwise), gather
+    (bitwise, every sequence and shard), partials and merged outputs."""
+    import decode_attention_paged_kv_amd as P
+
+    say(f"[parity] {w.name} N={w.n_seqs} Hq={w.n_q_heads} Hkv={w.n_kv_heads} dk={w.dk} dv={w.dv} "
+        f"bs={w.block_size} {w.dtype} S={w.n_shards} I={w.interleave} lens={list(w.context_lens)[:8]}")
+    Tc = wl.make_tensors(w, "cpu", fill=fill, seed=seed)
+    H = {k: to_np(v) for k, v in Tc.items()}
+    dev = torch.device("cuda")
+    T = {k: (None if v is None else v.to(dev)) for k, v in Tc.items()}
+    step = run_library(w, T, partition_tokens)
+    Tp, Pmax = step.partition_tokens, step.max_partitions
+    ref = pa.decode_step(H["q"], H["k_new"], H["v_new"], H["k_cache"], H["v_cache"],
+                         w.block_table, w.context_lens, w.n_shards, w.interleave, w.block_size,
+                         Tp, Pmax, w.scale_f32, w.dv)
+    assert int(step.err_flag.item()) == 0, f"{w.name}: device error flag {int(step.err_flag.item())}"
+    assert np.array_equal(to_np(step.slot_mapping), ref["slots"]), f"{w.name}: slot mapping"
+    assert bits_equal(to_np(T["k_cache"]), ref["k_cache"]), f"{w.name}: k_cache after append"
+    if ref["v_cache"] is not None:
+        assert bits_equal(to_np(T["v_cache"]), ref["v_cache"]), f"{w.name}: v_cache after append"
+    # gather through the library's address generation
+    for b in range(w.n_seqs):
+        L = int(w.context_lens[b])
+        for r in range(w.n_shards):
+            Lr = P.pa_shard_length(L, w.n_shards, w.interleave, r)
+            kg = torch.empty(max(Lr, 1), w.n_kv_heads, w.dk, dtype=T["q"].dtype, device=dev)
+            vg = torch.empty(max(Lr, 1), w.n_kv_heads, w.dv, dtype=T["q"].dtype, device=dev)
+            P.pa_gather_kv(T["k_cache"], T["v_cache"], T["block_table"], b, r, L, w.n_shards,
+                           w.interleave, kg, vg, step.err_flag)
+            kr, vr = pa.gather_shard(ref["k_cache"], ref["v_cache"], w.block_table[b], L, r,
+                                     w.n_shards, w.interleave, w.block_size, w.dv)
+            assert bits_equal(to_np(kg)[:Lr], kr) and bits_equal(to_np(vg)[:Lr], vr), \
+                f"{w.name}: gather seq {b} shard {r}"
+    torch.cuda.synchronize()
+    assert int(step.err_flag.item()) == 0
+    compare_outputs(f"{w.name} partials", w.dtype, to_np(step.part_out), to_np(step.part_lse),
+                    ref["part_o"], ref["part_lse"], rel_l2)
+    compare_outputs(f"{w.name} merged", w.dtype, to_np(step.out), to_np(step.lse), ref["o"],
+                    ref["lse"], rel_l2)
+    return step, ref
+
+
+def check_large(w, sample_seqs, partition_tokens=None, fill="normal", rel_l2=REL_L2):
+    """Full-size parity: the step runs at the workload's real size in the launch
+    configuration the benchmark times; routing is compared for every sequence,
+    the append for the whole pool (every slot but the new ones unchanged, the new
+    ones equal to the new rows), and the attention for ``sample_seqs``, whose
+    blocks are copied out of the pre-step pool and handed to the oracle."""
+    import decode_attention_paged_kv_amd as P
+
+    say(f"[parity-large] {w.name} N={w.n_seqs} sum(L)={int(w.context_lens.sum())} "
+        f"S={w.n_shards} I={w.interleave} fill={fill} sample={list(sample_seqs)}")
+    dev = torch.device("cuda")
+    T = wl.make_tensors(w, dev, fill=fill)
+    k_before = T["k_cache"].clone()
+    v_before = None if T["v_cache"] is None else T["v_cache"].clone()
+    step = run_library(w, T, partition_tokens)
+    assert int(step.err_flag.item()) == 0, f"{w.name}: device error flag"
+    slots_ref = pa.slot_mapping(w.block_table, w.context_lens, w.n_shards, w.interleave, w.block_size)
+    assert np.array_equal(to_np(step.slot_mapping), slots_ref), f"{w.name}: slot mapping"
+    # append: compare slot-major views on the device
+    bs = w.block_size
+    sl = torch.from_numpy(slots_ref).to(dev)
+
+    def slot_major_k(x):            # [NB][Hkv][bs][dk] -> [NB*bs][Hkv*dk]
+        return x.view(torch.int16 if x.dtype == torch.bfloat16 else torch.int32).permute(0, 2, 1, 3).reshape(x.shape[0] * bs, -1)
+
+    def slot_major_v(x):            # [NB][Hkv][dv][bs] -> [NB*bs][Hkv*dv]
+        return x.view(torch.int16 if x.dtype == torch.bfloat16 else torch.int32).permute(0, 3, 1, 2).reshape(x.shape[0] * bs, -1)
+
+    for after, before, new, fn in ((T["k_cache"], k_before, T["k_new"], slot_major_k),
+                                   (T["v_cache"], v_before, T["v_new"], slot_major_v)):
+        if after is None:
+            continue
+        A, B = fn(after), fn(before)
+        changed = torch.nonzero((A != B).any(dim=1)).flatten().cpu().numpy()
+        assert set(changed.tolist()) <= set(slots_ref.tolist()), f"{w.name}: append touched other slots"
+        newbits = new.reshape(new.shape[0], -1).view(A.dtype)
+        assert torch.equal(A[sl], newbits), f"{w.name}: appended rows differ"
+    del A, B
+    Tp, Pmax = step.partition_tokens, step.max_partitions
+    for b in sample_seqs:
+        L = int(w.context_lens[b])
+        ids = np.unique(w.block_table[b][w.block_table[b] >= 0])
+        remap = {int(x): i for i, x in enumerate(ids)}
+        bt_b = np.vectorize(lambda x: remap.get(int(x), -1))(w.block_table[b:b + 1])
+        idx = torch.from_numpy(ids).to(dev)
+        kc = to_np(k_before.index_select(0, idx))
+        vc = None if v_before is None else to_np(v_before.index_select(0, idx))
+        kn = to_np(T["k_new"][b:b + 1])
+        vn = None if T["v_new"] is None else to_np(T["v_new"][b:b + 1])
+        qb = to_np(T["q"][b:b + 1])
+        ref = pa.decode_step(qb, kn, vn, kc, vc, bt_b.astype(np.int32), w.context_lens[b:b + 1],
+                             w.n_shards, w.interleave, bs, Tp, Pmax, w.scale_f32, w.dv)
+        # the gather of each shard, bit for bit
+        for r in range(w.n_shards):
+            Lr = P.pa_shard_length(L, w.n_shards, w.interleave, r)
+            kg = torch.empty(max(Lr, 1), w.n_kv_heads, w.dk, dtype=T["q"].dtype, device=dev)
+            vg = torch.empty(max(Lr, 1), w.n_kv_heads, w.dv, dtype=T["q"].dtype, device=dev)
+            P.pa_gather_kv(T["k_cache"], T["v_cache"], T["block_table"], b, r, L, w.n_shards,
+                           w.interleave, kg, vg, step.err_flag)
+            kr, vr = pa.gather_shard(ref["k_cache"], ref["v_cache"], bt_b[0], L, r, w.n_shards,
+                                     w.interleave, bs, w.dv)
+            assert bits_equal(to_np(kg)[:Lr], kr) and bits_equal(to_np(vg)[:Lr], vr), \
+                f"{w.name}: gather seq {b} shard {r}"
+        compare_outputs(f"{w.name} seq {b} partials", w.dtype, to_np(step.part_out[b:b + 1]),
+                        to_np(step.part_lse[b:b + 1]), ref["part_o"], ref["part_lse"], rel_l2)
+        compare_outputs(f"{w.name} seq {b} merged", w.dtype, to_np(step.out[b:b + 1]),
+                        to_np(step.lse[b:b + 1]), ref["o"], ref["lse"], rel_l2)
+    torch.cuda.synchronize()
+    assert int(step.err_flag.item()) == 0
+    return step

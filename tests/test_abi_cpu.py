@@ -1,0 +1,90 @@
+"""The C-ABI library on the CPU: it loads, exports every entry point that
+include/pa.h declares, its host helpers compute the placement closed forms, and
+argument errors are reported without launching anything (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from conftest import ROOT
+
+pytest.importorskip("torch")
+P = pytest.importorskip("decode_attention_paged_kv_amd")
+from oracle import paged_attention as pa  # noqa: E402
+
+
+def declared_functions():
+    names = []
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names += re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(pa_\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert {"pa_kv_append", "pa_decode", "pa_merge_lse", "pa_slot_mapping", "pa_gather_kv"} <= set(names)
+    lib = ctypes.CDLL(P.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+@pytest.mark.parametrize("L,S,I", [(0, 1, 1), (1, 4, 16), (67, 4, 1), (67, 4, 16), (200000, 4, 1),
+                                   (200000, 4, 16), (1000, 3, 7), (5, 4, 16), (123457, 5, 3)])
+def test_shard_length_matches_oracle(L, S, I):
+    got = [P.pa_shard_length(L, S, I, r) for r in range(S)]
+    assert got == list(pa.shard_lengths(L, S, I))
+    for T in (1, 16, 1024):
+        assert P.pa_max_partitions(L, S, I, T) == pa.max_partitions(L, S, I, T)
+
+
+def test_host_helpers_reject_bad_arguments():
+    assert P.pa_shard_length(10, 0, 1, 0) == -1
+    assert P.pa_shard_length(10, 2, 0, 0) == -1
+    assert P.pa_shard_length(10, 2, 1, 2) == -1
+    assert P.pa_max_partitions(10, 1, 1, 0) == -1
+    T = P.pa_default_partition_tokens(8, 8, 200000, 1, 1, 16)
+    assert T > 0 and T % 16 == 0
+    assert P.pa_default_partition_tokens(1, 8, 200000, 4, 16, 64) % 64 == 0
+
+
+def _call_decode(**over):
+    args = dict(q=1, k=1, v=1, bt=1, lens=1, n=1, hq=4, hkv=1, dk=64, dv=64, bs=4, nb=64, mb=17,
+                S=1, I=1, T=4, P=17, scale=0.125, dt=0, po=1, pl=1)
+    args.update(over)
+    a = args
+    vp = lambda x: None if x is None else ctypes.c_void_p(0x1000)  # never dereferenced: rejected first
+    return P.lib.pa_decode(vp(a["q"]), vp(a["k"]), vp(a["v"]), vp(a["bt"]), vp(a["lens"]), a["n"],
+                           a["hq"], a["hkv"], a["dk"], a["dv"], a["bs"], a["nb"], a["mb"], a["S"],
+                           a["I"], a["T"], a["P"], a["scale"], a["dt"], vp(a["po"]), vp(a["pl"]),
+                           None, None)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(q=None), -1), (dict(po=None), -1), (dict(dt=7), -3), (dict(hq=6, hkv=4), -2),
+    (dict(dk=577), -3), (dict(dv=513), -3), (dict(v=None, dv=65), -2), (dict(bs=0), -3),
+    (dict(bs=257), -3), (dict(S=0), -2), (dict(I=0), -2), (dict(T=6), -2), (dict(T=0), -2),
+    (dict(P=0), -4), (dict(n=-1), -2), (dict(mb=0), -2),
+])
+def test_decode_rejects_bad_arguments_without_launch(over, status):
+    assert _call_decode(**over) == status
+    assert P.lib.pa_last_error().decode() != ""
+
+
+def test_other_entry_points_reject_bad_arguments():
+    vp = ctypes.c_void_p(0x1000)
+    assert P.lib.pa_kv_append(None, None, vp, None, vp, 1, 1, 64, 64, 4, 64, 0, None, None) == -1
+    assert P.lib.pa_kv_append(vp, vp, vp, None, vp, 1, 1, 64, 64, 4, 64, 0, None, None) == -1
+    assert P.lib.pa_kv_append(vp, None, vp, None, vp, 1, 1, 64, 64, 4, 64, 5, None, None) == -3
+    assert P.lib.pa_merge_lse(None, vp, 1, 1, 1, 64, vp, 0, None, None) == -1
+    assert P.lib.pa_merge_lse(vp, vp, 1, 0, 1, 64, vp, 0, None, None) == -2
+    assert P.lib.pa_merge_lse(vp, vp, 1, 1, 1, 1024, vp, 0, None, None) == -3
+    assert P.lib.pa_slot_mapping(vp, vp, 1, 0, 1, 4, 17, 64, vp, None, None) == -2
+    assert P.lib.pa_gather_kv(vp, vp, vp, 0, 4, 67, 1, 64, 64, 4, 64, 17, 4, 1, 0, vp, vp, None, None) == -2
+    # zero-size work is accepted and launches nothing
+    assert P.lib.pa_kv_append(vp, vp, vp, vp, vp, 0, 1, 64, 64, 4, 64, 0, None, None) == 0
+    assert _call_decode(n=0) == 0

@@ -1,0 +1,206 @@
+"""HIP library vs the fp64 oracle on the GPU (parity proper).
+
+Small workloads are compared whole: routing, append and gather bit for bit,
+every partition's output and LSE, and the merged result.  The full-size
+workloads run at their real sizes with the partition size the benchmark uses
+and are compared on sampled sequences (see ``gpu_harness.check_large``)."""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from gpu_harness import check_large, check_small, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import decode_attention_paged_kv_amd  # noqa: F401  (fails loudly if the library is missing)
+
+
+# ------------------------------------------------------------------ the named workloads
+@pytest.mark.parametrize("L", [67, 68])
+def test_tiny(L):
+    """1 sequence, 4/1 heads, head 64, fp32, 4-token blocks, 64-block pool (context
+    counted with and without an extra token, so both readings are covered)."""
+    check_small(wl.tiny(context_len=L))
+
+
+def test_tiny_single_partition_and_sharded():
+    w = wl.tiny()
+    check_small(w, partition_tokens=68)
+    for I in (1, 16):
+        check_small(wl.small(f"tiny_S4_I{I}", [67], 4, 1, 64, 64, 4, wl.F32, n_shards=4,
+                             interleave=I, partition_tokens=8, scale=0.125, seed=1))
+
+
+def test_batch():
+    """Continuous-batching step: 64 ragged sequences, 32/8 heads, head 128, bf16."""
+    check_small(wl.batch())
+
+
+def test_long():
+    """8 sequences, log-normal lengths around 142K, 4,096-token partitions."""
+    w = wl.long()
+    order = np.argsort(w.context_lens)
+    check_large(w, [int(order[0]), int(order[-1])])
+
+
+@pytest.mark.parametrize("I", [1, 16])
+def test_dcp(I):
+    """One 200,000-token sequence in 4 interleaved shards."""
+    check_large(wl.dcp(interleave=I), [0])
+
+
+def test_latent():
+    """128 query heads on one 576-wide latent head, shared 2,048-token prefixes."""
+    w = wl.latent()
+    order = np.argsort(w.context_lens)
+    check_large(w, [int(order[0]), int(order[-1])], rel_l2=LATENT_REL_L2)
+
+
+LATENT_REL_L2 = 4e-3
+
+
+# ------------------------------------------------------------------ exact probes at full size
+@pytest.mark.parametrize("make", [lambda: wl.dcp(interleave=16), lambda: wl.long()])
+def test_mean_probe_full_size(make):
+    """q = 0: every weight is exactly 1/L, values are small integers, so the output
+    is the exact mean of each sequence's values -- any dropped, repeated or
+    misaddressed token moves it."""
+    w = make()
+    check_large(w, [int(np.argmax(w.context_lens))], fill="mean_probe")
+
+
+# ------------------------------------------------------------------ shapes and edge cases
+SWEEP = [
+    # name, lens, hq, hkv, dk, dv, bs, dtype, S, I, T, latent, prefix(group, tokens)
+    ("gqa128_ragged", [1, 15, 16, 17, 300, 1000], 32, 8, 128, 128, 16, wl.BF16, 1, 1, 256, False, None),
+    ("gqa128_f32", [1, 33, 250], 32, 8, 128, 128, 16, wl.F32, 1, 1, 64, False, None),
+    ("dcp_small_I1", [1, 5, 63, 64, 65, 700], 64, 8, 128, 128, 16, wl.BF16, 4, 1, 32, False, None),
+    ("dcp_small_I16", [1, 5, 63, 64, 65, 700], 64, 8, 128, 128, 16, wl.BF16, 4, 16, 32, False, None),
+    ("mha64", [3, 40, 129], 8, 8, 64, 64, 16, wl.BF16, 1, 1, 32, False, None),
+    ("g8_d64", [70, 513], 64, 8, 64, 64, 16, wl.BF16, 1, 1, 128, False, None),
+    ("bs1", [1, 2, 9], 4, 2, 32, 32, 1, wl.F32, 2, 3, 4, False, None),
+    ("bs256", [1, 255, 256, 257, 900], 8, 2, 64, 64, 256, wl.BF16, 1, 1, 256, False, None),
+    ("odd_dims", [7, 30], 6, 3, 40, 24, 8, wl.BF16, 3, 2, 8, False, None),
+    ("empty_seqs", [0, 1, 0, 20], 8, 4, 64, 64, 16, wl.BF16, 2, 16, 16, False, None),
+    ("latent_small", [129, 200, 700, 1500], 128, 1, 576, 512, 64, wl.BF16, 1, 1, 256, True, (4, 128)),
+    ("latent_f32", [65, 300], 16, 1, 576, 512, 64, wl.F32, 1, 1, 128, True, None),
+]
+
+
+@pytest.mark.parametrize("case", SWEEP, ids=[c[0] for c in SWEEP])
+def test_sweep(case):
+    name, lens, hq, hkv, dk, dv, bs, dt, S, I, T, latent, prefix = case
+    pg, pt = prefix or (1, 0)
+    w = wl.small(name, lens, hq, hkv, dk, dv, bs, dt, n_shards=S, interleave=I,
+                 partition_tokens=T, latent=latent, prefix_group=pg, prefix_tokens=pt, seed=zlib.crc32(name.encode()) % 1000)
+    check_small(w, rel_l2=LATENT_REL_L2 if (latent and hq >= 16 and dt == wl.BF16) else 1e-4)
+
+
+def test_partition_size_independence():
+    """Different partition sizes give the same merged result (within tolerance)."""
+    w = wl.small("tsz", [1000, 77], 32, 8, 128, 128, 16, wl.BF16, partition_tokens=16, seed=5)
+    a, _ = check_small(w, partition_tokens=16)
+    b, _ = check_small(w, partition_tokens=1024)
+    d = (a.out - b.out).abs().max().item()
+    say(f"  partition 16 vs 1024: max|do|={d:.3g}")
+    assert d < 1e-5
+
+
+def test_deterministic_and_placement_invariant():
+    """Two runs give bitwise identical results, and so do two different physical
+    placements of the same logical content."""
+    import decode_attention_paged_kv_amd as P
+
+    outs = []
+    for seed in (7, 8):
+        w = wl.small("perm", [300, 41], 32, 8, 128, 128, 16, wl.BF16, partition_tokens=64, seed=seed)
+        T = wl.make_tensors(w, "cuda", seed=0)
+        # rewrite the pools so token i of sequence b holds the same rows in both placements
+        g = torch.Generator(device="cuda").manual_seed(123)
+        Kl = torch.randn(2, 300, 8, 128, generator=g, device="cuda").to(torch.bfloat16)
+        Vl = torch.randn(2, 300, 8, 128, generator=g, device="cuda").to(torch.bfloat16)
+        tid = torch.from_numpy(w.token_id).cuda()
+        own = torch.full_like(tid, -1)
+        for b in range(2):
+            for phys in w.block_table[b, 0]:
+                if phys >= 0:
+                    own[int(phys)] = b
+        live = torch.from_numpy(w.live).cuda() & (own >= 0)
+        pos = live.nonzero()
+        bsel, i = own[pos[:, 0], pos[:, 1]], tid[pos[:, 0], pos[:, 1]]
+        T["k_cache"][pos[:, 0], :, pos[:, 1], :] = Kl[bsel, i]
+        T["v_cache"][pos[:, 0], :, :, pos[:, 1]] = Vl[bsel, i]
+        Ls = torch.tensor([300, 41], device="cuda") - 1
+        T["k_new"].copy_(Kl[torch.arange(2, device="cuda"), Ls])
+        T["v_new"].copy_(Vl[torch.arange(2, device="cuda"), Ls])
+        T["q"].copy_(torch.randn(2, 32, 128, generator=g, device="cuda").to(torch.bfloat16))
+        runs = []
+        for _ in range(2):
+            step = P.DecodeStep(2, 32, 8, 128, 128, 16, 300, partition_tokens=64, device="cuda")
+            out, lse = step(T["q"], T["k_new"], T["v_new"], T["k_cache"], T["v_cache"],
+                            T["block_table"], T["context_lens"])
+            torch.cuda.synchronize()
+            runs.append((out.clone(), lse.clone()))
+        assert torch.equal(runs[0][0], runs[1][0]) and torch.equal(runs[0][1], runs[1][1])
+        outs.append(runs[0])
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
+def test_bf16_output():
+    """bf16 output: within half an ulp of bf16 plus the bf16 tolerance."""
+    import decode_attention_paged_kv_amd as P
+    from gpu_harness import to_np
+    from oracle import paged_attention as pa
+
+    w = wl.batch()
+    Tc = wl.make_tensors(w, "cpu")
+    T = {k: (None if v is None else v.cuda()) for k, v in Tc.items()}
+    H = {k: to_np(v) for k, v in Tc.items()}
+    step = P.DecodeStep(w.n_seqs, 32, 8, 128, 128, 16, int(w.context_lens.max()), device="cuda",
+                        out_dtype=torch.bfloat16)
+    out, lse = step(T["q"], T["k_new"], T["v_new"], T["k_cache"], T["v_cache"], T["block_table"],
+                    T["context_lens"])
+    ref = pa.decode_step(H["q"], H["k_new"], H["v_new"], H["k_cache"], H["v_cache"], w.block_table,
+                         w.context_lens, 1, 1, 16, step.partition_tokens, step.max_partitions,
+                         w.scale_f32, 128)
+    o = pa.widen(to_np(out))
+    half_ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(ref["o"]), 1e-30))) - 8)
+    assert np.all(np.abs(o - ref["o"]) <= half_ulp + 5e-3)
+
+
+def test_error_flag_on_bad_block_id():
+    """A block id outside the pool is skipped and reported in the error flag; the
+    kernels still finish normally (the bound check is the kernels' own)."""
+    import decode_attention_paged_kv_amd as P
+
+    w = wl.small("bad", [40, 40], 8, 2, 64, 64, 16, wl.BF16, partition_tokens=16, seed=9)
+    T = wl.make_tensors(w, "cuda")
+    T["block_table"][1, 0, 1] = w.n_blocks + 5
+    step = P.DecodeStep(2, 8, 2, 64, 64, 16, 40, partition_tokens=16, device="cuda")
+    step(T["q"], T["k_new"], T["v_new"], T["k_cache"], T["v_cache"], T["block_table"],
+         T["context_lens"])
+    torch.cuda.synchronize()
+    assert int(step.err_flag.item()) & P.ERR_BLOCK_ID
+    assert torch.isfinite(step.out[0]).all()
+
+
+def test_error_flag_on_short_table():
+    """A context longer than the block table holds is reported, not read."""
+    import decode_attention_paged_kv_amd as P
+
+    w = wl.small("short", [40], 8, 2, 64, 64, 16, wl.BF16, partition_tokens=16, seed=9)
+    T = wl.make_tensors(w, "cuda")
+    lens = torch.tensor([90], dtype=torch.int32, device="cuda")      # table holds 48 tokens
+    step = P.DecodeStep(1, 8, 2, 64, 64, 16, 96, partition_tokens=16, device="cuda")
+    P.pa_decode(T["q"], T["k_cache"], T["v_cache"], T["block_table"], lens, 1, 1, 16,
+                step.max_partitions, step.scale, step.part_out, step.part_lse, err_flag=step.err_flag)
+    torch.cuda.synchronize()
+    assert int(step.err_flag.item()) & P.ERR_CAPACITY

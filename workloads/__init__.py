@@ -98,7 +98,7 @@ def plan(w: Workload) -> Workload:
     N, S, I, bs = w.n_seqs, w.n_shards, w.interleave, w.block_size
     counts = [_split_counts(int(L), S, I) for L in w.context_lens]
     nblk = [[-(-int(c) // bs) for c in cs] for cs in counts]
-    maxblk = max(max(r) for r in nblk)
+    maxblk = max(1, max(max(r) for r in nblk))
     shared_blocks = w.prefix_tokens // bs
     if w.prefix_tokens:
         # the shared prefix is whole blocks and every sequence appends after it,
@@ -139,12 +139,15 @@ def plan(w: Workload) -> Workload:
             phys = bt[b, r, loc // bs].astype(np.int64)
             live[phys, loc % bs] = True
             tok[phys, loc % bs] = mine
+        if L == 0:                      # an empty sequence appends nothing
+            new_slot[b] = -1
+            continue
         r_new = ((L - 1) // I) % S
         loc_new = int(counts[b][r_new]) - 1
         phys_new = int(bt[b, r_new, loc_new // bs])
         new_slot[b] = phys_new * bs + loc_new % bs
     # the appended token's slot holds nothing until kv_append writes it
-    for s in new_slot:
+    for s in new_slot[new_slot >= 0]:
         live[s // bs, s % bs] = False
     w.block_table, w.live, w.token_id, w.new_slot = bt, live, tok, new_slot
     return w
@@ -258,7 +261,7 @@ def make_tensors(w: Workload, device="cpu", fill: str = "normal", seed: int | No
             k_cache[..., :dv] = val[:, None, :, :].expand(NB, Hkv, bs, dv)
         else:
             v_cache.copy_(val.transpose(1, 2)[:, None, :, :].expand(NB, Hkv, dv, bs))
-        Lm1 = torch.from_numpy(w.context_lens.astype(np.int64) - 1).to(dev)
+        Lm1 = torch.from_numpy(np.maximum(w.context_lens.astype(np.int64) - 1, 0)).to(dev)
         newv = ((31 * Lm1[:, None] + j[None, :]) % 16).to(dt)         # [N][dv]
         if w.latent:
             k_new[..., :dv] = newv[:, None, :]
