@@ -158,7 +158,7 @@ def cpu_baseline(w, T, budget_s=12.0):
                       f"step in the fp64 NumPy oracle), {elapsed:.2f} s"}
 
 
-def run_config(name, steps, warmup, with_cpu):
+def run_config(name, steps, warmup, with_cpu, partition_tokens=0):
     import numpy as np
     import torch
 
@@ -166,6 +166,8 @@ def run_config(name, steps, warmup, with_cpu):
     import workloads as wl
 
     w = make_workload(name)
+    if partition_tokens:
+        w.partition_tokens = partition_tokens
     dev = torch.device("cuda", 0)
     T = wl.make_tensors(w, dev)
     step = P.DecodeStep(w.n_seqs, w.n_q_heads, w.n_kv_heads, w.dk, w.dv, w.block_size,
@@ -188,6 +190,28 @@ def run_config(name, steps, warmup, with_cpu):
     return res
 
 
+def calibrate_copy(steps, nbytes=2 << 30):
+    """A plain copy kernel of known size: reads and writes ``nbytes`` per launch.
+    Its rocprofv3 FETCH_SIZE / WRITE_SIZE against ``nbytes`` give the counters'
+    scale for the HBM traffic of the decode kernel."""
+    import torch
+
+    src = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda").normal_()
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        dst.copy_(src)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    return {"kernel": "copy", "bytes_read_per_launch": nbytes, "bytes_written_per_launch": nbytes,
+            "ms": round(ms, 5), "GBs_read_plus_write": round(2 * nbytes / (ms * 1e-3) / 1e9, 1)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -197,13 +221,20 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--secondary", action="store_true",
                     help="also time the other workloads (reported under 'secondary')")
+    ap.add_argument("--partition-tokens", type=int, default=0,
+                    help="override the workload's partition size (tokens)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="time a plain 2 GiB device-to-device copy (reference for HBM counters)")
     a = ap.parse_args()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only (DCP shards are emulated as "
               "partitions on a single device); use --gpus 1", file=sys.stderr)
         sys.exit(2)
 
-    r = run_config(a.config, a.steps, a.warmup, not a.no_cpu_baseline)
+    if a.calibrate_copy:
+        print(json.dumps(calibrate_copy(a.steps)), flush=True)
+        return
+    r = run_config(a.config, a.steps, a.warmup, not a.no_cpu_baseline, a.partition_tokens)
     w = r["w"]
     traffic = measured_traffic(a.config, r["kv_bytes"])
     line = {

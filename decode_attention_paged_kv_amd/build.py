@@ -37,12 +37,15 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
 
 
-def build(verbose: bool = False, jobs: int = 8, extra_flags=()) -> str:
+def build(verbose: bool = False, jobs: int = 8, extra_flags=(), out: str = LIB,
+          build_dir: str = BUILD) -> str:
+    """Compile and link; ``extra_flags`` go to every hipcc compile, ``out`` is the
+    library path."""
     hipcc = _hipcc()
-    os.makedirs(BUILD, exist_ok=True)
+    os.makedirs(build_dir, exist_ok=True)
 
     def compile_one(src):
-        obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+        obj = os.path.join(build_dir, os.path.basename(src) + ".o")
         cmd = [hipcc, "-x", "hip", "-c", src, "-o", obj, *HIPFLAGS, *extra_flags]
         if verbose:
             print(" ".join(cmd), flush=True)
@@ -53,15 +56,15 @@ def build(verbose: bool = False, jobs: int = 8, extra_flags=()) -> str:
 
     with ThreadPoolExecutor(max_workers=jobs) as ex:
         objs = list(ex.map(compile_one, sources()))
-    tmp = LIB + ".tmp"
+    tmp = out + ".tmp"
     cmd = [hipcc, "-shared", f"--offload-arch={ARCH}", "-fPIC", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     p = subprocess.run(cmd, capture_output=True, text=True)
     if p.returncode != 0:
         raise RuntimeError(f"link failed:\n{p.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -1,0 +1,346 @@
+// decode_gqa.hip -- paged decode attention on the matrix cores for bf16 GQA/MHA heads
+// (head size 64 or 128, block size a multiple of 16, up to 16 query heads per KV head
+// per workgroup).
+//
+// What is computed is the same as in decode_generic.hip: for each partition of a shard's
+// local tokens, o = softmax(scale * q.K) V and lse = ln sum exp(scale * q.k), keys and
+// values read through the block table (PagedAttention page, ai-compass.weeybrid.co.jp,
+// block-table section), outputs and LSEs per partition for the merge (DCP page,
+// soroban.highreso.jp, DCP mechanism section).
+//
+// How it maps onto gfx950:
+//  * One workgroup = one (partition, sequence x shard, KV head, group of <= 16 query
+//    heads); its NW waves split the partition's 16-token sub-tiles into contiguous
+//    ranges and merge their (max, sum, output) through LDS at the end.  Each K/V byte
+//    is read by exactly one wave, so K/V go straight from HBM into registers (no LDS
+//    staging: there is no reuse to stage for).
+//  * Scores S^T[token][head] = K (16 x D) . Q^T (D x 16) on v_mfma_f32_16x16x32_bf16:
+//    lane (row = lane % 16, group = lane / 16) supplies 8 consecutive head-dim values
+//    of key row `row` -- one 16-byte load per MFMA -- and the result leaves scores of
+//    tokens 4*group .. 4*group+3 for head lane % 16 in each lane.
+//  * Output O^T[d][head] += V^T (16 x 32 tokens) . P^T (32 tokens x 16 heads) on the
+//    same instruction.  The value cache stores each block as [d][token], so a lane's
+//    operand (4 tokens of one d row, per 16-token sub-tile) is one 8-byte load, and the
+//    weights P^T a lane needs are exactly the scores it already holds: no shuffles.
+//  * The softmax weights enter P.V as two bf16 terms, hi = bf16(p) and
+//    lo = bf16(p - hi), so they keep ~16 significant bits; K, V and q are used exactly.
+//  * Online softmax in base 2: scores stay raw, p = exp2(s*c - m*c) with
+//    c = scale * log2(e); the running max is shared by the four lanes of a head with two
+//    cross-lane exchanges per 32 tokens; each lane keeps its own partial sum until the
+//    end.  The output is rescaled only when some running max moved.
+//  * Masked tokens (past the partition end) take score -inf by select and their value
+//    entries are zeroed by select, so unused cache slots (whatever they hold) never
+//    reach the sums.
+//  * Block ids: each wave loads 64 consecutive block-table entries with one vector load
+//    and reads them back one at a time with readlane.  Loads of the next 32 tokens are
+//    issued before the current 32 are processed (two register buffers).
+#include <math.h>
+
+#include "pa_common.h"
+#include "pa_launch.h"
+
+namespace pa {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef float f32x4_t __attribute__((__vector_size__(4 * sizeof(float))));
+typedef uint32_t u32x4_t __attribute__((__vector_size__(4 * sizeof(uint32_t))));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ inline f32x4_t mfma16x16x32(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ inline float xor_max(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16));
+  return fmaxf(v, __shfl_xor(v, 32));
+}
+
+__device__ inline float xor_sum(float v) {
+  v += __shfl_xor(v, 16);
+  return v + __shfl_xor(v, 32);
+}
+
+// Keep the bf16 halves of a 32-bit word whose tokens are valid.
+__device__ inline uint32_t keep(uint32_t w, bool lo_ok, bool hi_ok) {
+  return w & ((lo_ok ? 0x0000ffffu : 0u) | (hi_ok ? 0xffff0000u : 0u));
+}
+
+template <int D>
+struct Tile {
+  static constexpr int KJ = D / 32;  // score MFMAs per sub-tile
+  static constexpr int NT = D / 16;  // output tiles of 16 d rows
+  bf16x8_t k[2][KJ];
+  uint2 v[2][NT];
+  int tok0[2];  // local token of the first row of each sub-tile (-1: no sub-tile)
+};
+
+template <int D, int NW, bool PREFETCH>
+__global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeArgs a) {
+  using TileT = Tile<D>;
+  constexpr int KJ = TileT::KJ;
+  constexpr int NT = TileT::NT;
+  const uint16_t* __restrict__ q = static_cast<const uint16_t*>(a.q);
+  const uint16_t* __restrict__ kc = static_cast<const uint16_t*>(a.k_cache);
+  const uint16_t* __restrict__ vc = static_cast<const uint16_t*>(a.v_cache);
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int col = lane & 15;   // key row (A operand) / head (B operand, results)
+  const int grp = lane >> 4;   // k-slot group
+  const int p = blockIdx.x;
+  const int b = blockIdx.y / a.n_shards;
+  const int r = blockIdx.y % a.n_shards;
+  const int g = a.hq / a.hkv;
+  const int chunks = (g + 15) >> 4;
+  const int kvh = blockIdx.z / chunks;
+  const int chunk = blockIdx.z % chunks;
+  const int h0 = kvh * g + chunk * 16;
+  const int nh = min(16, g - chunk * 16);
+  const int bs = a.bs;
+
+  const int L = a.context_lens[b];
+  const int Lr = L > 0 ? shard_len(L, a.n_shards, a.interleave, r) : 0;
+  const int T = a.part_tokens;
+  if (p == 0 && threadIdx.x == 0 && (Lr + T - 1) / T > a.max_parts) raise_flag(a.flag, kErrCapacity);
+  const int t_begin = p * T;
+  const int t_end = min(t_begin + T, Lr);
+  const int64_t out_row = ((int64_t(b) * a.n_shards + r) * a.max_parts + p) * a.hq + h0;
+  if (t_begin >= t_end) {
+    for (int i = threadIdx.x; i < nh * D; i += 64 * NW) a.part_out[out_row * D + i] = 0.f;
+    if (threadIdx.x < nh) a.part_lse[out_row + threadIdx.x] = -INFINITY;
+    return;
+  }
+
+  // query operand: lane (head col, group grp) holds q[h0+col][32j + 8grp .. +7]
+  bf16x8_t qop[KJ];
+  {
+    const uint16_t* qrow = q + (int64_t(b) * a.hq + h0 + col) * D + 8 * grp;
+#pragma unroll
+    for (int j = 0; j < KJ; ++j) {
+      if (col < nh)
+        qop[j] = *reinterpret_cast<const bf16x8_t*>(qrow + 32 * j);
+      else
+        qop[j] = bf16x8_t{};
+    }
+  }
+
+  // this wave's contiguous range of 32-token steps
+  const int u0 = t_begin >> 4;                   // first sub-tile (T and bs are multiples of 16)
+  const int n_u = (t_end - t_begin + 15) >> 4;   // sub-tiles in the partition
+  const int n_steps = (n_u + 1) >> 1;
+  const int per = n_steps / NW, extra = n_steps % NW;
+  const int s_lo = wave * per + min(wave, extra);
+  const int s_hi = s_lo + per + (wave < extra ? 1 : 0);
+
+  const int spb = bs >> 4;  // sub-tiles per block
+  const int32_t* row = a.block_table + (int64_t(b) * a.n_shards + r) * a.max_blocks;
+  const int64_t kv_stride = int64_t(bs) * D;     // elements per (block, kv head)
+  int tbl_base = -(1 << 30);
+  int tbl = -1;
+
+  auto block_of = [&](int e) -> int {            // e: logical block entry (wave-uniform)
+    if (e - tbl_base >= 64 || e < tbl_base) {
+      tbl_base = e;
+      const int ee = e + lane;
+      int v = -1;
+      if (ee < a.max_blocks) {
+        v = row[ee];
+        if (v < 0 || v >= a.n_blocks) v = -2;    // invalid id: reported when used
+      } else {
+        v = -3;                                  // beyond the table row
+      }
+      tbl = v;
+    }
+    return __builtin_amdgcn_readlane(tbl, e - tbl_base);
+  };
+
+  auto load = [&](TileT& tl, int s) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int u_rel = 2 * s + t;
+      tl.tok0[t] = -1;
+      if (u_rel < n_u) {
+        const int u = u0 + u_rel;
+        const int e = u / spb;
+        const int phys = block_of(e);
+        if (phys >= 0) {
+          tl.tok0[t] = u << 4;
+          const int64_t base = (int64_t(phys) * a.hkv + kvh) * kv_stride;
+          const int sub = (u - e * spb) << 4;
+          const uint16_t* kp = kc + base + int64_t(sub + col) * D + 8 * grp;
+#pragma unroll
+          for (int j = 0; j < KJ; ++j) tl.k[t][j] = *reinterpret_cast<const bf16x8_t*>(kp + 32 * j);
+          const uint16_t* vp = vc + base + int64_t(col) * bs + sub + 4 * grp;
+#pragma unroll
+          for (int n = 0; n < NT; ++n)
+            tl.v[t][n] = *reinterpret_cast<const uint2*>(vp + int64_t(16 * n) * bs);
+        } else if (lane == 0) {
+          raise_flag(a.flag, phys == -3 ? kErrCapacity : kErrBlockId);
+        }
+      }
+    }
+  };
+
+  const float c = a.scale * kLog2e;
+  float m = -INFINITY;  // running max of raw scores, head col
+  float lsum = 0.f;     // this lane's partial sum of weights
+  f32x4_t o[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) o[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](const TileT& tl) {
+    float sc[2][4];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+      if (tl.tok0[t] >= 0) {
+#pragma unroll
+        for (int j = 0; j < KJ; ++j) acc = mfma16x16x32(tl.k[t][j], qop[j], acc);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tok = tl.tok0[t] + 4 * grp + i;
+        const bool ok = tl.tok0[t] >= 0 && tok < t_end;
+        sc[t][i] = ok ? acc[i] : -INFINITY;
+      }
+    }
+    float mt = m;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mt = fmaxf(mt, sc[t][i]);
+    mt = xor_max(mt);
+    const float alpha = (mt == -INFINITY) ? 1.f : exp2f((m - mt) * c);
+    m = mt;
+    const float mc = mt * c;
+    float pv[2][4];
+    float psum = 0.f;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pv[t][i] = exp2f(fmaf(sc[t][i], c, -mc));
+        psum += pv[t][i];
+      }
+    lsum = fmaf(lsum, alpha, psum);
+    if (__any(alpha != 1.f)) {
+#pragma unroll
+      for (int n = 0; n < NT; ++n) o[n] *= alpha;
+    }
+    bf16x8_t phi, plo;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const __bf16 h = (__bf16)pv[t][i];
+        phi[4 * t + i] = h;
+        plo[4 * t + i] = (__bf16)(pv[t][i] - (float)h);
+      }
+    // value operand; tokens that are masked (or sub-tiles not loaded) contribute zeros
+    bool ok[2][4];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ok[t][i] = tl.tok0[t] >= 0 && tl.tok0[t] + 4 * grp + i < t_end;
+    const bool full = ok[0][0] && ok[0][3] && ok[1][0] && ok[1][3];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      uint2 va = tl.v[0][n], vb = tl.v[1][n];
+      if (!__all(full)) {
+        va.x = keep(va.x, ok[0][0], ok[0][1]);
+        va.y = keep(va.y, ok[0][2], ok[0][3]);
+        vb.x = keep(vb.x, ok[1][0], ok[1][1]);
+        vb.y = keep(vb.y, ok[1][2], ok[1][3]);
+      }
+      const u32x4_t w = {va.x, va.y, vb.x, vb.y};
+      const bf16x8_t vop = __builtin_bit_cast(bf16x8_t, w);
+      o[n] = mfma16x16x32(vop, phi, o[n]);
+      o[n] = mfma16x16x32(vop, plo, o[n]);
+    }
+  };
+
+  if (PREFETCH) {
+    if (s_lo < s_hi) {
+      TileT A, B;
+      load(A, s_lo);
+      int s = s_lo;
+      while (true) {
+        if (s + 1 < s_hi) load(B, s + 1);
+        compute(A);
+        if (++s >= s_hi) break;
+        if (s + 1 < s_hi) load(A, s + 1);
+        compute(B);
+        if (++s >= s_hi) break;
+      }
+    }
+  } else {
+    for (int s = s_lo; s < s_hi; ++s) {
+      TileT A;
+      load(A, s);
+      compute(A);
+    }
+  }
+
+  // ---- merge the waves' partial results through LDS
+  __shared__ float m_s[NW][16];
+  __shared__ float l_s[NW][16];
+  __shared__ float o_s[NW][D][17];
+  const float lt = xor_sum(lsum);
+  if (grp == 0) {
+    m_s[wave][col] = m;
+    l_s[wave][col] = lt;
+  }
+#pragma unroll
+  for (int n = 0; n < NT; ++n)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o_s[wave][16 * n + 4 * grp + i][col] = o[n][i];
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < nh * D; idx += 64 * NW) {
+    const int hh = idx / D, d = idx % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w2 = 0; w2 < NW; ++w2) M = fmaxf(M, m_s[w2][hh]);
+    float Ls = 0.f, acc = 0.f;
+#pragma unroll
+    for (int w2 = 0; w2 < NW; ++w2) {
+      const float mw = m_s[w2][hh];
+      const float f = (mw == -INFINITY) ? 0.f : exp2f((mw - M) * c);
+      Ls = fmaf(f, l_s[w2][hh], Ls);
+      acc = fmaf(f, o_s[w2][d][hh], acc);
+    }
+    a.part_out[(out_row + hh) * D + d] = acc / Ls;
+    if (d == 0) a.part_lse[out_row + hh] = (M * c + log2f(Ls)) * kLn2;
+  }
+}
+
+}  // namespace
+
+bool gqa_supported(const DecodeArgs& a) {
+  return a.dtype == kBF16 && a.v_cache != nullptr && a.dk == a.dv && (a.dk == 64 || a.dk == 128) &&
+         a.bs % 16 == 0;
+}
+
+#ifndef PA_GQA_WAVES
+#define PA_GQA_WAVES 4
+#endif
+#ifndef PA_GQA_PREFETCH
+#define PA_GQA_PREFETCH 1
+#endif
+
+hipError_t launch_decode_gqa(const DecodeArgs& a, hipStream_t st) {
+  const int g = a.hq / a.hkv;
+  const int chunks = (g + 15) / 16;
+  const dim3 grid(a.max_parts, a.n_seqs * a.n_shards, a.hkv * chunks);
+  constexpr int NW = PA_GQA_WAVES;
+  constexpr bool PF = PA_GQA_PREFETCH != 0;
+  if (a.dk == 128)
+    hipLaunchKernelGGL((decode_gqa_kernel<128, NW, PF>), grid, dim3(64 * NW), 0, st, a);
+  else
+    hipLaunchKernelGGL((decode_gqa_kernel<64, NW, PF>), grid, dim3(64 * NW), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace pa

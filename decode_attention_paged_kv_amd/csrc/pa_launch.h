@@ -34,6 +34,10 @@ hipError_t launch_gather(const void* k_cache, const void* v_cache, const int32_t
                          int max_blocks, int dtype, void* k_out, void* v_out, int* flag,
                          hipStream_t st);
 hipError_t launch_decode_generic(const DecodeArgs& a, hipStream_t st);
+bool gqa_supported(const DecodeArgs& a);
+hipError_t launch_decode_gqa(const DecodeArgs& a, hipStream_t st);
+bool mla_supported(const DecodeArgs& a);
+hipError_t launch_decode_mla(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_merge(const float* part_out, const float* part_lse, int n_seqs, int n_parts,
                         int hq, int dv, void* out, int out_dtype, float* lse, hipStream_t st);
 
