@@ -35,8 +35,8 @@ def make_workload(name):
 
     return {
         "long": lambda: wl.long(),
-        "dcp1": lambda: wl.dcp(interleave=1, partition_tokens=1024),
-        "dcp16": lambda: wl.dcp(interleave=16, partition_tokens=1024),
+        "dcp1": lambda: wl.dcp(interleave=1),
+        "dcp16": lambda: wl.dcp(interleave=16),
         "batch": lambda: wl.batch(),
         "latent": lambda: wl.latent(),
         "tiny": lambda: wl.tiny(),
@@ -47,9 +47,9 @@ DESCRIBE = {
     "long": "long-context decode: 8 seqs, L log-normal (median 142K, sigma 0.5, clip [16384, 200000]), "
             "32 q / 8 kv heads, d 128, bf16, block 16, split-KV partitions of 4096 tokens",
     "dcp1": "DCP emulation: 1 seq of 200000 tokens, 64 q / 8 kv heads, d 128, bf16, block 16, "
-            "S=4 interleaved shards, I=1, partitions of 1024 local tokens",
+            "S=4 interleaved shards, I=1, partition size chosen by pa_choose_partition_tokens",
     "dcp16": "DCP emulation: 1 seq of 200000 tokens, 64 q / 8 kv heads, d 128, bf16, block 16, "
-             "S=4 interleaved shards, I=16, partitions of 1024 local tokens",
+             "S=4 interleaved shards, I=16, partition size chosen by pa_choose_partition_tokens",
     "batch": "continuous-batching step: 64 seqs, L = U[8,32] + U[16,96], 32 q / 8 kv heads, d 128, "
              "bf16, block 16",
     "latent": "latent (MLA-style) cache: 32 seqs, L U[4096, 65536], 128 q heads on 1 kv head, "
@@ -172,7 +172,8 @@ def run_config(name, steps, warmup, with_cpu, partition_tokens=0):
     T = wl.make_tensors(w, dev)
     step = P.DecodeStep(w.n_seqs, w.n_q_heads, w.n_kv_heads, w.dk, w.dv, w.block_size,
                         int(w.context_lens.max()), w.n_shards, w.interleave,
-                        w.partition_tokens, w.scale_f32, device=dev)
+                        w.partition_tokens, w.scale_f32, device=dev,
+                        context_lens_host=w.context_lens, kv_dtype=T["q"].dtype, latent=w.latent)
     cpu = cpu_baseline(w, T) if with_cpu else None
     t = time_gpu(w, T, step, steps, warmup)
     assert int(step.err_flag.item()) == 0, "device error flag set"

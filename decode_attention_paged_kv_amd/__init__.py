@@ -6,7 +6,7 @@ slot routing, kv append, the partitioned attention and the LSE merge.
 """
 from ._lib import (  # noqa: F401
     ERR_BLOCK_ID, ERR_CAPACITY, ERR_SLOT, LIB_PATH, PA_BF16, PA_F32, PaError, lib,
-    pa_decode, pa_default_partition_tokens, pa_gather_kv, pa_kv_append, pa_max_partitions,
+    pa_choose_partition_tokens, pa_decode, pa_default_partition_tokens, pa_gather_kv, pa_kv_append, pa_max_partitions,
     pa_merge_lse, pa_shard_length, pa_slot_mapping,
 )
 from .step import DecodeStep  # noqa: F401

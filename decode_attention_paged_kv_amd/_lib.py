@@ -37,6 +37,7 @@ _SIGS = {
     "pa_shard_length": [_i32, _i32, _i32, _i32],
     "pa_max_partitions": [_i32, _i32, _i32, _i32],
     "pa_default_partition_tokens": [_i32, _i32, _i32, _i32, _i32, _i32],
+    "pa_choose_partition_tokens": [_p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32],
     "pa_last_error": [],
 }
 for _name, _args in _SIGS.items():
@@ -97,6 +98,18 @@ def pa_max_partitions(max_context_len: int, n_shards: int, interleave: int, part
 def pa_default_partition_tokens(n_seqs, n_kv_heads, max_context_len, n_shards, interleave, block_size) -> int:
     return int(lib.pa_default_partition_tokens(n_seqs, n_kv_heads, max_context_len, n_shards,
                                                interleave, block_size))
+
+
+def pa_choose_partition_tokens(context_lens_host, n_q_heads, n_kv_heads, dk, dv, block_size,
+                               dtype, latent, n_shards=1, interleave=1) -> int:
+    """``context_lens_host``: host sequence of ints; ``dtype``: torch dtype."""
+    import numpy as np
+
+    lens = np.ascontiguousarray(np.asarray(context_lens_host, dtype=np.int32))
+    code = PA_F32 if dtype == torch.float32 else PA_BF16
+    return int(lib.pa_choose_partition_tokens(lens.ctypes.data_as(ctypes.c_void_p), int(lens.size),
+                                              n_q_heads, n_kv_heads, dk, dv, block_size, code,
+                                              int(bool(latent)), n_shards, interleave))
 
 
 # ------------------------------------------------------------------ entry points

@@ -53,9 +53,7 @@ __global__ __launch_bounds__(kThreads) void decode_generic_kernel(DecodeArgs a) 
   const int t_end = min(t_begin + T, Lr);
 
   const int64_t out_row = ((int64_t(b) * a.n_shards + r) * a.max_parts + p) * a.hq;
-  if (t_begin >= t_end) {  // empty partition
-    for (int i = tid; i < nh * dv; i += kThreads)
-      a.part_out[(out_row + h0 + i / dv) * dv + i % dv] = 0.f;
+  if (t_begin >= t_end) {  // empty partition: lse = -inf, output rows left unwritten
     if (tid < nh) a.part_lse[out_row + h0 + tid] = -INFINITY;
     return;
   }
@@ -153,6 +151,16 @@ __global__ __launch_bounds__(kThreads) void decode_generic_kernel(DecodeArgs a) 
 }
 
 }  // namespace
+
+int generic_workgroups_per_cu(int dtype) {
+  int n = 0;
+  const void* f = dtype == kF32 ? (const void*)decode_generic_kernel<kF32> : (const void*)decode_generic_kernel<kBF16>;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, f, kThreads, 0) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  return n;
+}
 
 hipError_t launch_decode_generic(const DecodeArgs& a, hipStream_t st) {
   const int g = a.hq / a.hkv;

@@ -68,18 +68,18 @@ __device__ inline uint32_t keep(uint32_t w, bool lo_ok, bool hi_ok) {
   return w & ((lo_ok ? 0x0000ffffu : 0u) | (hi_ok ? 0xffff0000u : 0u));
 }
 
-template <int D>
+template <int D, int SUBS>
 struct Tile {
   static constexpr int KJ = D / 32;  // score MFMAs per sub-tile
   static constexpr int NT = D / 16;  // output tiles of 16 d rows
-  bf16x8_t k[2][KJ];
-  uint2 v[2][NT];
-  int tok0[2];  // local token of the first row of each sub-tile (-1: no sub-tile)
+  bf16x8_t k[SUBS][KJ];
+  uint2 v[SUBS][NT];
+  int tok0[SUBS];  // local token of the first row of each sub-tile (-1: no sub-tile)
 };
 
-template <int D, int NW, bool PREFETCH>
+template <int D, int NW, bool PREFETCH, int SUBS>
 __global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeArgs a) {
-  using TileT = Tile<D>;
+  using TileT = Tile<D, SUBS>;
   constexpr int KJ = TileT::KJ;
   constexpr int NT = TileT::NT;
   const uint16_t* __restrict__ q = static_cast<const uint16_t*>(a.q);
@@ -108,8 +108,7 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeArgs a) {
   const int t_begin = p * T;
   const int t_end = min(t_begin + T, Lr);
   const int64_t out_row = ((int64_t(b) * a.n_shards + r) * a.max_parts + p) * a.hq + h0;
-  if (t_begin >= t_end) {
-    for (int i = threadIdx.x; i < nh * D; i += 64 * NW) a.part_out[out_row * D + i] = 0.f;
+  if (t_begin >= t_end) {  // empty partition: lse = -inf, output rows left unwritten
     if (threadIdx.x < nh) a.part_lse[out_row + threadIdx.x] = -INFINITY;
     return;
   }
@@ -127,10 +126,10 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeArgs a) {
     }
   }
 
-  // this wave's contiguous range of 32-token steps
+  // this wave's contiguous range of steps of SUBS 16-token sub-tiles
   const int u0 = t_begin >> 4;                   // first sub-tile (T and bs are multiples of 16)
   const int n_u = (t_end - t_begin + 15) >> 4;   // sub-tiles in the partition
-  const int n_steps = (n_u + 1) >> 1;
+  const int n_steps = (n_u + SUBS - 1) / SUBS;
   const int per = n_steps / NW, extra = n_steps % NW;
   const int s_lo = wave * per + min(wave, extra);
   const int s_hi = s_lo + per + (wave < extra ? 1 : 0);
@@ -157,31 +156,45 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeArgs a) {
     return __builtin_amdgcn_readlane(tbl, e - tbl_base);
   };
 
+  // all key loads of a step are issued before its value loads, so the scores can start
+  // while the values are still on their way
   auto load = [&](TileT& tl, int s) {
+    int64_t base[SUBS];
+    int sub[SUBS];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int u_rel = 2 * s + t;
+    for (int t = 0; t < SUBS; ++t) {
+      const int u_rel = SUBS * s + t;
       tl.tok0[t] = -1;
+      base[t] = 0;
+      sub[t] = 0;
       if (u_rel < n_u) {
         const int u = u0 + u_rel;
         const int e = u / spb;
         const int phys = block_of(e);
         if (phys >= 0) {
           tl.tok0[t] = u << 4;
-          const int64_t base = (int64_t(phys) * a.hkv + kvh) * kv_stride;
-          const int sub = (u - e * spb) << 4;
-          const uint16_t* kp = kc + base + int64_t(sub + col) * D + 8 * grp;
-#pragma unroll
-          for (int j = 0; j < KJ; ++j) tl.k[t][j] = *reinterpret_cast<const bf16x8_t*>(kp + 32 * j);
-          const uint16_t* vp = vc + base + int64_t(col) * bs + sub + 4 * grp;
-#pragma unroll
-          for (int n = 0; n < NT; ++n)
-            tl.v[t][n] = *reinterpret_cast<const uint2*>(vp + int64_t(16 * n) * bs);
+          base[t] = (int64_t(phys) * a.hkv + kvh) * kv_stride;
+          sub[t] = (u - e * spb) << 4;
         } else if (lane == 0) {
           raise_flag(a.flag, phys == -3 ? kErrCapacity : kErrBlockId);
         }
       }
     }
+#pragma unroll
+    for (int t = 0; t < SUBS; ++t)
+      if (tl.tok0[t] >= 0) {
+        const uint16_t* kp = kc + base[t] + int64_t(sub[t] + col) * D + 8 * grp;
+#pragma unroll
+        for (int j = 0; j < KJ; ++j) tl.k[t][j] = *reinterpret_cast<const bf16x8_t*>(kp + 32 * j);
+      }
+#pragma unroll
+    for (int t = 0; t < SUBS; ++t)
+      if (tl.tok0[t] >= 0) {
+        const uint16_t* vp = vc + base[t] + int64_t(col) * bs + sub[t] + 4 * grp;
+#pragma unroll
+        for (int n = 0; n < NT; ++n)
+          tl.v[t][n] = *reinterpret_cast<const uint2*>(vp + int64_t(16 * n) * bs);
+      }
   };
 
   const float c = a.scale * kLog2e;
@@ -192,9 +205,9 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeArgs a) {
   for (int n = 0; n < NT; ++n) o[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   auto compute = [&](const TileT& tl) {
-    float sc[2][4];
+    float sc[SUBS][4];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < SUBS; ++t) {
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
       if (tl.tok0[t] >= 0) {
 #pragma unroll
@@ -209,17 +222,17 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeArgs a) {
     }
     float mt = m;
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < SUBS; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i) mt = fmaxf(mt, sc[t][i]);
     mt = xor_max(mt);
     const float alpha = (mt == -INFINITY) ? 1.f : exp2f((m - mt) * c);
     m = mt;
     const float mc = mt * c;
-    float pv[2][4];
+    float pv[SUBS][4];
     float psum = 0.f;
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < SUBS; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         pv[t][i] = exp2f(fmaf(sc[t][i], c, -mc));
@@ -230,35 +243,41 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeArgs a) {
 #pragma unroll
       for (int n = 0; n < NT; ++n) o[n] *= alpha;
     }
-    bf16x8_t phi, plo;
+    // value operand; tokens that are masked (or sub-tiles not loaded) contribute zeros
+    bool ok[SUBS][4];
+    bool full = true;
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < SUBS; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const __bf16 h = (__bf16)pv[t][i];
-        phi[4 * t + i] = h;
-        plo[4 * t + i] = (__bf16)(pv[t][i] - (float)h);
+        ok[t][i] = tl.tok0[t] >= 0 && tl.tok0[t] + 4 * grp + i < t_end;
+        full = full && ok[t][i];
       }
-    // value operand; tokens that are masked (or sub-tiles not loaded) contribute zeros
-    bool ok[2][4];
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t2 = 0; t2 < SUBS; t2 += 2) {   // one MFMA k-step = two sub-tiles (32 tokens)
+      bf16x8_t phi, plo;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) ok[t][i] = tl.tok0[t] >= 0 && tl.tok0[t] + 4 * grp + i < t_end;
-    const bool full = ok[0][0] && ok[0][3] && ok[1][0] && ok[1][3];
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int n = 0; n < NT; ++n) {
-      uint2 va = tl.v[0][n], vb = tl.v[1][n];
-      if (!__all(full)) {
-        va.x = keep(va.x, ok[0][0], ok[0][1]);
-        va.y = keep(va.y, ok[0][2], ok[0][3]);
-        vb.x = keep(vb.x, ok[1][0], ok[1][1]);
-        vb.y = keep(vb.y, ok[1][2], ok[1][3]);
+        for (int i = 0; i < 4; ++i) {
+          const __bf16 h = (__bf16)pv[t2 + t][i];
+          phi[4 * t + i] = h;
+          plo[4 * t + i] = (__bf16)(pv[t2 + t][i] - (float)h);
+        }
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        uint2 va = tl.v[t2][n], vb = tl.v[t2 + 1][n];
+        if (!__all(full)) {
+          va.x = keep(va.x, ok[t2][0], ok[t2][1]);
+          va.y = keep(va.y, ok[t2][2], ok[t2][3]);
+          vb.x = keep(vb.x, ok[t2 + 1][0], ok[t2 + 1][1]);
+          vb.y = keep(vb.y, ok[t2 + 1][2], ok[t2 + 1][3]);
+        }
+        const u32x4_t w = {va.x, va.y, vb.x, vb.y};
+        const bf16x8_t vop = __builtin_bit_cast(bf16x8_t, w);
+        o[n] = mfma16x16x32(vop, phi, o[n]);
+        o[n] = mfma16x16x32(vop, plo, o[n]);
       }
-      const u32x4_t w = {va.x, va.y, vb.x, vb.y};
-      const bf16x8_t vop = __builtin_bit_cast(bf16x8_t, w);
-      o[n] = mfma16x16x32(vop, phi, o[n]);
-      o[n] = mfma16x16x32(vop, plo, o[n]);
     }
   };
 
@@ -324,11 +343,27 @@ bool gqa_supported(const DecodeArgs& a) {
 }
 
 #ifndef PA_GQA_WAVES
-#define PA_GQA_WAVES 4
+#define PA_GQA_WAVES 8
 #endif
 #ifndef PA_GQA_PREFETCH
-#define PA_GQA_PREFETCH 1
+#define PA_GQA_PREFETCH 0
 #endif
+#ifndef PA_GQA_SUBS
+#define PA_GQA_SUBS 2
+#endif
+
+int gqa_workgroup_threads() { return 64 * PA_GQA_WAVES; }
+
+int gqa_workgroups_per_cu(int dk) {
+  int n = 0;
+  const void* f = dk == 128 ? (const void*)decode_gqa_kernel<128, PA_GQA_WAVES, PA_GQA_PREFETCH != 0, PA_GQA_SUBS>
+                            : (const void*)decode_gqa_kernel<64, PA_GQA_WAVES, PA_GQA_PREFETCH != 0, PA_GQA_SUBS>;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, f, 64 * PA_GQA_WAVES, 0) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  return n;
+}
 
 hipError_t launch_decode_gqa(const DecodeArgs& a, hipStream_t st) {
   const int g = a.hq / a.hkv;
@@ -337,9 +372,9 @@ hipError_t launch_decode_gqa(const DecodeArgs& a, hipStream_t st) {
   constexpr int NW = PA_GQA_WAVES;
   constexpr bool PF = PA_GQA_PREFETCH != 0;
   if (a.dk == 128)
-    hipLaunchKernelGGL((decode_gqa_kernel<128, NW, PF>), grid, dim3(64 * NW), 0, st, a);
+    hipLaunchKernelGGL((decode_gqa_kernel<128, NW, PF, PA_GQA_SUBS>), grid, dim3(64 * NW), 0, st, a);
   else
-    hipLaunchKernelGGL((decode_gqa_kernel<64, NW, PF>), grid, dim3(64 * NW), 0, st, a);
+    hipLaunchKernelGGL((decode_gqa_kernel<64, NW, PF, PA_GQA_SUBS>), grid, dim3(64 * NW), 0, st, a);
   return hipGetLastError();
 }
 

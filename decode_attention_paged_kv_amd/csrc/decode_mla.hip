@@ -126,8 +126,7 @@ __global__ __launch_bounds__(64 * NW) void decode_mla_kernel(DecodeArgs a) {
   const int t_begin = p * T;
   const int t_end = min(t_begin + T, Lr);
   const int64_t out_row = ((int64_t(b) * a.n_shards + r) * a.max_parts + p) * a.hq + h0;
-  if (t_begin >= t_end) {
-    for (int i = tid; i < HEADS * DV; i += 64 * NW) a.part_out[out_row * DV + i] = 0.f;
+  if (t_begin >= t_end) {  // empty partition: lse = -inf, output rows left unwritten
     if (tid < HEADS) a.part_lse[out_row + tid] = -INFINITY;
     return;
   }
@@ -401,6 +400,16 @@ __global__ __launch_bounds__(64 * NW) void decode_mla_kernel(DecodeArgs a) {
 bool mla_supported(const DecodeArgs& a) {
   return a.dtype == kBF16 && a.v_cache == nullptr && a.dk == DK && a.dv == DV &&
          a.hq == HEADS * a.hkv && a.bs % TT == 0;
+}
+
+int mla_workgroups_per_cu() {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, (const void*)decode_mla_kernel, 64 * NW, 0) !=
+      hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  return n;
 }
 
 hipError_t launch_decode_mla(const DecodeArgs& a, hipStream_t st) {

@@ -4,7 +4,8 @@
 // section) finishes a decode step by sharing the LSE of every partial result,
 // correcting each partial output with its weight and summing.  Written out: with
 // lse = M + ln sum_p exp(lse_p - M), M = max_p lse_p, part p has weight exp(lse_p - lse).
-// Parts with lse_p = -inf are empty and skipped (no -inf - -inf is ever formed).
+// Parts with lse_p = -inf are empty and skipped (no -inf - -inf is ever formed); their
+// part_out rows are never read.
 //
 // One workgroup per (sequence, head).
 #include <math.h>
@@ -32,18 +33,22 @@ __device__ inline float block_reduce(float v, float* red, bool is_max) {
   return r;
 }
 
-// Threads form a (part group) x (column group) grid: each thread owns VEC consecutive
-// output columns and sums every PG-th part, so PG parts are read at once; the PG
-// partial sums are then added through LDS.
+// Each workgroup covers CB consecutive output columns of one (sequence, head).  Parts
+// with lse = -inf are empty (their part_out rows are never read); the others are listed
+// compactly in LDS.  Threads form a (part group) x (column group) grid: each owns VEC
+// consecutive columns and sums every npg-th listed part, so npg parts are read at once
+// with no data-dependent branch; the npg partial sums are then added through LDS.
 template <int VEC>
 __global__ __launch_bounds__(kThreads) void merge_kernel(const float* __restrict__ part_out,
                                                          const float* __restrict__ part_lse,
-                                                         int n_parts, int hq, int dv, void* out,
-                                                         int out_dtype, float* lse_out) {
+                                                         int n_parts, int hq, int dv, int cb,
+                                                         void* out, int out_dtype, float* lse_out) {
   const int b = blockIdx.x / hq;
   const int h = blockIdx.x % hq;
   __shared__ float red[kThreads / 64];
   __shared__ float w_s[kChunk];
+  __shared__ int idx_s[kChunk];
+  __shared__ int cnt_s[kThreads / 64];
   __shared__ float acc_s[kThreads * VEC];
   const float* lse_p = part_lse + int64_t(b) * n_parts * hq + h;       // stride hq
   const float* o_p = part_out + (int64_t(b) * n_parts * hq + h) * dv;  // stride hq*dv
@@ -62,45 +67,58 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const float* __restrict
     total = m + logf(s);
   }
 
-  // this workgroup's columns: [col0, col0 + ncols), at most 128 column groups
-  const int col0 = blockIdx.y * 128 * VEC;
-  const int ncols = min(128 * VEC, dv - col0);
-  const int ncg = ncols / VEC;                 // column groups (VEC divides dv)
-  const int npg = kThreads / ncg;              // part groups (>= 2)
+  const int col0 = blockIdx.y * cb;
+  const int ncols = min(cb, dv - col0);
+  const int ncg = ncols / VEC;                 // column groups (VEC divides dv and cb)
+  const int npg = kThreads / ncg;              // part groups
   const int cg = threadIdx.x % ncg;
   const int pg = threadIdx.x / ncg;
   const bool active = pg < npg;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   float acc[VEC];
 #pragma unroll
   for (int k = 0; k < VEC; ++k) acc[k] = 0.f;
+  const int64_t stride = int64_t(hq) * dv;
   for (int p0 = 0; p0 < n_parts && total != -INFINITY; p0 += kChunk) {
     const int np = min(kChunk, n_parts - p0);
-    __syncthreads();
-    for (int i = threadIdx.x; i < np; i += kThreads) {
-      const float x = lse_p[int64_t(p0 + i) * hq];
-      w_s[i] = (x != -INFINITY) ? expf(x - total) : 0.f;
+    // list the non-empty parts of this chunk, in order, with their weights
+    int base = 0;
+    for (int i0 = 0; i0 < np; i0 += kThreads) {
+      __syncthreads();
+      const int i = i0 + threadIdx.x;
+      float w = 0.f;
+      if (i < np) {
+        const float x = lse_p[int64_t(p0 + i) * hq];
+        if (x != -INFINITY) w = expf(x - total);
+      }
+      const unsigned long long ball = __ballot(w != 0.f);
+      if (lane == 0) cnt_s[wv] = __popcll(ball);
+      __syncthreads();
+      int before = base;
+      for (int j = 0; j < wv; ++j) before += cnt_s[j];
+      if (w != 0.f) {
+        const int pos = before + __popcll(ball & ((1ull << lane) - 1ull));
+        w_s[pos] = w;
+        idx_s[pos] = p0 + i;
+      }
+      for (int j = 0; j < kThreads / 64; ++j) base += cnt_s[j];
     }
     __syncthreads();
     if (active) {
-      // no data-dependent branch in the loop, so the loads of several parts are in
-      // flight together
-      const float* src = o_p + int64_t(p0) * hq * dv + col0 + cg * VEC;
-      const int64_t stride = int64_t(hq) * dv;
+      const float* src = o_p + col0 + cg * VEC;
 #pragma unroll 8
-      for (int i = pg; i < np; i += npg) {
+      for (int i = pg; i < base; i += npg) {
         const float wi = w_s[i];
-        const float* sp = src + i * stride;
+        const float* sp = src + int64_t(idx_s[i]) * stride;
         if (VEC == 4) {
           const float4 v = *reinterpret_cast<const float4*>(sp);
-          const bool use = wi != 0.f;   // select, not branch: an empty part's values never enter
-          acc[0] = use ? fmaf(wi, v.x, acc[0]) : acc[0];
-          acc[1 % VEC] = use ? fmaf(wi, v.y, acc[1 % VEC]) : acc[1 % VEC];
-          acc[2 % VEC] = use ? fmaf(wi, v.z, acc[2 % VEC]) : acc[2 % VEC];
-          acc[3 % VEC] = use ? fmaf(wi, v.w, acc[3 % VEC]) : acc[3 % VEC];
+          acc[0] = fmaf(wi, v.x, acc[0]);
+          acc[1 % VEC] = fmaf(wi, v.y, acc[1 % VEC]);
+          acc[2 % VEC] = fmaf(wi, v.z, acc[2 % VEC]);
+          acc[3 % VEC] = fmaf(wi, v.w, acc[3 % VEC]);
         } else {
-          const bool use = wi != 0.f;
 #pragma unroll
-          for (int k = 0; k < VEC; ++k) acc[k] = use ? fmaf(wi, sp[k], acc[k]) : acc[k];
+          for (int k = 0; k < VEC; ++k) acc[k] = fmaf(wi, sp[k], acc[k]);
         }
       }
     }
@@ -126,12 +144,19 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const float* __restrict
 
 hipError_t launch_merge(const float* part_out, const float* part_lse, int n_seqs, int n_parts,
                         int hq, int dv, void* out, int out_dtype, float* lse, hipStream_t st) {
-  if (dv % 4 == 0)
-    hipLaunchKernelGGL(merge_kernel<4>, dim3(n_seqs * hq, (dv + 511) / 512), dim3(kThreads), 0,
-                       st, part_out, part_lse, n_parts, hq, dv, out, out_dtype, lse);
+  // Column blocks: narrow (more workgroups, more parts read at once) when there are few
+  // (sequence, head) rows or many parts; at most 128 column groups per workgroup.
+  const int vec = dv % 4 == 0 ? 4 : 1;
+  int cb = 128 * vec;
+  if (int64_t(n_seqs) * hq < 1024 || n_parts >= 64) cb = 8 * vec;
+  if (cb > dv) cb = dv;
+  const dim3 grid(n_seqs * hq, (dv + cb - 1) / cb);
+  if (vec == 4)
+    hipLaunchKernelGGL(merge_kernel<4>, grid, dim3(kThreads), 0, st, part_out, part_lse, n_parts,
+                       hq, dv, cb, out, out_dtype, lse);
   else
-    hipLaunchKernelGGL(merge_kernel<1>, dim3(n_seqs * hq, (dv + 127) / 128), dim3(kThreads), 0,
-                       st, part_out, part_lse, n_parts, hq, dv, out, out_dtype, lse);
+    hipLaunchKernelGGL(merge_kernel<1>, grid, dim3(kThreads), 0, st, part_out, part_lse, n_parts,
+                       hq, dv, cb, out, out_dtype, lse);
   return hipGetLastError();
 }
 

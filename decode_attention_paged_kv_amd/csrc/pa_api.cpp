@@ -3,6 +3,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <algorithm>
 #include <string>
 
 #include "../../include/pa.h"
@@ -84,6 +85,65 @@ int32_t pa_default_partition_tokens(int32_t n_seqs, int32_t n_kv_heads, int32_t 
   while (T > 256 && rows * ((longest + T - 1) / T) < want_units) T /= 2;
   T = ((T + block_size - 1) / block_size) * block_size;
   return T;
+}
+
+int32_t pa_choose_partition_tokens(const int32_t* context_lens_host, int32_t n_seqs,
+                                   int32_t n_q_heads, int32_t n_kv_heads, int32_t dk, int32_t dv,
+                                   int32_t block_size, int32_t dtype, int32_t latent,
+                                   int32_t n_shards, int32_t interleave) {
+  if (!context_lens_host || n_seqs < 1 || n_q_heads < 1 || n_kv_heads < 1 ||
+      n_q_heads % n_kv_heads != 0 || block_size < 1 || block_size > PA_MAX_BLOCK_SIZE ||
+      n_shards < 1 || interleave < 1 || int64_t(n_shards) * interleave > (int64_t(1) << 30) ||
+      !valid_dtype(dtype))
+    return -1;
+  pa::DecodeArgs a{};
+  a.hq = n_q_heads;
+  a.hkv = n_kv_heads;
+  a.dk = dk;
+  a.dv = dv;
+  a.bs = block_size;
+  a.dtype = dtype;
+  a.v_cache = latent ? nullptr : static_cast<const void*>(&a);  // only its NULL-ness matters
+  const pa::KernelChoice kc = pa::choose_kernel(a);
+  int cus = 0, dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0) {
+    (void)hipGetLastError();
+    cus = 256;  // MI355X
+  }
+  const int64_t slots = int64_t(cus) * (kc.workgroups_per_cu > 0 ? kc.workgroups_per_cu : 2);
+  // Cost of a partition size T, in token-times: the units (one workgroup each) run in
+  // ceil(units / slots) rounds of about T tokens plus a fixed per-unit cost (prologue,
+  // and writing then merging the partition's output rows).
+  const int64_t partial_bytes = int64_t(n_q_heads / n_kv_heads) * dv * 4 * 2;
+  const int64_t token_bytes = int64_t(latent ? dk : dk + dv) * (dtype == PA_F32 ? 4 : 2);
+  const int64_t overhead = 128 + partial_bytes / (token_bytes > 0 ? token_bytes : 1);
+  int32_t longest = 0;
+  for (int b = 0; b < n_seqs; ++b)
+    longest = std::max(longest, pa::shard_len(std::max(context_lens_host[b], 0), n_shards, interleave, 0));
+  if (longest == 0) return block_size;
+  const int32_t max_m = (longest + block_size - 1) / block_size;
+  const int32_t step = std::max(1, max_m / 512);
+  int32_t best_T = block_size * max_m;
+  double best_cost = 1e300;
+  for (int32_t m = 1; m <= max_m; m += (m < 16 ? 1 : step)) {
+    const int64_t T = int64_t(block_size) * m;
+    int64_t units = 0;
+    for (int b = 0; b < n_seqs; ++b)
+      for (int r = 0; r < n_shards; ++r) {
+        const int64_t Lr = pa::shard_len(std::max(context_lens_host[b], 0), n_shards, interleave, r);
+        units += (Lr + T - 1) / T;
+      }
+    units *= kc.units_per_partition;
+    const int64_t rounds = (units + slots - 1) / slots;
+    const double cost = double(rounds) * double(std::min<int64_t>(T, longest) + overhead);
+    if (cost < best_cost * (1 - 1e-9)) {
+      best_cost = cost;
+      best_T = int32_t(T);
+    }
+  }
+  return best_T;
 }
 
 int pa_slot_mapping(const int32_t* block_table, const int32_t* context_lens, int32_t n_seqs,

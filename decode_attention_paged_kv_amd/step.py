@@ -13,9 +13,16 @@ from . import _lib as L
 class DecodeStep:
     def __init__(self, n_seqs, n_q_heads, n_kv_heads, dk, dv, block_size, max_context_len,
                  n_shards=1, interleave=1, partition_tokens=0, scale=None, device="cuda",
-                 out_dtype=torch.float32):
+                 out_dtype=torch.float32, context_lens_host=None, kv_dtype=torch.bfloat16,
+                 latent=False):
+        """``partition_tokens=0`` picks a size: from the host context lengths when given
+        (``pa_choose_partition_tokens``), else from the longest context alone."""
         self.n_seqs, self.hq, self.hkv, self.dk, self.dv = n_seqs, n_q_heads, n_kv_heads, dk, dv
         self.block_size, self.n_shards, self.interleave = block_size, n_shards, interleave
+        if not partition_tokens and context_lens_host is not None:
+            partition_tokens = L.pa_choose_partition_tokens(context_lens_host, n_q_heads, n_kv_heads,
+                                                            dk, dv, block_size, kv_dtype, latent,
+                                                            n_shards, interleave)
         if not partition_tokens:
             partition_tokens = L.pa_default_partition_tokens(n_seqs, n_kv_heads, max_context_len,
                                                              n_shards, interleave, block_size)

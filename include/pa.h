@@ -123,7 +123,8 @@ int pa_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_ca
  *              passed (a longer context sets *err_flag and its excess is dropped).
  *   scale      multiplies q.k before the softmax.
  *   part_out   float32 [n_seqs][n_shards][Pmax][n_q_heads][dv]: softmax-weighted mean
- *              of the partition's values; 0 for an empty partition.
+ *              of the partition's values.  Rows of an empty partition are NOT written
+ *              (their weight in any merge is zero); pa_merge_lse never reads them.
  *   part_lse   float32 [n_seqs][n_shards][Pmax][n_q_heads]: natural log of the sum of
  *              exp(scale*q.k) over the partition; -inf for an empty partition.
  *   Unsupported: dk or dv outside [1, PA_MAX_HEAD_DIM], dv > 512, block_size outside
@@ -141,7 +142,7 @@ int pa_decode(const void* q, const void* k_cache, const void* v_cache,
  * over all its tokens ([DCP], DCP mechanism section: gather the LSEs, reweight each
  * partial output, sum).  With lse = log(sum_p exp(lse_p)), part p has weight
  * exp(lse_p - lse); parts with lse_p = -inf have weight 0; if every part is empty the
- * output is 0 and lse is -inf.
+ * output is 0 and lse is -inf.  part_out rows of parts with lse_p = -inf are not read.
  *   part_out float32 [n_seqs][n_parts][n_q_heads][dv], part_lse float32
  *   [n_seqs][n_parts][n_q_heads] (pa_decode's outputs with n_parts = n_shards*Pmax).
  *   out      [n_seqs][n_q_heads][dv] of out_dtype (PA_F32, or PA_BF16 rounded to nearest
@@ -179,6 +180,19 @@ int32_t pa_max_partitions(int32_t max_context_len, int32_t n_shards, int32_t int
  */
 int32_t pa_default_partition_tokens(int32_t n_seqs, int32_t n_kv_heads, int32_t max_context_len,
                                     int32_t n_shards, int32_t interleave, int32_t block_size);
+
+/*
+ * pa_choose_partition_tokens -- a partition size for a step whose context lengths the
+ * caller knows on the host (context_lens_host: HOST int32 [n_seqs]).  Picks the multiple
+ * of block_size that minimises (rounds of workgroups) x (tokens per workgroup + a fixed
+ * per-workgroup cost), using the occupancy of the kernel pa_decode would run for this
+ * shape (latent != 0: value = first dv entries of the key row) and the device's compute
+ * unit count.  A heuristic of this library.  Returns -1 on invalid arguments.
+ */
+int32_t pa_choose_partition_tokens(const int32_t* context_lens_host, int32_t n_seqs,
+                                   int32_t n_q_heads, int32_t n_kv_heads, int32_t dk, int32_t dv,
+                                   int32_t block_size, int32_t dtype, int32_t latent,
+                                   int32_t n_shards, int32_t interleave);
 
 /* Message of the last failed call on this thread ("" if none). */
 const char* pa_last_error(void);

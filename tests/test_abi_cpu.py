@@ -88,3 +88,18 @@ def test_other_entry_points_reject_bad_arguments():
     # zero-size work is accepted and launches nothing
     assert P.lib.pa_kv_append(vp, vp, vp, vp, vp, 0, 1, 64, 64, 4, 64, 0, None, None) == 0
     assert _call_decode(n=0) == 0
+
+
+def test_choose_partition_tokens():
+    import torch
+
+    import workloads as wl
+
+    for w in (wl.batch(), wl.dcp(16), wl.small("x", [5, 900], 8, 2, 64, 64, 32, wl.BF16)):
+        T = P.pa_choose_partition_tokens(w.context_lens, w.n_q_heads, w.n_kv_heads, w.dk, w.dv,
+                                         w.block_size, torch.bfloat16, w.latent, w.n_shards,
+                                         w.interleave)
+        assert T > 0 and T % w.block_size == 0
+    lens = np.array([10], np.int32)
+    assert P.lib.pa_choose_partition_tokens(None, 1, 4, 1, 64, 64, 4, 0, 0, 1, 1) == -1
+    assert P.pa_choose_partition_tokens(lens, 6, 4, 64, 64, 4, torch.float32, False) == -1
