@@ -228,7 +228,7 @@ def main():
                     help="time a plain 2 GiB device-to-device copy (reference for HBM counters)")
     a = ap.parse_args()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on one GPU only (DCP shards are emulated as "
+        print("bench.py: this library runs on one GPU (DCP shards are emulated as "
               "partitions on a single device); use --gpus 1", file=sys.stderr)
         sys.exit(2)
 

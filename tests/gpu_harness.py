@@ -1,7 +1,7 @@
 """Run a workload through the HIP library and through the fp64 oracle, and
 compare them.  Used by the ``gpu``-marked tests and by ``__graft_entry__.smoke``.
 
-Tolerances (the benchmark spec, stated per input type):
+Tolerances, per input type:
 * fp32 inputs: output max-abs 1e-5, LSE max-abs 1e-5;
 * bf16 inputs: output max-abs 5e-3, LSE max-abs 1e-3;
 plus a relative L2 bound on the whole output, ||o - o*|| / ||o*||, because at

@@ -15,7 +15,7 @@ and the slot of the token the step appends are NaN-poisoned, so a kernel that
 reads a value it should not read produces NaN instead of a silently plausible
 number.
 
-The five workloads are the configurations the north star of the build names:
+The five workloads:
 ``tiny`` (1 sequence, fp32), ``batch`` (continuous-batching step, 64 ragged
 sequences), ``long`` (8 sequences with log-normal lengths around 142K),
 ``dcp`` (one 200K sequence split into 4 interleaved shards) and ``latent``
