@@ -62,6 +62,10 @@ constexpr int P_STRIDE = TT + 8;                    // bf16 per weight row (80 B
 constexpr float kLazy = 8.f;                        // log2 headroom before the max moves
 constexpr int QL = 8;                               // query k-steps kept in LDS (rest in registers)
 constexpr int QR = DK / 32 - QL;                    // query k-steps kept in registers
+#ifndef PA_MLA_QG
+#define PA_MLA_QG 2
+#endif
+constexpr int QG = PA_MLA_QG;                       // k-steps of score operands read together
 constexpr int TBL = 512;                            // block-table entries staged in LDS
 
 // Workgroup barrier without a memory fence: this wave's LDS reads/writes are drained
@@ -256,15 +260,26 @@ __global__ __launch_bounds__(64 * NW) void decode_mla_kernel(DecodeArgs a) {
     f32x4_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
     if (valid > 0) {
       const lds_char_t* krow = tile + c16 * ROW_BYTES + 16 * g16;
+      // operands are read in groups of QG k-steps and then consumed, so several LDS
+      // reads are in flight together instead of one read, one wait, one MFMA
 #pragma unroll
-      for (int ks = 0; ks < DK / 32; ++ks) {
-        const bf16x8_t qk = ks < QL
-            ? *reinterpret_cast<const lds_bf16x8_t*>(qlds + ks * HEADS * 64)
-            : qop[ks < QL ? 0 : ks - QL];
+      for (int k0 = 0; k0 < DK / 32; k0 += QG) {
+        bf16x8_t kop[QG][2], qk[QG];
 #pragma unroll
-        for (int th = 0; th < 2; ++th)
-          acc[th] = mfma16(*reinterpret_cast<const lds_bf16x8_t*>(krow + 16 * th * ROW_BYTES + 64 * ks),
-                           qk, acc[th]);
+        for (int j = 0; j < QG; ++j) {
+          const int ks = k0 + j;
+          qk[j] = ks < QL ? *reinterpret_cast<const lds_bf16x8_t*>(qlds + ks * HEADS * 64)
+                          : qop[ks < QL ? 0 : ks - QL];
+#pragma unroll
+          for (int th = 0; th < 2; ++th)
+            kop[j][th] = *reinterpret_cast<const lds_bf16x8_t*>(krow + 16 * th * ROW_BYTES + 64 * ks);
+        }
+#pragma unroll
+        for (int j = 0; j < QG; ++j)
+#pragma unroll
+          for (int th = 0; th < 2; ++th) acc[th] = mfma16(kop[j][th], qk[j], acc[th]);
+        __builtin_amdgcn_sched_group_barrier(0x100, 3 * QG, 0);   // the group's LDS reads first
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * QG, 0);   // then its MFMAs
       }
     }
     float sc[2][4];

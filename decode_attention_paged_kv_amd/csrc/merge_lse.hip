@@ -145,10 +145,11 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const float* __restrict
 hipError_t launch_merge(const float* part_out, const float* part_lse, int n_seqs, int n_parts,
                         int hq, int dv, void* out, int out_dtype, float* lse, hipStream_t st) {
   // Column blocks: narrow (more workgroups, more parts read at once) when there are few
-  // (sequence, head) rows or many parts; at most 128 column groups per workgroup.
+  // (sequence, head) rows to spread over the GPU; otherwise wide (at most 128 column
+  // groups per workgroup), so each workgroup has enough work.
   const int vec = dv % 4 == 0 ? 4 : 1;
   int cb = 128 * vec;
-  if (int64_t(n_seqs) * hq < 1024 || n_parts >= 64) cb = 8 * vec;
+  if (int64_t(n_seqs) * hq < 1024) cb = 8 * vec;
   if (cb > dv) cb = dv;
   const dim3 grid(n_seqs * hq, (dv + cb - 1) / cb);
   if (vec == 4)
