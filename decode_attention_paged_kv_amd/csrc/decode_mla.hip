@@ -6,28 +6,44 @@
 // What is computed is the same as in decode_generic.hip (softmax attention of each
 // partition, output plus LSE; keys and values through the block table).  With 128 heads
 // on one KV head both products are real dense contractions (about 240 flops per byte
-// read), so both run on the matrix cores.
+// read), so both run on the matrix cores (v_mfma_f32_32x32x16_bf16).
 //
-// One workgroup = one (partition, sequence x shard, KV head) with all 128 heads and eight
-// waves (two per SIMD).  The partition is walked in 32-token tiles; each tile (32 rows x
-// 1152 B, contiguous inside a block) is copied HBM -> LDS with global_load_lds_dwordx4
-// (no registers involved) one tile ahead of the one being computed.
-//  * Scores: wave w owns heads 16w..16w+15 and keeps their query rows in registers
-//    (18 operands of v_mfma_f32_16x16x32_bf16).  S^T[token][head] = K_tile . Q^T with the
-//    key operand one 16-byte LDS read per lane per MFMA; each lane ends with 8 tokens of
-//    one head, so the row max needs two cross-lane exchanges.
-//  * Softmax in base 2 with a lazily moved maximum: the reference max of a head moves
-//    only when a score exceeds it by more than 8 (log2 units), so weights stay below 2^8
-//    and the output accumulators are rarely rescaled; the final division by the sum makes
-//    the result exact for any reference value.  Weights enter the output product rounded
-//    to bf16 once; the normaliser (and so the LSE) sums them unrounded in fp32.
-//  * Output: wave w owns value columns 64w..64w+63 of all 128 heads, O^T[d][head] +=
-//    V^T . P^T on v_mfma_f32_32x32x16_bf16.  The V^T operand (8 tokens of one value
-//    column per lane) comes straight from the row-major tile with two ds_read_b64_tr_b16
-//    transposing reads; the weights of all heads pass through LDS.
-//  * Tokens past the partition end get score -inf and zero value by select.
-// LDS rows are padded to 1168 B (73 x 16 B) so the 16 rows read together start in
-// different banks.
+// One workgroup = one (partition, sequence x shard, KV head) with all 128 heads and four
+// waves, one per SIMD.  Wave w owns heads 32w .. 32w+31 from end to end, so waves share
+// nothing but the key/value tiles:
+//  * Tiles of 32 tokens (32 rows x 1152 B, contiguous inside a block) are copied HBM ->
+//    LDS with global_load_lds_dwordx4 (no registers involved) into a ring of three
+//    buffers.  The loop is software-pipelined by one tile: iteration i computes the
+//    scores of tile i+1 and, between those MFMAs, issues the copy of tile i+2 and the
+//    softmax of tile i; then the output MFMAs of tile i.  One barrier per tile both
+//    publishes a landed tile and frees the buffer of the tile before it.  A single wave
+//    per SIMD keeps the matrix core busy only with work placed in the shadow of its own
+//    MFMAs, hence this interleaving.
+//  * Scores: S^T[token][head] = K_tile . Q^T over 36 k-steps.  24 k-steps of the wave's
+//    32 query rows live in registers for the whole partition, 12 in LDS; the key operand
+//    is one 16-byte LDS read per lane per MFMA.
+//  * Softmax in base 2 against a reference max per head that is fixed by the first tile
+//    holding a valid token of the partition and never moved: later weights may exceed 1
+//    (exactly representable growth, up to 2^64), so the output accumulators are never
+//    rescaled inside the loop and stay in the AGPR file without a branch over them.  The
+//    final division by the sum makes the result exact for any reference value.  If a
+//    score ever exceeds the reference by more than 64 (log2 units) the workgroup starts
+//    the partition over in two passes: the first finds each head's exact max, the second
+//    accumulates with weights <= 1.  Each lane holds 16 tokens of one head, so a tile's
+//    row max is one cross-lane exchange.  Weights enter the output product rounded to
+//    bf16 once; the normaliser (and so the LSE) sums them unrounded in fp32.
+//  * Output: O^T[value column][head] += V^T . P^T, 16 column tiles of 32 x 32.  The
+//    score accumulator's layout is exactly the layout of the P^T operand (same token
+//    order on both operands), so weights never leave registers; the V^T operand (8
+//    tokens of one value column per lane) comes from the row-major tile with two
+//    ds_read_b64_tr_b16 transposing reads.
+//  * Tokens past the partition end get score -inf; the copy of the last, partial tile
+//    fills their rows with the partition's last row, and a tile whose block id is
+//    invalid is copied from a zero tile, so every value the weights meet is finite and a
+//    masked token adds exactly 0.
+// LDS tiles are unpadded and swizzled at 16-byte granularity: chunk c of token row t sits
+// at position c ^ g(t), g(t) = 4*bit1(t) + bits2..3(t), which spreads both the 32 rows of
+// a key-operand read and the 4 rows of a transposing read over distinct banks.
 #include <math.h>
 
 #include "pa_common.h"
@@ -37,7 +53,6 @@ namespace pa {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((__vector_size__(8 * sizeof(__bf16))));
-typedef float f32x4_t __attribute__((__vector_size__(4 * sizeof(float))));
 typedef float f32x16_t __attribute__((__vector_size__(16 * sizeof(float))));
 typedef short s16x4_t __attribute__((__vector_size__(4 * sizeof(short))));
 typedef short s16x8_t __attribute__((__vector_size__(8 * sizeof(short))));
@@ -48,73 +63,110 @@ typedef __attribute__((address_space(3))) char lds_char_t;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int DK = 576, DV = 512, HEADS = 128;
-constexpr int NW = 8;                               // waves per workgroup
+constexpr int NW = 4;                               // waves per workgroup (one per SIMD)
+constexpr int HW = HEADS / NW;                      // 32 heads per wave
 constexpr int TT = 32;                              // tokens per tile
-constexpr int ROW_CHUNKS = DK * 2 / 16;             // 72 chunks of 16 B per key row
-constexpr int ROW_SLOTS = ROW_CHUNKS + 1;           // padded LDS row
-constexpr int ROW_BYTES = ROW_SLOTS * 16;           // 1168
-constexpr int TILE_SLOTS = TT * ROW_SLOTS;          // 2336
-constexpr int ROUNDS = (TILE_SLOTS + 64 * NW - 1) / (64 * NW);  // copies per wave per tile
-constexpr int BUF_BYTES = ROUNDS * 64 * NW * 16;    // every wave issues ROUNDS copies
-constexpr int QH = HEADS / NW;                      // 16 heads per wave for the scores
-constexpr int PVC = DV / NW;                        // 64 value columns per wave for the output
-constexpr int P_STRIDE = TT + 8;                    // bf16 per weight row (80 B)
-constexpr float kLazy = 8.f;                        // log2 headroom before the max moves
-constexpr int QL = 8;                               // query k-steps kept in LDS (rest in registers)
-constexpr int QR = DK / 32 - QL;                    // query k-steps kept in registers
-#ifndef PA_MLA_QG
-#define PA_MLA_QG 2
-#endif
-constexpr int QG = PA_MLA_QG;                       // k-steps of score operands read together
-constexpr int TBL = 512;                            // block-table entries staged in LDS
+constexpr int ROW_BYTES = DK * 2;                   // 1152
+constexpr int ROW_CHUNKS = ROW_BYTES / 16;          // 72 chunks of 16 B per row
+constexpr int TILE_SLOTS = TT * ROW_CHUNKS;         // 2304
+constexpr int TILE_BYTES = TILE_SLOTS * 16;         // 36864
+constexpr int COPIES = TILE_SLOTS / (64 * NW);      // copies per wave per tile (9)
+constexpr int NBUF = 3;                             // tile buffers
+constexpr int KSTEPS = DK / 16;                     // 36 k-steps of the score product
+constexpr int MT = DV / 32;                         // 16 value-column tiles
+constexpr int TBL = 256;                            // block-table entries staged in LDS
+constexpr int QL = 12;                              // query k-steps kept in LDS (rest in registers)
+static_assert(TILE_SLOTS % (64 * NW) == 0, "tile copies must split evenly over the waves");
+static_assert(ROW_CHUNKS % 8 == 0, "the swizzle permutes aligned groups of 8 chunks");
+
+// Chunk swizzle of token row t (see the header).
+__device__ inline int swz(int t) { return (((t >> 1) & 1) << 2) | ((t >> 2) & 3); }
+
+// vmcnt(n) with expcnt/lgkmcnt left alone.
+#define PA_WAIT_VM(n) \
+  __builtin_amdgcn_s_waitcnt(((n) & 15) | ((((n) >> 4) & 3) << 14) | (7 << 4) | (15 << 8))
 
 // Workgroup barrier without a memory fence: this wave's LDS reads/writes are drained
 // first (lgkmcnt 0); the asynchronous HBM -> LDS copies are waited for separately with
-// vmcnt, so a copy still in flight for the next tile does not hold the barrier.
+// vmcnt, so copies still in flight for later tiles do not hold the barrier.
 __device__ inline void lds_barrier() {
   __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0), vmcnt/expcnt unchanged
   __builtin_amdgcn_s_barrier();
 }
 
-// 16-byte asynchronous copy HBM -> LDS (global_load_lds_dwordx4): each lane copies 16 B
-// from its own address; the 64 lanes' data land at consecutive 16-byte slots starting at
+// 16-byte asynchronous copy HBM -> LDS (global_load_lds_dwordx4): lane i copies 16 B
+// from base + off_i; the 64 lanes' data land at consecutive 16-byte slots starting at
 // LDS byte address `lds_addr` (wave-uniform, passed in M0).  Issued through asm so the
 // compiler does not attach its own conservative waits to later LDS reads; the kernel
 // waits for these copies explicitly with vmcnt before the barrier that publishes a tile.
-__device__ inline void copy16_to_lds(const void* gptr, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+__device__ inline void copy16_to_lds(const char* base, uint32_t off, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :
-               : "v"(gptr), "s"(lds_addr)
+               : "v"(off), "s"(base), "s"(lds_addr)
                : "memory", "m0");
+}
+
+// The copies take their base address in SGPRs: the value is wave-uniform, and this
+// makes it so for the compiler too.
+__device__ inline const char* uniform_ptr(const char* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(v >> 32));
+  return reinterpret_cast<const char*>((uint64_t(hi) << 32) | lo);
 }
 
 __device__ inline uint32_t lds_address(const void* p) {
   return uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)p));
 }
 
-__device__ inline f32x4_t mfma16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+// Both products are written out as asm so that each accumulator stays in one register
+// file: the 16 output tiles take the whole AGPR file and the score accumulator lives in
+// VGPRs; the compiler's own choice moves them between the two on every tile.  The
+// compiler does not see inside these statements, so they carry their wait states: three
+// before each MFMA (for an operand just written by a VALU instruction or an accvgpr
+// write), none between MFMAs that accumulate into exactly the same registers, and a
+// drain of 21 after the last score MFMA of a tile and 24 after the last output MFMA,
+// before any VALU instruction reads the result.
+__device__ inline f32x16_t mfma32_vgpr_first(bf16x8_t a, bf16x8_t b) {
+  f32x16_t d;
+  asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+  return d;
 }
-__device__ inline f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+__device__ inline void mfma32_vgpr_acc(f32x16_t& d, bf16x8_t a, bf16x8_t b) {
+  asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+}
+__device__ inline void mfma32_vgpr_last(f32x16_t& d, bf16x8_t a, bf16x8_t b) {
+  asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 4"
+               : "+v"(d) : "v"(a), "v"(b));
+}
+__device__ inline void mfma32_agpr_acc(f32x16_t& d, bf16x8_t a, bf16x8_t b) {
+  asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
+}
+// Pins a value of an output tile to the AGPR file (the compiler copies it in), so that
+// every definition of the loop-carried output tiles is an AGPR one and the loop keeps
+// them there.
+__device__ inline f32x16_t to_agpr(f32x16_t v) {
+  f32x16_t d;
+  asm volatile("" : "=a"(d) : "0"(v));
+  return d;
 }
 
-__global__ __launch_bounds__(64 * NW) void decode_mla_kernel(DecodeArgs a) {
+// Source of the copy of a tile whose block id is invalid (zero-initialised device memory).
+__device__ __attribute__((aligned(16))) char g_zero_tile[TILE_BYTES];
+
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void decode_mla_kernel(DecodeArgs a) {
   const uint16_t* __restrict__ q = static_cast<const uint16_t*>(a.q);
   const char* __restrict__ kc = static_cast<const char*>(a.k_cache);
 
-  __shared__ __attribute__((aligned(16))) char kt0[BUF_BYTES];   // two tile buffers, kept as
-  __shared__ __attribute__((aligned(16))) char kt1[BUF_BYTES];   // separate objects
-  __shared__ __attribute__((aligned(16))) uint16_t p_s[HEADS * P_STRIDE];
-  __shared__ float alpha_s[HEADS];
-  __shared__ float m_s[HEADS], l_s[HEADS];
-  __shared__ __attribute__((aligned(16))) uint16_t q_s[QL * HEADS * 32];   // [k-step][head][32]
+  __shared__ __attribute__((aligned(16))) char kt[NBUF * TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) uint16_t q_s[QL * 2 * HEADS * 8];   // [ks][k-group][head][8]
   __shared__ int32_t tbl_s[TBL];   // block-table entries of the partition, TBL at a time
+  __shared__ __attribute__((aligned(16))) int ovf_s[2][NW];   // [tile parity][wave]: overflow seen
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int c16 = lane & 15, g16 = lane >> 4;   // 16x16x32 operand row/col, k-group
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r32 = lane & 31, c32 = lane >> 5;   // 32x32x16 operand row/col, k-group
   const int p = blockIdx.x;
   const int b = blockIdx.y / a.n_shards;
@@ -147,7 +199,7 @@ __global__ __launch_bounds__(64 * NW) void decode_mla_kernel(DecodeArgs a) {
   auto stage_table = [&](int base) {
     for (int j = tid; j < TBL; j += 64 * NW) {
       const int e = base + j;
-      int v = -1;
+      int v;
       if (e < a.max_blocks) {
         v = row[e];
         if (v < 0 || v >= a.n_blocks) v = -2;
@@ -158,11 +210,19 @@ __global__ __launch_bounds__(64 * NW) void decode_mla_kernel(DecodeArgs a) {
     }
   };
   stage_table(tbl_base);
+  __syncthreads();
 
-  // physical block of tile i (uniform); -1 if invalid (flag raised, tile skipped)
+  // physical block of tile i (uniform); -1 if invalid (flag raised)
   auto tile_block = [&](int i) -> int {
     const int e = (t_begin + i * TT) / bs;
-    const int v = tbl_s[e - tbl_base];
+    if (e - tbl_base >= TBL || e < tbl_base) {   // other chunk of the table (long partitions)
+      PA_WAIT_VM(0);
+      __syncthreads();
+      tbl_base = e;
+      stage_table(tbl_base);
+      __syncthreads();
+    }
+    const int v = __builtin_amdgcn_readfirstlane(tbl_s[e - tbl_base]);
     if (v < 0) {
       if (tid == 0) raise_flag(a.flag, v == -3 ? kErrCapacity : kErrBlockId);
       return -1;
@@ -170,244 +230,387 @@ __global__ __launch_bounds__(64 * NW) void decode_mla_kernel(DecodeArgs a) {
     return v;
   };
 
-  // HBM -> LDS copy of tile i.  LDS slot s holds tile row s / 73, chunk s % 73 (chunk 72
-  // is the row pad, filled from chunk 71).  Each wave instruction writes 64 consecutive
-  // slots.  Every wave issues exactly ROUNDS copies with all lanes on -- slots past the
-  // tile re-read the tile's last chunk into spare LDS, and a tile with an invalid block
-  // re-reads row 0 of block 0 -- so a fixed vmcnt separates one tile's copies from the
-  // next one's.
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  auto issue_tile = [&](int i, char* dst, int phys) {
+  // Copy of tile i: LDS slot s of the tile holds token row s / 72, chunk (s % 72) ^ g(row).
+  // Wave w's k-th copy writes slots (k*NW + w)*64 .. +63.  begin_tile resolves the
+  // block; copy_piece(k) issues copy k (the pieces are spread over the score MFMAs).
+  // The offsets are recomputed at each copy from an opaque copy of the lane id: hoisted
+  // out of the tile loop they would hold nine registers the loop needs.  In the last,
+  // partial tile, rows past the partition end repeat its last row.
+  const uint32_t kt_lds = lds_address(kt);
+  uint32_t bad = 0;   // bit (i % NBUF): tile i has an invalid block
+  struct Copy {
+    const char* src;
+    uint32_t dst;
+    int rows;
+  };
+  auto begin_tile = [&](int i) -> Copy {
+    const int phys = __builtin_amdgcn_readfirstlane(tile_block(i));
     const int tok0 = t_begin + i * TT;
     const char* src = phys >= 0
-        ? kc + ((int64_t(phys) * a.hkv + kvh) * bs + (tok0 % bs)) * int64_t(DK * 2)
-        : kc;
-    const uint32_t dst_lds = lds_address(dst);
-#pragma unroll
-    for (int k = 0; k < ROUNDS; ++k) {
-      const int base = (k * NW + wave_u) * 64;
-      const int s = base + lane;
-      int t = s / ROW_SLOTS;
-      int cc = s - t * ROW_SLOTS;
-      cc = cc < ROW_CHUNKS ? cc : ROW_CHUNKS - 1;
-      uint32_t off = uint32_t(t * (DK * 2) + cc * 16);
-      if (s >= TILE_SLOTS) off = uint32_t((TT - 1) * (DK * 2) + (ROW_CHUNKS - 1) * 16);
-      if (phys < 0) off = 0;
-      copy16_to_lds(src + off, dst_lds + uint32_t(base) * 16);
-    }
+        ? kc + ((int64_t(phys) * a.hkv + kvh) * bs + (tok0 % bs)) * int64_t(ROW_BYTES)
+        : g_zero_tile;
+    const uint32_t slot = uint32_t(i % NBUF);
+    bad = (bad & ~(1u << slot)) | (uint32_t(phys < 0) << slot);
+    return Copy{uniform_ptr(src), kt_lds + slot * TILE_BYTES, phys < 0 ? TT : min(TT, t_end - tok0)};
   };
+  // Slot s = (k NW + w) 64 + lane = s0 + 256 k: with s0 = 72 t0 + x0 and 256 = 3*72 + 40,
+  // row t = t0 + 3k + q and chunk x = y - 72 q for y = x0 + 40k, q = floor(y / 72) =
+  // (57 y) >> 12 (exact for y < 392; here y <= 71 + 40*8).
+  const int t0 = (wave * 64 + lane) / ROW_CHUNKS;
+  const int x0 = (wave * 64 + lane) % ROW_CHUNKS;
+  static_assert(NW * 64 == 3 * ROW_CHUNKS + 40 && COPIES <= 9, "slot stepping above");
+  auto copy_piece = [&](const Copy& cp, int k) {
+    int t0o = t0, x0o = x0;
+    asm volatile("" : "+v"(t0o), "+v"(x0o));
+    const uint32_t y = uint32_t(x0o + 40 * k);
+    const uint32_t qq = __umul24(y, 57u) >> 12;   // 24-bit multiplies: full rate
+    const int t = t0o + 3 * k + int(qq);
+    const uint32_t x = y - __umul24(qq, uint32_t(ROW_CHUNKS));
+    const uint32_t row_src = uint32_t(min(t, cp.rows - 1));
+    const uint32_t off = __umul24(row_src, uint32_t(ROW_BYTES)) + ((x ^ uint32_t(swz(t))) << 4);
+    copy16_to_lds(cp.src, off, cp.dst + uint32_t((k * NW + wave) * 64 * 16));
+  };
+  auto issue_tile = [&](int i) {
+    const Copy cp = begin_tile(i);
+#pragma unroll
+    for (int k = 0; k < COPIES; ++k) copy_piece(cp, k);
+  };
+  auto tile_valid = [&](int i) { return (bad >> (i % NBUF)) & 1 ? 0 : min(TT, t_end - (t_begin + i * TT)); };
 
-  // query operand of the scores: lane (head 16w + c16, k-group g16) needs q[head][32ks +
-  // 8g16 .. +7] for k-steps ks = 0..17.  The first QL k-steps of all heads sit in LDS
-  // ([ks][head][32]), the rest in registers.
+  // Query operand (B of the score product): lane (head 32w + r32, k-group c32) needs
+  // q[head][16 ks + 8 c32 .. +7] for k-steps ks = 0..35.  The first QL k-steps of all
+  // heads sit in LDS as [ks][k-group][head][8] (a wave's read is 1 KB of consecutive
+  // 16-byte pieces), the rest in registers for the whole partition.
+  bf16x8_t qop[KSTEPS - QL];
   {
     const uint16_t* qb = q + (int64_t(b) * a.hq + h0) * DK;
-    for (int i = tid; i < QL * HEADS * 4; i += 64 * NW) {   // 16-byte pieces
-      const int ks = i / (HEADS * 4), rem = i % (HEADS * 4), hh = rem / 4, part = rem % 4;
-      *reinterpret_cast<uint4*>(q_s + (ks * HEADS + hh) * 32 + 8 * part) =
-          *reinterpret_cast<const uint4*>(qb + int64_t(hh) * DK + 32 * ks + 8 * part);
+    for (int i = tid; i < QL * 2 * HEADS; i += 64 * NW) {   // 16-byte pieces
+      const int ks = i / (2 * HEADS), g = (i / HEADS) % 2, hh = i % HEADS;
+      *reinterpret_cast<uint4*>(q_s + 8 * i) =
+          *reinterpret_cast<const uint4*>(qb + int64_t(hh) * DK + 16 * ks + 8 * g);
     }
-  }
-  bf16x8_t qop[QR];
-  {
-    const uint16_t* qrow = q + (int64_t(b) * a.hq + h0 + QH * wave + c16) * DK + 8 * g16;
+    const uint16_t* qrow = q + (int64_t(b) * a.hq + h0 + HW * wave + r32) * DK + 8 * c32;
 #pragma unroll
-    for (int j = 0; j < QR; ++j) qop[j] = *reinterpret_cast<const bf16x8_t*>(qrow + 32 * (QL + j));
+    for (int ks = QL; ks < KSTEPS; ++ks)
+      qop[ks - QL] = *reinterpret_cast<const bf16x8_t*>(qrow + 16 * ks);
   }
+  const lds_char_t* qlds = (const lds_char_t*)q_s + (c32 * HEADS + HW * wave + r32) * 16;
   // settle every global load issued so far here, so that no wait for them is placed
   // inside the tile loop (where it would also wait for the tile copies in flight)
-  __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
-  const lds_char_t* qlds = (const lds_char_t*)q_s + ((QH * wave + c16) * 32 + 8 * g16) * 2;
-  __syncthreads();
+  PA_WAIT_VM(0);
+  __syncthreads();   // q_s written
 
-  f32x16_t o[2][4];   // [32-column tile][32-head tile]
+  // Key operand (A of the score product): lane (token r32, k-group c32) reads chunk
+  // 2 ks + c32 of row r32: byte 1152 r32 + 128 (ks / 4) + 16 ((2 (ks % 4) + c32) ^ g).
+  uint32_t ka[4];
+  {
+    const int g = swz(r32);
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
+    for (int j = 0; j < 4; ++j) ka[j] = uint32_t(r32 * ROW_BYTES + (((2 * j + c32) ^ g) << 4));
+  }
+  // Value operand (A of the output product) through ds_read_b64_tr_b16: in 16-lane group
+  // G = lane / 16, lane j reads token row 16 kv + 8 h + 4 (G / 2) + j / 4 (h = 0: first
+  // read, h = 1: second), bytes 64 mt + 32 (G % 2) + 8 (j % 4) .. +7 of the value.  The
+  // chunk is 4 mt + x with x = 2 (G % 2) + (j % 4) / 2; its swizzled position is
+  // 4 (mt ^ g2) + (x ^ (g % 4)), so for even mt the byte is base + 64 mt + 64 g2 and for
+  // odd mt base + 64 mt - 64 g2.
+  uint32_t va[2][2];   // [h][mt parity]
+  {
+    const int G = lane >> 4, j = lane & 15;
+    const int x = 2 * (G & 1) + ((j & 3) >> 1);
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) o[mt][nt][e] = 0.f;
+    for (int h = 0; h < 2; ++h) {
+      const int t = 8 * h + 4 * (G >> 1) + (j >> 2);
+      const int g = swz(t);
+      const int base = t * ROW_BYTES + ((x ^ (g & 3)) << 4) + 8 * (j & 1);
+      va[h][0] = uint32_t(base + 64 * (g >> 2));
+      va[h][1] = uint32_t(base - 64 * (g >> 2));
+    }
+  }
 
   const float c = a.scale * kLog2e;
-  const int my_head = QH * wave + c16;
-  float m_used = -INFINITY;   // reference max (raw score) of head my_head
-  float lsum = 0.f;           // this lane's share of the sum of weights
+  constexpr float kOverflow = 64.f;
+  auto tile_ptr = [&](int i) { return (const lds_char_t*)kt + (i % NBUF) * TILE_BYTES; };
 
-  // one tile: prefetch tile i+1 into `next`, then compute tile i from `cur`
-  auto step = [&](int i, const char* cur, char* next, int phys_cur) -> int {
-    int phys_next = -1;
-    if (i + 1 < n_tiles) {
-      const int e_next = (t_begin + (i + 1) * TT) / bs;
-      if (e_next - tbl_base >= TBL) {   // next chunk of the table (rare: T > TBL blocks)
-        __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
-        __syncthreads();
-        tbl_base = e_next;
-        stage_table(tbl_base);
-        __syncthreads();
-      }
-      phys_next = tile_block(i + 1);
-      issue_tile(i + 1, next, phys_next);
-      __builtin_amdgcn_s_waitcnt((ROUNDS & 15) | (7 << 4) | (15 << 8));  // this tile landed
-    } else {
-      __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
+  // The 36 score MFMAs of the tile at `tile` into s.  Key operands are read KA k-steps
+  // ahead of their MFMA; the scheduling fences keep the order as written, so the reads
+  // do not all move up front, and filler(ks) -- other work of the wave -- issues in the
+  // shadow of MFMA ks.  The per-tile operand bases are opaque so that the compiler keeps
+  // the constant parts as instruction offsets instead of one register per read.
+  auto scores = [&](const lds_char_t* tile, f32x16_t& s, auto&& filler) {
+    const lds_char_t* kb[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      kb[j] = tile + ka[j];
+      asm volatile("" : "+v"(kb[j]));
     }
-    lds_barrier();
-    const int tok0 = t_begin + i * TT;
-    const int valid = phys_cur >= 0 ? min(TT, t_end - tok0) : 0;
-    const lds_char_t* tile = (const lds_char_t*)cur;
+    constexpr int KA = 3;
+    bf16x8_t kop[KA + 1], qlo[KA + 1];
+    auto kread = [&](int ks) {
+      return *reinterpret_cast<const lds_bf16x8_t*>(kb[ks & 3] + 128 * (ks >> 2));
+    };
+    auto qread = [&](int ks) {
+      return *reinterpret_cast<const lds_bf16x8_t*>(qlds + ks * (2 * HEADS * 16));
+    };
+#pragma unroll
+    for (int ks = 0; ks < KA; ++ks) {
+      kop[ks] = kread(ks);
+      if (ks < QL) qlo[ks] = qread(ks);
+    }
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      if (ks + KA < KSTEPS) {
+        kop[(ks + KA) % (KA + 1)] = kread(ks + KA);
+        if (ks + KA < QL) qlo[(ks + KA) % (KA + 1)] = qread(ks + KA);
+      }
+      const bf16x8_t kk = kop[ks % (KA + 1)];
+      const bf16x8_t qq = ks < QL ? qlo[ks % (KA + 1)] : qop[ks < QL ? 0 : ks - QL];
+      if (ks == 0)
+        s = mfma32_vgpr_first(kk, qq);
+      else if (ks + 1 < KSTEPS)
+        mfma32_vgpr_acc(s, kk, qq);
+      else
+        mfma32_vgpr_last(s, kk, qq);
+      __builtin_amdgcn_sched_barrier(0);
+      filler(ks);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  auto no_filler = [](int) {};
 
-    // ---- scores of this wave's 16 heads: two 16-token halves of the tile
-    f32x4_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-    if (valid > 0) {
-      const lds_char_t* krow = tile + c16 * ROW_BYTES + 16 * g16;
-      // operands are read in groups of QG k-steps and then consumed, so several LDS
-      // reads are in flight together instead of one read, one wait, one MFMA
+  // Row max of tile i's scores: lane holds head r32, tokens 8 (e / 4) + 4 c32 + e % 4.
+  auto masked = [&](const f32x16_t& s, int valid, float (&sc)[16]) {
+    const int lim = valid - 4 * c32;
 #pragma unroll
-      for (int k0 = 0; k0 < DK / 32; k0 += QG) {
-        bf16x8_t kop[QG][2], qk[QG];
+    for (int e = 0; e < 16; ++e) sc[e] = 8 * (e >> 2) + (e & 3) < lim ? s[e] : -INFINITY;
+  };
+  auto row_max = [&](const float (&sc)[16]) {
+    float mx = -INFINITY;
 #pragma unroll
-        for (int j = 0; j < QG; ++j) {
-          const int ks = k0 + j;
-          qk[j] = ks < QL ? *reinterpret_cast<const lds_bf16x8_t*>(qlds + ks * HEADS * 64)
-                          : qop[ks < QL ? 0 : ks - QL];
-#pragma unroll
-          for (int th = 0; th < 2; ++th)
-            kop[j][th] = *reinterpret_cast<const lds_bf16x8_t*>(krow + 16 * th * ROW_BYTES + 64 * ks);
-        }
-#pragma unroll
-        for (int j = 0; j < QG; ++j)
-#pragma unroll
-          for (int th = 0; th < 2; ++th) acc[th] = mfma16(kop[j][th], qk[j], acc[th]);
-        __builtin_amdgcn_sched_group_barrier(0x100, 3 * QG, 0);   // the group's LDS reads first
-        __builtin_amdgcn_sched_group_barrier(0x008, 2 * QG, 0);   // then its MFMAs
-      }
-    }
-    float sc[2][4];
-#pragma unroll
-    for (int th = 0; th < 2; ++th)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {   // token 16*th + 4*g16 + e of head my_head
-        const int tok = 16 * th + 4 * g16 + e;
-        sc[th][e] = tok < valid ? acc[th][e] : -INFINITY;
-      }
-    float mt = -INFINITY;
-#pragma unroll
-    for (int th = 0; th < 2; ++th)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) mt = fmaxf(mt, sc[th][e]);
-    mt = fmaxf(mt, __shfl_xor(mt, 16));
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    float alpha = 1.f;
-    if (mt != -INFINITY && (m_used == -INFINITY || (mt - m_used) * c > kLazy)) {
-      alpha = (m_used == -INFINITY) ? 0.f : exp2f((m_used - mt) * c);
-      m_used = mt;
-    }
-    const float mc = (m_used == -INFINITY) ? 0.f : m_used * c;
-    float part = 0.f;
-    uint32_t pw[2][2];
-#pragma unroll
-    for (int th = 0; th < 2; ++th) {
-      uint16_t hb[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float pe = exp2f(fmaf(sc[th][e], c, -mc));
-        part += pe;
-        hb[e] = __builtin_bit_cast(uint16_t, (__bf16)pe);
-      }
-      pw[th][0] = uint32_t(hb[0]) | (uint32_t(hb[1]) << 16);
-      pw[th][1] = uint32_t(hb[2]) | (uint32_t(hb[3]) << 16);
-    }
-    lsum = fmaf(lsum, alpha, part);
-#pragma unroll
-    for (int th = 0; th < 2; ++th) {
-      uint2 w2;
-      w2.x = pw[th][0];
-      w2.y = pw[th][1];
-      *reinterpret_cast<uint2*>(p_s + my_head * P_STRIDE + 16 * th + 4 * g16) = w2;
-    }
-    if (g16 == 0) alpha_s[my_head] = alpha;
-    lds_barrier();
-
-    // ---- output columns 64w .. 64w+63 of all heads
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const float al = alpha_s[32 * nt + r32];
-      if (__any(al != 1.f)) {
-#pragma unroll
-        for (int mt2 = 0; mt2 < 2; ++mt2) o[mt2][nt] *= al;
-      }
-    }
-    if (valid > 0) {
-      const int j16 = lane & 15;
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        // V^T operand: lane (value column n0 + j16, k-group) holds tokens kb .. kb+7
-        const int kb = 16 * ks + 8 * (g16 >> 1);
-        bf16x8_t aop[2];
-#pragma unroll
-        for (int mt2 = 0; mt2 < 2; ++mt2) {
-          const int n0 = PVC * wave + 32 * mt2 + 16 * (g16 & 1);
-          const lds_char_t* base0 = tile + (kb + (j16 >> 2)) * ROW_BYTES + (n0 + 4 * (j16 & 3)) * 2;
-          s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)base0);
-          s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(base0 + 4 * ROW_BYTES));
-          if (valid < TT) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              lo[e] = (kb + e < valid) ? lo[e] : short(0);
-              hi[e] = (kb + 4 + e < valid) ? hi[e] : short(0);
-            }
-          }
-          const s16x8_t cat = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          aop[mt2] = __builtin_bit_cast(bf16x8_t, cat);
-        }
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-          // P^T operand: lane (head 32nt + r32, k-group c32) holds tokens 16ks + 8c32 .. +7
-          const bf16x8_t bop = *reinterpret_cast<const lds_bf16x8_t*>(
-              (const lds_char_t*)p_s + ((32 * nt + r32) * P_STRIDE + 16 * ks + 8 * c32) * 2);
-#pragma unroll
-          for (int mt2 = 0; mt2 < 2; ++mt2) o[mt2][nt] = mfma32(aop[mt2], bop, o[mt2][nt]);
-        }
-      }
-    }
-    lds_barrier();
-    return phys_next;
+    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[e]);
+    return fmaxf(mx, __shfl_xor(mx, 32));
   };
 
-  int phys = tile_block(0);
-  issue_tile(0, kt0, phys);
-  for (int i = 0; i < n_tiles; i += 2) {
-    phys = step(i, kt0, kt1, phys);
-    if (i + 1 >= n_tiles) break;
-    phys = step(i + 1, kt1, kt0, phys);
-  }
+  // The 32 output MFMAs of tile `tile` with weights pop; value operands VA tiles ahead;
+  // filler(n) issues in the shadow of MFMA n.
+  auto outputs = [&](const lds_char_t* tile, const bf16x8_t (&pop)[2], f32x16_t (&o)[MT],
+                     auto&& filler) {
+    const lds_char_t* vb[2][2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int par = 0; par < 2; ++par) {
+        vb[h][par] = tile + va[h][par];
+        asm volatile("" : "+v"(vb[h][par]));
+      }
+    constexpr int VA = 2, NV = 2 * MT;
+    bf16x8_t vop[VA + 1];
+    auto vread = [&](int n) {   // operand n = kv * MT + m
+      const int kv = n / MT, m = n % MT;
+      const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4_t*)(vb[0][m & 1] + 64 * m + 16 * ROW_BYTES * kv));
+      const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4_t*)(vb[1][m & 1] + 64 * m + 16 * ROW_BYTES * kv));
+      const s16x8_t cat = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      return __builtin_bit_cast(bf16x8_t, cat);
+    };
+#pragma unroll
+    for (int n = 0; n < VA; ++n) vop[n] = vread(n);
+#pragma unroll
+    for (int n = 0; n < NV; ++n) {
+      if (n + VA < NV) vop[(n + VA) % (VA + 1)] = vread(n + VA);
+      mfma32_agpr_acc(o[n % MT], vop[n % (VA + 1)], pop[n / MT]);
+      __builtin_amdgcn_sched_barrier(0);
+      filler(n);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
 
-  // ---- finish: total weight per head, then o / l
-  float lt = lsum + __shfl_xor(lsum, 16);
-  lt += __shfl_xor(lt, 32);
-  if (g16 == 0) {
-    m_s[my_head] = m_used;
-    l_s[my_head] = lt;
-  }
-  __syncthreads();
+  auto zero_tiles = [&](f32x16_t (&o)[MT]) {
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    const int hh = 32 * nt + r32;
-    const float inv = 1.f / l_s[hh];
+    for (int m = 0; m < MT; ++m) {
+      f32x16_t z;
 #pragma unroll
-    for (int mt2 = 0; mt2 < 2; ++mt2)
+      for (int e = 0; e < 16; ++e) z[e] = 0.f;
+      o[m] = to_agpr(z);
+    }
+  };
+  auto any_overflow = [&](int parity) {
+    const int4 f = *reinterpret_cast<const int4*>(&ovf_s[parity][0]);
+    return (f.x | f.y | f.z | f.w) != 0;
+  };
+
+  // Accumulating pass, software-pipelined by one tile: iteration i computes the scores
+  // of tile i+1 and, in the shadow of those MFMAs, issues the copy of tile i+2 and the
+  // softmax of tile i; then tile i's output MFMAs.  Buffers: tile i (output), tile i+1
+  // (scores), tile i+2 (in flight).  A head whose m_ref is still -inf takes the max of
+  // its first tile with a valid token; the pass stops (returns false) as soon as a score
+  // exceeds m_ref by more than kOverflow (never, when m_ref is already the exact max).
+  auto pass_acc = [&](float& m_ref, f32x16_t (&o)[MT], float& lsum) -> bool {
+    if (tbl_base != e_first) {
+      PA_WAIT_VM(0);
+      __syncthreads();
+      tbl_base = e_first;
+      stage_table(tbl_base);
+      __syncthreads();
+    }
+    issue_tile(0);
+    if (n_tiles > 1) {
+      issue_tile(1);
+      PA_WAIT_VM(COPIES);
+    } else {
+      PA_WAIT_VM(0);
+    }
+    lds_barrier();
+    f32x16_t s_cur;
+    scores(tile_ptr(0), s_cur, no_filler);
+
+    bool ok = true;
+    for (int i = 0; i < n_tiles; ++i) {
+      const bool has_next = i + 1 < n_tiles;
+      if (has_next) PA_WAIT_VM(0);   // tile i+1 landed (the only copies in flight)
+      // everyone's copies of tile i+1 are in, everyone is done with tile i-1 (whose buffer
+      // tile i+2 takes), and tile i-1's overflow flags are visible
+      lds_barrier();
+      if (i > 0 && any_overflow((i - 1) & 1)) {
+        ok = false;
+        break;
+      }
+      const int valid = tile_valid(i);
+      float sc[16], m0 = -INFINITY, m1 = -INFINITY, mx = -INFINITY, mxo = -INFINITY, mc = 0.f;
+      float part = 0.f, pe[16];
+      bf16x8_t pop[2];
+      // softmax of tile i in small pieces (each fits the shadow of one MFMA): masks, row
+      // max, reference and overflow flag, weights, packing
+      constexpr int kSoftSteps = 30;
+      auto softmax_piece = [&](int step) {
+        if (step < 4) {
+          const int lim = valid - 4 * c32;
+#pragma unroll
+          for (int e = 4 * step; e < 4 * step + 4; ++e)
+            sc[e] = 8 * (e >> 2) + (e & 3) < lim ? s_cur[e] : -INFINITY;
+        } else if (step == 4) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) m0 = fmaxf(m0, sc[e]);
+        } else if (step == 5) {
+#pragma unroll
+          for (int e = 8; e < 16; ++e) m1 = fmaxf(m1, sc[e]);
+        } else if (step == 6) {
+          mx = fmaxf(m0, m1);
+          mxo = __shfl_xor(mx, 32);
+        } else if (step == 8) {
+          mx = fmaxf(mx, mxo);
+          if (m_ref == -INFINITY) m_ref = mx;   // first tile with a valid token of this head
+          const bool ovf = __any(mx != -INFINITY && (mx - m_ref) * c > kOverflow);
+          if (lane == 0) ovf_s[i & 1][wave] = ovf ? 1 : 0;
+          mc = (m_ref == -INFINITY) ? 0.f : m_ref * c;
+        } else if (step >= 9 && step < 25) {
+          const int e = step - 9;
+          pe[e] = __builtin_amdgcn_exp2f(fmaf(sc[e], c, -mc));
+          part += pe[e];
+        } else if (step >= 25 && step < 29) {
+          const int e0 = 4 * (step - 25);
+#pragma unroll
+          for (int e = e0; e < e0 + 4; ++e) pop[e >> 3][e & 7] = (__bf16)pe[e];
+        } else if (step == 29) {
+          lsum += part;
+        }
+      };
+      const bool copy_next = i + 2 < n_tiles;
+      Copy cp{};
+      if (copy_next) cp = begin_tile(i + 2);
+      f32x16_t s_next = s_cur;
+      if (has_next) {
+        scores(tile_ptr(i + 1), s_next, [&](int ks) {
+          if (ks >= 2 && ks < 2 + kSoftSteps) softmax_piece(ks - 2);
+        });
+      } else {
+#pragma unroll
+        for (int step = 0; step < kSoftSteps; ++step) softmax_piece(step);
+      }
+      // one copy of the output MFMAs in the loop: a branch around them would join the
+      // output tiles in a phi outside the AGPR file.  The copies of tile i+2 go in their
+      // shadow.
+      outputs(tile_ptr(i), pop, o, [&](int n) {
+        if ((n & 1) && (n >> 1) < COPIES && copy_next) copy_piece(cp, n >> 1);
+      });
+      s_cur = s_next;
+    }
+    if (ok) {   // the last tile's flags: no later iteration reads them
+      lds_barrier();
+      ok = !any_overflow((n_tiles - 1) & 1);
+    }
+    __syncthreads();
+    return ok;
+  };
+
+  // Scores-only pass: m_ref becomes each head's exact max over the partition.
+  auto pass_max = [&](float& m_ref) {
+    if (tbl_base != e_first) {
+      PA_WAIT_VM(0);
+      __syncthreads();
+      tbl_base = e_first;
+      stage_table(tbl_base);
+      __syncthreads();
+    }
+    for (int i = 0; i < NBUF - 1 && i < n_tiles; ++i) issue_tile(i);
+    for (int i = 0; i < n_tiles; ++i) {
+      const int ahead = min(NBUF - 2, n_tiles - 1 - i);
+      if (ahead >= 1) {
+        PA_WAIT_VM(COPIES);
+      } else {
+        PA_WAIT_VM(0);
+      }
+      lds_barrier();
+      if (i + NBUF - 1 < n_tiles) issue_tile(i + NBUF - 1);
+      f32x16_t s;
+      scores(tile_ptr(i), s, no_filler);
+      float sc[16];
+      masked(s, tile_valid(i), sc);
+      m_ref = fmaxf(m_ref, row_max(sc));
+    }
+    __syncthreads();
+  };
+
+  // total weight per head, then o / l (after the last output MFMA drained)
+  auto finish = [&](f32x16_t (&o)[MT], float m_ref, float lsum) {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+                 : "+a"(o[0]), "+a"(o[1]), "+a"(o[2]), "+a"(o[3]), "+a"(o[4]), "+a"(o[5]),
+                   "+a"(o[6]), "+a"(o[7]), "+a"(o[8]), "+a"(o[9]), "+a"(o[10]), "+a"(o[11]),
+                   "+a"(o[12]), "+a"(o[13]), "+a"(o[14]), "+a"(o[15]));
+    const float lt = lsum + __shfl_xor(lsum, 32);
+    const float inv = 1.f / lt;
+    const int hh = HW * wave + r32;
+    float* orow = a.part_out + (out_row + hh) * DV + 4 * c32;
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        const int d = PVC * wave + 32 * mt2 + 8 * jj + 4 * c32;
         float4 v;
-        v.x = o[mt2][nt][4 * jj + 0] * inv;
-        v.y = o[mt2][nt][4 * jj + 1] * inv;
-        v.z = o[mt2][nt][4 * jj + 2] * inv;
-        v.w = o[mt2][nt][4 * jj + 3] * inv;
-        *reinterpret_cast<float4*>(a.part_out + (out_row + hh) * DV + d) = v;
+        v.x = o[m][4 * jj + 0] * inv;
+        v.y = o[m][4 * jj + 1] * inv;
+        v.z = o[m][4 * jj + 2] * inv;
+        v.w = o[m][4 * jj + 3] * inv;
+        *reinterpret_cast<float4*>(orow + 32 * m + 8 * jj) = v;
+        __builtin_amdgcn_sched_barrier(0);
       }
+    if (c32 == 0) a.part_lse[out_row + hh] = (m_ref * c + log2f(lt)) * kLn2;
+  };
+
+  f32x16_t o[MT];   // O^T tiles: [32-column tile]; lane holds head r32
+  float m_ref = -INFINITY;   // reference max (raw score) of head r32 of this wave
+  float lsum;                // this lane's share of the sum of weights
+  // The accumulating pass runs once, or -- after a score far above the first tile's
+  // max -- a second time against each head's exact max, found by a scores-only pass.
+  for (;;) {
+    zero_tiles(o);
+    lsum = 0.f;
+    if (pass_acc(m_ref, o, lsum)) break;
+    float m_exact = -INFINITY;
+    pass_max(m_exact);
+    m_ref = m_exact;
   }
-  if (tid < HEADS) a.part_lse[out_row + tid] = (m_s[tid] * c + log2f(l_s[tid])) * kLn2;
+  finish(o, m_ref, lsum);
 }
 
 }  // namespace

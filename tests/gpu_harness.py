@@ -89,14 +89,17 @@ def compare_outputs(name, dtype, o, lse, o_ref, lse_ref, rel_l2=REL_L2, out_tol=
     assert rel <= rel_l2, f"{name}: output relative L2 {rel:.3g} > {rel_l2}"
 
 
-def check_small(w, partition_tokens=None, fill="normal", rel_l2=REL_L2, seed=None):
+def check_small(w, partition_tokens=None, fill="normal", rel_l2=REL_L2, seed=None, tweak=None):
     """Whole-workload parity: routing, append (whole pool, bitwise), gather
-    (bitwise, every sequence and shard), partials and merged outputs."""
+    (bitwise, every sequence and shard), partials and merged outputs.  ``tweak``,
+    if given, edits the CPU tensors in place before both sides see them."""
     import decode_attention_paged_kv_amd as P
 
     say(f"[parity] {w.name} N={w.n_seqs} Hq={w.n_q_heads} Hkv={w.n_kv_heads} dk={w.dk} dv={w.dv} "
         f"bs={w.block_size} {w.dtype} S={w.n_shards} I={w.interleave} lens={list(w.context_lens)[:8]}")
     Tc = wl.make_tensors(w, "cpu", fill=fill, seed=seed)
+    if tweak is not None:
+        tweak(Tc)
     H = {k: to_np(v) for k, v in Tc.items()}
     dev = torch.device("cuda")
     T = {k: (None if v is None else v.to(dev)) for k, v in Tc.items()}

@@ -192,6 +192,41 @@ def test_error_flag_on_bad_block_id():
     assert torch.isfinite(step.out[0]).all()
 
 
+def test_latent_score_far_above_first_tile():
+    """Each sequence's appended token carries a key whose score is ~120 (log2 units)
+    above every other: the latent kernel, whose reference max comes from the first
+    tile of a partition, has to redo that partition against the exact max.  In the
+    700-token sequence only the second partition holds the spike."""
+    w = wl.small("latent_spike", [150, 700], 128, 1, 576, 512, 64, wl.BF16, partition_tokens=512,
+                 latent=True, seed=11)
+
+    def spike(T):
+        T["q"][:, :, 0] += 10.0
+        T["k_new"][:, :, 0] = 200.0
+
+    step, ref = check_small(w, tweak=spike, rel_l2=LATENT_REL_L2)
+    # every head's spike is > 64 log2 units (44 nats) above the other scores (< ~5 nats)
+    assert ref["lse"].min() > 50.0
+
+
+def test_error_flag_on_bad_block_id_latent():
+    """Latent kernel: a tile whose block id is invalid is skipped (copied from zeros,
+    weights 0) and reported; the outputs stay finite."""
+    import decode_attention_paged_kv_amd as P
+
+    w = wl.small("bad_latent", [300, 300], 128, 1, 576, 512, 64, wl.BF16, partition_tokens=128,
+                 latent=True, seed=12)
+    T = wl.make_tensors(w, "cuda")
+    T["block_table"][1, 0, 2] = w.n_blocks + 5
+    step = P.DecodeStep(2, 128, 1, 576, 512, 64, 300, partition_tokens=128, device="cuda",
+                        kv_dtype=torch.bfloat16, latent=True)
+    step(T["q"], T["k_new"], T["v_new"], T["k_cache"], T["v_cache"], T["block_table"],
+         T["context_lens"])
+    torch.cuda.synchronize()
+    assert int(step.err_flag.item()) & P.ERR_BLOCK_ID
+    assert torch.isfinite(step.out).all()
+
+
 def test_error_flag_on_short_table():
     """A context longer than the block table holds is reported, not read."""
     import decode_attention_paged_kv_amd as P
