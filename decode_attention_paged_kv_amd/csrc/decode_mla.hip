@@ -115,6 +115,14 @@ __device__ inline const char* uniform_ptr(const char* p) {
   return reinterpret_cast<const char*>((uint64_t(hi) << 32) | lo);
 }
 
+// Pins a value at this point of the instruction stream: empty asm statements keep their
+// order with the MFMA statements, so work between two pins stays in that MFMA's shadow
+// instead of being moved by the compiler's own passes.
+template <typename T>
+__device__ inline void pin(T& v) {
+  asm volatile("" : "+v"(v));
+}
+
 __device__ inline uint32_t lds_address(const void* p) {
   return uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)p));
 }
@@ -212,8 +220,10 @@ void decode_mla_kernel(DecodeArgs a) {
   stage_table(tbl_base);
   __syncthreads();
 
-  // physical block of tile i (uniform); -1 if invalid (flag raised)
-  auto tile_block = [&](int i) -> int {
+  // Block-table entry of tile i as read from LDS (restaging first if the entry lies in
+  // another chunk of the table); finish_tile turns it into the wave-uniform block id.
+  // Split so that the LDS read can be issued early and its latency hidden.
+  auto table_entry = [&](int i) -> int {
     const int e = (t_begin + i * TT) / bs;
     if (e - tbl_base >= TBL || e < tbl_base) {   // other chunk of the table (long partitions)
       PA_WAIT_VM(0);
@@ -222,12 +232,7 @@ void decode_mla_kernel(DecodeArgs a) {
       stage_table(tbl_base);
       __syncthreads();
     }
-    const int v = __builtin_amdgcn_readfirstlane(tbl_s[e - tbl_base]);
-    if (v < 0) {
-      if (tid == 0) raise_flag(a.flag, v == -3 ? kErrCapacity : kErrBlockId);
-      return -1;
-    }
-    return v;
+    return tbl_s[e - tbl_base];
   };
 
   // Copy of tile i: LDS slot s of the tile holds token row s / 72, chunk (s % 72) ^ g(row).
@@ -243,8 +248,12 @@ void decode_mla_kernel(DecodeArgs a) {
     uint32_t dst;
     int rows;
   };
-  auto begin_tile = [&](int i) -> Copy {
-    const int phys = __builtin_amdgcn_readfirstlane(tile_block(i));
+  auto finish_tile = [&](int i, int entry) -> Copy {
+    int phys = __builtin_amdgcn_readfirstlane(entry);
+    if (phys < 0) {   // invalid block id (-2) or an entry past the row (-3)
+      if (tid == 0) raise_flag(a.flag, phys == -3 ? kErrCapacity : kErrBlockId);
+      phys = -1;
+    }
     const int tok0 = t_begin + i * TT;
     const char* src = phys >= 0
         ? kc + ((int64_t(phys) * a.hkv + kvh) * bs + (tok0 % bs)) * int64_t(ROW_BYTES)
@@ -253,22 +262,41 @@ void decode_mla_kernel(DecodeArgs a) {
     bad = (bad & ~(1u << slot)) | (uint32_t(phys < 0) << slot);
     return Copy{uniform_ptr(src), kt_lds + slot * TILE_BYTES, phys < 0 ? TT : min(TT, t_end - tok0)};
   };
+  auto begin_tile = [&](int i) -> Copy { return finish_tile(i, table_entry(i)); };
   // Slot s = (k NW + w) 64 + lane = s0 + 256 k: with s0 = 72 t0 + x0 and 256 = 3*72 + 40,
   // row t = t0 + 3k + q and chunk x = y - 72 q for y = x0 + 40k, q = floor(y / 72) =
-  // (57 y) >> 12 (exact for y < 392; here y <= 71 + 40*8).
+  // (57 y) >> 12 (exact for y < 392; here y <= 71 + 40*8).  Offsets of a full tile are
+  // computed once; the last, partial tile recomputes them with its rows clamped.
   const int t0 = (wave * 64 + lane) / ROW_CHUNKS;
   const int x0 = (wave * 64 + lane) % ROW_CHUNKS;
   static_assert(NW * 64 == 3 * ROW_CHUNKS + 40 && COPIES <= 9, "slot stepping above");
-  auto copy_piece = [&](const Copy& cp, int k) {
+  auto slot_offset = [&](int k, int rows) -> uint32_t {
     int t0o = t0, x0o = x0;
     asm volatile("" : "+v"(t0o), "+v"(x0o));
     const uint32_t y = uint32_t(x0o + 40 * k);
     const uint32_t qq = __umul24(y, 57u) >> 12;   // 24-bit multiplies: full rate
     const int t = t0o + 3 * k + int(qq);
     const uint32_t x = y - __umul24(qq, uint32_t(ROW_CHUNKS));
-    const uint32_t row_src = uint32_t(min(t, cp.rows - 1));
-    const uint32_t off = __umul24(row_src, uint32_t(ROW_BYTES)) + ((x ^ uint32_t(swz(t))) << 4);
-    copy16_to_lds(cp.src, off, cp.dst + uint32_t((k * NW + wave) * 64 * 16));
+    const uint32_t row_src = uint32_t(min(t, rows - 1));
+    return __umul24(row_src, uint32_t(ROW_BYTES)) + ((x ^ uint32_t(swz(t))) << 4);
+  };
+  uint32_t full_off[COPIES];
+#pragma unroll
+  for (int k = 0; k < COPIES; ++k) {
+    full_off[k] = slot_offset(k, TT);
+    asm volatile("" : "+v"(full_off[k]));
+  }
+  auto copy_piece = [&](const Copy& cp, int k) {
+    const uint32_t dst = cp.dst + uint32_t((k * NW + wave) * 64 * 16);
+    if (cp.rows == TT) {
+      copy16_to_lds(cp.src, full_off[k], dst);
+    } else {   // partial tile (a separate asm statement, so the two are not merged)
+      const uint32_t off = slot_offset(k, cp.rows);
+      asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 ; partial tile"
+                   :
+                   : "v"(off), "s"(cp.src), "s"(dst)
+                   : "memory", "m0");
+    }
   };
   auto issue_tile = [&](int i) {
     const Copy cp = begin_tile(i);
@@ -472,69 +500,97 @@ void decode_mla_kernel(DecodeArgs a) {
       // everyone's copies of tile i+1 are in, everyone is done with tile i-1 (whose buffer
       // tile i+2 takes), and tile i-1's overflow flags are visible
       lds_barrier();
-      if (i > 0 && any_overflow((i - 1) & 1)) {
-        ok = false;
-        break;
-      }
+      // LDS reads consumed later, so their latency hides under the MFMAs: tile i-1's
+      // overflow flags (checked at the end of the iteration) and tile i+2's table entry
+      const int4 flags = *reinterpret_cast<const int4*>(&ovf_s[(i + 1) & 1][0]);
+      const bool copy_next = i + 2 < n_tiles;
+      const int entry = copy_next ? table_entry(i + 2) : 0;
       const int valid = tile_valid(i);
       float sc[16], m0 = -INFINITY, m1 = -INFINITY, mx = -INFINITY, mxo = -INFINITY, mc = 0.f;
       float part = 0.f, pe[16];
       bf16x8_t pop[2];
-      // softmax of tile i in small pieces (each fits the shadow of one MFMA): masks, row
-      // max, reference and overflow flag, weights, packing
-      constexpr int kSoftSteps = 30;
+      // Softmax of tile i in small pieces, each a few VALU instructions (the shadow of one
+      // MFMA): masks, row max, reference and overflow flag, weights, packing.  Steps 0..18
+      // run among the score MFMAs of tile i+1, steps 19..29 among the first output MFMAs
+      // of tile i (whose second k-step needs the second weight operand only from MFMA 16).
       auto softmax_piece = [&](int step) {
         if (step < 4) {
-          const int lim = valid - 4 * c32;
+          int lim = valid - 4 * c32;
+          pin(lim);
 #pragma unroll
-          for (int e = 4 * step; e < 4 * step + 4; ++e)
-            sc[e] = 8 * (e >> 2) + (e & 3) < lim ? s_cur[e] : -INFINITY;
+          for (int e = 4 * step; e < 4 * step + 4; ++e) {
+            float v = s_cur[e];
+            pin(v);
+            sc[e] = 8 * (e >> 2) + (e & 3) < lim ? v : -INFINITY;
+            pin(sc[e]);
+          }
         } else if (step == 4) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) m0 = fmaxf(m0, sc[e]);
+          pin(m0);
         } else if (step == 5) {
 #pragma unroll
           for (int e = 8; e < 16; ++e) m1 = fmaxf(m1, sc[e]);
+          pin(m1);
         } else if (step == 6) {
           mx = fmaxf(m0, m1);
           mxo = __shfl_xor(mx, 32);
+          pin(mxo);
         } else if (step == 8) {
           mx = fmaxf(mx, mxo);
           if (m_ref == -INFINITY) m_ref = mx;   // first tile with a valid token of this head
           const bool ovf = __any(mx != -INFINITY && (mx - m_ref) * c > kOverflow);
           if (lane == 0) ovf_s[i & 1][wave] = ovf ? 1 : 0;
           mc = (m_ref == -INFINITY) ? 0.f : m_ref * c;
-        } else if (step >= 9 && step < 25) {
-          const int e = step - 9;
+          pin(mc);
+          pin(m_ref);
+        } else if ((step >= 9 && step < 17) || (step >= 19 && step < 27)) {
+          const int e = step < 17 ? step - 9 : step - 11;
           pe[e] = __builtin_amdgcn_exp2f(fmaf(sc[e], c, -mc));
           part += pe[e];
-        } else if (step >= 25 && step < 29) {
-          const int e0 = 4 * (step - 25);
+          pin(pe[e]);
+          pin(part);
+        } else if (step == 17 || step == 18 || step == 27 || step == 28) {
+          const int e0 = step < 19 ? 4 * (step - 17) : 8 + 4 * (step - 27);
 #pragma unroll
           for (int e = e0; e < e0 + 4; ++e) pop[e >> 3][e & 7] = (__bf16)pe[e];
+          pin(pop[e0 >> 3]);
         } else if (step == 29) {
           lsum += part;
         }
       };
-      const bool copy_next = i + 2 < n_tiles;
+      constexpr int kFirstSteps = 19;   // steps among the score MFMAs
       Copy cp{};
-      if (copy_next) cp = begin_tile(i + 2);
       f32x16_t s_next = s_cur;
       if (has_next) {
+        // slot ks: the copy of tile i+2 every fourth MFMA (ks = 1, 5, .., 33), softmax
+        // steps in the other slots, in order
         scores(tile_ptr(i + 1), s_next, [&](int ks) {
-          if (ks >= 2 && ks < 2 + kSoftSteps) softmax_piece(ks - 2);
+          if ((ks & 3) == 1) {
+            const int k = ks >> 2;
+            if (copy_next) {
+              if (k == 0) cp = finish_tile(i + 2, entry);
+              copy_piece(cp, k);
+            }
+          } else {
+            const int step = ks - (ks + 2) / 4;   // index among the non-copy slots
+            if (step < kFirstSteps) softmax_piece(step);
+          }
         });
       } else {
 #pragma unroll
-        for (int step = 0; step < kSoftSteps; ++step) softmax_piece(step);
+        for (int step = 0; step < kFirstSteps; ++step) softmax_piece(step);
       }
       // one copy of the output MFMAs in the loop: a branch around them would join the
-      // output tiles in a phi outside the AGPR file.  The copies of tile i+2 go in their
-      // shadow.
+      // output tiles in a phi outside the AGPR file
       outputs(tile_ptr(i), pop, o, [&](int n) {
-        if ((n & 1) && (n >> 1) < COPIES && copy_next) copy_piece(cp, n >> 1);
+        if (n < 30 - kFirstSteps) softmax_piece(kFirstSteps + n);
       });
       s_cur = s_next;
+      if (i > 0 && (flags.x | flags.y | flags.z | flags.w) != 0) {   // tile i-1 overflowed
+        ok = false;
+        break;
+      }
     }
     if (ok) {   // the last tile's flags: no later iteration reads them
       lds_barrier();
