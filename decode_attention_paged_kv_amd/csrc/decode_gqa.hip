@@ -32,8 +32,10 @@
 //    entries are zeroed by select, so unused cache slots (whatever they hold) never
 //    reach the sums.
 //  * Block ids: each wave loads 64 consecutive block-table entries with one vector load
-//    and reads them back one at a time with readlane.  Loads of the next 32 tokens are
-//    issued before the current 32 are processed (two register buffers).
+//    and reads them back one at a time with readlane.  The next step's keys are loaded
+//    into the key registers as soon as the scores have used them, its values into the
+//    value registers as soon as the output product has, so each wave keeps a step of
+//    loads in flight while it computes, without a second register buffer.
 #include <math.h>
 
 #include "pa_common.h"
@@ -70,14 +72,23 @@ __device__ inline uint32_t keep(uint32_t w, bool lo_ok, bool hi_ok) {
 
 template <int D, int SUBS>
 struct Tile {
+  static_assert(SUBS % 2 == 0, "the output product takes sub-tiles in pairs");
   static constexpr int KJ = D / 32;  // score MFMAs per sub-tile
   static constexpr int NT = D / 16;  // output tiles of 16 d rows
   bf16x8_t k[SUBS][KJ];
   uint2 v[SUBS][NT];
-  int tok0[SUBS];  // local token of the first row of each sub-tile (-1: no sub-tile)
 };
 
-template <int D, int NW, bool PREFETCH, int SUBS>
+// Where a step's sub-tiles are: local token of the first row (-1: no sub-tile), cache
+// offset of its (block, KV head) and row within the block (both 0 when absent).
+template <int SUBS>
+struct Step {
+  int tok0[SUBS];
+  int64_t base[SUBS];
+  int sub[SUBS];
+};
+
+template <int D, int NW, int SUBS>
 __global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeArgs a) {
   using TileT = Tile<D, SUBS>;
   constexpr int KJ = TileT::KJ;
@@ -156,45 +167,50 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeArgs a) {
     return __builtin_amdgcn_readlane(tbl, e - tbl_base);
   };
 
-  // all key loads of a step are issued before its value loads, so the scores can start
-  // while the values are still on their way
-  auto load = [&](TileT& tl, int s) {
-    int64_t base[SUBS];
-    int sub[SUBS];
+  // Loads are split by operand: the next step's keys go into the key registers as soon as
+  // the scores have consumed them, its values into the value registers as soon as the
+  // output product has, so every wave keeps a step of loads in flight while it computes.
+  using StepT = Step<SUBS>;
+  auto locate = [&](StepT& st, int s) {
 #pragma unroll
     for (int t = 0; t < SUBS; ++t) {
       const int u_rel = SUBS * s + t;
-      tl.tok0[t] = -1;
-      base[t] = 0;
-      sub[t] = 0;
+      st.tok0[t] = -1;
+      st.base[t] = 0;
+      st.sub[t] = 0;
       if (u_rel < n_u) {
         const int u = u0 + u_rel;
         const int e = u / spb;
         const int phys = block_of(e);
         if (phys >= 0) {
-          tl.tok0[t] = u << 4;
-          base[t] = (int64_t(phys) * a.hkv + kvh) * kv_stride;
-          sub[t] = (u - e * spb) << 4;
+          st.tok0[t] = u << 4;
+          st.base[t] = (int64_t(phys) * a.hkv + kvh) * kv_stride;
+          st.sub[t] = (u - e * spb) << 4;
         } else if (lane == 0) {
           raise_flag(a.flag, phys == -3 ? kErrCapacity : kErrBlockId);
         }
       }
     }
+  };
+  // Loads are unconditional (an absent sub-tile reads the first rows of block 0, which
+  // always exist, and is masked afterwards), so the compiler's waits can count loads
+  // exactly instead of waiting for all of them after a branch.
+  auto load_k = [&](TileT& tl, const StepT& st) {
 #pragma unroll
-    for (int t = 0; t < SUBS; ++t)
-      if (tl.tok0[t] >= 0) {
-        const uint16_t* kp = kc + base[t] + int64_t(sub[t] + col) * D + 8 * grp;
+    for (int t = 0; t < SUBS; ++t) {
+      const uint16_t* kp = kc + st.base[t] + int64_t(st.sub[t] + col) * D + 8 * grp;
 #pragma unroll
-        for (int j = 0; j < KJ; ++j) tl.k[t][j] = *reinterpret_cast<const bf16x8_t*>(kp + 32 * j);
-      }
+      for (int j = 0; j < KJ; ++j) tl.k[t][j] = *reinterpret_cast<const bf16x8_t*>(kp + 32 * j);
+    }
+  };
+  auto load_v = [&](TileT& tl, const StepT& st) {
 #pragma unroll
-    for (int t = 0; t < SUBS; ++t)
-      if (tl.tok0[t] >= 0) {
-        const uint16_t* vp = vc + base[t] + int64_t(col) * bs + sub[t] + 4 * grp;
+    for (int t = 0; t < SUBS; ++t) {
+      const uint16_t* vp = vc + st.base[t] + int64_t(col) * bs + st.sub[t] + 4 * grp;
 #pragma unroll
-        for (int n = 0; n < NT; ++n)
-          tl.v[t][n] = *reinterpret_cast<const uint2*>(vp + int64_t(16 * n) * bs);
-      }
+      for (int n = 0; n < NT; ++n)
+        tl.v[t][n] = *reinterpret_cast<const uint2*>(vp + int64_t(16 * n) * bs);
+    }
   };
 
   const float c = a.scale * kLog2e;
@@ -204,22 +220,25 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeArgs a) {
 #pragma unroll
   for (int n = 0; n < NT; ++n) o[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](const TileT& tl) {
+  // one step: scores of the sub-tiles, then after_scores() (the key registers are free),
+  // softmax and the output product, then after_output() (the value registers are free)
+  auto compute = [&](TileT& tl, const StepT& st, auto&& after_scores, auto&& after_output) {
     float sc[SUBS][4];
 #pragma unroll
     for (int t = 0; t < SUBS; ++t) {
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-      if (tl.tok0[t] >= 0) {
+      if (st.tok0[t] >= 0) {
 #pragma unroll
         for (int j = 0; j < KJ; ++j) acc = mfma16x16x32(tl.k[t][j], qop[j], acc);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int tok = tl.tok0[t] + 4 * grp + i;
-        const bool ok = tl.tok0[t] >= 0 && tok < t_end;
+        const int tok = st.tok0[t] + 4 * grp + i;
+        const bool ok = st.tok0[t] >= 0 && tok < t_end;
         sc[t][i] = ok ? acc[i] : -INFINITY;
       }
     }
+    after_scores();
     float mt = m;
 #pragma unroll
     for (int t = 0; t < SUBS; ++t)
@@ -250,7 +269,7 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeArgs a) {
     for (int t = 0; t < SUBS; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        ok[t][i] = tl.tok0[t] >= 0 && tl.tok0[t] + 4 * grp + i < t_end;
+        ok[t][i] = st.tok0[t] >= 0 && st.tok0[t] + 4 * grp + i < t_end;
         full = full && ok[t][i];
       }
 #pragma unroll
@@ -279,27 +298,26 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeArgs a) {
         o[n] = mfma16x16x32(vop, plo, o[n]);
       }
     }
+    after_output();
   };
 
-  if (PREFETCH) {
-    if (s_lo < s_hi) {
-      TileT A, B;
-      load(A, s_lo);
-      int s = s_lo;
-      while (true) {
-        if (s + 1 < s_hi) load(B, s + 1);
-        compute(A);
-        if (++s >= s_hi) break;
-        if (s + 1 < s_hi) load(A, s + 1);
-        compute(B);
-        if (++s >= s_hi) break;
-      }
-    }
-  } else {
+  if (s_lo < s_hi) {
+    TileT A;
+    StepT cur, nxt;
+    locate(cur, s_lo);
+    load_k(A, cur);
+    load_v(A, cur);
     for (int s = s_lo; s < s_hi; ++s) {
-      TileT A;
-      load(A, s);
-      compute(A);
+      // the step after the wave's last is located as absent (block 0, masked): its loads
+      // are issued anyway, so no branch sits around a load
+      compute(
+          A, cur,
+          [&] {
+            locate(nxt, s + 1 < s_hi ? s + 1 : n_steps);
+            load_k(A, nxt);
+          },
+          [&] { load_v(A, nxt); });
+      cur = nxt;
     }
   }
 
@@ -345,9 +363,6 @@ bool gqa_supported(const DecodeArgs& a) {
 #ifndef PA_GQA_WAVES
 #define PA_GQA_WAVES 8
 #endif
-#ifndef PA_GQA_PREFETCH
-#define PA_GQA_PREFETCH 0
-#endif
 #ifndef PA_GQA_SUBS
 #define PA_GQA_SUBS 2
 #endif
@@ -356,8 +371,8 @@ int gqa_workgroup_threads() { return 64 * PA_GQA_WAVES; }
 
 int gqa_workgroups_per_cu(int dk) {
   int n = 0;
-  const void* f = dk == 128 ? (const void*)decode_gqa_kernel<128, PA_GQA_WAVES, PA_GQA_PREFETCH != 0, PA_GQA_SUBS>
-                            : (const void*)decode_gqa_kernel<64, PA_GQA_WAVES, PA_GQA_PREFETCH != 0, PA_GQA_SUBS>;
+  const void* f = dk == 128 ? (const void*)decode_gqa_kernel<128, PA_GQA_WAVES, PA_GQA_SUBS>
+                            : (const void*)decode_gqa_kernel<64, PA_GQA_WAVES, PA_GQA_SUBS>;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, f, 64 * PA_GQA_WAVES, 0) != hipSuccess) {
     (void)hipGetLastError();
     return 0;
@@ -370,11 +385,10 @@ hipError_t launch_decode_gqa(const DecodeArgs& a, hipStream_t st) {
   const int chunks = (g + 15) / 16;
   const dim3 grid(a.max_parts, a.n_seqs * a.n_shards, a.hkv * chunks);
   constexpr int NW = PA_GQA_WAVES;
-  constexpr bool PF = PA_GQA_PREFETCH != 0;
   if (a.dk == 128)
-    hipLaunchKernelGGL((decode_gqa_kernel<128, NW, PF, PA_GQA_SUBS>), grid, dim3(64 * NW), 0, st, a);
+    hipLaunchKernelGGL((decode_gqa_kernel<128, NW, PA_GQA_SUBS>), grid, dim3(64 * NW), 0, st, a);
   else
-    hipLaunchKernelGGL((decode_gqa_kernel<64, NW, PF, PA_GQA_SUBS>), grid, dim3(64 * NW), 0, st, a);
+    hipLaunchKernelGGL((decode_gqa_kernel<64, NW, PA_GQA_SUBS>), grid, dim3(64 * NW), 0, st, a);
   return hipGetLastError();
 }
 
