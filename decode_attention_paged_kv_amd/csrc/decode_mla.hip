@@ -8,8 +8,9 @@
 // on one KV head both products are real dense contractions (about 240 flops per byte
 // read), so both run on the matrix cores (v_mfma_f32_32x32x16_bf16).
 //
-// One workgroup = one (partition, sequence x shard, KV head) with all 128 heads and four
-// waves, one per SIMD.  Wave w owns heads 32w .. 32w+31 from end to end, so waves share
+// The grid holds as many workgroups as can be resident at once; each takes every G-th
+// unit of work -- a (partition, sequence x shard, KV head), numbered densely over the
+// non-empty ones -- with all 128 heads and four waves, one per SIMD.  Wave w owns heads 32w .. 32w+31 from end to end, so waves share
 // nothing but the key/value tiles:
 //  * Tiles of 32 tokens (32 rows x 1152 B, contiguous inside a block) are copied HBM ->
 //    LDS with global_load_lds_dwordx4 (no registers involved) into a ring of three
@@ -45,6 +46,9 @@
 // at position c ^ g(t), g(t) = 4*bit1(t) + bits2..3(t), which spreads both the 32 rows of
 // a key-operand read and the 4 rows of a transposing read over distinct banks.
 #include <math.h>
+
+#include <algorithm>
+#include <atomic>
 
 #include "pa_common.h"
 #include "pa_launch.h"
@@ -176,24 +180,63 @@ void decode_mla_kernel(DecodeArgs a) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r32 = lane & 31, c32 = lane >> 5;   // 32x32x16 operand row/col, k-group
-  const int p = blockIdx.x;
-  const int b = blockIdx.y / a.n_shards;
-  const int r = blockIdx.y % a.n_shards;
-  const int kvh = blockIdx.z;
-  const int h0 = kvh * HEADS;
   const int bs = a.bs;
-
-  const int L = a.context_lens[b];
-  const int Lr = L > 0 ? shard_len(L, a.n_shards, a.interleave, r) : 0;
   const int T = a.part_tokens;
-  if (p == 0 && tid == 0 && (Lr + T - 1) / T > a.max_parts) raise_flag(a.flag, kErrCapacity);
-  const int t_begin = p * T;
-  const int t_end = min(t_begin + T, Lr);
-  const int64_t out_row = ((int64_t(b) * a.n_shards + r) * a.max_parts + p) * a.hq + h0;
-  if (t_begin >= t_end) {  // empty partition: lse = -inf, output rows left unwritten
-    if (tid < HEADS) a.part_lse[out_row + tid] = -INFINITY;
-    return;
-  }
+  const int Y = a.n_seqs * a.n_shards;   // (sequence, shard) pairs
+
+  // Units of work are the non-empty (pair y, partition p, KV head) triples, numbered
+  // densely in that order (KV head fastest); workgroup g takes units g, g + G, g + 2G, ..
+  // (G = the grid), so the work is spread evenly however the lengths fall, and every
+  // workgroup stays resident.  Pair y has min(ceil(L_y / T), max_parts) partitions (more
+  // is a capacity error, flagged).  Each wave walks the pairs in chunks of 64 with a
+  // prefix sum over its lanes; the walk only moves forward, as the units do.
+  auto parts_of = [&](int y) -> int {
+    if (y >= Y) return 0;
+    const int L = a.context_lens[y / a.n_shards];
+    const int Lr = L > 0 ? shard_len(L, a.n_shards, a.interleave, y % a.n_shards) : 0;
+    const int n = (Lr + T - 1) / T;
+    if (n > a.max_parts) raise_flag(a.flag, kErrCapacity);
+    return min(n, a.max_parts);
+  };
+  int w_chunk = 0;   // first pair of the walker's chunk
+  int w_base = 0;    // partition slots before it
+  int w_cnt = 0, w_incl = 0, w_total = 0;   // lane's count and inclusive prefix; chunk total
+  auto load_chunk = [&]() {
+    w_cnt = parts_of(w_chunk + lane);
+    w_incl = w_cnt;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int v = __shfl_up(w_incl, d);
+      if (lane >= d) w_incl += v;
+    }
+    w_total = __builtin_amdgcn_readfirstlane(__shfl(w_incl, 63));
+  };
+  load_chunk();
+
+  for (int unit = blockIdx.x;; unit += gridDim.x) {
+    // ---- resolve unit -> (pair y, partition p, KV head kvh); stop past the last pair
+    const int slot = unit / a.hkv;
+    const int kvh = unit - slot * a.hkv;
+    while (slot >= w_base + w_total && w_chunk < Y) {
+      w_base += w_total;
+      w_chunk += 64;
+      load_chunk();
+    }
+    if (w_chunk >= Y) break;
+    const int rel = slot - w_base;
+    const uint64_t hit = __ballot(w_incl > rel);
+    const int j = __builtin_amdgcn_readfirstlane(__builtin_ctzll(hit));
+    const int y = w_chunk + j;
+    const int p = rel - (__builtin_amdgcn_readfirstlane(__shfl(w_incl - w_cnt, j)));
+    const int b = y / a.n_shards;
+    const int r = y - b * a.n_shards;
+    const int h0 = kvh * HEADS;
+    const int L = a.context_lens[b];
+    const int Lr = shard_len(L, a.n_shards, a.interleave, r);
+    const int t_begin = p * T;
+    const int t_end = min(t_begin + T, Lr);
+    const int64_t out_row = ((int64_t(b) * a.n_shards + r) * a.max_parts + p) * a.hq + h0;
+    __syncthreads();   // the previous unit is done with the LDS
 
   const int32_t* row = a.block_table + (int64_t(b) * a.n_shards + r) * a.max_blocks;
   const int n_tiles = (t_end - t_begin + TT - 1) / TT;
@@ -667,6 +710,15 @@ void decode_mla_kernel(DecodeArgs a) {
     m_ref = m_exact;
   }
   finish(o, m_ref, lsum);
+  }
+
+  // partitions past a pair's last one: lse = -inf (their output rows are not written)
+  for (int y = blockIdx.x; y < Y; y += gridDim.x) {
+    const int n = parts_of(y);
+    for (int p = n; p < a.max_parts; ++p)
+      for (int i = tid; i < a.hq; i += 64 * NW)
+        a.part_lse[(int64_t(y) * a.max_parts + p) * a.hq + i] = -INFINITY;
+  }
 }
 
 }  // namespace
@@ -686,9 +738,28 @@ int mla_workgroups_per_cu() {
   return n;
 }
 
+int mla_grid(const DecodeArgs& a) {
+  // every workgroup resident: the CUs times the workgroups that fit on one, no more than
+  // there can be units
+  static std::atomic<int> per_cu{0};
+  int wpc = per_cu.load(std::memory_order_relaxed);
+  if (wpc <= 0) {
+    wpc = mla_workgroups_per_cu();
+    if (wpc <= 0) wpc = 1;
+    per_cu.store(wpc, std::memory_order_relaxed);
+  }
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
+    (void)hipGetLastError();
+    cus = 256;
+  }
+  const int64_t units = int64_t(a.n_seqs) * a.n_shards * a.max_parts * a.hkv;
+  return int(std::max<int64_t>(1, std::min<int64_t>(int64_t(cus) * wpc, units)));
+}
+
 hipError_t launch_decode_mla(const DecodeArgs& a, hipStream_t st) {
-  const dim3 grid(a.max_parts, a.n_seqs * a.n_shards, a.hkv);
-  hipLaunchKernelGGL(decode_mla_kernel, grid, dim3(64 * NW), 0, st, a);
+  hipLaunchKernelGGL(decode_mla_kernel, dim3(mla_grid(a)), dim3(64 * NW), 0, st, a);
   return hipGetLastError();
 }
 

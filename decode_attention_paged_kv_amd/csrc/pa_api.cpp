@@ -4,6 +4,7 @@
 #include <stdio.h>
 
 #include <algorithm>
+#include <vector>
 #include <string>
 
 #include "../../include/pa.h"
@@ -105,38 +106,84 @@ int32_t pa_choose_partition_tokens(const int32_t* context_lens_host, int32_t n_s
   a.dtype = dtype;
   a.v_cache = latent ? nullptr : static_cast<const void*>(&a);  // only its NULL-ness matters
   const pa::KernelChoice kc = pa::choose_kernel(a);
-  int cus = 0, dev = 0;
+  int cus = 0, xccs = 0, dev = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       cus <= 0) {
     (void)hipGetLastError();
     cus = 256;  // MI355X
   }
-  const int64_t slots = int64_t(cus) * (kc.workgroups_per_cu > 0 ? kc.workgroups_per_cu : 2);
-  // Cost of a partition size T, in token-times: the units (one workgroup each) run in
-  // ceil(units / slots) rounds of about T tokens plus a fixed per-unit cost (prologue,
-  // and writing then merging the partition's output rows).
+  if (hipDeviceGetAttribute(&xccs, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess || xccs <= 0 ||
+      cus % xccs != 0) {
+    (void)hipGetLastError();
+    xccs = cus == 256 ? 8 : 1;
+  }
+  // Cost of a partition size T, in token-times.  Workgroups are dispatched to the XCDs
+  // round-robin by their linear id (x fastest: the partition index), each XCD running
+  // (its CUs x workgroups per CU) at a time; the busiest XCD sets the number of rounds,
+  // each about T tokens plus a fixed per-unit cost (prologue, and writing then merging
+  // the partition's output rows).
+  const int64_t slots_per_xcd = int64_t(cus / xccs) * (kc.workgroups_per_cu > 0 ? kc.workgroups_per_cu : 2);
   const int64_t partial_bytes = int64_t(n_q_heads / n_kv_heads) * dv * 4 * 2;
   const int64_t token_bytes = int64_t(latent ? dk : dk + dv) * (dtype == PA_F32 ? 4 : 2);
   const int64_t overhead = 128 + partial_bytes / (token_bytes > 0 ? token_bytes : 1);
+  std::vector<int32_t> shard_len_v(size_t(n_seqs) * n_shards);
   int32_t longest = 0;
   for (int b = 0; b < n_seqs; ++b)
-    longest = std::max(longest, pa::shard_len(std::max(context_lens_host[b], 0), n_shards, interleave, 0));
+    for (int r = 0; r < n_shards; ++r) {
+      const int32_t Lr = pa::shard_len(std::max(context_lens_host[b], 0), n_shards, interleave, r);
+      shard_len_v[size_t(b) * n_shards + r] = Lr;
+      longest = std::max(longest, Lr);
+    }
   if (longest == 0) return block_size;
+  const int64_t Y = int64_t(n_seqs) * n_shards, Z = kc.units_per_partition;
   const int32_t max_m = (longest + block_size - 1) / block_size;
-  const int32_t step = std::max(1, max_m / 512);
+  // every multiple of the block size while the scan stays cheap, else a coarser grid
+  const int64_t work = int64_t(max_m) * Y * Z;
+  const int32_t step = work <= (int64_t(1) << 24) ? 1 : std::max<int32_t>(1, max_m / 512);
   int32_t best_T = block_size * max_m;
   double best_cost = 1e300;
+  std::vector<int64_t> per_xcd(static_cast<size_t>(xccs), 0);
+  std::vector<int64_t> load;
   for (int32_t m = 1; m <= max_m; m += (m < 16 ? 1 : step)) {
     const int64_t T = int64_t(block_size) * m;
-    int64_t units = 0;
-    for (int b = 0; b < n_seqs; ++b)
-      for (int r = 0; r < n_shards; ++r) {
-        const int64_t Lr = pa::shard_len(std::max(context_lens_host[b], 0), n_shards, interleave, r);
-        units += (Lr + T - 1) / T;
+    if (kc.persistent) {
+      // resident grid: unit u (pairs in order, then partitions, KV head fastest) goes to
+      // workgroup u mod G; the busiest workgroup's tokens plus per-unit costs decide
+      int64_t units = 0;
+      for (int64_t y = 0; y < Y; ++y) units += (shard_len_v[size_t(y)] + T - 1) / T * Z;
+      if (units == 0) continue;
+      const int64_t G = std::min<int64_t>(int64_t(cus) * (kc.workgroups_per_cu > 0 ? kc.workgroups_per_cu : 1), units);
+      load.assign(size_t(G), 0);
+      int64_t u = 0;
+      for (int64_t y = 0; y < Y; ++y) {
+        const int64_t Lr = shard_len_v[size_t(y)];
+        for (int64_t t0 = 0; t0 < Lr; t0 += T)
+          for (int64_t z = 0; z < Z; ++z, ++u) load[size_t(u % G)] += std::min<int64_t>(T, Lr - t0) + overhead;
       }
-    units *= kc.units_per_partition;
-    const int64_t rounds = (units + slots - 1) / slots;
+      const double cost = double(*std::max_element(load.begin(), load.end()));
+      if (cost < best_cost * (1 - 1e-9)) {
+        best_cost = cost;
+        best_T = int32_t(T);
+      }
+      continue;
+    }
+    const int64_t parts = (longest + T - 1) / T;   // grid x
+    std::fill(per_xcd.begin(), per_xcd.end(), 0);
+    for (int64_t y = 0; y < Y; ++y) {
+      const int64_t n_p = (shard_len_v[size_t(y)] + T - 1) / T;   // non-empty partitions
+      if (n_p == 0) continue;
+      for (int64_t z = 0; z < Z; ++z) {
+        // ids parts*(y + Y z) + p for p < n_p, counted per residue mod xccs
+        const int64_t base = (parts * (y + Y * z)) % xccs;
+        for (int x = 0; x < xccs; ++x) {
+          const int64_t first = ((x - base) % xccs + xccs) % xccs;   // smallest p with id % xccs == x
+          if (first < n_p) per_xcd[size_t(x)] += (n_p - 1 - first) / xccs + 1;
+        }
+      }
+    }
+    int64_t rounds = 0;
+    for (int x = 0; x < xccs; ++x) rounds = std::max(rounds, (per_xcd[size_t(x)] + slots_per_xcd - 1) / slots_per_xcd);
     const double cost = double(rounds) * double(std::min<int64_t>(T, longest) + overhead);
     if (cost < best_cost * (1 - 1e-9)) {
       best_cost = cost;

@@ -15,6 +15,7 @@ hipError_t dispatch_decode(const DecodeArgs& a, hipStream_t st);
 struct KernelChoice {
   int units_per_partition;
   int workgroups_per_cu;
+  bool persistent;   // a resident grid deals the units round-robin (else one per workgroup)
 };
 KernelChoice choose_kernel(const DecodeArgs& a);
 
