@@ -58,10 +58,17 @@ DESCRIBE = {
 }
 
 
-def kernel_source_hash():
+# Source files that make up each decode kernel: a committed counter summary stays valid
+# while these are unchanged.
+KERNEL_FILES = {"decode_gqa_kernel": ["decode_gqa.hip", "pa_common.h", "pa_launch.h"],
+                "decode_mla_kernel": ["decode_mla.hip", "pa_common.h", "pa_launch.h"],
+                "decode_generic_kernel": ["decode_generic.hip", "pa_common.h", "pa_launch.h"]}
+
+
+def kernel_source_hash(kernel):
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "decode_attention_paged_kv_amd", "csrc")
-    for fn in sorted(os.listdir(csrc)):
+    for fn in sorted(KERNEL_FILES[kernel]):
         with open(os.path.join(csrc, fn), "rb") as f:
             h.update(fn.encode() + f.read())
     return h.hexdigest()[:16]
@@ -69,13 +76,14 @@ def kernel_source_hash():
 
 def measured_traffic(config, launches_bytes):
     """HBM bytes per decode launch from the committed rocprofv3 counter summary,
-    if it was taken of the current kernel sources; else None."""
+    if it was taken of the current sources of that kernel; else None."""
     path = os.path.join(ROOT, "profiles", f"decode_{config}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         d = json.load(f)
-    if d.get("kernel_source_hash") != kernel_source_hash():
+    kernel = d.get("kernel")
+    if kernel not in KERNEL_FILES or d.get("kernel_source_hash") != kernel_source_hash(kernel):
         return None
     return d.get("hbm_bytes_per_launch")
 
