@@ -3,10 +3,13 @@
 ``pa_*`` functions mirror the C ABI in ``include/pa.h`` one to one (see ``_lib``).
 ``DecodeStep`` strings the four calls of one decode step together on one stream:
 slot routing, kv append, the partitioned attention and the LSE merge.
+``BlockPool`` is the host-side block accounting (fork, copy-on-write, reuse) whose
+copies ``pa_copy_blocks`` carries out on the device.
 """
 from ._lib import (  # noqa: F401
-    ERR_BLOCK_ID, ERR_CAPACITY, ERR_SLOT, LIB_PATH, PA_BF16, PA_F32, PaError, lib,
-    pa_choose_partition_tokens, pa_decode, pa_default_partition_tokens, pa_gather_kv, pa_kv_append, pa_max_partitions,
-    pa_merge_lse, pa_shard_length, pa_slot_mapping,
+    ERR_BLOCK_ID, ERR_CAPACITY, ERR_SLOT, LIB_PATH, PA_BF16, PA_F32, BlockPool, PaError,
+    PoolExhausted, lib, pa_choose_partition_tokens, pa_copy_blocks, pa_decode,
+    pa_default_partition_tokens, pa_gather_kv, pa_kv_append, pa_max_partitions, pa_merge_lse,
+    pa_shard_length, pa_slot_mapping,
 )
 from .step import DecodeStep  # noqa: F401

@@ -38,12 +38,30 @@ _SIGS = {
     "pa_max_partitions": [_i32, _i32, _i32, _i32],
     "pa_default_partition_tokens": [_i32, _i32, _i32, _i32, _i32, _i32],
     "pa_choose_partition_tokens": [_p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32],
+    "pa_copy_blocks": [_p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i64, _i32, _p, _p],
+    "pa_pool_add": [_p, _i64, _i64],
+    "pa_pool_append": [_p, _i64, _i64, _p, _i32, _p],
+    "pa_pool_fork": [_p, _i64, _i64],
+    "pa_pool_finish": [_p, _i64],
     "pa_last_error": [],
 }
 for _name, _args in _SIGS.items():
     _fn = getattr(lib, _name)
     _fn.argtypes = _args
     _fn.restype = ctypes.c_char_p if _name == "pa_last_error" else ctypes.c_int32
+# pool calls whose result is not a status
+for _name, _args, _res in (("pa_pool_create", [_i64, _i32], _p),
+                           ("pa_pool_destroy", [_p], None),
+                           ("pa_pool_num_free", [_p], _i64),
+                           ("pa_pool_length", [_p, _i64], _i64),
+                           ("pa_pool_num_blocks", [_p, _i64], _i64),
+                           ("pa_pool_refcount", [_p, _i64], _i32),
+                           ("pa_pool_table", [_p, _i64, _p, _i64], _i64)):
+    _fn = getattr(lib, _name)
+    _fn.argtypes = _args
+    _fn.restype = _res
+
+PA_ERR_EXHAUSTED, PA_ERR_SEQUENCE = -6, -7
 
 
 class PaError(RuntimeError):
@@ -208,3 +226,85 @@ def pa_gather_kv(k_cache, v_cache, block_table, seq, shard, context_len, n_shard
                             context_len, hkv, dk, dv, bs, nb, block_table.shape[2], n_shards,
                             interleave, _dtype_code(k_cache), _ptr(k_out), _ptr(v_out),
                             _ptr(err_flag), _stream(k_cache)))
+
+
+def pa_copy_blocks(k_cache, v_cache, pairs, err_flag=None):
+    """``pairs``: int64 GPU tensor ``[n][2]`` of (source, destination) block ids."""
+    _need(k_cache, None, 4, "k_cache")
+    _need(v_cache, k_cache.dtype, 4, "v_cache")
+    _need(pairs, torch.int64, 2, "pairs")
+    _need(err_flag, torch.int32, None, "err_flag")
+    nb, hkv, bs, dk = k_cache.shape
+    dv = 0
+    if v_cache is not None:
+        dv = v_cache.shape[2]
+        if tuple(v_cache.shape) != (nb, hkv, dv, bs):
+            raise ValueError("v_cache must be [n_blocks][n_kv_heads][dv][block_size]")
+    if pairs.shape[1] != 2:
+        raise ValueError("pairs must be [n][2]")
+    _check(lib.pa_copy_blocks(_ptr(k_cache), _ptr(v_cache), _ptr(pairs), pairs.shape[0], hkv, dk,
+                              dv, bs, nb, _dtype_code(k_cache), _ptr(err_flag), _stream(k_cache)))
+
+
+class PoolExhausted(PaError):
+    """The pool has too few free blocks for the request; nothing changed."""
+
+
+class BlockPool:
+    """Host-side block accounting (pa_pool_* in include/pa.h).  Sequence ids are ints."""
+
+    def __init__(self, n_blocks: int, block_size: int):
+        self._h = lib.pa_pool_create(int(n_blocks), int(block_size))
+        if not self._h:
+            raise PaError(-2, lib.pa_last_error().decode())
+        self.n_blocks = int(n_blocks)
+        self.block_size = int(block_size)
+
+    def __del__(self):
+        h, self._h = getattr(self, "_h", None), None
+        if h:
+            lib.pa_pool_destroy(h)
+
+    @staticmethod
+    def _status(rc):
+        if rc == PA_ERR_EXHAUSTED:
+            raise PoolExhausted(rc, lib.pa_last_error().decode())
+        _check(rc)
+
+    def add(self, seq: int, n_tokens: int = 0) -> None:
+        self._status(lib.pa_pool_add(self._h, seq, n_tokens))
+
+    def append(self, seq: int, n_tokens: int = 1):
+        """Returns the copy-on-write block copies, a list of (source, destination)."""
+        buf = (ctypes.c_int64 * 2)()
+        made = ctypes.c_int32(0)
+        self._status(lib.pa_pool_append(self._h, seq, n_tokens, buf, 1, ctypes.byref(made)))
+        return [(int(buf[0]), int(buf[1]))] if made.value else []
+
+    def fork(self, parent: int, child: int) -> None:
+        self._status(lib.pa_pool_fork(self._h, parent, child))
+
+    def finish(self, seq: int) -> None:
+        self._status(lib.pa_pool_finish(self._h, seq))
+
+    def num_free(self) -> int:
+        return int(lib.pa_pool_num_free(self._h))
+
+    def length(self, seq: int) -> int:
+        return int(lib.pa_pool_length(self._h, seq))
+
+    def num_blocks(self, seq: int) -> int:
+        return int(lib.pa_pool_num_blocks(self._h, seq))
+
+    def refcount(self, block: int) -> int:
+        return int(lib.pa_pool_refcount(self._h, block))
+
+    def table(self, seq: int):
+        n = self.num_blocks(seq)
+        if n < 0:
+            raise PaError(PA_ERR_SEQUENCE, f"no sequence {seq}")
+        buf = (ctypes.c_int32 * max(n, 1))()
+        got = lib.pa_pool_table(self._h, seq, buf, n)
+        if got != n:
+            raise PaError(PA_ERR_SEQUENCE, f"pa_pool_table returned {got}")
+        return [int(buf[j]) for j in range(n)]

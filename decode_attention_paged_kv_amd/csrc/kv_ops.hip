@@ -1,4 +1,4 @@
-// kv_ops.hip -- slot routing, kv append and the block-table gather.
+// kv_ops.hip -- slot routing, kv append, block copies and the block-table gather.
 //
 // kv append: a decode step stores the new token's key and value rows before the
 // attention reads them (qiita.com/systemdesignsimple "KV cache and continuous
@@ -6,6 +6,11 @@
 // is exact for any element type.
 // Slot routing and gather: placement by the DCP interleave rule and block-table
 // lookup, as in pa_common.h.
+// Block copy: a sequence about to write into a block it shares with others first
+// gets a private copy of that block (ai-compass.weeybrid.co.jp, "What is
+// PagedAttention?", section "Sharing common blocks and copy-on-write").
+#include <algorithm>
+
 #include "pa_common.h"
 #include "pa_launch.h"
 
@@ -80,7 +85,57 @@ __global__ void gather_kernel(const RAW* __restrict__ k_cache, const RAW* __rest
   }
 }
 
+// Block copy for copy-on-write: blockIdx.x is the pair, blockIdx.z the tensor (0 = keys,
+// 1 = values); the workgroups along y share the block's bytes in W-sized words.  A block
+// of one tensor is contiguous (all KV heads of one physical block), so the copy is a
+// plain contiguous move with coalesced loads and stores.
+template <typename W>
+__global__ void copy_blocks_kernel(char* __restrict__ k_cache, char* __restrict__ v_cache,
+                                   const int64_t* __restrict__ pairs, int64_t k_words,
+                                   int64_t v_words, int64_t n_blocks, int* flag) {
+  const int64_t i = blockIdx.x;
+  const int64_t src = pairs[2 * i];
+  const int64_t dst = pairs[2 * i + 1];
+  if (src < 0 || src >= n_blocks || dst < 0 || dst >= n_blocks) {
+    if (blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0) raise_flag(flag, kErrBlockId);
+    return;
+  }
+  if (src == dst) return;
+  const bool values = blockIdx.z != 0;
+  const int64_t words = values ? v_words : k_words;
+  W* base = reinterpret_cast<W*>(values ? v_cache : k_cache);
+  const W* s = base + src * words;
+  W* d = base + dst * words;
+  const int64_t stride = int64_t(gridDim.y) * blockDim.x;
+  for (int64_t e = int64_t(blockIdx.y) * blockDim.x + threadIdx.x; e < words; e += stride)
+    d[e] = s[e];
+}
+
 }  // namespace
+
+hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int64_t* pairs, int n_pairs,
+                              int64_t k_bytes, int64_t v_bytes, int64_t n_blocks, int* flag,
+                              hipStream_t st) {
+  // Widest word that divides both tensors' block sizes and both base addresses.
+  uint64_t bits = uint64_t(k_bytes) | uint64_t(reinterpret_cast<uintptr_t>(k_cache));
+  if (v_cache != nullptr) bits |= uint64_t(v_bytes) | uint64_t(reinterpret_cast<uintptr_t>(v_cache));
+  const int word = (bits % 16 == 0) ? 16 : (bits % 8 == 0) ? 8 : (bits % 4 == 0) ? 4 : (bits % 2 == 0) ? 2 : 1;
+  const int threads = 256;
+  const int64_t biggest = std::max(k_bytes, v_cache != nullptr ? v_bytes : int64_t(0)) / word;
+  const int64_t split = std::min<int64_t>((biggest + threads - 1) / threads, 64);
+  const dim3 grid(n_pairs, unsigned(std::max<int64_t>(split, 1)), v_cache != nullptr ? 2 : 1);
+  char* k = static_cast<char*>(k_cache);
+  char* v = static_cast<char*>(v_cache);
+  const int64_t kw = k_bytes / word, vw = v_bytes / word;
+  switch (word) {
+    case 16: hipLaunchKernelGGL(copy_blocks_kernel<uint4>, grid, dim3(threads), 0, st, k, v, pairs, kw, vw, n_blocks, flag); break;
+    case 8: hipLaunchKernelGGL(copy_blocks_kernel<uint2>, grid, dim3(threads), 0, st, k, v, pairs, kw, vw, n_blocks, flag); break;
+    case 4: hipLaunchKernelGGL(copy_blocks_kernel<uint32_t>, grid, dim3(threads), 0, st, k, v, pairs, kw, vw, n_blocks, flag); break;
+    case 2: hipLaunchKernelGGL(copy_blocks_kernel<uint16_t>, grid, dim3(threads), 0, st, k, v, pairs, kw, vw, n_blocks, flag); break;
+    default: hipLaunchKernelGGL(copy_blocks_kernel<uint8_t>, grid, dim3(threads), 0, st, k, v, pairs, kw, vw, n_blocks, flag); break;
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_slot_mapping(const int32_t* bt, const int32_t* lens, int n_seqs, int S, int I,
                                int bs, int max_blocks, int64_t n_blocks, int64_t* slots, int* flag,

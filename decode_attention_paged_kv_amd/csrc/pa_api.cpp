@@ -11,10 +11,13 @@
 #include "pa_common.h"
 #include "pa_launch.h"
 #include "pa_dispatch.h"
+#include "pa_error.h"
+
+namespace pa {
 
 namespace {
-
 thread_local std::string g_last_error;
+}
 
 int fail(int code, const char* fmt, ...) {
   char buf[512];
@@ -30,6 +33,15 @@ int ok() {
   g_last_error.clear();
   return PA_OK;
 }
+
+const char* last_error() { return g_last_error.c_str(); }
+
+}  // namespace pa
+
+namespace {
+
+using pa::fail;
+using pa::ok;
 
 int hip_status(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(PA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
@@ -57,7 +69,7 @@ int check_placement(int32_t n_shards, int32_t interleave, int32_t block_size) {
 
 extern "C" {
 
-const char* pa_last_error(void) { return g_last_error.c_str(); }
+const char* pa_last_error(void) { return pa::last_error(); }
 
 int32_t pa_shard_length(int32_t context_len, int32_t n_shards, int32_t interleave, int32_t shard) {
   if (context_len < 0 || n_shards < 1 || interleave < 1 || shard < 0 || shard >= n_shards) return -1;
@@ -233,6 +245,29 @@ int pa_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_ca
                                          n_kv_heads, dk, dv, block_size, n_blocks, dtype, err_flag,
                                          (hipStream_t)stream),
                     "pa_kv_append launch");
+}
+
+int pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* pairs, int32_t n_pairs,
+                   int32_t n_kv_heads, int32_t dk, int32_t dv, int32_t block_size, int64_t n_blocks,
+                   int32_t dtype, int32_t* err_flag, void* stream) {
+  REQUIRE(k_cache && pairs, PA_ERR_NULL, "pa_copy_blocks: k_cache and pairs must be non-NULL");
+  REQUIRE(valid_dtype(dtype), PA_ERR_UNSUPPORTED, "dtype=%d is not PA_F32 or PA_BF16", dtype);
+  REQUIRE(n_pairs >= 0 && n_pairs <= (1 << 22), PA_ERR_SHAPE, "n_pairs=%d must be in [0, 2^22]",
+          n_pairs);
+  REQUIRE(n_kv_heads >= 1 && n_kv_heads <= 65535, PA_ERR_SHAPE, "n_kv_heads=%d out of range", n_kv_heads);
+  REQUIRE(dk >= 1 && dk <= PA_MAX_HEAD_DIM, PA_ERR_UNSUPPORTED, "dk=%d must be in [1, %d]", dk, PA_MAX_HEAD_DIM);
+  REQUIRE(v_cache == nullptr || (dv >= 1 && dv <= PA_MAX_HEAD_DIM), PA_ERR_UNSUPPORTED,
+          "dv=%d must be in [1, %d]", dv, PA_MAX_HEAD_DIM);
+  REQUIRE(block_size >= 1 && block_size <= PA_MAX_BLOCK_SIZE, PA_ERR_UNSUPPORTED,
+          "block_size=%d must be in [1, %d]", block_size, PA_MAX_BLOCK_SIZE);
+  REQUIRE(n_blocks >= 1, PA_ERR_SHAPE, "n_blocks=%lld must be >= 1", (long long)n_blocks);
+  if (n_pairs == 0) return ok();
+  const int64_t es = dtype == PA_F32 ? 4 : 2;
+  const int64_t k_bytes = int64_t(n_kv_heads) * block_size * dk * es;
+  const int64_t v_bytes = v_cache != nullptr ? int64_t(n_kv_heads) * block_size * dv * es : 0;
+  return hip_status(pa::launch_copy_blocks(k_cache, v_cache, pairs, n_pairs, k_bytes, v_bytes,
+                                           n_blocks, err_flag, (hipStream_t)stream),
+                    "pa_copy_blocks launch");
 }
 
 int pa_decode(const void* q, const void* k_cache, const void* v_cache,

@@ -29,6 +29,9 @@ hipError_t launch_slot_mapping(const int32_t* bt, const int32_t* lens, int n_seq
 hipError_t launch_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                             const int64_t* slots, int n_tokens, int hkv, int dk, int dv, int bs,
                             int64_t n_blocks, int dtype, int* flag, hipStream_t st);
+hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int64_t* pairs, int n_pairs,
+                              int64_t k_bytes, int64_t v_bytes, int64_t n_blocks, int* flag,
+                              hipStream_t st);
 hipError_t launch_gather(const void* k_cache, const void* v_cache, const int32_t* bt_row,
                          int L_r, int hkv, int dk, int dv, int bs, int64_t n_blocks,
                          int max_blocks, int dtype, void* k_out, void* v_out, int* flag,

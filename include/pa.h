@@ -72,7 +72,10 @@ typedef enum pa_status {
   PA_ERR_SHAPE = -2,        /* a size is out of range or sizes are inconsistent   */
   PA_ERR_UNSUPPORTED = -3,  /* valid but not implemented (dtype, head size, ...)  */
   PA_ERR_BUFFER = -4,       /* a caller buffer is too small for the request       */
-  PA_ERR_HIP = -5           /* the HIP runtime reported an error on launch        */
+  PA_ERR_HIP = -5,          /* the HIP runtime reported an error on launch        */
+  PA_ERR_EXHAUSTED = -6,    /* a block pool has too few free blocks; nothing changed */
+  PA_ERR_SEQUENCE = -7      /* a block pool does not know the sequence id, or the id
+                               of a new sequence is already in use                  */
 } pa_status;
 
 typedef enum pa_dtype { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
@@ -167,6 +170,62 @@ int pa_gather_kv(const void* k_cache, const void* v_cache, const int32_t* block_
                  int32_t n_shards, int32_t interleave, int32_t dtype, void* k_out, void* v_out,
                  int32_t* err_flag, void* stream);
 
+/*
+ * pa_copy_blocks -- copy whole cache blocks, for copy-on-write ([PA], "Sharing common
+ * blocks and copy-on-write": before a sequence writes into a block other sequences
+ * share, it gets its own copy).  For each pair i, block pairs[2i] (source) is copied to
+ * block pairs[2i+1] (destination): all KV heads, the keys and, unless v_cache is NULL
+ * (latent cache), the values; bit-exact.
+ *   pairs: DEVICE int64 [n_pairs][2].  A pair with an id outside [0, n_blocks) is
+ *   skipped and sets *err_flag; src == dst is a no-op.  Destinations must be distinct
+ *   and must not be the source of another pair of the same call (else the content of
+ *   those blocks is unspecified).  Sizes as in pa_kv_append.
+ */
+int pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* pairs, int32_t n_pairs,
+                   int32_t n_kv_heads, int32_t dk, int32_t dv, int32_t block_size, int64_t n_blocks,
+                   int32_t dtype, int32_t* err_flag, void* stream);
+
+/*
+ * Block pool -- host-side accounting of a shared pool of fixed-size blocks ([PA]):
+ * each sequence has a table of physical blocks in logical order; a token goes into the
+ * last block while it has room, else into a newly taken block (block-table section);
+ * a finished sequence returns its blocks for anyone to reuse, nothing is compacted
+ * ("Reusing blocks freed when a request ends"); sequences forked from a parent share its
+ * blocks under a reference count, and a sequence about to write into a shared last
+ * block first takes a copy of it ("Sharing common blocks and copy-on-write"); when the
+ * pool runs out the request has to wait (limits section).
+ * Policy of this library: free blocks are handed out first-in first-out (initially
+ * 0, 1, .., n_blocks-1; a block whose count drops to 0 goes to the back).  All calls
+ * are HOST calls on an object that is not thread-safe; sequence ids are any int64 the
+ * caller chooses.  pa_pool_append is all-or-nothing: if the free blocks do not cover
+ * the new blocks and copies it needs, it changes nothing and returns PA_ERR_EXHAUSTED.
+ */
+typedef struct pa_block_pool pa_block_pool;
+/* NULL on invalid arguments or out of memory. */
+pa_block_pool* pa_pool_create(int64_t n_blocks, int32_t block_size);
+void pa_pool_destroy(pa_block_pool* pool);
+/* a new sequence (id not in use) with n_tokens tokens to store (0 allowed) */
+int pa_pool_add(pa_block_pool* pool, int64_t seq, int64_t n_tokens);
+/* store n_tokens more tokens of `seq`.  Copy-on-write copies made on the way are
+ * written to copies (HOST int64 [max_copies][2], (source, destination) block pairs, in
+ * order; they go to pa_copy_blocks before the new tokens are written); *n_copies gets
+ * their number (a single call makes at most one).  PA_ERR_BUFFER if max_copies is too
+ * small (nothing changed). */
+int pa_pool_append(pa_block_pool* pool, int64_t seq, int64_t n_tokens, int64_t* copies,
+                   int32_t max_copies, int32_t* n_copies);
+/* `child` (id not in use) starts with `parent`'s tokens, sharing its blocks */
+int pa_pool_fork(pa_block_pool* pool, int64_t parent, int64_t child);
+/* the sequence ends; blocks no other sequence uses become free */
+int pa_pool_finish(pa_block_pool* pool, int64_t seq);
+/* accounting: -1 on an unknown sequence or block */
+int64_t pa_pool_num_free(const pa_block_pool* pool);
+int64_t pa_pool_length(const pa_block_pool* pool, int64_t seq);
+int64_t pa_pool_num_blocks(const pa_block_pool* pool, int64_t seq);
+int32_t pa_pool_refcount(const pa_block_pool* pool, int64_t block);
+/* the sequence's physical block ids in logical order into table (HOST int32
+ * [capacity]); returns their number, or -1 (unknown sequence or capacity too small) */
+int64_t pa_pool_table(const pa_block_pool* pool, int64_t seq, int32_t* table, int64_t capacity);
+
 /* Host helpers (no device work).  Return -1 on invalid arguments. */
 int32_t pa_shard_length(int32_t context_len, int32_t n_shards, int32_t interleave, int32_t shard);
 int32_t pa_max_partitions(int32_t max_context_len, int32_t n_shards, int32_t interleave,
@@ -184,10 +243,12 @@ int32_t pa_default_partition_tokens(int32_t n_seqs, int32_t n_kv_heads, int32_t 
 /*
  * pa_choose_partition_tokens -- a partition size for a step whose context lengths the
  * caller knows on the host (context_lens_host: HOST int32 [n_seqs]).  Picks the multiple
- * of block_size that minimises (rounds of workgroups) x (tokens per workgroup + a fixed
- * per-workgroup cost), using the occupancy of the kernel pa_decode would run for this
- * shape (latent != 0: value = first dv entries of the key row) and the device's compute
- * unit count.  A heuristic of this library.  Returns -1 on invalid arguments.
+ * of block_size that minimises a model of how the kernel pa_decode would run for this
+ * shape (latent != 0: value = first dv entries of the key row) is dispatched: the
+ * busiest workgroup's tokens plus a fixed per-unit cost when the kernel keeps a resident
+ * grid, else the busiest XCD's rounds of workgroups x (partition tokens + that cost),
+ * with the kernel's occupancy and the device's compute-unit and XCD counts.  A heuristic
+ * of this library.  Returns -1 on invalid arguments.
  */
 int32_t pa_choose_partition_tokens(const int32_t* context_lens_host, int32_t n_seqs,
                                    int32_t n_q_heads, int32_t n_kv_heads, int32_t dk, int32_t dv,

@@ -149,6 +149,21 @@ def kv_append(k_cache: np.ndarray, v_cache, k_new: np.ndarray, v_new, slots: np.
     return k_out, v_out
 
 
+def copy_blocks(k_cache: np.ndarray, v_cache, pairs):
+    """Copy whole physical blocks, bit for bit: for each (source, destination) pair
+    every KV head's keys (and values, unless the cache is latent) of the source
+    block overwrite the destination's.  This is the private copy a sequence takes
+    before writing into a block it shares ([PA], "Sharing common blocks and
+    copy-on-write").  Pairs apply in order; returns new arrays."""
+    k_out = k_cache.copy()
+    v_out = None if v_cache is None else v_cache.copy()
+    for src, dst in pairs:
+        k_out[int(dst)] = k_out[int(src)]
+        if v_out is not None:
+            v_out[int(dst)] = v_out[int(src)]
+    return k_out, v_out
+
+
 def _rows(k_cache, v_cache, phys: np.ndarray, off: np.ndarray, dv: int):
     k = k_cache[phys, :, off, :]                        # [n][Hkv][dk]
     if v_cache is None:

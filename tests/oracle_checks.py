@@ -20,7 +20,10 @@ What each check compares against:
 * ``gather``         -- the oracle's gather equals that record, bit for bit;
 * ``slots``          -- the oracle's slot for each new token equals the generator's;
 * ``merge``          -- S interleaved shards merged equal the unsharded result, for
-                        two partition sizes, and merging is associative.
+                        two partition sizes, and merging is associative;
+* ``copy_on_write``  -- forked sequences appending through the block manager, with its
+                        block copies applied, read back exactly their own rows (kept
+                        in a per-sequence Python list).
 """
 from __future__ import annotations
 
@@ -291,6 +294,59 @@ def check_merge():
     return None
 
 
+def check_copy_on_write():
+    """Forked sequences that each append their own tokens, with the block copies the
+    block manager asks for carried out by ``copy_blocks``, read back through their
+    tables exactly the rows written for them: the shared prefix, then their own.  The
+    expected rows come from a per-sequence Python list, never from the cache."""
+    from oracle import block_manager as bm
+
+    for latent in (False, True):
+        bs, hkv, dk, dv, nb = 4, 2, 3, 2, 24
+        r = _rng(11)
+        cache = {"k": np.zeros((nb, hkv, bs, dk), np.float32),
+                 "v": None if latent else np.zeros((nb, hkv, dv, bs), np.float32)}
+        m = bm.BlockManager(nb, bs)
+        rows = {}                                     # seq -> list of (k_row, v_row)
+
+        def write(seq, n):
+            for _ in range(n):
+                before = len(m.copies)
+                m.append(seq, 1)
+                cache["k"], cache["v"] = pa.copy_blocks(cache["k"], cache["v"], m.copies[before:])
+                i = m.lengths[seq] - 1
+                slot = m.tables[seq][i // bs] * bs + i % bs
+                kn = r.standard_normal((1, hkv, dk)).astype(np.float32)
+                vn = None if latent else r.standard_normal((1, hkv, dv)).astype(np.float32)
+                cache["k"], cache["v"] = pa.kv_append(cache["k"], cache["v"], kn, vn,
+                                                      np.array([slot]), bs)
+                rows[seq].append((kn[0], kn[0][:, :dv] if latent else vn[0]))
+
+        m.add("P")
+        rows["P"] = []
+        write("P", 6)
+        for c in ("a", "b", "c"):
+            m.fork("P", c)
+            rows[c] = list(rows["P"])
+        write("a", 3)
+        write("b", 1)
+        write("P", 2)
+        m.fork("b", "d")
+        rows["d"] = list(rows["b"])
+        write("d", 5)
+        write("b", 2)
+        if len(m.copies) < 3:
+            return "copy-on-write: the scenario made fewer copies than planned"
+        for seq, want in rows.items():
+            bt = np.full((1, 8), -1, np.int32)
+            bt[0, :len(m.tables[seq])] = m.tables[seq]
+            K, V = pa.gather_sequence(cache["k"], cache["v"], bt, m.lengths[seq], 1, 1, bs, dv)
+            if not (np.array_equal(K, np.stack([x[0] for x in want]))
+                    and np.array_equal(V, np.stack([x[1] for x in want]))):
+                return f"copy-on-write (latent={latent}): sequence {seq} reads other rows"
+    return None
+
+
 ALL_CHECKS = {
     "bruteforce": check_bruteforce,
     "closed_forms": check_closed_forms,
@@ -300,4 +356,5 @@ ALL_CHECKS = {
     "gather": check_gather,
     "slots": check_slots,
     "merge": check_merge,
+    "copy_on_write": check_copy_on_write,
 }

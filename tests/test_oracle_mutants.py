@@ -17,6 +17,7 @@ _merge = pa.merge_lse
 _members = pa.shard_members
 _gather_shard = pa.gather_shard
 _kv_append = pa.kv_append
+_copy_blocks = pa.copy_blocks
 
 
 def _attn_variant(kind):
@@ -99,6 +100,19 @@ def _append_wrong_offset(k_cache, v_cache, k_new, v_new, slots, bs):
     return _kv_append(k_cache, v_cache, k_new, v_new, np.asarray(slots) + 1, bs)
 
 
+def _copy_keys_only(k_cache, v_cache, pairs):
+    k, _ = _copy_blocks(k_cache, None, pairs)
+    return k, None if v_cache is None else v_cache.copy()
+
+
+def _copy_reversed(k_cache, v_cache, pairs):
+    return _copy_blocks(k_cache, v_cache, [(d, s) for s, d in pairs])
+
+
+def _copy_nothing(k_cache, v_cache, pairs):
+    return k_cache.copy(), None if v_cache is None else v_cache.copy()
+
+
 MUTANTS = {
     "attention.head_map": ("attention", _attn_variant("head_map")),
     "attention.no_scale": ("attention", _attn_variant("no_scale")),
@@ -114,6 +128,9 @@ MUTANTS = {
     "gather.offset": ("gather_shard", _gather_offset_shift),
     "gather.v_from_k": ("gather_shard", _gather_v_from_k),
     "append.offset": ("kv_append", _append_wrong_offset),
+    "copy.keys_only": ("copy_blocks", _copy_keys_only),
+    "copy.reversed": ("copy_blocks", _copy_reversed),
+    "copy.nothing": ("copy_blocks", _copy_nothing),
 }
 
 
