@@ -23,7 +23,13 @@ What each check compares against:
                         two partition sizes, and merging is associative;
 * ``copy_on_write``  -- forked sequences appending through the block manager, with its
                         block copies applied, read back exactly their own rows (kept
-                        in a per-sequence Python list).
+                        in a per-sequence Python list);
+* ``fp8_table``      -- the E4M3 code values equal torch's float8_e4m3fn decoding;
+* ``fp8_rounding``   -- quantised codes equal torch's float8_e4m3fn cast inside the
+                        range (ties, subnormals, bf16 inputs, four scales), the error is
+                        within half an ulp, and the saturation/NaN readings hold;
+* ``fp8_decode``     -- the E4M3 step equals causal SDPA (fp64) over K/V decoded by
+                        torch and scaled per head, new rows cast by torch.
 """
 from __future__ import annotations
 
@@ -347,6 +353,143 @@ def check_copy_on_write():
     return None
 
 
+# ----------------------------------------------------------------------------------
+# FP8 (E4M3) cache: the oracle's code table and rounding against torch's float8_e4m3fn
+# conversions, the format's error bound, and the step against SDPA on values decoded
+# by torch
+# ----------------------------------------------------------------------------------
+def check_fp8_table():
+    import torch
+
+    from oracle import fp8_kv as f8
+
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    if not np.array_equal(np.isnan(ref), np.isnan(f8.E4M3)):
+        return "fp8 table: NaN codes differ from torch's float8_e4m3fn"
+    fin = ~np.isnan(ref)
+    if not np.array_equal(ref[fin], f8.E4M3[fin]) or f8.E4M3[0x7E] != 448.0:
+        return "fp8 table: values differ from torch's float8_e4m3fn"
+    return None
+
+
+def _fp8_probe_values():
+    """float32 values spanning every binade of E4M3, exact code values, the midpoints
+    between neighbouring codes (ties), the subnormal range and signed zeros."""
+    from oracle import fp8_kv as f8
+
+    r = _rng(41)
+    x = r.standard_normal(20000) * 2.0 ** r.integers(-14, 9, 20000)
+    pos = f8.E4M3[:0x7F]
+    mids = (pos[:-1] + pos[1:]) / 2
+    x = np.concatenate([x, pos, -pos, mids, -mids, [0.0, -0.0, 2.0 ** -10, 3 * 2.0 ** -11]])
+    return x.astype(np.float32)
+
+
+def check_fp8_rounding():
+    import torch
+
+    from oracle import fp8_kv as f8
+
+    x = _fp8_probe_values()
+    for s in (1.0, 0.37, 3.1, 2.0 ** -5):
+        s32 = np.float32(s)
+        y = torch.from_numpy(x) / torch.tensor(s32)
+        ref = y.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        got = f8.quantize(x, s32)
+        inside = np.abs(y.numpy()) < 448          # torch does not saturate; compared apart
+        if not np.array_equal(got[inside], ref[inside]):
+            return f"fp8 rounding (scale {s}): codes differ from torch's float8_e4m3fn cast"
+        # the format's own bound: half a unit in the last place
+        yv = y.numpy().astype(np.float64)
+        err = np.abs(f8.E4M3[got[inside]] - yv[inside])
+        bound = np.maximum(np.abs(yv[inside]) * 2.0 ** -4, 2.0 ** -10)
+        if np.any(err > bound):
+            return f"fp8 rounding (scale {s}): error above half an ulp"
+    # bf16 input rows are widened exactly before the division
+    xb = torch.from_numpy(x[:5000]).to(torch.bfloat16)
+    bits = xb.view(torch.int16).numpy().view(np.uint16)
+    yb = xb.float() / torch.tensor(np.float32(0.37))
+    ref = yb.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    inside = np.abs(yb.numpy()) < 448
+    if not np.array_equal(f8.quantize(bits, np.float32(0.37))[inside], ref[inside]):
+        return "fp8 rounding: bf16 inputs"
+    # saturation and NaN (the readings: +-448 beyond the range, NaN keeps its sign)
+    sat = f8.quantize(np.array([448, 449, 463.9, 464, 1e6, np.inf, -np.inf, -500, np.nan,
+                                -np.nan], np.float32), np.float32(1.0))
+    if sat.tolist() != [0x7E] * 6 + [0xFE, 0xFE, 0x7F, 0xFF]:
+        return f"fp8 saturation: {[hex(c) for c in sat]}"
+    return None
+
+
+def fp8_workloads():
+    import workloads as wl
+
+    return [
+        wl.small("f8_gqa", [5, 33, 17], 4, 2, 16, 16, 8, wl.BF16, partition_tokens=8, seed=51,
+                 kv_dtype=wl.FP8),
+        wl.small("f8_tensor_scale", [9, 40], 6, 3, 8, 8, 4, wl.F32, partition_tokens=16, seed=52,
+                 kv_dtype=wl.FP8, scale_per_head=False),
+        wl.small("f8_dcp", [3, 41, 64], 4, 2, 8, 8, 4, wl.BF16, n_shards=4, interleave=3,
+                 partition_tokens=4, seed=53, kv_dtype=wl.FP8),
+        wl.small("f8_latent", [17, 70], 8, 1, 24, 16, 8, wl.BF16, latent=True, partition_tokens=16,
+                 seed=54, kv_dtype=wl.FP8),
+    ]
+
+
+def check_fp8_decode():
+    """The E4M3 step equals the last row of causal SDPA (fp64) over K/V decoded with
+    torch's float8_e4m3fn conversion and multiplied by each head's scale; the
+    appended token's rows are torch's cast of new_row / scale."""
+    import torch
+    import torch.nn.functional as F
+
+    from oracle import fp8_kv as f8
+
+    def decode_torch(codes, scales, head_axis):
+        vals = torch.from_numpy(np.ascontiguousarray(codes)).view(torch.float8_e4m3fn).double().numpy()
+        shape = [1] * vals.ndim
+        shape[head_axis] = -1
+        return vals * scales.astype(np.float64).reshape(shape)
+
+    for w in fp8_workloads():
+        T = tensors_np(w)
+        Tp = w.partition_tokens
+        pmax = pa.max_partitions(int(w.context_lens.max()), w.n_shards, w.interleave, Tp)
+        res = f8.decode_step(T["q"], T["k_new"], T["v_new"], T["k_cache"], T["v_cache"],
+                             T["k_scale"], T["v_scale"], w.block_table, w.context_lens,
+                             w.n_shards, w.interleave, w.block_size, Tp, pmax, w.scale_f32, w.dv)
+        ks = np.resize(T["k_scale"], w.n_kv_heads).astype(np.float32)
+        vs = None if T["v_scale"] is None else np.resize(T["v_scale"], w.n_kv_heads).astype(np.float32)
+        for b in range(w.n_seqs):
+            Kc, Vc = contiguous_from_generator(w, T, b)    # codes; the new row is raw input
+            L = Kc.shape[0]
+            K = np.empty(Kc.shape)
+            V = np.empty(Vc.shape)
+            K[:L - 1] = decode_torch(Kc[:L - 1], ks, 1)
+            newk = torch.from_numpy(pa.widen(T["k_new"][b]).astype(np.float32))
+            kq = (newk / torch.from_numpy(ks)[:, None]).to(torch.float8_e4m3fn)
+            K[L - 1] = kq.double().numpy() * ks[:, None]
+            if T["v_new"] is None:
+                V[:] = K[:, :, :w.dv]
+            else:
+                V[:L - 1] = decode_torch(Vc[:L - 1], vs, 1)
+                newv = torch.from_numpy(pa.widen(T["v_new"][b]).astype(np.float32))
+                vq = (newv / torch.from_numpy(vs)[:, None]).to(torch.float8_e4m3fn)
+                V[L - 1] = vq.double().numpy() * vs[:, None]
+            r = _rng(200 + b)
+            Q = r.standard_normal((L, w.n_q_heads, w.dk))
+            Q[L - 1] = pa.widen(T["q"][b])
+            qt = torch.from_numpy(Q).permute(1, 0, 2)[None]
+            kt = torch.from_numpy(K).permute(1, 0, 2)[None]
+            vt = torch.from_numpy(np.ascontiguousarray(V)).permute(1, 0, 2)[None]
+            ref = F.scaled_dot_product_attention(qt, kt, vt, is_causal=True, scale=w.scale_f32,
+                                                 enable_gqa=True)[0, :, L - 1, :].numpy()
+            err = np.max(np.abs(res["o"][b] - ref))
+            if not err <= 1e-12:
+                return f"fp8 sdpa {w.name} seq {b}: |do|={err:.3g}"
+    return None
+
+
 ALL_CHECKS = {
     "bruteforce": check_bruteforce,
     "closed_forms": check_closed_forms,
@@ -357,4 +500,7 @@ ALL_CHECKS = {
     "slots": check_slots,
     "merge": check_merge,
     "copy_on_write": check_copy_on_write,
+    "fp8_table": check_fp8_table,
+    "fp8_rounding": check_fp8_rounding,
+    "fp8_decode": check_fp8_decode,
 }

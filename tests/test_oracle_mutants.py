@@ -10,6 +10,7 @@ import numpy as np
 import pytest
 
 import oracle_checks as oc
+from oracle import fp8_kv as f8
 from oracle import paged_attention as pa
 
 _attention = pa.attention
@@ -18,6 +19,9 @@ _members = pa.shard_members
 _gather_shard = pa.gather_shard
 _kv_append = pa.kv_append
 _copy_blocks = pa.copy_blocks
+_quantize = f8.quantize
+_dequantize_cache = f8.dequantize_cache
+_E4M3 = f8.E4M3.copy()
 
 
 def _attn_variant(kind):
@@ -113,6 +117,45 @@ def _copy_nothing(k_cache, v_cache, pairs):
     return k_cache.copy(), None if v_cache is None else v_cache.copy()
 
 
+def _quantize_truncate(x, scale):
+    """round toward zero instead of to nearest"""
+    y = (f8.to_f32(x) / np.asarray(scale, np.float32)).astype(np.float32)
+    a = np.abs(y).astype(np.float64)
+    code = (np.searchsorted(f8._POS, a, side="right") - 1).clip(0, f8.MAX_CODE)
+    code = np.where(np.isnan(y), f8.NAN_CODE, code)
+    return (code | np.where(np.signbit(y), 0x80, 0)).astype(np.uint8)
+
+
+def _quantize_ties_up(x, scale):
+    """ties go to the larger magnitude instead of the even code"""
+    codes = _quantize(x, scale)
+    y = (f8.to_f32(x) / np.asarray(scale, np.float32)).astype(np.float64)
+    mag = codes & 0x7F
+    up = np.minimum(mag + 1, f8.MAX_CODE)
+    tie = (mag < f8.MAX_CODE) & (np.abs(np.abs(y) - f8.E4M3[mag]) == np.abs(f8.E4M3[up] - np.abs(y))) \
+        & (f8.E4M3[up] > np.abs(y))
+    return np.where(tie, up | (codes & 0x80), codes).astype(np.uint8)
+
+
+def _quantize_times_scale(x, scale):
+    """multiplies by the scale instead of dividing"""
+    return _quantize(x, 1.0 / np.asarray(scale, np.float32))
+
+
+def _dequantize_v_unscaled(k_cache, v_cache, k_scale, v_scale):
+    kd, vd = _dequantize_cache(k_cache, v_cache, k_scale, v_scale)
+    if v_cache is not None:
+        vd = f8.dequantize(v_cache, 1.0)
+    return kd, vd
+
+
+def _dequantize_heads_reversed(k_cache, v_cache, k_scale, v_scale):
+    hkv = k_cache.shape[1]
+    ks = f8.head_scales(k_scale, hkv)[::-1]
+    vs = None if v_scale is None else f8.head_scales(v_scale, hkv)[::-1]
+    return _dequantize_cache(k_cache, v_cache, ks, vs)
+
+
 MUTANTS = {
     "attention.head_map": ("attention", _attn_variant("head_map")),
     "attention.no_scale": ("attention", _attn_variant("no_scale")),
@@ -132,12 +175,42 @@ MUTANTS = {
     "copy.reversed": ("copy_blocks", _copy_reversed),
     "copy.nothing": ("copy_blocks", _copy_nothing),
 }
+FP8_MUTANTS = {
+    "fp8.truncate": ("quantize", _quantize_truncate),
+    "fp8.ties_up": ("quantize", _quantize_ties_up),
+    "fp8.times_scale": ("quantize", _quantize_times_scale),
+    "fp8.v_unscaled": ("dequantize_cache", _dequantize_v_unscaled),
+    "fp8.heads_reversed": ("dequantize_cache", _dequantize_heads_reversed),
+}
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_mutant_is_caught(name, monkeypatch):
     attr, fn = MUTANTS[name]
     monkeypatch.setattr(pa, attr, fn)
+    failures = []
+    for check in oc.ALL_CHECKS.values():
+        try:
+            msg = check()
+        except Exception as e:          # a crash is also a detection
+            msg = f"raised {type(e).__name__}"
+        if msg:
+            failures.append(msg)
+            break
+    assert failures, f"planted mistake {name} passed every pin"
+
+
+@pytest.mark.parametrize("name", sorted(FP8_MUTANTS) + ["fp8.subnormal_table"])
+def test_fp8_mutant_is_caught(name, monkeypatch):
+    if name == "fp8.subnormal_table":
+        bad = _E4M3.copy()
+        bad[1:8] *= 2.0                                # subnormals with the wrong exponent
+        bad[0x81:0x88] *= 2.0
+        monkeypatch.setattr(f8, "E4M3", bad)
+        monkeypatch.setattr(f8, "_POS", bad[:0x7F])
+    else:
+        attr, fn = FP8_MUTANTS[name]
+        monkeypatch.setattr(f8, attr, fn)
     failures = []
     for check in oc.ALL_CHECKS.values():
         try:

@@ -29,6 +29,7 @@ import numpy as np
 
 BF16 = "bf16"
 F32 = "f32"
+FP8 = "fp8"      # cache element type only: OCP E4M3 codes with float32 scales
 
 
 @dataclass
@@ -39,7 +40,7 @@ class Workload:
     dk: int
     dv: int
     block_size: int
-    dtype: str
+    dtype: str                          # q and new K/V rows (and the cache unless kv_dtype)
     context_lens: np.ndarray            # int32 [N], includes the appended token
     n_shards: int = 1
     interleave: int = 1
@@ -51,6 +52,8 @@ class Workload:
     spare_frac: float = 0.10            # extra never-used blocks in the pool
     n_blocks: int = 0                   # physical pool size (0 -> computed)
     seed: int = 0
+    kv_dtype: str = ""                  # "" -> same as dtype; FP8 -> E4M3 codes
+    scale_per_head: bool = True         # FP8: one scale per KV head (else one per tensor)
     # filled by plan():
     block_table: np.ndarray = field(default=None, repr=False)
     live: np.ndarray = field(default=None, repr=False)       # bool [NB][bs]: holds a stored token
@@ -70,6 +73,14 @@ class Workload:
         return 4 if self.dtype == F32 else 2
 
     @property
+    def cache_dtype(self) -> str:
+        return self.kv_dtype or self.dtype
+
+    @property
+    def kv_elem_bytes(self) -> int:
+        return {F32: 4, BF16: 2, FP8: 1}[self.cache_dtype]
+
+    @property
     def scale_f32(self) -> float:
         s = self.scale if self.scale else 1.0 / np.sqrt(self.dk)
         return float(np.float32(s))
@@ -82,7 +93,7 @@ class Workload:
         """Bytes of K and V read per token per step (V counted once when it is
         part of the K row)."""
         per_head = self.dk if self.latent else self.dk + self.dv
-        return self.n_kv_heads * per_head * self.elem_bytes
+        return self.n_kv_heads * per_head * self.kv_elem_bytes
 
 
 def _split_counts(L: int, n_shards: int, interleave: int) -> np.ndarray:
@@ -209,12 +220,22 @@ def latent(seed: int = 5, n_seqs: int = 32, lo: int = 4096, hi: int = 65536) -> 
 
 def small(name: str, lens, hq: int, hkv: int, dk: int, dv: int, bs: int, dtype: str,
           n_shards: int = 1, interleave: int = 1, partition_tokens: int = 0, latent: bool = False,
-          seed: int = 0, prefix_group: int = 1, prefix_tokens: int = 0, scale: float = 0.0) -> Workload:
+          seed: int = 0, prefix_group: int = 1, prefix_tokens: int = 0, scale: float = 0.0,
+          kv_dtype: str = "", scale_per_head: bool = True) -> Workload:
     """Any small shape, for parity sweeps."""
     return plan(Workload(name, hq, hkv, dk, dv, bs, dtype, np.asarray(lens, np.int32),
                          n_shards=n_shards, interleave=interleave,
                          partition_tokens=partition_tokens, latent=latent, seed=seed,
-                         prefix_group=prefix_group, prefix_tokens=prefix_tokens, scale=scale))
+                         prefix_group=prefix_group, prefix_tokens=prefix_tokens, scale=scale,
+                         kv_dtype=kv_dtype, scale_per_head=scale_per_head))
+
+
+def with_fp8_cache(w: Workload, per_head: bool = True) -> Workload:
+    """The same workload (same layout and seed) with an E4M3 cache."""
+    import dataclasses
+
+    w2 = dataclasses.replace(w, name=w.name + "_fp8", kv_dtype=FP8, scale_per_head=per_head)
+    return w2
 
 
 # --------------------------------------------------------------------------------------
@@ -234,6 +255,13 @@ def make_tensors(w: Workload, device="cpu", fill: str = "normal", seed: int | No
     ``v_cache [NB][Hkv][dv][bs]`` (None for latent), ``block_table``,
     ``context_lens`` and ``slot_mapping`` (int64, where the generator put the new
     tokens; the library computes its own).
+
+    An FP8 cache (``w.kv_dtype == FP8``) holds uint8 E4M3 codes: fp32 normals times
+    16 cast by torch's float8_e4m3fn conversion (values of roughly N(0, 16^2));
+    unused slots hold the NaN code 0x7F.  The dict then also has ``k_scale`` and
+    ``v_scale`` (float32, one per KV head or one per tensor, drawn from
+    U[0.5, 2] / 16, so the stored values read back as roughly N(0, 1)); new rows
+    and q stay in ``w.dtype``.  ``mean_probe`` is not available for FP8.
     """
     import torch
 
@@ -247,6 +275,30 @@ def make_tensors(w: Workload, device="cpu", fill: str = "normal", seed: int | No
         return torch.randn(*shape, generator=g, device=dev, dtype=torch.float32).to(dt)
 
     live = torch.from_numpy(w.live).to(dev)
+    if w.cache_dtype == FP8:
+        if fill != "normal":
+            raise ValueError("an FP8 cache takes fill='normal' only")
+
+        def codes(*shape):
+            x = torch.randn(*shape, generator=g, device=dev, dtype=torch.float32) * 16.0
+            return x.to(torch.float8_e4m3fn).view(torch.uint8)
+
+        k_cache = codes(NB, Hkv, bs, dk)
+        v_cache = None if w.latent else codes(NB, Hkv, dv, bs)
+        q = randn(N, Hq, dk)
+        k_new = randn(N, Hkv, dk)
+        v_new = None if w.latent else randn(N, Hkv, dv)
+        n_sc = Hkv if w.scale_per_head else 1
+        k_scale = (0.5 + 1.5 * torch.rand(n_sc, generator=g, device=dev)) / 16.0
+        v_scale = None if w.latent else (0.5 + 1.5 * torch.rand(n_sc, generator=g, device=dev)) / 16.0
+        k_cache.masked_fill_(~live[:, None, :, None], 0x7F)
+        if v_cache is not None:
+            v_cache.masked_fill_(~live[:, None, None, :], 0x7F)
+        return dict(q=q, k_new=k_new, v_new=v_new, k_cache=k_cache, v_cache=v_cache,
+                    k_scale=k_scale, v_scale=v_scale,
+                    block_table=torch.from_numpy(w.block_table).to(dev),
+                    context_lens=torch.from_numpy(w.context_lens.astype(np.int32)).to(dev),
+                    slot_mapping=torch.from_numpy(w.new_slot).to(dev))
     k_cache = randn(NB, Hkv, bs, dk)
     v_cache = None if w.latent else randn(NB, Hkv, dv, bs)
     q = randn(N, Hq, dk)
