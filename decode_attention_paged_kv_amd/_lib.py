@@ -17,7 +17,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("PAGEDATTN_LIB", os.path.join(_HERE, "libpagedattn.so"))
 
-PA_F32, PA_BF16 = 0, 1
+PA_F32, PA_BF16, PA_FP8_E4M3 = 0, 1, 2
 ERR_BLOCK_ID, ERR_CAPACITY, ERR_SLOT = 1, 2, 4
 
 if not os.path.exists(LIB_PATH):
@@ -38,6 +38,10 @@ _SIGS = {
     "pa_max_partitions": [_i32, _i32, _i32, _i32],
     "pa_default_partition_tokens": [_i32, _i32, _i32, _i32, _i32, _i32],
     "pa_choose_partition_tokens": [_p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32],
+    "pa_kv_append_fp8": [_p, _p, _i32, _p, _p, _p, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32, _i64,
+                         _p, _p],
+    "pa_decode_fp8": [_p, _p, _p, _p, _p, _i32, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i64, _i32,
+                      _i32, _i32, _i32, _i32, _f32, _i32, _p, _p, _p, _p],
     "pa_copy_blocks": [_p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i64, _i32, _p, _p],
     "pa_pool_add": [_p, _i64, _i64],
     "pa_pool_append": [_p, _i64, _i64, _p, _i32, _p],
@@ -83,11 +87,14 @@ def _stream(t):
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
 
-def _dtype_code(t):
+def _dtype_code(t, cache=False):
+    """Element type code; a cache may also hold E4M3 codes (uint8)."""
     if t.dtype == torch.float32:
         return PA_F32
     if t.dtype == torch.bfloat16:
         return PA_BF16
+    if cache and t.dtype == torch.uint8:
+        return PA_FP8_E4M3
     raise TypeError(f"unsupported element type {t.dtype}")
 
 
@@ -120,11 +127,12 @@ def pa_default_partition_tokens(n_seqs, n_kv_heads, max_context_len, n_shards, i
 
 def pa_choose_partition_tokens(context_lens_host, n_q_heads, n_kv_heads, dk, dv, block_size,
                                dtype, latent, n_shards=1, interleave=1) -> int:
-    """``context_lens_host``: host sequence of ints; ``dtype``: torch dtype."""
+    """``context_lens_host``: host sequence of ints; ``dtype``: torch dtype of the cache
+    (``torch.uint8`` = E4M3 codes read with bf16 queries)."""
     import numpy as np
 
     lens = np.ascontiguousarray(np.asarray(context_lens_host, dtype=np.int32))
-    code = PA_F32 if dtype == torch.float32 else PA_BF16
+    code = {torch.float32: PA_F32, torch.bfloat16: PA_BF16, torch.uint8: PA_FP8_E4M3}[dtype]
     return int(lib.pa_choose_partition_tokens(lens.ctypes.data_as(ctypes.c_void_p), int(lens.size),
                                               n_q_heads, n_kv_heads, dk, dv, block_size, code,
                                               int(bool(latent)), n_shards, interleave))
@@ -195,6 +203,77 @@ def pa_decode(q, k_cache, v_cache, block_table, context_lens, n_shards, interlea
                          _stream(q)))
 
 
+def _scales(k_scale, v_scale, hkv, latent):
+    _need(k_scale, torch.float32, 1, "k_scale")
+    if latent:
+        if v_scale is not None:
+            raise ValueError("a latent cache takes no v_scale")
+    else:
+        _need(v_scale, torch.float32, 1, "v_scale")
+        if v_scale is None or v_scale.numel() != k_scale.numel():
+            raise ValueError("v_scale must match k_scale in size")
+    n = k_scale.numel()
+    if n not in (1, hkv):
+        raise ValueError(f"need 1 or {hkv} scales, got {n}")
+    return n
+
+
+def pa_kv_append_fp8(k_new, v_new, k_cache, v_cache, k_scale, v_scale, slot_mapping, err_flag=None):
+    """E4M3 cache (uint8 codes): new rows (fp32 or bf16) quantised with per-head or
+    per-tensor float32 scales."""
+    _need(k_new, None, 3, "k_new")
+    _need(k_cache, torch.uint8, 4, "k_cache")
+    _need(v_new, k_new.dtype, 3, "v_new")
+    _need(v_cache, torch.uint8, 4, "v_cache")
+    _need(slot_mapping, torch.int64, 1, "slot_mapping")
+    _need(err_flag, torch.int32, None, "err_flag")
+    n, hkv, dk = k_new.shape
+    nb, hkv2, bs, dk2 = k_cache.shape
+    dv = 0 if v_new is None else v_new.shape[2]
+    if hkv2 != hkv or dk2 != dk or slot_mapping.shape[0] != n:
+        raise ValueError("k_new / k_cache / slot_mapping shapes disagree")
+    if v_cache is not None and tuple(v_cache.shape) != (nb, hkv, dv, bs):
+        raise ValueError("v_cache must be [n_blocks][n_kv_heads][dv][block_size]")
+    ns = _scales(k_scale, v_scale, hkv, v_cache is None)
+    _check(lib.pa_kv_append_fp8(_ptr(k_new), _ptr(v_new), _dtype_code(k_new), _ptr(k_cache),
+                                _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), ns, _ptr(slot_mapping),
+                                n, hkv, dk, dv, bs, nb, _ptr(err_flag), _stream(k_cache)))
+
+
+def pa_decode_fp8(q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens, n_shards,
+                  interleave, partition_tokens, max_partitions, scale, part_out, part_lse, dv=None,
+                  err_flag=None):
+    """pa_decode over an E4M3 cache (uint8 codes) with its scales."""
+    _need(q, None, 3, "q")
+    _need(k_cache, torch.uint8, 4, "k_cache")
+    _need(v_cache, torch.uint8, 4, "v_cache")
+    _need(block_table, torch.int32, 3, "block_table")
+    _need(context_lens, torch.int32, 1, "context_lens")
+    _need(part_out, torch.float32, 5, "part_out")
+    _need(part_lse, torch.float32, 4, "part_lse")
+    _need(err_flag, torch.int32, None, "err_flag")
+    n, hq, dk = q.shape
+    nb, hkv, bs, dk2 = k_cache.shape
+    if dv is None:
+        dv = v_cache.shape[2] if v_cache is not None else dk
+    if dk2 != dk:
+        raise ValueError("q and k_cache head sizes differ")
+    if v_cache is not None and tuple(v_cache.shape) != (nb, hkv, dv, bs):
+        raise ValueError("v_cache must be [n_blocks][n_kv_heads][dv][block_size]")
+    if tuple(part_out.shape) != (n, n_shards, max_partitions, hq, dv):
+        raise ValueError(f"part_out must be {(n, n_shards, max_partitions, hq, dv)}")
+    if tuple(part_lse.shape) != (n, n_shards, max_partitions, hq):
+        raise ValueError(f"part_lse must be {(n, n_shards, max_partitions, hq)}")
+    if block_table.shape[0] != n or block_table.shape[1] != n_shards or context_lens.shape[0] != n:
+        raise ValueError("block_table / context_lens shapes disagree with q")
+    ns = _scales(k_scale, v_scale, hkv, v_cache is None)
+    _check(lib.pa_decode_fp8(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+                             ns, _ptr(block_table), _ptr(context_lens), n, hq, hkv, dk, dv, bs, nb,
+                             block_table.shape[2], n_shards, interleave, partition_tokens,
+                             max_partitions, float(scale), _dtype_code(q), _ptr(part_out),
+                             _ptr(part_lse), _ptr(err_flag), _stream(q)))
+
+
 def pa_merge_lse(part_out, part_lse, out, lse=None):
     """``part_out [N][P...][Hq][dv]`` (any number of part axes), ``out [N][Hq][dv]``."""
     _need(part_out, torch.float32, None, "part_out")
@@ -224,7 +303,7 @@ def pa_gather_kv(k_cache, v_cache, block_table, seq, shard, context_len, n_shard
         raise ValueError(f"k_out/v_out need {L_r} rows")
     _check(lib.pa_gather_kv(_ptr(k_cache), _ptr(v_cache), _ptr(block_table), seq, shard,
                             context_len, hkv, dk, dv, bs, nb, block_table.shape[2], n_shards,
-                            interleave, _dtype_code(k_cache), _ptr(k_out), _ptr(v_out),
+                            interleave, _dtype_code(k_cache, cache=True), _ptr(k_out), _ptr(v_out),
                             _ptr(err_flag), _stream(k_cache)))
 
 
@@ -243,7 +322,8 @@ def pa_copy_blocks(k_cache, v_cache, pairs, err_flag=None):
     if pairs.shape[1] != 2:
         raise ValueError("pairs must be [n][2]")
     _check(lib.pa_copy_blocks(_ptr(k_cache), _ptr(v_cache), _ptr(pairs), pairs.shape[0], hkv, dk,
-                              dv, bs, nb, _dtype_code(k_cache), _ptr(err_flag), _stream(k_cache)))
+                              dv, bs, nb, _dtype_code(k_cache, cache=True), _ptr(err_flag),
+                              _stream(k_cache)))
 
 
 class PoolExhausted(PaError):

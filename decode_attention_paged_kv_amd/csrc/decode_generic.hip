@@ -10,8 +10,10 @@
 // through the block table (PagedAttention page, ai-compass.weeybrid.co.jp, block-table
 // section).
 //
-// This kernel covers every shape and element type the ABI accepts (including fp32 and
-// tiny head sizes); the MFMA kernels take the large bf16 shapes.
+// This kernel covers every shape and element type the ABI accepts (including fp32,
+// tiny head sizes and E4M3 caches); the MFMA kernels take the large bf16 shapes.
+// E4M3 cache: a stored value is code * scale (per KV head or per tensor); the key
+// scale is folded into the score multiplier and the value scale applied to the output.
 #include <math.h>
 
 #include "pa_common.h"
@@ -25,11 +27,12 @@ constexpr int kHeads = 16;  // query heads per workgroup
 constexpr int kTile = 32;   // tokens per tile
 constexpr int kAcc = kHeads * 512 / kThreads;
 
-template <int DT>
+template <int QT, int KT>
 __global__ __launch_bounds__(kThreads) void decode_generic_kernel(DecodeArgs a) {
-  using E = Elem<DT>;
+  using EQ = Elem<QT>;
+  using E = Elem<KT>;
   using raw = typename E::raw;
-  const raw* q = static_cast<const raw*>(a.q);
+  const typename EQ::raw* q = static_cast<const typename EQ::raw*>(a.q);
   const raw* kc = static_cast<const raw*>(a.k_cache);
   const raw* vc = static_cast<const raw*>(a.v_cache);
 
@@ -64,8 +67,14 @@ __global__ __launch_bounds__(kThreads) void decode_generic_kernel(DecodeArgs a) 
   __shared__ int64_t kbase_s[kTile], vbase_s[kTile];
   __shared__ int ok_s[kTile];
 
+  float score_mul = a.scale, out_mul = 1.f;
+  if (KT == kFP8) {
+    const int si = a.n_scales > 1 ? kvh : 0;
+    score_mul = a.scale * a.k_scale[si];
+    out_mul = vc ? a.v_scale[si] : a.k_scale[si];
+  }
   for (int i = tid; i < nh * dk; i += kThreads)
-    q_s[i] = E::load(q, (int64_t(b) * a.hq + h0 + i / dk) * dk + i % dk);
+    q_s[i] = EQ::load(q, (int64_t(b) * a.hq + h0 + i / dk) * dk + i % dk);
   if (tid < kHeads) {
     m_s[tid] = -INFINITY;
     l_s[tid] = 0.f;
@@ -103,7 +112,7 @@ __global__ __launch_bounds__(kThreads) void decode_generic_kernel(DecodeArgs a) 
         const int64_t kb = kbase_s[tt];
         float dot = 0.f;
         for (int d = 0; d < dk; ++d) dot = fmaf(q_s[hh * dk + d], E::load(kc, kb + d), dot);
-        s = dot * a.scale;
+        s = dot * score_mul;
       }
       s_s[hh][tt] = s;
     }
@@ -145,16 +154,24 @@ __global__ __launch_bounds__(kThreads) void decode_generic_kernel(DecodeArgs a) 
   for (int k = 0; k < kAcc; ++k) {
     const int idx = tid + k * kThreads;
     const int hh = idx / dv, d = idx % dv;
-    if (hh < nh) a.part_out[(out_row + h0 + hh) * dv + d] = acc[k] / l_s[hh];
+    if (hh < nh) a.part_out[(out_row + h0 + hh) * dv + d] = acc[k] / l_s[hh] * out_mul;
   }
   if (tid < nh) a.part_lse[out_row + h0 + tid] = m_s[tid] + logf(l_s[tid]);
 }
 
 }  // namespace
 
-int generic_workgroups_per_cu(int dtype) {
+static const void* generic_kernel(int dtype, int kv_dtype) {
+  if (kv_dtype == kFP8)
+    return dtype == kF32 ? (const void*)decode_generic_kernel<kF32, kFP8>
+                         : (const void*)decode_generic_kernel<kBF16, kFP8>;
+  return dtype == kF32 ? (const void*)decode_generic_kernel<kF32, kF32>
+                       : (const void*)decode_generic_kernel<kBF16, kBF16>;
+}
+
+int generic_workgroups_per_cu(int dtype, int kv_dtype) {
   int n = 0;
-  const void* f = dtype == kF32 ? (const void*)decode_generic_kernel<kF32> : (const void*)decode_generic_kernel<kBF16>;
+  const void* f = generic_kernel(dtype, kv_dtype);
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, f, kThreads, 0) != hipSuccess) {
     (void)hipGetLastError();
     return 0;
@@ -166,10 +183,16 @@ hipError_t launch_decode_generic(const DecodeArgs& a, hipStream_t st) {
   const int g = a.hq / a.hkv;
   const int chunks = (g + kHeads - 1) / kHeads;
   const dim3 grid(a.max_parts, a.n_seqs * a.n_shards, a.hkv * chunks);
-  if (a.dtype == kF32)
-    hipLaunchKernelGGL(decode_generic_kernel<kF32>, grid, dim3(kThreads), 0, st, a);
-  else
-    hipLaunchKernelGGL(decode_generic_kernel<kBF16>, grid, dim3(kThreads), 0, st, a);
+  if (a.kv_dtype == kFP8) {
+    if (a.dtype == kF32)
+      hipLaunchKernelGGL((decode_generic_kernel<kF32, kFP8>), grid, dim3(kThreads), 0, st, a);
+    else
+      hipLaunchKernelGGL((decode_generic_kernel<kBF16, kFP8>), grid, dim3(kThreads), 0, st, a);
+  } else if (a.dtype == kF32) {
+    hipLaunchKernelGGL((decode_generic_kernel<kF32, kF32>), grid, dim3(kThreads), 0, st, a);
+  } else {
+    hipLaunchKernelGGL((decode_generic_kernel<kBF16, kBF16>), grid, dim3(kThreads), 0, st, a);
+  }
   return hipGetLastError();
 }
 

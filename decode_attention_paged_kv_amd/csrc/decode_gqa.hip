@@ -31,12 +31,21 @@
 //  * Masked tokens (past the partition end) take score -inf by select and their value
 //    entries are zeroed by select, so unused cache slots (whatever they hold) never
 //    reach the sums.
+//  * E4M3 cache (codes times a per-head or per-tensor scale): keys and values are
+//    loaded as codes -- half the bytes -- and widened to bf16 in registers right
+//    before their MFMA (every E4M3 value is exact in bf16).  A lane's key bytes for the
+//    score MFMAs of a sub-tile are D/4 consecutive bytes (one or two 16-byte loads),
+//    dimension grp*D/4 + 8j + e for MFMA j, element e; the query operand is taken in
+//    the same order (a dot product does not depend on the order of its terms).  The
+//    key scale joins the score multiplier and the value scale the final division.
 //  * Block ids: each wave loads 64 consecutive block-table entries with one vector load
 //    and reads them back one at a time with readlane.  The next step's keys are loaded
 //    into the key registers as soon as the scores have used them, its values into the
 //    value registers as soon as the output product has, so each wave keeps a step of
 //    loads in flight while it computes, without a second register buffer.
 #include <math.h>
+
+#include <type_traits>
 
 #include "pa_common.h"
 #include "pa_launch.h"
@@ -45,6 +54,7 @@ namespace pa {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef __bf16 bf16x2_t __attribute__((__vector_size__(2 * sizeof(__bf16))));
 typedef float f32x4_t __attribute__((__vector_size__(4 * sizeof(float))));
 typedef uint32_t u32x4_t __attribute__((__vector_size__(4 * sizeof(uint32_t))));
 
@@ -70,13 +80,46 @@ __device__ inline uint32_t keep(uint32_t w, bool lo_ok, bool hi_ok) {
   return w & ((lo_ok ? 0x0000ffffu : 0u) | (hi_ok ? 0xffff0000u : 0u));
 }
 
-template <int D, int SUBS>
+// Two E4M3 codes (bytes 2*hi, 2*hi+1 of w) as two bf16, exactly.
+template <bool HI>
+__device__ inline uint32_t e4m3x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+
+template <int D, int SUBS, int KT>
 struct Tile {
   static_assert(SUBS % 2 == 0, "the output product takes sub-tiles in pairs");
+  static constexpr bool F8 = KT == kFP8;
   static constexpr int KJ = D / 32;  // score MFMAs per sub-tile
   static constexpr int NT = D / 16;  // output tiles of 16 d rows
-  bf16x8_t k[SUBS][KJ];
-  uint2 v[SUBS][NT];
+  // bf16: one 16-byte word per score MFMA; E4M3: the lane's D/4 key bytes
+  static constexpr int KW = F8 ? D / 64 : KJ;
+  u32x4_t k[SUBS][KW];
+  // 4 tokens of one d row: 8 bytes (bf16) or 4 (E4M3)
+  using VWord = typename std::conditional<F8, uint32_t, uint2>::type;
+  VWord v[SUBS][NT];
+
+  // key operand of score MFMA j of sub-tile t
+  __device__ inline bf16x8_t key(int t, int j) const {
+    if constexpr (F8) {
+      const u32x4_t w = k[t][j >> 1];
+      const uint32_t d0 = (j & 1) ? w[2] : w[0];
+      const uint32_t d1 = (j & 1) ? w[3] : w[1];
+      const u32x4_t x = {e4m3x2_to_bf16x2<false>(d0), e4m3x2_to_bf16x2<true>(d0),
+                         e4m3x2_to_bf16x2<false>(d1), e4m3x2_to_bf16x2<true>(d1)};
+      return __builtin_bit_cast(bf16x8_t, x);
+    } else {
+      return __builtin_bit_cast(bf16x8_t, k[t][j]);
+    }
+  }
+  // 4 tokens of d row 16n + col of sub-tile t, as bf16
+  __device__ inline uint2 value(int t, int n) const {
+    if constexpr (F8) {
+      return uint2{e4m3x2_to_bf16x2<false>(v[t][n]), e4m3x2_to_bf16x2<true>(v[t][n])};
+    } else {
+      return v[t][n];
+    }
+  }
 };
 
 // Where a step's sub-tiles are: local token of the first row (-1: no sub-tile), cache
@@ -88,14 +131,17 @@ struct Step {
   int sub[SUBS];
 };
 
-template <int D, int NW, int SUBS>
+template <int D, int NW, int SUBS, int KT>
 __global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeArgs a) {
-  using TileT = Tile<D, SUBS>;
+  using TileT = Tile<D, SUBS, KT>;
+  using raw = typename Elem<KT>::raw;
+  constexpr bool F8 = TileT::F8;
   constexpr int KJ = TileT::KJ;
   constexpr int NT = TileT::NT;
+  constexpr int KW = TileT::KW;
   const uint16_t* __restrict__ q = static_cast<const uint16_t*>(a.q);
-  const uint16_t* __restrict__ kc = static_cast<const uint16_t*>(a.k_cache);
-  const uint16_t* __restrict__ vc = static_cast<const uint16_t*>(a.v_cache);
+  const raw* __restrict__ kc = static_cast<const raw*>(a.k_cache);
+  const raw* __restrict__ vc = static_cast<const raw*>(a.v_cache);
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -124,14 +170,15 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeArgs a) {
     return;
   }
 
-  // query operand: lane (head col, group grp) holds q[h0+col][32j + 8grp .. +7]
+  // query operand: lane (head col, group grp) holds q[h0+col][32j + 8grp .. +7] (bf16
+  // cache) or q[h0+col][grp*D/4 + 8j .. +7] (E4M3 cache), the order of the key operand
   bf16x8_t qop[KJ];
   {
-    const uint16_t* qrow = q + (int64_t(b) * a.hq + h0 + col) * D + 8 * grp;
+    const uint16_t* qrow = q + (int64_t(b) * a.hq + h0 + col) * D + (F8 ? grp * (D / 4) : 8 * grp);
 #pragma unroll
     for (int j = 0; j < KJ; ++j) {
       if (col < nh)
-        qop[j] = *reinterpret_cast<const bf16x8_t*>(qrow + 32 * j);
+        qop[j] = *reinterpret_cast<const bf16x8_t*>(qrow + (F8 ? 8 * j : 32 * j));
       else
         qop[j] = bf16x8_t{};
     }
@@ -198,22 +245,29 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeArgs a) {
   auto load_k = [&](TileT& tl, const StepT& st) {
 #pragma unroll
     for (int t = 0; t < SUBS; ++t) {
-      const uint16_t* kp = kc + st.base[t] + int64_t(st.sub[t] + col) * D + 8 * grp;
+      const raw* kp = kc + st.base[t] + int64_t(st.sub[t] + col) * D + (F8 ? grp * (D / 4) : 8 * grp);
 #pragma unroll
-      for (int j = 0; j < KJ; ++j) tl.k[t][j] = *reinterpret_cast<const bf16x8_t*>(kp + 32 * j);
+      for (int w = 0; w < KW; ++w)
+        tl.k[t][w] = *reinterpret_cast<const u32x4_t*>(kp + (F8 ? 16 * w : 32 * w));
     }
   };
   auto load_v = [&](TileT& tl, const StepT& st) {
 #pragma unroll
     for (int t = 0; t < SUBS; ++t) {
-      const uint16_t* vp = vc + st.base[t] + int64_t(col) * bs + st.sub[t] + 4 * grp;
+      const raw* vp = vc + st.base[t] + int64_t(col) * bs + st.sub[t] + 4 * grp;
 #pragma unroll
       for (int n = 0; n < NT; ++n)
-        tl.v[t][n] = *reinterpret_cast<const uint2*>(vp + int64_t(16 * n) * bs);
+        tl.v[t][n] = *reinterpret_cast<const typename TileT::VWord*>(vp + int64_t(16 * n) * bs);
     }
   };
 
-  const float c = a.scale * kLog2e;
+  float key_scale = 1.f, value_scale = 1.f;
+  if constexpr (F8) {
+    const int si = a.n_scales > 1 ? kvh : 0;
+    key_scale = a.k_scale[si];
+    value_scale = a.v_scale[si];
+  }
+  const float c = a.scale * key_scale * kLog2e;
   float m = -INFINITY;  // running max of raw scores, head col
   float lsum = 0.f;     // this lane's partial sum of weights
   f32x4_t o[NT];
@@ -229,7 +283,7 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeArgs a) {
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
       if (st.tok0[t] >= 0) {
 #pragma unroll
-        for (int j = 0; j < KJ; ++j) acc = mfma16x16x32(tl.k[t][j], qop[j], acc);
+        for (int j = 0; j < KJ; ++j) acc = mfma16x16x32(tl.key(t, j), qop[j], acc);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -285,7 +339,7 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeArgs a) {
         }
 #pragma unroll
       for (int n = 0; n < NT; ++n) {
-        uint2 va = tl.v[t2][n], vb = tl.v[t2 + 1][n];
+        uint2 va = tl.value(t2, n), vb = tl.value(t2 + 1, n);
         if (!__all(full)) {
           va.x = keep(va.x, ok[t2][0], ok[t2][1]);
           va.y = keep(va.y, ok[t2][2], ok[t2][3]);
@@ -348,7 +402,7 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeArgs a) {
       Ls = fmaf(f, l_s[w2][hh], Ls);
       acc = fmaf(f, o_s[w2][d][hh], acc);
     }
-    a.part_out[(out_row + hh) * D + d] = acc / Ls;
+    a.part_out[(out_row + hh) * D + d] = acc / Ls * value_scale;
     if (d == 0) a.part_lse[out_row + hh] = (M * c + log2f(Ls)) * kLn2;
   }
 }
@@ -356,8 +410,8 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeArgs a) {
 }  // namespace
 
 bool gqa_supported(const DecodeArgs& a) {
-  return a.dtype == kBF16 && a.v_cache != nullptr && a.dk == a.dv && (a.dk == 64 || a.dk == 128) &&
-         a.bs % 16 == 0;
+  return a.dtype == kBF16 && (a.kv_dtype == kBF16 || a.kv_dtype == kFP8) && a.v_cache != nullptr &&
+         a.dk == a.dv && (a.dk == 64 || a.dk == 128) && a.bs % 16 == 0;
 }
 
 #ifndef PA_GQA_WAVES
@@ -366,14 +420,28 @@ bool gqa_supported(const DecodeArgs& a) {
 #ifndef PA_GQA_SUBS
 #define PA_GQA_SUBS 2
 #endif
+#ifndef PA_GQA_SUBS_FP8
+#define PA_GQA_SUBS_FP8 4   // an E4M3 sub-tile has half the bytes: twice as many in flight
+#endif
 
-int gqa_workgroup_threads() { return 64 * PA_GQA_WAVES; }
+namespace {
+template <int D, int KT>
+const void* gqa_kernel() {
+  constexpr int NW = PA_GQA_WAVES;
+  constexpr int SUBS = KT == kFP8 ? PA_GQA_SUBS_FP8 : PA_GQA_SUBS;
+  return (const void*)decode_gqa_kernel<D, NW, SUBS, KT>;
+}
 
-int gqa_workgroups_per_cu(int dk) {
+const void* gqa_kernel_for(int dk, int kv_dtype) {
+  if (kv_dtype == kFP8) return dk == 128 ? gqa_kernel<128, kFP8>() : gqa_kernel<64, kFP8>();
+  return dk == 128 ? gqa_kernel<128, kBF16>() : gqa_kernel<64, kBF16>();
+}
+}  // namespace
+
+int gqa_workgroups_per_cu(int dk, int kv_dtype) {
   int n = 0;
-  const void* f = dk == 128 ? (const void*)decode_gqa_kernel<128, PA_GQA_WAVES, PA_GQA_SUBS>
-                            : (const void*)decode_gqa_kernel<64, PA_GQA_WAVES, PA_GQA_SUBS>;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, f, 64 * PA_GQA_WAVES, 0) != hipSuccess) {
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gqa_kernel_for(dk, kv_dtype),
+                                                   64 * PA_GQA_WAVES, 0) != hipSuccess) {
     (void)hipGetLastError();
     return 0;
   }
@@ -384,12 +452,8 @@ hipError_t launch_decode_gqa(const DecodeArgs& a, hipStream_t st) {
   const int g = a.hq / a.hkv;
   const int chunks = (g + 15) / 16;
   const dim3 grid(a.max_parts, a.n_seqs * a.n_shards, a.hkv * chunks);
-  constexpr int NW = PA_GQA_WAVES;
-  if (a.dk == 128)
-    hipLaunchKernelGGL((decode_gqa_kernel<128, NW, PA_GQA_SUBS>), grid, dim3(64 * NW), 0, st, a);
-  else
-    hipLaunchKernelGGL((decode_gqa_kernel<64, NW, PA_GQA_SUBS>), grid, dim3(64 * NW), 0, st, a);
-  return hipGetLastError();
+  void* args[] = {const_cast<DecodeArgs*>(&a)};
+  return hipLaunchKernel(gqa_kernel_for(a.dk, a.kv_dtype), grid, dim3(64 * PA_GQA_WAVES), args, 0, st);
 }
 
 }  // namespace pa

@@ -6,6 +6,9 @@
 // is exact for any element type.
 // Slot routing and gather: placement by the DCP interleave rule and block-table
 // lookup, as in pa_common.h.
+// E4M3 append: the KV cache may be kept in an 8-bit floating type to take fewer bytes
+// per token (soroban.highreso.jp, DCP page, the passage that sets DCP beside KV-cache
+// quantisation); new rows are quantised with a scale on the way in.
 // Block copy: a sequence about to write into a block it shares with others first
 // gets a private copy of that block (ai-compass.weeybrid.co.jp, "What is
 // PagedAttention?", section "Sharing common blocks and copy-on-write").
@@ -57,6 +60,44 @@ __global__ void kv_append_kernel(const RAW* __restrict__ k_new, const RAW* __res
     const RAW* vs = v_new + (int64_t(n) * hkv + h) * dv;
     RAW* vd = v_cache + (blk * hkv + h) * int64_t(dv) * bs + off;
     for (int d = threadIdx.x; d < dv; d += blockDim.x) vd[int64_t(d) * bs] = vs[d];
+  }
+}
+
+// E4M3 cache: each element of the new rows becomes the code of element / scale (the
+// scale of its KV head, or the tensor's), rounded as f32_to_e4m3 describes.  The
+// division is IEEE (correctly rounded), so the code is a function of the inputs alone.
+template <int DT>
+__global__ void kv_append_fp8_kernel(const void* __restrict__ k_new_, const void* __restrict__ v_new_,
+                                     uint8_t* __restrict__ k_cache, uint8_t* __restrict__ v_cache,
+                                     const float* __restrict__ k_scale,
+                                     const float* __restrict__ v_scale, int n_scales,
+                                     const int64_t* __restrict__ slots, int hkv, int dk, int dv,
+                                     int bs, int64_t n_blocks, int* flag) {
+  using E = Elem<DT>;
+  using raw = typename E::raw;
+  const raw* k_new = static_cast<const raw*>(k_new_);
+  const raw* v_new = static_cast<const raw*>(v_new_);
+  const int n = blockIdx.x;
+  const int h = blockIdx.y;
+  const int64_t slot = slots[n];
+  if (slot < 0) return;
+  if (slot >= n_blocks * bs) {
+    if (threadIdx.x == 0) raise_flag(flag, kErrSlot);
+    return;
+  }
+  const int64_t blk = slot / bs;
+  const int off = int(slot % bs);
+  const int si = n_scales > 1 ? h : 0;
+  const float ks = k_scale[si];
+  const int64_t ksrc = (int64_t(n) * hkv + h) * dk;
+  uint8_t* kd = k_cache + ((blk * hkv + h) * bs + off) * dk;
+  for (int e = threadIdx.x; e < dk; e += blockDim.x) kd[e] = f32_to_e4m3(__fdiv_rn(E::load(k_new, ksrc + e), ks));
+  if (v_cache != nullptr) {
+    const float vs = v_scale[si];
+    const int64_t vsrc = (int64_t(n) * hkv + h) * dv;
+    uint8_t* vd = v_cache + (blk * hkv + h) * int64_t(dv) * bs + off;
+    for (int d = threadIdx.x; d < dv; d += blockDim.x)
+      vd[int64_t(d) * bs] = f32_to_e4m3(__fdiv_rn(E::load(v_new, vsrc + d), vs));
   }
 }
 
@@ -113,6 +154,21 @@ __global__ void copy_blocks_kernel(char* __restrict__ k_cache, char* __restrict_
 
 }  // namespace
 
+hipError_t launch_kv_append_fp8(const void* k_new, const void* v_new, int new_dtype,
+                                uint8_t* k_cache, uint8_t* v_cache, const float* k_scale,
+                                const float* v_scale, int n_scales, const int64_t* slots,
+                                int n_tokens, int hkv, int dk, int dv, int bs, int64_t n_blocks,
+                                int* flag, hipStream_t st) {
+  const dim3 grid(n_tokens, hkv);
+  if (new_dtype == kF32)
+    hipLaunchKernelGGL(kv_append_fp8_kernel<kF32>, grid, dim3(64), 0, st, k_new, v_new, k_cache,
+                       v_cache, k_scale, v_scale, n_scales, slots, hkv, dk, dv, bs, n_blocks, flag);
+  else
+    hipLaunchKernelGGL(kv_append_fp8_kernel<kBF16>, grid, dim3(64), 0, st, k_new, v_new, k_cache,
+                       v_cache, k_scale, v_scale, n_scales, slots, hkv, dk, dv, bs, n_blocks, flag);
+  return hipGetLastError();
+}
+
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int64_t* pairs, int n_pairs,
                               int64_t k_bytes, int64_t v_bytes, int64_t n_blocks, int* flag,
                               hipStream_t st) {
@@ -168,7 +224,11 @@ hipError_t launch_gather(const void* k_cache, const void* v_cache, const int32_t
                          int max_blocks, int dtype, void* k_out, void* v_out, int* flag,
                          hipStream_t st) {
   const dim3 grid(L_r, hkv);
-  if (dtype == kF32) {
+  if (dtype == kFP8) {
+    hipLaunchKernelGGL(gather_kernel<uint8_t>, grid, dim3(64), 0, st, (const uint8_t*)k_cache,
+                       (const uint8_t*)v_cache, bt_row, hkv, dk, dv, bs, n_blocks, max_blocks,
+                       (uint8_t*)k_out, (uint8_t*)v_out, flag);
+  } else if (dtype == kF32) {
     hipLaunchKernelGGL(gather_kernel<uint32_t>, grid, dim3(64), 0, st, (const uint32_t*)k_cache,
                        (const uint32_t*)v_cache, bt_row, hkv, dk, dv, bs, n_blocks, max_blocks,
                        (uint32_t*)k_out, (uint32_t*)v_out, flag);

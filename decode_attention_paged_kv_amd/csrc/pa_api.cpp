@@ -49,6 +49,8 @@ int hip_status(hipError_t e, const char* what) {
 }
 
 bool valid_dtype(int32_t dt) { return dt == PA_F32 || dt == PA_BF16; }
+bool valid_cache_dtype(int32_t dt) { return valid_dtype(dt) || dt == PA_FP8_E4M3; }
+int64_t elem_bytes(int32_t dt) { return dt == PA_F32 ? 4 : dt == PA_BF16 ? 2 : 1; }
 
 #define REQUIRE(cond, code, ...) \
   do {                           \
@@ -107,7 +109,7 @@ int32_t pa_choose_partition_tokens(const int32_t* context_lens_host, int32_t n_s
   if (!context_lens_host || n_seqs < 1 || n_q_heads < 1 || n_kv_heads < 1 ||
       n_q_heads % n_kv_heads != 0 || block_size < 1 || block_size > PA_MAX_BLOCK_SIZE ||
       n_shards < 1 || interleave < 1 || int64_t(n_shards) * interleave > (int64_t(1) << 30) ||
-      !valid_dtype(dtype))
+      !valid_cache_dtype(dtype))
     return -1;
   pa::DecodeArgs a{};
   a.hq = n_q_heads;
@@ -115,7 +117,8 @@ int32_t pa_choose_partition_tokens(const int32_t* context_lens_host, int32_t n_s
   a.dk = dk;
   a.dv = dv;
   a.bs = block_size;
-  a.dtype = dtype;
+  a.dtype = dtype == PA_FP8_E4M3 ? PA_BF16 : dtype;  // E4M3 cache: bf16 queries
+  a.kv_dtype = dtype;
   a.v_cache = latent ? nullptr : static_cast<const void*>(&a);  // only its NULL-ness matters
   const pa::KernelChoice kc = pa::choose_kernel(a);
   int cus = 0, xccs = 0, dev = 0;
@@ -137,7 +140,7 @@ int32_t pa_choose_partition_tokens(const int32_t* context_lens_host, int32_t n_s
   // the partition's output rows).
   const int64_t slots_per_xcd = int64_t(cus / xccs) * (kc.workgroups_per_cu > 0 ? kc.workgroups_per_cu : 2);
   const int64_t partial_bytes = int64_t(n_q_heads / n_kv_heads) * dv * 4 * 2;
-  const int64_t token_bytes = int64_t(latent ? dk : dk + dv) * (dtype == PA_F32 ? 4 : 2);
+  const int64_t token_bytes = int64_t(latent ? dk : dk + dv) * elem_bytes(dtype);
   const int64_t overhead = 128 + partial_bytes / (token_bytes > 0 ? token_bytes : 1);
   std::vector<int32_t> shard_len_v(size_t(n_seqs) * n_shards);
   int32_t longest = 0;
@@ -251,7 +254,8 @@ int pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* pairs, int32_t n
                    int32_t n_kv_heads, int32_t dk, int32_t dv, int32_t block_size, int64_t n_blocks,
                    int32_t dtype, int32_t* err_flag, void* stream) {
   REQUIRE(k_cache && pairs, PA_ERR_NULL, "pa_copy_blocks: k_cache and pairs must be non-NULL");
-  REQUIRE(valid_dtype(dtype), PA_ERR_UNSUPPORTED, "dtype=%d is not PA_F32 or PA_BF16", dtype);
+  REQUIRE(valid_cache_dtype(dtype), PA_ERR_UNSUPPORTED,
+          "dtype=%d is not PA_F32, PA_BF16 or PA_FP8_E4M3", dtype);
   REQUIRE(n_pairs >= 0 && n_pairs <= (1 << 22), PA_ERR_SHAPE, "n_pairs=%d must be in [0, 2^22]",
           n_pairs);
   REQUIRE(n_kv_heads >= 1 && n_kv_heads <= 65535, PA_ERR_SHAPE, "n_kv_heads=%d out of range", n_kv_heads);
@@ -262,7 +266,7 @@ int pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* pairs, int32_t n
           "block_size=%d must be in [1, %d]", block_size, PA_MAX_BLOCK_SIZE);
   REQUIRE(n_blocks >= 1, PA_ERR_SHAPE, "n_blocks=%lld must be >= 1", (long long)n_blocks);
   if (n_pairs == 0) return ok();
-  const int64_t es = dtype == PA_F32 ? 4 : 2;
+  const int64_t es = elem_bytes(dtype);
   const int64_t k_bytes = int64_t(n_kv_heads) * block_size * dk * es;
   const int64_t v_bytes = v_cache != nullptr ? int64_t(n_kv_heads) * block_size * dv * es : 0;
   return hip_status(pa::launch_copy_blocks(k_cache, v_cache, pairs, n_pairs, k_bytes, v_bytes,
@@ -270,14 +274,51 @@ int pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* pairs, int32_t n
                     "pa_copy_blocks launch");
 }
 
-int pa_decode(const void* q, const void* k_cache, const void* v_cache,
-              const int32_t* block_table, const int32_t* context_lens, int32_t n_seqs,
-              int32_t n_q_heads, int32_t n_kv_heads, int32_t dk, int32_t dv, int32_t block_size,
-              int64_t n_blocks, int32_t max_blocks_per_shard, int32_t n_shards, int32_t interleave,
-              int32_t partition_tokens, int32_t max_partitions, float scale, int32_t dtype,
-              float* part_out, float* part_lse, int32_t* err_flag, void* stream) {
+int pa_kv_append_fp8(const void* k_new, const void* v_new, int32_t new_dtype, uint8_t* k_cache,
+                     uint8_t* v_cache, const float* k_scale, const float* v_scale,
+                     int32_t n_scales, const int64_t* slot_mapping, int32_t n_tokens,
+                     int32_t n_kv_heads, int32_t dk, int32_t dv, int32_t block_size,
+                     int64_t n_blocks, int32_t* err_flag, void* stream) {
+  REQUIRE(k_new && k_cache && slot_mapping && k_scale, PA_ERR_NULL,
+          "pa_kv_append_fp8: k_new, k_cache, k_scale and slot_mapping must be non-NULL");
+  REQUIRE((v_new == nullptr) == (v_cache == nullptr), PA_ERR_NULL,
+          "pa_kv_append_fp8: v_new and v_cache must both be NULL (latent cache) or both non-NULL");
+  REQUIRE(v_cache == nullptr || v_scale != nullptr, PA_ERR_NULL,
+          "pa_kv_append_fp8: v_scale must be non-NULL with a value cache");
+  REQUIRE(valid_dtype(new_dtype), PA_ERR_UNSUPPORTED, "new_dtype=%d is not PA_F32 or PA_BF16",
+          new_dtype);
+  REQUIRE(n_tokens >= 0, PA_ERR_SHAPE, "n_tokens=%d must be >= 0", n_tokens);
+  REQUIRE(n_kv_heads >= 1 && n_kv_heads <= 65535, PA_ERR_SHAPE, "n_kv_heads=%d out of range", n_kv_heads);
+  REQUIRE(n_scales == 1 || n_scales == n_kv_heads, PA_ERR_SHAPE,
+          "n_scales=%d must be 1 or n_kv_heads=%d", n_scales, n_kv_heads);
+  REQUIRE(dk >= 1 && dk <= PA_MAX_HEAD_DIM, PA_ERR_UNSUPPORTED, "dk=%d must be in [1, %d]", dk, PA_MAX_HEAD_DIM);
+  REQUIRE(v_cache == nullptr || (dv >= 1 && dv <= PA_MAX_HEAD_DIM), PA_ERR_UNSUPPORTED,
+          "dv=%d must be in [1, %d]", dv, PA_MAX_HEAD_DIM);
+  REQUIRE(block_size >= 1 && block_size <= PA_MAX_BLOCK_SIZE, PA_ERR_UNSUPPORTED,
+          "block_size=%d must be in [1, %d]", block_size, PA_MAX_BLOCK_SIZE);
+  REQUIRE(n_blocks >= 1, PA_ERR_SHAPE, "n_blocks=%lld must be >= 1", (long long)n_blocks);
+  if (n_tokens == 0) return ok();
+  return hip_status(pa::launch_kv_append_fp8(k_new, v_new, new_dtype, k_cache, v_cache, k_scale,
+                                             v_scale, n_scales, slot_mapping, n_tokens, n_kv_heads,
+                                             dk, dv, block_size, n_blocks, err_flag,
+                                             (hipStream_t)stream),
+                    "pa_kv_append_fp8 launch");
+}
+
+}  // extern "C"
+
+namespace {
+
+// Checks shared by pa_decode and pa_decode_fp8; fills the kernel arguments.
+int check_decode(const char* fn, const void* q, const void* k_cache, const void* v_cache,
+                 const int32_t* block_table, const int32_t* context_lens, int32_t n_seqs,
+                 int32_t n_q_heads, int32_t n_kv_heads, int32_t dk, int32_t dv, int32_t block_size,
+                 int64_t n_blocks, int32_t max_blocks_per_shard, int32_t n_shards,
+                 int32_t interleave, int32_t partition_tokens, int32_t max_partitions, float scale,
+                 int32_t dtype, float* part_out, float* part_lse, int32_t* err_flag,
+                 pa::DecodeArgs* out) {
   REQUIRE(q && k_cache && block_table && context_lens && part_out && part_lse, PA_ERR_NULL,
-          "pa_decode: q, k_cache, block_table, context_lens, part_out and part_lse must be non-NULL");
+          "%s: q, k_cache, block_table, context_lens, part_out and part_lse must be non-NULL", fn);
   REQUIRE(valid_dtype(dtype), PA_ERR_UNSUPPORTED, "dtype=%d is not PA_F32 or PA_BF16", dtype);
   REQUIRE(n_seqs >= 0, PA_ERR_SHAPE, "n_seqs=%d must be >= 0", n_seqs);
   REQUIRE(n_q_heads >= 1 && n_kv_heads >= 1 && n_q_heads % n_kv_heads == 0, PA_ERR_SHAPE,
@@ -298,12 +339,61 @@ int pa_decode(const void* q, const void* k_cache, const void* v_cache,
           "n_seqs*n_shards=%lld exceeds 65535", (long long)n_seqs * n_shards);
   REQUIRE(n_kv_heads * ((n_q_heads / n_kv_heads + 15) / 16) <= 65535, PA_ERR_SHAPE,
           "too many heads");
-  if (n_seqs == 0) return ok();
   pa::DecodeArgs a{q,        k_cache,         v_cache,    block_table, context_lens, n_seqs,
                    n_q_heads, n_kv_heads,     dk,         dv,          block_size,   n_blocks,
                    max_blocks_per_shard, n_shards, interleave, partition_tokens, max_partitions,
                    scale,    dtype,           part_out,   part_lse,    err_flag};
+  a.kv_dtype = dtype;
+  a.k_scale = a.v_scale = nullptr;
+  a.n_scales = 0;
+  *out = a;
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_decode(const void* q, const void* k_cache, const void* v_cache,
+              const int32_t* block_table, const int32_t* context_lens, int32_t n_seqs,
+              int32_t n_q_heads, int32_t n_kv_heads, int32_t dk, int32_t dv, int32_t block_size,
+              int64_t n_blocks, int32_t max_blocks_per_shard, int32_t n_shards, int32_t interleave,
+              int32_t partition_tokens, int32_t max_partitions, float scale, int32_t dtype,
+              float* part_out, float* part_lse, int32_t* err_flag, void* stream) {
+  pa::DecodeArgs a;
+  if (int rc = check_decode("pa_decode", q, k_cache, v_cache, block_table, context_lens, n_seqs,
+                            n_q_heads, n_kv_heads, dk, dv, block_size, n_blocks,
+                            max_blocks_per_shard, n_shards, interleave, partition_tokens,
+                            max_partitions, scale, dtype, part_out, part_lse, err_flag, &a))
+    return rc;
+  if (n_seqs == 0) return ok();
   return hip_status(pa::dispatch_decode(a, (hipStream_t)stream), "pa_decode launch");
+}
+
+int pa_decode_fp8(const void* q, const uint8_t* k_cache, const uint8_t* v_cache,
+                  const float* k_scale, const float* v_scale, int32_t n_scales,
+                  const int32_t* block_table, const int32_t* context_lens, int32_t n_seqs,
+                  int32_t n_q_heads, int32_t n_kv_heads, int32_t dk, int32_t dv,
+                  int32_t block_size, int64_t n_blocks, int32_t max_blocks_per_shard,
+                  int32_t n_shards, int32_t interleave, int32_t partition_tokens,
+                  int32_t max_partitions, float scale, int32_t q_dtype, float* part_out,
+                  float* part_lse, int32_t* err_flag, void* stream) {
+  pa::DecodeArgs a;
+  if (int rc = check_decode("pa_decode_fp8", q, k_cache, v_cache, block_table, context_lens,
+                            n_seqs, n_q_heads, n_kv_heads, dk, dv, block_size, n_blocks,
+                            max_blocks_per_shard, n_shards, interleave, partition_tokens,
+                            max_partitions, scale, q_dtype, part_out, part_lse, err_flag, &a))
+    return rc;
+  REQUIRE(k_scale && (v_cache == nullptr || v_scale), PA_ERR_NULL,
+          "pa_decode_fp8: k_scale (and v_scale with a value cache) must be non-NULL");
+  REQUIRE(n_scales == 1 || n_scales == n_kv_heads, PA_ERR_SHAPE,
+          "n_scales=%d must be 1 or n_kv_heads=%d", n_scales, n_kv_heads);
+  if (n_seqs == 0) return ok();
+  a.kv_dtype = PA_FP8_E4M3;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.n_scales = n_scales;
+  return hip_status(pa::dispatch_decode(a, (hipStream_t)stream), "pa_decode_fp8 launch");
 }
 
 int pa_merge_lse(const float* part_out, const float* part_lse, int32_t n_seqs, int32_t n_parts,
@@ -329,7 +419,8 @@ int pa_gather_kv(const void* k_cache, const void* v_cache, const int32_t* block_
                  int32_t* err_flag, void* stream) {
   REQUIRE(k_cache && block_table && k_out && v_out, PA_ERR_NULL,
           "pa_gather_kv: k_cache, block_table, k_out and v_out must be non-NULL");
-  REQUIRE(valid_dtype(dtype), PA_ERR_UNSUPPORTED, "dtype=%d is not PA_F32 or PA_BF16", dtype);
+  REQUIRE(valid_cache_dtype(dtype), PA_ERR_UNSUPPORTED,
+          "dtype=%d is not PA_F32, PA_BF16 or PA_FP8_E4M3", dtype);
   if (int rc = check_placement(n_shards, interleave, block_size)) return rc;
   REQUIRE(seq >= 0 && shard >= 0 && shard < n_shards && context_len >= 0, PA_ERR_SHAPE,
           "seq=%d, shard=%d (n_shards=%d), context_len=%d out of range", seq, shard, n_shards,

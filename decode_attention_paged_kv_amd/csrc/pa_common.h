@@ -17,7 +17,7 @@
 
 namespace pa {
 
-enum : int { kF32 = 0, kBF16 = 1 };
+enum : int { kF32 = 0, kBF16 = 1, kFP8 = 2 };  // kFP8: OCP E4M3 cache codes
 
 constexpr int kMaxHeadDim = 576;
 constexpr int kMaxBlockSize = 256;
@@ -72,6 +72,31 @@ __device__ inline uint16_t f32_to_bf16_bits(float f) {
   return uint16_t(rounded >> 16);
 }
 
+// fp32 -> E4M3 code: round to nearest, ties to the even code; magnitudes of 448 and
+// above (infinities too) saturate to +-448; NaN gives the NaN code with its sign.
+// E4M3: 1 sign, 4 exponent bits (bias 7), 3 mantissa bits; exponent field 0 holds the
+// subnormals m * 2^-9.
+__device__ inline uint8_t f32_to_e4m3(float y) {
+  const uint32_t u = __float_as_uint(y);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7fffffffu;
+  if (a > 0x7f800000u) return uint8_t(sign | 0x7fu);  // NaN
+  if (a >= 0x43e00000u) return uint8_t(sign | 0x7eu); // |y| >= 448
+  if (a < 0x3c800000u) {
+    // |y| < 2^-6: the nearest multiple of 2^-9 (scaling by 512 is exact); a result of 8
+    // is 2^-6, whose code is 0x08 as well
+    const float m = __builtin_rintf(__uint_as_float(a) * 512.0f);
+    return uint8_t(sign | uint32_t(m));
+  }
+  // normal: keep 3 of the 23 fraction bits, round to nearest even (a carry moves into
+  // the exponent), then rebias the exponent from 127 to 7
+  const uint32_t r = a + 0x7ffffu + ((a >> 20) & 1u);
+  return uint8_t(sign | (((r >> 23) - 120u) << 3) | ((r >> 20) & 7u));
+}
+
+// E4M3 code -> fp32, exact (the hardware conversion reads the OCP E4M3 format).
+__device__ inline float e4m3_to_f32(uint8_t c) { return __builtin_amdgcn_cvt_f32_fp8(int(c), 0); }
+
 template <int DT>
 struct Elem;
 template <>
@@ -83,6 +108,11 @@ template <>
 struct Elem<kBF16> {
   using raw = uint16_t;
   static __device__ inline float load(const raw* p, int64_t i) { return bf16_bits_to_f32(p[i]); }
+};
+template <>
+struct Elem<kFP8> {
+  using raw = uint8_t;
+  static __device__ inline float load(const raw* p, int64_t i) { return e4m3_to_f32(p[i]); }
 };
 
 }  // namespace pa

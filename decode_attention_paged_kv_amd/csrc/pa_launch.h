@@ -21,6 +21,10 @@ struct DecodeArgs {
   float* part_out;
   float* part_lse;
   int* flag;
+  int kv_dtype;            // cache element type: dtype, or kFP8 (E4M3 codes)
+  const float* k_scale;    // kFP8: value = code * scale, per KV head (n_scales ==
+  const float* v_scale;    //   hkv) or per tensor (n_scales == 1); NULL otherwise
+  int n_scales;
 };
 
 hipError_t launch_slot_mapping(const int32_t* bt, const int32_t* lens, int n_seqs, int S, int I,
@@ -29,6 +33,11 @@ hipError_t launch_slot_mapping(const int32_t* bt, const int32_t* lens, int n_seq
 hipError_t launch_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                             const int64_t* slots, int n_tokens, int hkv, int dk, int dv, int bs,
                             int64_t n_blocks, int dtype, int* flag, hipStream_t st);
+hipError_t launch_kv_append_fp8(const void* k_new, const void* v_new, int new_dtype,
+                                uint8_t* k_cache, uint8_t* v_cache, const float* k_scale,
+                                const float* v_scale, int n_scales, const int64_t* slots,
+                                int n_tokens, int hkv, int dk, int dv, int bs, int64_t n_blocks,
+                                int* flag, hipStream_t st);
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int64_t* pairs, int n_pairs,
                               int64_t k_bytes, int64_t v_bytes, int64_t n_blocks, int* flag,
                               hipStream_t st);
@@ -41,9 +50,9 @@ bool gqa_supported(const DecodeArgs& a);
 hipError_t launch_decode_gqa(const DecodeArgs& a, hipStream_t st);
 bool mla_supported(const DecodeArgs& a);
 hipError_t launch_decode_mla(const DecodeArgs& a, hipStream_t st);
-int gqa_workgroups_per_cu(int dk);
+int gqa_workgroups_per_cu(int dk, int kv_dtype);
 int mla_workgroups_per_cu();
-int generic_workgroups_per_cu(int dtype);
+int generic_workgroups_per_cu(int dtype, int kv_dtype);
 hipError_t launch_merge(const float* part_out, const float* part_lse, int n_seqs, int n_parts,
                         int hq, int dv, void* out, int out_dtype, float* lse, hipStream_t st);
 

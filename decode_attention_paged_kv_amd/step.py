@@ -1,7 +1,9 @@
 """One decode step on one stream: slot routing, kv append, attention, LSE merge.
 
 ``DecodeStep`` owns the step's output and scratch tensors (allocated once, with
-torch, for a maximum context length) and issues the four library calls.
+torch, for a maximum context length) and issues the four library calls.  A cache of
+``torch.uint8`` holds E4M3 codes and takes its scales with each call (the ``_fp8``
+entry points).
 """
 from __future__ import annotations
 
@@ -44,21 +46,32 @@ class DecodeStep:
         L.pa_slot_mapping(block_table, context_lens, self.n_shards, self.interleave,
                           self.block_size, n_blocks, self.slot_mapping, self.err_flag)
 
-    def append(self, k_new, v_new, k_cache, v_cache):
-        L.pa_kv_append(k_new, v_new, k_cache, v_cache, self.slot_mapping, self.err_flag)
+    def append(self, k_new, v_new, k_cache, v_cache, k_scale=None, v_scale=None):
+        if k_cache.dtype == torch.uint8:
+            L.pa_kv_append_fp8(k_new, v_new, k_cache, v_cache, k_scale, v_scale, self.slot_mapping,
+                               self.err_flag)
+        else:
+            L.pa_kv_append(k_new, v_new, k_cache, v_cache, self.slot_mapping, self.err_flag)
 
-    def attend(self, q, k_cache, v_cache, block_table, context_lens):
-        L.pa_decode(q, k_cache, v_cache, block_table, context_lens, self.n_shards, self.interleave,
-                    self.partition_tokens, self.max_partitions, self.scale, self.part_out,
-                    self.part_lse, dv=self.dv, err_flag=self.err_flag)
+    def attend(self, q, k_cache, v_cache, block_table, context_lens, k_scale=None, v_scale=None):
+        if k_cache.dtype == torch.uint8:
+            L.pa_decode_fp8(q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens,
+                            self.n_shards, self.interleave, self.partition_tokens,
+                            self.max_partitions, self.scale, self.part_out, self.part_lse,
+                            dv=self.dv, err_flag=self.err_flag)
+        else:
+            L.pa_decode(q, k_cache, v_cache, block_table, context_lens, self.n_shards,
+                        self.interleave, self.partition_tokens, self.max_partitions, self.scale,
+                        self.part_out, self.part_lse, dv=self.dv, err_flag=self.err_flag)
 
     def merge(self):
         L.pa_merge_lse(self.part_out, self.part_lse, self.out, self.lse)
 
-    def __call__(self, q, k_new, v_new, k_cache, v_cache, block_table, context_lens):
+    def __call__(self, q, k_new, v_new, k_cache, v_cache, block_table, context_lens, k_scale=None,
+                 v_scale=None):
         """The whole step; returns ``(out, lse)`` (views of this object's buffers)."""
         self.route(block_table, context_lens, k_cache.shape[0])
-        self.append(k_new, v_new, k_cache, v_cache)
-        self.attend(q, k_cache, v_cache, block_table, context_lens)
+        self.append(k_new, v_new, k_cache, v_cache, k_scale, v_scale)
+        self.attend(q, k_cache, v_cache, block_table, context_lens, k_scale, v_scale)
         self.merge()
         return self.out, self.lse

@@ -32,7 +32,8 @@
  *    the offending token or block is skipped and, if `err_flag` is non-NULL, a
  *    nonzero value is stored in *err_flag (never cleared by the library).
  *  - Element types: PA_F32 (IEEE binary32) or PA_BF16 (bfloat16).  q, K and V of one
- *    call share one type.  Partial outputs and LSEs are always float32.
+ *    call share one type, except for an E4M3 cache (pa_kv_append_fp8, pa_decode_fp8).
+ *    Partial outputs and LSEs are always float32.
  *
  * Layout of the paged cache (one layer)
  * -------------------------------------
@@ -78,7 +79,10 @@ typedef enum pa_status {
                                of a new sequence is already in use                  */
 } pa_status;
 
-typedef enum pa_dtype { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
+/* PA_FP8_E4M3: OCP 8-bit floating point E4M3 (1 sign, 4 exponent bits with bias 7,
+ * 3 mantissa bits; exponent field 0 is subnormal; S.1111.111 is NaN; no infinities;
+ * largest magnitude 448).  A cache element type only (see pa_kv_append_fp8). */
+typedef enum pa_dtype { PA_F32 = 0, PA_BF16 = 1, PA_FP8_E4M3 = 2 } pa_dtype;
 
 /* Largest supported sizes. */
 #define PA_MAX_HEAD_DIM 576
@@ -114,6 +118,28 @@ int pa_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_ca
                  int32_t* err_flag, void* stream);
 
 /*
+ * pa_kv_append_fp8 -- pa_kv_append for a cache stored as E4M3 codes (one byte per
+ * element).  The KV cache may be kept in an 8-bit floating type so that a token takes
+ * fewer bytes ([DCP], the passage that sets DCP beside KV-cache quantisation; element
+ * size as a factor of bytes per token: [KVB], "How KV-cache memory limits
+ * concurrency").  Element e of a new key row of KV head h is stored as the code of
+ * k_new[e] / k_scale[h] (k_scale[0] when n_scales == 1): the quotient is formed in
+ * float32 (IEEE division) and rounded to the nearest E4M3 value, ties to the even code;
+ * magnitudes of 448 and above (and infinities) become +-448, NaN the NaN code.  Values
+ * likewise with v_scale.  A stored code c reads back as value(c) * scale.
+ *   k_new, v_new: [n_tokens][n_kv_heads][dk|dv] of new_dtype (PA_F32 or PA_BF16).
+ *   k_cache, v_cache: uint8 codes in the layout of the paged cache.
+ *   k_scale, v_scale: DEVICE float32 [n_scales], n_scales = 1 (per tensor) or
+ *   n_kv_heads (per KV head); positive and finite (not checked).  v_scale and v_cache
+ *   are NULL for the latent cache.  Slots as in pa_kv_append.
+ */
+int pa_kv_append_fp8(const void* k_new, const void* v_new, int32_t new_dtype, uint8_t* k_cache,
+                     uint8_t* v_cache, const float* k_scale, const float* v_scale,
+                     int32_t n_scales, const int64_t* slot_mapping, int32_t n_tokens,
+                     int32_t n_kv_heads, int32_t dk, int32_t dv, int32_t block_size,
+                     int64_t n_blocks, int32_t* err_flag, void* stream);
+
+/*
  * pa_decode -- attention of one query token per sequence over its paged K/V, split
  * into shards and partitions, each emitting an output and its LSE ([PA]: attention
  * follows the block table; [DCP]: local attention per shard returning output + LSE).
@@ -141,6 +167,23 @@ int pa_decode(const void* q, const void* k_cache, const void* v_cache,
               float* part_out, float* part_lse, int32_t* err_flag, void* stream);
 
 /*
+ * pa_decode_fp8 -- pa_decode over an E4M3 cache written by pa_kv_append_fp8: every
+ * stored key (value) element is taken as value(code) * k_scale[h] (v_scale[h]; index 0
+ * when n_scales == 1), for KV head h; the latent cache (v_cache == NULL) takes the
+ * value from the key row, with k_scale.  q is of q_dtype (PA_F32 or PA_BF16); the other
+ * arguments and the outputs are as in pa_decode.  Cache base addresses must be 16-byte
+ * aligned.
+ */
+int pa_decode_fp8(const void* q, const uint8_t* k_cache, const uint8_t* v_cache,
+                  const float* k_scale, const float* v_scale, int32_t n_scales,
+                  const int32_t* block_table, const int32_t* context_lens, int32_t n_seqs,
+                  int32_t n_q_heads, int32_t n_kv_heads, int32_t dk, int32_t dv,
+                  int32_t block_size, int64_t n_blocks, int32_t max_blocks_per_shard,
+                  int32_t n_shards, int32_t interleave, int32_t partition_tokens,
+                  int32_t max_partitions, float scale, int32_t q_dtype, float* part_out,
+                  float* part_lse, int32_t* err_flag, void* stream);
+
+/*
  * pa_merge_lse -- combine the partials of each (sequence, head) into the attention
  * over all its tokens ([DCP], DCP mechanism section: gather the LSEs, reweight each
  * partial output, sum).  With lse = log(sum_p exp(lse_p)), part p has weight
@@ -163,6 +206,7 @@ int pa_merge_lse(const float* part_out, const float* part_lse, int32_t n_seqs, i
  *   k_out [L_r][n_kv_heads][dk], v_out [L_r][n_kv_heads][dv] (v_out from the first dv
  *   entries of the key rows when v_cache is NULL); L_r = pa_shard_length(L, ...).
  *   Rows whose block id is invalid are left unwritten and set *err_flag.
+ *   dtype PA_FP8_E4M3 copies the codes.
  */
 int pa_gather_kv(const void* k_cache, const void* v_cache, const int32_t* block_table,
                  int32_t seq, int32_t shard, int32_t context_len, int32_t n_kv_heads, int32_t dk,
@@ -179,7 +223,7 @@ int pa_gather_kv(const void* k_cache, const void* v_cache, const int32_t* block_
  *   pairs: DEVICE int64 [n_pairs][2].  A pair with an id outside [0, n_blocks) is
  *   skipped and sets *err_flag; src == dst is a no-op.  Destinations must be distinct
  *   and must not be the source of another pair of the same call (else the content of
- *   those blocks is unspecified).  Sizes as in pa_kv_append.
+ *   those blocks is unspecified).  Sizes as in pa_kv_append; dtype may be PA_FP8_E4M3.
  */
 int pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* pairs, int32_t n_pairs,
                    int32_t n_kv_heads, int32_t dk, int32_t dv, int32_t block_size, int64_t n_blocks,
@@ -247,7 +291,8 @@ int32_t pa_default_partition_tokens(int32_t n_seqs, int32_t n_kv_heads, int32_t 
  * shape (latent != 0: value = first dv entries of the key row) is dispatched: the
  * busiest workgroup's tokens plus a fixed per-unit cost when the kernel keeps a resident
  * grid, else the busiest XCD's rounds of workgroups x (partition tokens + that cost),
- * with the kernel's occupancy and the device's compute-unit and XCD counts.  A heuristic
+ * with the kernel's occupancy and the device's compute-unit and XCD counts.  dtype
+ * PA_FP8_E4M3 means an E4M3 cache read with bf16 queries (pa_decode_fp8).  A heuristic
  * of this library.  Returns -1 on invalid arguments.
  */
 int32_t pa_choose_partition_tokens(const int32_t* context_lens_host, int32_t n_seqs,

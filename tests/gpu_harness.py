@@ -12,6 +12,10 @@ weights kept to >= 16 significant bits gives ~1e-6; the bound is 1e-4.  Kernels
 that round the weights to bf16 once (8 significant bits, relative error <= 2^-9
 per weight, ~2e-3 in L2 on random data) are held to 4e-3 (``rel_l2`` argument).
 kv append, slot routing and the gather are compared bit for bit.
+
+An E4M3 cache (``w.kv_dtype == FP8``) is compared with the oracle's ``fp8_kv``
+step: the stored codes bit for bit, outputs with the tolerances of the query type
+(the kernels read the same dequantised values the oracle does).
 """
 from __future__ import annotations
 
@@ -21,6 +25,7 @@ import numpy as np
 import torch
 
 import workloads as wl
+from oracle import fp8_kv as f8
 from oracle import paged_attention as pa
 
 TOL = {wl.F32: dict(out=1e-5, lse=1e-5), wl.BF16: dict(out=5e-3, lse=1e-3)}
@@ -55,9 +60,10 @@ def run_library(w, T, partition_tokens=None, out_dtype=torch.float32):
     step = P.DecodeStep(w.n_seqs, w.n_q_heads, w.n_kv_heads, w.dk, w.dv, w.block_size,
                         int(w.context_lens.max()), w.n_shards, w.interleave, Tp, w.scale_f32,
                         device=T["q"].device, out_dtype=out_dtype,
-                        context_lens_host=w.context_lens, kv_dtype=T["q"].dtype, latent=w.latent)
+                        context_lens_host=w.context_lens, kv_dtype=T["k_cache"].dtype,
+                        latent=w.latent)
     out, lse = step(T["q"], T["k_new"], T["v_new"], T["k_cache"], T["v_cache"],
-                    T["block_table"], T["context_lens"])
+                    T["block_table"], T["context_lens"], T.get("k_scale"), T.get("v_scale"))
     torch.cuda.synchronize()
     return step
 
@@ -89,6 +95,17 @@ def compare_outputs(name, dtype, o, lse, o_ref, lse_ref, rel_l2=REL_L2, out_tol=
     assert rel <= rel_l2, f"{name}: output relative L2 {rel:.3g} > {rel_l2}"
 
 
+def oracle_step(w, H, block_table, context_lens, Tp, Pmax):
+    """The oracle's step on numpy inputs ``H`` (E4M3 caches through ``fp8_kv``)."""
+    if w.cache_dtype == wl.FP8:
+        return f8.decode_step(H["q"], H["k_new"], H["v_new"], H["k_cache"], H["v_cache"],
+                              H["k_scale"], H["v_scale"], block_table, context_lens, w.n_shards,
+                              w.interleave, w.block_size, Tp, Pmax, w.scale_f32, w.dv)
+    return pa.decode_step(H["q"], H["k_new"], H["v_new"], H["k_cache"], H["v_cache"],
+                          block_table, context_lens, w.n_shards, w.interleave, w.block_size,
+                          Tp, Pmax, w.scale_f32, w.dv)
+
+
 def check_small(w, partition_tokens=None, fill="normal", rel_l2=REL_L2, seed=None, tweak=None):
     """Whole-workload parity: routing, append (whole pool, bitwise), gather
     (bitwise, every sequence and shard), partials and merged outputs.  ``tweak``,
@@ -105,9 +122,8 @@ def check_small(w, partition_tokens=None, fill="normal", rel_l2=REL_L2, seed=Non
     T = {k: (None if v is None else v.to(dev)) for k, v in Tc.items()}
     step = run_library(w, T, partition_tokens)
     Tp, Pmax = step.partition_tokens, step.max_partitions
-    ref = pa.decode_step(H["q"], H["k_new"], H["v_new"], H["k_cache"], H["v_cache"],
-                         w.block_table, w.context_lens, w.n_shards, w.interleave, w.block_size,
-                         Tp, Pmax, w.scale_f32, w.dv)
+    ref = oracle_step(w, H, w.block_table, w.context_lens, Tp, Pmax)
+    kdt = T["k_cache"].dtype
     assert int(step.err_flag.item()) == 0, f"{w.name}: device error flag {int(step.err_flag.item())}"
     assert np.array_equal(to_np(step.slot_mapping), ref["slots"]), f"{w.name}: slot mapping"
     assert bits_equal(to_np(T["k_cache"]), ref["k_cache"]), f"{w.name}: k_cache after append"
@@ -118,8 +134,8 @@ def check_small(w, partition_tokens=None, fill="normal", rel_l2=REL_L2, seed=Non
         L = int(w.context_lens[b])
         for r in range(w.n_shards):
             Lr = P.pa_shard_length(L, w.n_shards, w.interleave, r)
-            kg = torch.empty(max(Lr, 1), w.n_kv_heads, w.dk, dtype=T["q"].dtype, device=dev)
-            vg = torch.empty(max(Lr, 1), w.n_kv_heads, w.dv, dtype=T["q"].dtype, device=dev)
+            kg = torch.empty(max(Lr, 1), w.n_kv_heads, w.dk, dtype=kdt, device=dev)
+            vg = torch.empty(max(Lr, 1), w.n_kv_heads, w.dv, dtype=kdt, device=dev)
             P.pa_gather_kv(T["k_cache"], T["v_cache"], T["block_table"], b, r, L, w.n_shards,
                            w.interleave, kg, vg, step.err_flag)
             kr, vr = pa.gather_shard(ref["k_cache"], ref["v_cache"], w.block_table[b], L, r,
@@ -157,20 +173,30 @@ def check_large(w, sample_seqs, partition_tokens=None, fill="normal", rel_l2=REL
     bs = w.block_size
     sl = torch.from_numpy(slots_ref).to(dev)
 
+    def bits(x):
+        return x.view({torch.bfloat16: torch.int16, torch.float32: torch.int32,
+                       torch.uint8: torch.uint8}[x.dtype])
+
     def slot_major_k(x):            # [NB][Hkv][bs][dk] -> [NB*bs][Hkv*dk]
-        return x.view(torch.int16 if x.dtype == torch.bfloat16 else torch.int32).permute(0, 2, 1, 3).reshape(x.shape[0] * bs, -1)
+        return bits(x).permute(0, 2, 1, 3).reshape(x.shape[0] * bs, -1)
 
     def slot_major_v(x):            # [NB][Hkv][dv][bs] -> [NB*bs][Hkv*dv]
-        return x.view(torch.int16 if x.dtype == torch.bfloat16 else torch.int32).permute(0, 3, 1, 2).reshape(x.shape[0] * bs, -1)
+        return bits(x).permute(0, 3, 1, 2).reshape(x.shape[0] * bs, -1)
 
-    for after, before, new, fn in ((T["k_cache"], k_before, T["k_new"], slot_major_k),
-                                   (T["v_cache"], v_before, T["v_new"], slot_major_v)):
+    fp8 = w.cache_dtype == wl.FP8
+    for after, before, new, fn, sc in ((T["k_cache"], k_before, T["k_new"], slot_major_k, T.get("k_scale")),
+                                       (T["v_cache"], v_before, T["v_new"], slot_major_v, T.get("v_scale"))):
         if after is None:
             continue
         A, B = fn(after), fn(before)
         changed = torch.nonzero((A != B).any(dim=1)).flatten().cpu().numpy()
         assert set(changed.tolist()) <= set(slots_ref.tolist()), f"{w.name}: append touched other slots"
-        newbits = new.reshape(new.shape[0], -1).view(A.dtype)
+        if fp8:     # the oracle's codes of the new rows under each head's scale
+            hs = f8.head_scales(to_np(sc), w.n_kv_heads)
+            want = f8.quantize(to_np(new), hs[None, :, None]).reshape(new.shape[0], -1)
+            newbits = torch.from_numpy(want).to(dev)
+        else:
+            newbits = new.reshape(new.shape[0], -1).view(A.dtype)
         assert torch.equal(A[sl], newbits), f"{w.name}: appended rows differ"
     del A, B
     Tp, Pmax = step.partition_tokens, step.max_partitions
@@ -185,13 +211,14 @@ def check_large(w, sample_seqs, partition_tokens=None, fill="normal", rel_l2=REL
         kn = to_np(T["k_new"][b:b + 1])
         vn = None if T["v_new"] is None else to_np(T["v_new"][b:b + 1])
         qb = to_np(T["q"][b:b + 1])
-        ref = pa.decode_step(qb, kn, vn, kc, vc, bt_b.astype(np.int32), w.context_lens[b:b + 1],
-                             w.n_shards, w.interleave, bs, Tp, Pmax, w.scale_f32, w.dv)
+        Hb = dict(q=qb, k_new=kn, v_new=vn, k_cache=kc, v_cache=vc,
+                  k_scale=to_np(T.get("k_scale")), v_scale=to_np(T.get("v_scale")))
+        ref = oracle_step(w, Hb, bt_b.astype(np.int32), w.context_lens[b:b + 1], Tp, Pmax)
         # the gather of each shard, bit for bit
         for r in range(w.n_shards):
             Lr = P.pa_shard_length(L, w.n_shards, w.interleave, r)
-            kg = torch.empty(max(Lr, 1), w.n_kv_heads, w.dk, dtype=T["q"].dtype, device=dev)
-            vg = torch.empty(max(Lr, 1), w.n_kv_heads, w.dv, dtype=T["q"].dtype, device=dev)
+            kg = torch.empty(max(Lr, 1), w.n_kv_heads, w.dk, dtype=T["k_cache"].dtype, device=dev)
+            vg = torch.empty(max(Lr, 1), w.n_kv_heads, w.dv, dtype=T["k_cache"].dtype, device=dev)
             P.pa_gather_kv(T["k_cache"], T["v_cache"], T["block_table"], b, r, L, w.n_shards,
                            w.interleave, kg, vg, step.err_flag)
             kr, vr = pa.gather_shard(ref["k_cache"], ref["v_cache"], bt_b[0], L, r, w.n_shards,

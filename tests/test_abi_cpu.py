@@ -103,3 +103,32 @@ def test_choose_partition_tokens():
     lens = np.array([10], np.int32)
     assert P.lib.pa_choose_partition_tokens(None, 1, 4, 1, 64, 64, 4, 0, 0, 1, 1) == -1
     assert P.pa_choose_partition_tokens(lens, 6, 4, 64, 64, 4, torch.float32, False) == -1
+
+
+def test_fp8_entry_points_reject_bad_arguments():
+    vp = ctypes.c_void_p(0x1000)
+    ap = P.lib.pa_kv_append_fp8
+    # k_new, v_new, new_dtype, k_cache, v_cache, k_scale, v_scale, n_scales, slots, n, hkv, dk, dv, bs, nb
+    assert ap(vp, vp, 1, vp, vp, None, vp, 1, vp, 1, 2, 64, 64, 16, 8, None, None) == -1   # no k_scale
+    assert ap(vp, vp, 1, vp, vp, vp, None, 1, vp, 1, 2, 64, 64, 16, 8, None, None) == -1   # no v_scale
+    assert ap(vp, vp, 2, vp, vp, vp, vp, 1, vp, 1, 2, 64, 64, 16, 8, None, None) == -3     # fp8 rows
+    assert ap(vp, vp, 1, vp, vp, vp, vp, 3, vp, 1, 2, 64, 64, 16, 8, None, None) == -2     # n_scales
+    assert ap(vp, vp, 1, vp, vp, vp, vp, 2, vp, 0, 2, 64, 64, 16, 8, None, None) == 0      # nothing to do
+    dp = P.lib.pa_decode_fp8
+
+    def dec(**over):
+        a = dict(q=vp, k=vp, v=vp, ks=vp, vs=vp, ns=1, bt=vp, lens=vp, n=1, hq=8, hkv=2, dk=64,
+                 dv=64, bs=16, nb=8, mb=4, S=1, I=1, T=16, P=4, scale=0.125, dt=1)
+        a.update(over)
+        return dp(a["q"], a["k"], a["v"], a["ks"], a["vs"], a["ns"], a["bt"], a["lens"], a["n"],
+                  a["hq"], a["hkv"], a["dk"], a["dv"], a["bs"], a["nb"], a["mb"], a["S"], a["I"],
+                  a["T"], a["P"], a["scale"], a["dt"], vp, vp, None, None)
+
+    assert dec(ks=None) == -1
+    assert dec(vs=None) == -1
+    assert dec(v=None, vs=None, n=0) == 0                  # latent: no value scale needed
+    assert dec(ns=3) == -2
+    assert dec(dt=2) == -3                                 # queries are not E4M3
+    assert dec(n=0) == 0
+    assert P.pa_choose_partition_tokens(np.array([1000], np.int32), 8, 2, 64, 64, 16,
+                                        __import__("torch").uint8, False) % 16 == 0
