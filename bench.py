@@ -4,13 +4,15 @@ A step is the whole hot path on one stream: slot routing of the new tokens,
 kv append, the partitioned attention (pa_decode) and the LSE merge.  Inputs are
 seeded synthetic tensors already resident in HBM.  Prints ONE JSON line.
 
-  python bench.py [--steps K] [--warmup W] [--config long|dcp1|dcp16|batch|latent|tiny]
+  python bench.py [--steps K] [--warmup W]
+                  [--config long|dcp1|dcp16|batch|latent|tiny|long_fp8|dcp1_fp8|dcp16_fp8]
                   [--no-cpu-baseline] [--secondary]
 
 The default workload is the long-context step (8 sequences, log-normal lengths
 around 142K tokens), the configuration the HBM-roofline target is stated for.
 ``value`` is KV-read GB/s over the whole step (algorithmic bytes: every stored
-K and V element of every sequence read once per step).  ``roofline`` prices the
+K and V element of every sequence read once per step; one byte per element for the
+``_fp8`` configurations, whose cache holds E4M3 codes).  ``roofline`` prices the
 decode kernel alone: the same algorithmic bytes over its average launch time,
 measured with HIP events around each launch inside the timed region.
 """
@@ -40,6 +42,9 @@ def make_workload(name):
         "batch": lambda: wl.batch(),
         "latent": lambda: wl.latent(),
         "tiny": lambda: wl.tiny(),
+        "long_fp8": lambda: wl.with_fp8_cache(wl.long(partition_tokens=0)),
+        "dcp1_fp8": lambda: wl.with_fp8_cache(wl.dcp(interleave=1)),
+        "dcp16_fp8": lambda: wl.with_fp8_cache(wl.dcp(interleave=16)),
     }[name]()
 
 
@@ -55,6 +60,13 @@ DESCRIBE = {
     "latent": "latent (MLA-style) cache: 32 seqs, L U[4096, 65536], 128 q heads on 1 kv head, "
               "key 576 / value 512 (view), bf16, block 64, 2048-token prefixes shared by 4",
     "tiny": "1 seq, L 67, 4 q / 1 kv head, d 64, fp32, block 4",
+    "long_fp8": "long-context decode with an E4M3 KV cache (per-KV-head scales): 8 seqs, L log-normal "
+                "(median 142K, sigma 0.5, clip [16384, 200000]), 32 q / 8 kv heads, d 128, bf16 q, "
+                "block 16, partition size chosen by pa_choose_partition_tokens",
+    "dcp1_fp8": "DCP emulation with an E4M3 KV cache: 1 seq of 200000 tokens, 64 q / 8 kv heads, "
+                "d 128, bf16 q, block 16, S=4 interleaved shards, I=1",
+    "dcp16_fp8": "DCP emulation with an E4M3 KV cache: 1 seq of 200000 tokens, 64 q / 8 kv heads, "
+                 "d 128, bf16 q, block 16, S=4 interleaved shards, I=16",
 }
 
 
@@ -91,8 +103,9 @@ def measured_traffic(config, launches_bytes):
 def time_gpu(w, T, step, steps, warmup):
     import torch
 
+    ks, vs = T.get("k_scale"), T.get("v_scale")
     args = (T["q"], T["k_new"], T["v_new"], T["k_cache"], T["v_cache"], T["block_table"],
-            T["context_lens"])
+            T["context_lens"], ks, vs)
     nb = T["k_cache"].shape[0]
     for _ in range(warmup):
         step(*args)
@@ -105,9 +118,9 @@ def time_gpu(w, T, step, steps, warmup):
     t0.record()
     for i in range(steps):
         step.route(T["block_table"], T["context_lens"], nb)
-        step.append(T["k_new"], T["v_new"], T["k_cache"], T["v_cache"])
+        step.append(T["k_new"], T["v_new"], T["k_cache"], T["v_cache"], ks, vs)
         ev[i][0].record()
-        step.attend(T["q"], T["k_cache"], T["v_cache"], T["block_table"], T["context_lens"])
+        step.attend(T["q"], T["k_cache"], T["v_cache"], T["block_table"], T["context_lens"], ks, vs)
         ev[i][1].record()
         step.merge()
     t1.record()
@@ -125,6 +138,7 @@ def cpu_baseline(w, T, budget_s=12.0):
     import numpy as np
     import torch
 
+    from oracle import fp8_kv as f8
     from oracle import paged_attention as pa
 
     def host(x):
@@ -150,10 +164,15 @@ def cpu_baseline(w, T, budget_s=12.0):
         Tp = w.partition_tokens or 4096
         pmax = pa.max_partitions(int(w.context_lens[b]), w.n_shards, w.interleave, Tp)
         t = time.perf_counter()
-        pa.decode_step(host(T["q"][b:b + 1]), host(T["k_new"][b:b + 1]),
-                       None if T["v_new"] is None else host(T["v_new"][b:b + 1]), kc, vc, bt,
-                       w.context_lens[b:b + 1], w.n_shards, w.interleave, w.block_size, Tp,
-                       max(pmax, 1), w.scale_f32, w.dv)
+        qn, kn = host(T["q"][b:b + 1]), host(T["k_new"][b:b + 1])
+        vn = None if T["v_new"] is None else host(T["v_new"][b:b + 1])
+        if w.cache_dtype == "fp8":
+            f8.decode_step(qn, kn, vn, kc, vc, host(T["k_scale"]), host(T.get("v_scale")), bt,
+                           w.context_lens[b:b + 1], w.n_shards, w.interleave, w.block_size, Tp,
+                           max(pmax, 1), w.scale_f32, w.dv)
+        else:
+            pa.decode_step(qn, kn, vn, kc, vc, bt, w.context_lens[b:b + 1], w.n_shards,
+                           w.interleave, w.block_size, Tp, max(pmax, 1), w.scale_f32, w.dv)
         elapsed += time.perf_counter() - t
         done_tokens += int(w.context_lens[b])
         seqs.append(b)
@@ -181,7 +200,10 @@ def run_config(name, steps, warmup, with_cpu, partition_tokens=0):
     step = P.DecodeStep(w.n_seqs, w.n_q_heads, w.n_kv_heads, w.dk, w.dv, w.block_size,
                         int(w.context_lens.max()), w.n_shards, w.interleave,
                         w.partition_tokens, w.scale_f32, device=dev,
-                        context_lens_host=w.context_lens, kv_dtype=T["q"].dtype, latent=w.latent)
+                        context_lens_host=w.context_lens, kv_dtype=T["k_cache"].dtype,
+                        latent=w.latent)
+    if not w.partition_tokens:
+        w.partition_tokens = step.partition_tokens
     cpu = cpu_baseline(w, T) if with_cpu else None
     t = time_gpu(w, T, step, steps, warmup)
     assert int(step.err_flag.item()) == 0, "device error flag set"
@@ -190,7 +212,9 @@ def run_config(name, steps, warmup, with_cpu, partition_tokens=0):
     ms = t["total_ms"] / steps
     dec_ms = t["decode_ms_mean"]
     achieved = kv_bytes / (dec_ms * 1e-3) / 1e9
+    tokens = int(np.sum(w.context_lens.astype(np.int64)))
     res = dict(w=w, step=step, kv_bytes=kv_bytes, ms_per_step=ms, decode_ms=dec_ms,
+               tokens_per_s_decode=tokens / (dec_ms * 1e-3),
                value=kv_bytes / (ms * 1e-3) / 1e9, seq_steps=w.n_seqs / (ms * 1e-3),
                achieved=achieved, timing=t, cpu=cpu)
     if w.latent:
@@ -262,10 +286,12 @@ def main():
         "config": {"workload": DESCRIBE[a.config], "name": a.config, "n_seqs": w.n_seqs,
                    "context_tokens": int(w.context_lens.sum()), "max_context": int(w.context_lens.max()),
                    "partition_tokens": r["step"].partition_tokens,
+                   "kv_cache": "e4m3 codes + float32 per-head scales" if w.cache_dtype == "fp8" else w.dtype,
                    "kv_bytes_per_step": r["kv_bytes"]},
         "hbm_frac": round(r["value"] / HBM_PEAK_GBS, 4),
         "seq_steps_per_s": round(r["seq_steps"], 2),
         "decode_ms": round(r["decode_ms"], 5),
+        "kv_tokens_per_s_decode": round(r["tokens_per_s_decode"], 1),
         "roofline": {"bound": "hbm", "achieved": round(r["achieved"], 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(r["achieved"] / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "kernel": "pa_decode",
@@ -277,13 +303,14 @@ def main():
         line["roofline"]["mfma_frac"] = round(r["tflops"] / MFMA_BF16_TFLOPS, 4)
     if a.secondary:
         sec = {}
-        for name in ("dcp1", "dcp16", "batch", "latent", "tiny"):
+        for name in ("dcp1", "dcp16", "batch", "latent", "tiny", "long_fp8", "dcp1_fp8", "dcp16_fp8"):
             if name == a.config:
                 continue
             s = run_config(name, a.steps, a.warmup, False)
             sec[name] = {"kv_GBs_step": round(s["value"], 2), "kv_GBs_decode": round(s["achieved"], 2),
                          "hbm_frac_decode": round(s["achieved"] / HBM_PEAK_GBS, 4),
                          "ms_per_step": round(s["ms_per_step"], 5), "decode_ms": round(s["decode_ms"], 5),
+                         "kv_tokens_per_s_decode": round(s["tokens_per_s_decode"], 1),
                          "seq_steps_per_s": round(s["seq_steps"], 2)}
             if "tflops" in s:
                 sec[name]["mfma_tflops"] = round(s["tflops"], 2)

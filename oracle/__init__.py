@@ -33,8 +33,10 @@ Modules:
 * ``fp8_kv``          -- a cache stored as FP8 E4M3 codes with float32 scales per
   tensor or per KV head: quantise on append, dequantise on read (the pages name FP8
   storage of the cache; the format, scaling and rounding are readings stated there).
+* ``multi_query``     -- a step with several new tokens per sequence, each attending
+  causally (over everything before it and itself): slots, partials and merge.
 
 Parity status of each function is stated in its docstring; every function here
 is pinned by a CPU test in ``tests/test_oracle_*.py`` (none is "parity unpinned").
 """
-from . import paged_attention, block_manager, fp8_kv  # noqa: F401
+from . import paged_attention, block_manager, fp8_kv, multi_query  # noqa: F401

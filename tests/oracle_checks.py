@@ -29,7 +29,12 @@ What each check compares against:
                         range (ties, subnormals, bf16 inputs, four scales), the error is
                         within half an ulp, and the saturation/NaN readings hold;
 * ``fp8_decode``     -- the E4M3 step equals causal SDPA (fp64) over K/V decoded by
-                        torch and scaled per head, new rows cast by torch.
+                        torch and scaled per head, new rows cast by torch;
+* ``multi_sdpa``     -- with several new tokens per sequence, each one's output equals
+                        its row of causal SDPA (fp64) over the whole sequence;
+* ``multi_as_prefixes`` -- each new token equals the single-token step on the sequence
+                        cut after it, one new token per sequence is the single-token
+                        step, and the new tokens' slots equal the generator's.
 """
 from __future__ import annotations
 
@@ -490,6 +495,129 @@ def check_fp8_decode():
     return None
 
 
+# ----------------------------------------------------------------------------------
+# several new tokens per sequence (causal among them)
+# ----------------------------------------------------------------------------------
+def multi_workloads():
+    import workloads as wl
+
+    return [
+        wl.small("mq_gqa", [5, 33, 17, 9], 4, 2, 16, 16, 8, wl.BF16, partition_tokens=8, seed=61,
+                 q_lens=[3, 5, 1, 0]),
+        wl.small("mq_dcp", [40, 64, 7], 4, 2, 8, 8, 4, wl.F32, n_shards=3, interleave=2,
+                 partition_tokens=4, seed=62, q_lens=[6, 2, 7]),
+        wl.small("mq_latent", [17, 70], 8, 1, 24, 16, 8, wl.BF16, latent=True, partition_tokens=16,
+                 seed=63, q_lens=[4, 4]),
+    ]
+
+
+def run_multi_step(w, T, partition_tokens=None):
+    from oracle import multi_query as mq
+
+    Tp = partition_tokens or w.partition_tokens or 16
+    pmax = pa.max_partitions(int(w.context_lens.max()), w.n_shards, w.interleave, Tp)
+    return mq.decode_step_multi(T["q"], w.query_start, T["k_new"], T["v_new"], T["k_cache"],
+                                T["v_cache"], w.block_table, w.context_lens, w.n_shards,
+                                w.interleave, w.block_size, Tp, pmax, w.scale_f32, w.dv)
+
+
+def contiguous_multi(w, T, b):
+    """Global-order K/V rows of sequence ``b`` from the generator's token record, with
+    its new tokens (the last ``q_lens[b]``) taken from the new rows."""
+    L, n = int(w.context_lens[b]), int(w.q_lens[b])
+    kc, vc = T["k_cache"], T["v_cache"]
+    K = np.empty((L, w.n_kv_heads, w.dk), kc.dtype)
+    V = np.empty((L, w.n_kv_heads, w.dv), kc.dtype)
+    seen = np.zeros(L, bool)
+    for r in range(w.n_shards):
+        for phys in w.block_table[b, r]:
+            if phys < 0:
+                continue
+            for o in range(w.block_size):
+                i = w.token_id[phys, o]
+                if i < 0 or i >= L or not w.live[phys, o]:
+                    continue
+                K[i] = kc[phys, :, o, :]
+                V[i] = kc[phys, :, o, :w.dv] if vc is None else vc[phys, :, :, o]
+                seen[i] = True
+    r0 = int(w.query_start[b])
+    for i in range(n):
+        K[L - n + i] = T["k_new"][r0 + i]
+        V[L - n + i] = T["k_new"][r0 + i][:, :w.dv] if T["v_new"] is None else T["v_new"][r0 + i]
+        seen[L - n + i] = True
+    assert seen.all()
+    return K, V
+
+
+def check_multi_sdpa():
+    """Each new token's output equals its row of full causal attention (PyTorch SDPA,
+    fp64) over the contiguous sequence; the other rows get random queries."""
+    import torch
+    import torch.nn.functional as F
+
+    for w in multi_workloads():
+        T = tensors_np(w)
+        res = run_multi_step(w, T)
+        for b in range(w.n_seqs):
+            n = int(w.q_lens[b])
+            if n == 0:
+                continue
+            K, V = contiguous_multi(w, T, b)
+            L = K.shape[0]
+            r = _rng(300 + b)
+            Q = r.standard_normal((L, w.n_q_heads, w.dk))
+            r0 = int(w.query_start[b])
+            Q[L - n:] = pa.widen(T["q"][r0:r0 + n])
+            qt = torch.from_numpy(Q).permute(1, 0, 2)[None]
+            kt = torch.from_numpy(pa.widen(K)).permute(1, 0, 2)[None]
+            vt = torch.from_numpy(np.ascontiguousarray(pa.widen(V))).permute(1, 0, 2)[None]
+            ref = F.scaled_dot_product_attention(qt, kt, vt, is_causal=True, scale=w.scale_f32,
+                                                 enable_gqa=True)[0, :, L - n:, :].numpy()
+            err = np.max(np.abs(res["o"][r0:r0 + n] - ref.transpose(1, 0, 2)))
+            if not err <= 1e-12:
+                return f"multi sdpa {w.name} seq {b}: |do|={err:.3g}"
+    return None
+
+
+def check_multi_as_prefixes():
+    """New token i of a sequence gets exactly the single-token step's result on the
+    sequence cut after it (same cache, same partitions), and one new token per
+    sequence is the single-token step itself (slots included)."""
+    import workloads as wl
+    from oracle import multi_query as mq
+
+    for w in multi_workloads():
+        T = tensors_np(w)
+        res = run_multi_step(w, T)
+        Tp = w.partition_tokens or 16
+        pmax = pa.max_partitions(int(w.context_lens.max()), w.n_shards, w.interleave, Tp)
+        for b in range(w.n_seqs):
+            n, L, r0 = int(w.q_lens[b]), int(w.context_lens[b]), int(w.query_start[b])
+            for i in range(n):
+                o, lse, _, _ = pa.decode(T["q"][r0 + i:r0 + i + 1], res["k_cache"], res["v_cache"],
+                                         w.block_table[b:b + 1], np.array([L - n + i + 1]),
+                                         w.n_shards, w.interleave, w.block_size, Tp, pmax,
+                                         w.scale_f32, w.dv)
+                if not (np.array_equal(o[0], res["o"][r0 + i]) and np.array_equal(lse[0], res["lse"][r0 + i])):
+                    return f"multi {w.name} seq {b} token {i}: differs from the cut sequence"
+    w1 = wl.small("mq_one", [5, 33, 17], 4, 2, 16, 16, 8, wl.BF16, partition_tokens=8, seed=64,
+                  q_lens=[1, 1, 1])
+    T = tensors_np(w1)
+    res = run_multi_step(w1, T)
+    ref = pa.decode_step(T["q"], T["k_new"], T["v_new"], T["k_cache"], T["v_cache"],
+                         w1.block_table, w1.context_lens, 1, 1, w1.block_size, 8,
+                         pa.max_partitions(int(w1.context_lens.max()), 1, 1, 8), w1.scale_f32, w1.dv)
+    if not (np.array_equal(res["slots"], ref["slots"]) and np.array_equal(res["o"], ref["o"])
+            and np.array_equal(res["lse"], ref["lse"])):
+        return "multi with one new token per sequence differs from the single-token step"
+    for w in multi_workloads():
+        if not np.array_equal(mq.slot_mapping_multi(w.block_table, w.context_lens, w.query_start,
+                                                    w.n_shards, w.interleave, w.block_size),
+                              w.new_slot):
+            return f"multi slots {w.name} differ from the generator's"
+    return None
+
+
 ALL_CHECKS = {
     "bruteforce": check_bruteforce,
     "closed_forms": check_closed_forms,
@@ -503,4 +631,6 @@ ALL_CHECKS = {
     "fp8_table": check_fp8_table,
     "fp8_rounding": check_fp8_rounding,
     "fp8_decode": check_fp8_decode,
+    "multi_sdpa": check_multi_sdpa,
+    "multi_as_prefixes": check_multi_as_prefixes,
 }

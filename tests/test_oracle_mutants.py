@@ -11,6 +11,7 @@ import pytest
 
 import oracle_checks as oc
 from oracle import fp8_kv as f8
+from oracle import multi_query as mq
 from oracle import paged_attention as pa
 
 _attention = pa.attention
@@ -22,6 +23,8 @@ _copy_blocks = pa.copy_blocks
 _quantize = f8.quantize
 _dequantize_cache = f8.dequantize_cache
 _E4M3 = f8.E4M3.copy()
+_mq_partials = mq.decode_multi_partials
+_mq_slots = mq.slot_mapping_multi
 
 
 def _attn_variant(kind):
@@ -211,6 +214,72 @@ def test_fp8_mutant_is_caught(name, monkeypatch):
     else:
         attr, fn = FP8_MUTANTS[name]
         monkeypatch.setattr(f8, attr, fn)
+    failures = []
+    for check in oc.ALL_CHECKS.values():
+        try:
+            msg = check()
+        except Exception as e:          # a crash is also a detection
+            msg = f"raised {type(e).__name__}"
+        if msg:
+            failures.append(msg)
+            break
+    assert failures, f"planted mistake {name} passed every pin"
+
+
+def _mq_shifted(shift):
+    """the causal bound moved by ``shift`` positions (clipped to the context)"""
+    def f(q, query_start, k_cache, v_cache, block_table, context_lens, S, I, bs, T, Pmax, scale, dv):
+        n = mq.query_counts(query_start)
+        rows, hq = q.shape[0], q.shape[1]
+        po = np.zeros((rows, S, Pmax, hq, dv))
+        pl = np.full((rows, S, Pmax, hq), -np.inf)
+        row = 0
+        for b, L in enumerate(np.asarray(context_lens)):
+            L = int(L)
+            for r in range(S):
+                K, V = pa.gather_shard(k_cache, v_cache, block_table[b], L, r, S, I, bs, dv)
+                members = pa.shard_members(L, S, I, r)
+                for i in range(int(n[b])):
+                    pos = min(L - int(n[b]) + i + shift, L - 1) if shift is not None else L - 1
+                    seen = int(np.count_nonzero(members <= pos))
+                    p = 0
+                    while p * T < K.shape[0]:
+                        lo, hi = p * T, min((p + 1) * T, seen)
+                        if hi > lo:
+                            po[row + i, r, p], pl[row + i, r, p] = pa.attention(q[row + i], K[lo:hi],
+                                                                                 V[lo:hi], scale)
+                        p += 1
+            row += int(n[b])
+        return po, pl
+    return f
+
+
+def _mq_rows_reversed(q, query_start, *args):
+    qs = np.asarray(query_start)
+    q2 = q.copy()
+    for b in range(len(qs) - 1):
+        q2[qs[b]:qs[b + 1]] = q[qs[b]:qs[b + 1]][::-1]
+    return _mq_partials(q2, query_start, *args)
+
+
+def _mq_slots_first_position(block_table, context_lens, query_start, S, I, bs):
+    out = _mq_slots(block_table, context_lens, query_start, S, I, bs)
+    return out[::-1].copy()
+
+
+MQ_MUTANTS = {
+    "mq.bound_plus1": ("decode_multi_partials", _mq_shifted(1)),
+    "mq.bound_minus1": ("decode_multi_partials", _mq_shifted(-1)),
+    "mq.no_causal": ("decode_multi_partials", _mq_shifted(None)),
+    "mq.rows_reversed": ("decode_multi_partials", _mq_rows_reversed),
+    "mq.slots_reversed": ("slot_mapping_multi", _mq_slots_first_position),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MQ_MUTANTS))
+def test_multi_query_mutant_is_caught(name, monkeypatch):
+    attr, fn = MQ_MUTANTS[name]
+    monkeypatch.setattr(mq, attr, fn)
     failures = []
     for check in oc.ALL_CHECKS.values():
         try:

@@ -54,15 +54,30 @@ class Workload:
     seed: int = 0
     kv_dtype: str = ""                  # "" -> same as dtype; FP8 -> E4M3 codes
     scale_per_head: bool = True         # FP8: one scale per KV head (else one per tensor)
+    q_lens: np.ndarray = None           # int32 [N]: new tokens per sequence (None: one each)
     # filled by plan():
     block_table: np.ndarray = field(default=None, repr=False)
     live: np.ndarray = field(default=None, repr=False)       # bool [NB][bs]: holds a stored token
     token_id: np.ndarray = field(default=None, repr=False)   # int64 [NB][bs]: global id, -1 unused
-    new_slot: np.ndarray = field(default=None, repr=False)   # int64 [N]: slot of the appended token
+    new_slot: np.ndarray = field(default=None, repr=False)   # int64 [rows]: slots of the appended tokens
 
     @property
     def n_seqs(self) -> int:
         return int(len(self.context_lens))
+
+    @property
+    def multi(self) -> bool:
+        return self.q_lens is not None
+
+    @property
+    def query_start(self) -> np.ndarray:
+        """int32 [N+1]: rows query_start[b] .. query_start[b+1]-1 of q are sequence b's."""
+        n = self.q_lens if self.multi else np.ones(self.n_seqs, np.int64)
+        return np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+
+    @property
+    def n_rows(self) -> int:
+        return int(self.query_start[-1])
 
     @property
     def group(self) -> int:
@@ -129,6 +144,10 @@ def plan(w: Workload) -> Workload:
     live = np.zeros((nb, bs), dtype=bool)
     tok = np.full((nb, bs), -1, dtype=np.int64)
     new_slot = np.empty(N, dtype=np.int64)
+    multi_slots: list = []
+    if w.multi:
+        w.q_lens = np.asarray(w.q_lens, dtype=np.int32)
+        assert w.q_lens.shape == (N,)
     prefix_of_group: dict = {}
     for b in range(N):
         L = int(w.context_lens[b])
@@ -150,6 +169,14 @@ def plan(w: Workload) -> Workload:
             phys = bt[b, r, loc // bs].astype(np.int64)
             live[phys, loc % bs] = True
             tok[phys, loc % bs] = mine
+        if w.multi:                     # the last q_lens[b] tokens are new
+            n_new = int(w.q_lens[b])
+            assert 0 <= n_new <= L
+            for pos in range(L - n_new, L):
+                r_new = (pos // I) % S
+                loc_new = int(_split_counts(pos, S, I)[r_new])   # earlier tokens on that shard
+                multi_slots.append(int(bt[b, r_new, loc_new // bs]) * bs + loc_new % bs)
+            continue
         if L == 0:                      # an empty sequence appends nothing
             new_slot[b] = -1
             continue
@@ -157,7 +184,9 @@ def plan(w: Workload) -> Workload:
         loc_new = int(counts[b][r_new]) - 1
         phys_new = int(bt[b, r_new, loc_new // bs])
         new_slot[b] = phys_new * bs + loc_new % bs
-    # the appended token's slot holds nothing until kv_append writes it
+    if w.multi:
+        new_slot = np.array(multi_slots, dtype=np.int64)
+    # the appended tokens' slots hold nothing until kv_append writes them
     for s in new_slot[new_slot >= 0]:
         live[s // bs, s % bs] = False
     w.block_table, w.live, w.token_id, w.new_slot = bt, live, tok, new_slot
@@ -221,13 +250,23 @@ def latent(seed: int = 5, n_seqs: int = 32, lo: int = 4096, hi: int = 65536) -> 
 def small(name: str, lens, hq: int, hkv: int, dk: int, dv: int, bs: int, dtype: str,
           n_shards: int = 1, interleave: int = 1, partition_tokens: int = 0, latent: bool = False,
           seed: int = 0, prefix_group: int = 1, prefix_tokens: int = 0, scale: float = 0.0,
-          kv_dtype: str = "", scale_per_head: bool = True) -> Workload:
-    """Any small shape, for parity sweeps."""
+          kv_dtype: str = "", scale_per_head: bool = True, q_lens=None) -> Workload:
+    """Any small shape, for parity sweeps (``q_lens``: new tokens per sequence)."""
     return plan(Workload(name, hq, hkv, dk, dv, bs, dtype, np.asarray(lens, np.int32),
                          n_shards=n_shards, interleave=interleave,
                          partition_tokens=partition_tokens, latent=latent, seed=seed,
                          prefix_group=prefix_group, prefix_tokens=prefix_tokens, scale=scale,
-                         kv_dtype=kv_dtype, scale_per_head=scale_per_head))
+                         kv_dtype=kv_dtype, scale_per_head=scale_per_head,
+                         q_lens=None if q_lens is None else np.asarray(q_lens, np.int32)))
+
+
+def speculative(seed: int = 2, q_len: int = 4) -> Workload:
+    """Verification of speculative tokens on the long-context batch: the 8 log-normal
+    sequences of ``long`` each bring ``q_len`` new tokens (the last of the context),
+    causal among themselves; 32/8 heads, head 128, bf16, 16-token blocks."""
+    L = long_lengths(seed)
+    return plan(Workload(f"spec{q_len}", 32, 8, 128, 128, 16, BF16, L, seed=seed,
+                         q_lens=np.full(L.size, q_len, np.int32)))
 
 
 def with_fp8_cache(w: Workload, per_head: bool = True) -> Workload:
@@ -270,6 +309,7 @@ def make_tensors(w: Workload, device="cpu", fill: str = "normal", seed: int | No
     g = torch.Generator(device=dev)
     g.manual_seed(int(w.seed if seed is None else seed) * 1000003 + 7)
     N, Hq, Hkv, dk, dv, bs, NB = w.n_seqs, w.n_q_heads, w.n_kv_heads, w.dk, w.dv, w.block_size, w.n_blocks
+    R = w.n_rows                        # query rows (one per new token)
 
     def randn(*shape):
         return torch.randn(*shape, generator=g, device=dev, dtype=torch.float32).to(dt)
@@ -285,9 +325,9 @@ def make_tensors(w: Workload, device="cpu", fill: str = "normal", seed: int | No
 
         k_cache = codes(NB, Hkv, bs, dk)
         v_cache = None if w.latent else codes(NB, Hkv, dv, bs)
-        q = randn(N, Hq, dk)
-        k_new = randn(N, Hkv, dk)
-        v_new = None if w.latent else randn(N, Hkv, dv)
+        q = randn(R, Hq, dk)
+        k_new = randn(R, Hkv, dk)
+        v_new = None if w.latent else randn(R, Hkv, dv)
         n_sc = Hkv if w.scale_per_head else 1
         k_scale = (0.5 + 1.5 * torch.rand(n_sc, generator=g, device=dev)) / 16.0
         v_scale = None if w.latent else (0.5 + 1.5 * torch.rand(n_sc, generator=g, device=dev)) / 16.0
@@ -298,13 +338,16 @@ def make_tensors(w: Workload, device="cpu", fill: str = "normal", seed: int | No
                     k_scale=k_scale, v_scale=v_scale,
                     block_table=torch.from_numpy(w.block_table).to(dev),
                     context_lens=torch.from_numpy(w.context_lens.astype(np.int32)).to(dev),
-                    slot_mapping=torch.from_numpy(w.new_slot).to(dev))
+                    slot_mapping=torch.from_numpy(w.new_slot).to(dev),
+                    query_start=torch.from_numpy(w.query_start).to(dev))
     k_cache = randn(NB, Hkv, bs, dk)
     v_cache = None if w.latent else randn(NB, Hkv, dv, bs)
-    q = randn(N, Hq, dk)
-    k_new = randn(N, Hkv, dk)
-    v_new = None if w.latent else randn(N, Hkv, dv)
+    q = randn(R, Hq, dk)
+    k_new = randn(R, Hkv, dk)
+    v_new = None if w.latent else randn(R, Hkv, dv)
     if fill == "mean_probe":
+        if w.multi:
+            raise ValueError("mean_probe is for one new token per sequence")
         q.zero_()
         tid = torch.from_numpy(w.token_id).to(dev)                    # [NB][bs]
         j = torch.arange(dv, device=dev)
@@ -328,4 +371,5 @@ def make_tensors(w: Workload, device="cpu", fill: str = "normal", seed: int | No
     return dict(q=q, k_new=k_new, v_new=v_new, k_cache=k_cache, v_cache=v_cache,
                 block_table=torch.from_numpy(w.block_table).to(dev),
                 context_lens=torch.from_numpy(w.context_lens.astype(np.int32)).to(dev),
-                slot_mapping=torch.from_numpy(w.new_slot).to(dev))
+                slot_mapping=torch.from_numpy(w.new_slot).to(dev),
+                query_start=torch.from_numpy(w.query_start).to(dev))
