@@ -42,6 +42,9 @@ _SIGS = {
                          _p, _p],
     "pa_decode_fp8": [_p, _p, _p, _p, _p, _i32, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i64, _i32,
                       _i32, _i32, _i32, _i32, _f32, _i32, _p, _p, _p, _p],
+    "pa_slot_mapping_multi": [_p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i64, _p, _p, _p],
+    "pa_decode_multi": [_p, _i32, _p, _i32, _i32, _p, _p, _i32, _p, _p, _i32, _p, _p, _i32, _i32, _i32,
+                        _i32, _i32, _i32, _i64, _i32, _i32, _i32, _i32, _i32, _f32, _p, _p, _p, _p],
     "pa_copy_blocks": [_p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i64, _i32, _p, _p],
     "pa_pool_add": [_p, _i64, _i64],
     "pa_pool_append": [_p, _i64, _i64, _p, _i32, _p],
@@ -272,6 +275,64 @@ def pa_decode_fp8(q, k_cache, v_cache, k_scale, v_scale, block_table, context_le
                              block_table.shape[2], n_shards, interleave, partition_tokens,
                              max_partitions, float(scale), _dtype_code(q), _ptr(part_out),
                              _ptr(part_lse), _ptr(err_flag), _stream(q)))
+
+
+def pa_slot_mapping_multi(block_table, context_lens, query_start, n_shards, interleave, block_size,
+                          n_blocks, slot_mapping, err_flag=None):
+    """Slots of every new token; ``query_start`` int32 [n_seqs+1] on the GPU."""
+    _need(block_table, torch.int32, 3, "block_table")
+    _need(context_lens, torch.int32, 1, "context_lens")
+    _need(query_start, torch.int32, 1, "query_start")
+    _need(slot_mapping, torch.int64, 1, "slot_mapping")
+    _need(err_flag, torch.int32, None, "err_flag")
+    n = context_lens.shape[0]
+    if block_table.shape[0] != n or block_table.shape[1] != n_shards or query_start.shape[0] != n + 1:
+        raise ValueError("block_table / context_lens / query_start shapes disagree")
+    _check(lib.pa_slot_mapping_multi(_ptr(block_table), _ptr(context_lens), _ptr(query_start), n,
+                                     slot_mapping.shape[0], n_shards, interleave, block_size,
+                                     block_table.shape[2], n_blocks, _ptr(slot_mapping),
+                                     _ptr(err_flag), _stream(block_table)))
+
+
+def pa_decode_multi(q, query_start, max_q_len, k_cache, v_cache, block_table, context_lens, n_shards,
+                    interleave, partition_tokens, max_partitions, scale, part_out, part_lse,
+                    k_scale=None, v_scale=None, dv=None, err_flag=None):
+    """Several new tokens per sequence (causal among them): ``q [rows][Hq][dk]``,
+    ``query_start`` int32 [n_seqs+1]; an E4M3 cache (uint8) takes its scales."""
+    _need(q, None, 3, "q")
+    _need(k_cache, None, 4, "k_cache")
+    _need(v_cache, k_cache.dtype, 4, "v_cache")
+    _need(query_start, torch.int32, 1, "query_start")
+    _need(block_table, torch.int32, 3, "block_table")
+    _need(context_lens, torch.int32, 1, "context_lens")
+    _need(part_out, torch.float32, 5, "part_out")
+    _need(part_lse, torch.float32, 4, "part_lse")
+    _need(err_flag, torch.int32, None, "err_flag")
+    rows, hq, dk = q.shape
+    nb, hkv, bs, dk2 = k_cache.shape
+    n = context_lens.shape[0]
+    if dv is None:
+        dv = v_cache.shape[2] if v_cache is not None else dk
+    if dk2 != dk:
+        raise ValueError("q and k_cache head sizes differ")
+    if v_cache is not None and tuple(v_cache.shape) != (nb, hkv, dv, bs):
+        raise ValueError("v_cache must be [n_blocks][n_kv_heads][dv][block_size]")
+    if tuple(part_out.shape) != (rows, n_shards, max_partitions, hq, dv):
+        raise ValueError(f"part_out must be {(rows, n_shards, max_partitions, hq, dv)}")
+    if tuple(part_lse.shape) != (rows, n_shards, max_partitions, hq):
+        raise ValueError(f"part_lse must be {(rows, n_shards, max_partitions, hq)}")
+    if block_table.shape[0] != n or block_table.shape[1] != n_shards or query_start.shape[0] != n + 1:
+        raise ValueError("block_table / context_lens / query_start shapes disagree")
+    kv_code = _dtype_code(k_cache, cache=True)
+    ns = 0
+    if kv_code == PA_FP8_E4M3:
+        ns = _scales(k_scale, v_scale, hkv, v_cache is None)
+    _check(lib.pa_decode_multi(_ptr(q), _dtype_code(q), _ptr(query_start), rows, int(max_q_len),
+                               _ptr(k_cache), _ptr(v_cache), kv_code, _ptr(k_scale), _ptr(v_scale),
+                               ns, _ptr(block_table), _ptr(context_lens), n, hq, hkv, dk, dv, bs, nb,
+                               block_table.shape[2], n_shards, interleave, partition_tokens,
+                               max_partitions, float(scale), _ptr(part_out), _ptr(part_lse),
+                               _ptr(err_flag), _stream(q)))
 
 
 def pa_merge_lse(part_out, part_lse, out, lse=None):

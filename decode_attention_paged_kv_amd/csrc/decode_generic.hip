@@ -1,7 +1,8 @@
 // decode_generic.hip -- paged decode attention for any supported shape (VALU, fp32 math).
 //
 // One workgroup computes one (partition, sequence x shard, KV head, chunk of up to 16
-// query heads of that KV head's group).  It walks the partition's local tokens in tiles
+// columns): a column is a query head of that KV head's group, or, with several new
+// tokens per sequence, a (new token, query head) pair with its own causal end.  It walks the partition's local tokens in tiles
 // of 32: scores of the tile (scale * q.k), an online-softmax update of the running max m,
 // sum l and output accumulator, then the weighted values.  At the end it writes
 // o = acc / l and lse = m + ln l for the partition (DCP page, soroban.highreso.jp,
@@ -40,24 +41,41 @@ __global__ __launch_bounds__(kThreads) void decode_generic_kernel(DecodeArgs a) 
   const int b = blockIdx.y / a.n_shards;
   const int r = blockIdx.y % a.n_shards;
   const int g = a.hq / a.hkv;
-  const int chunks = (g + kHeads - 1) / kHeads;
+  // columns: (new token, query head of this KV head) pairs, token major; kHeads of them
+  // per workgroup (one new token per sequence: the heads)
+  const int row0 = a.query_start ? a.query_start[b] : b;
+  const int nq = a.query_start ? a.query_start[b + 1] - row0 : 1;
+  const int chunks = (a.max_q * g + kHeads - 1) / kHeads;
   const int kvh = blockIdx.z / chunks;
-  const int chunk = blockIdx.z % chunks;
-  const int h0 = kvh * g + chunk * kHeads;
-  const int nh = min(kHeads, g - chunk * kHeads);
+  const int c0 = (blockIdx.z % chunks) * kHeads;
+  const int nh = min(kHeads, nq * g - c0);       // valid columns here
   const int tid = threadIdx.x;
   const int dk = a.dk, dv = a.dv, bs = a.bs;
 
   const int L = a.context_lens[b];
   const int Lr = L > 0 ? shard_len(L, a.n_shards, a.interleave, r) : 0;
   const int T = a.part_tokens;
-  if (p == 0 && tid == 0 && (Lr + T - 1) / T > a.max_parts) raise_flag(a.flag, kErrCapacity);
+  // several new tokens: more than the context holds, or rows outside the arrays, is an
+  // error (flagged, rows left unwritten); one per sequence: an empty context is allowed
+  const bool bad = a.query_start && (nq > L || nq > a.max_q || row0 < 0 || row0 + nq > a.n_rows);
+  if (p == 0 && tid == 0 && blockIdx.z == 0 && ((Lr + T - 1) / T > a.max_parts || bad))
+    raise_flag(a.flag, kErrCapacity);
+  if (nh <= 0 || bad) return;
   const int t_begin = p * T;
-  const int t_end = min(t_begin + T, Lr);
-
-  const int64_t out_row = ((int64_t(b) * a.n_shards + r) * a.max_parts + p) * a.hq;
+  auto col_row = [&](int hh) -> int64_t {   // q row * hq + head of column hh
+    const int qi = (c0 + hh) / g;
+    return int64_t(row0 + qi) * a.hq + kvh * g + (c0 + hh - qi * g);
+  };
+  auto out_row = [&](int hh) -> int64_t {
+    const int qi = (c0 + hh) / g;
+    return ((int64_t(row0 + qi) * a.n_shards + r) * a.max_parts + p) * a.hq + kvh * g + (c0 + hh - qi * g);
+  };
+  auto visible = [&](int hh) -> int {
+    return visible_on_shard(L - nq + (c0 + hh) / g, a.n_shards, a.interleave, r);
+  };
+  const int t_end = min(min(t_begin + T, Lr), visible(nh - 1));
   if (t_begin >= t_end) {  // empty partition: lse = -inf, output rows left unwritten
-    if (tid < nh) a.part_lse[out_row + h0 + tid] = -INFINITY;
+    if (tid < nh) a.part_lse[out_row(tid)] = -INFINITY;
     return;
   }
 
@@ -66,6 +84,8 @@ __global__ __launch_bounds__(kThreads) void decode_generic_kernel(DecodeArgs a) 
   __shared__ float m_s[kHeads], l_s[kHeads], alpha_s[kHeads];
   __shared__ int64_t kbase_s[kTile], vbase_s[kTile];
   __shared__ int ok_s[kTile];
+  __shared__ int lim_s[kHeads];
+  if (tid < kHeads) lim_s[tid] = tid < nh ? min(t_end, visible(tid)) : 0;
 
   float score_mul = a.scale, out_mul = 1.f;
   if (KT == kFP8) {
@@ -73,8 +93,7 @@ __global__ __launch_bounds__(kThreads) void decode_generic_kernel(DecodeArgs a) 
     score_mul = a.scale * a.k_scale[si];
     out_mul = vc ? a.v_scale[si] : a.k_scale[si];
   }
-  for (int i = tid; i < nh * dk; i += kThreads)
-    q_s[i] = EQ::load(q, (int64_t(b) * a.hq + h0 + i / dk) * dk + i % dk);
+  for (int i = tid; i < nh * dk; i += kThreads) q_s[i] = EQ::load(q, col_row(i / dk) * dk + i % dk);
   if (tid < kHeads) {
     m_s[tid] = -INFINITY;
     l_s[tid] = 0.f;
@@ -108,7 +127,7 @@ __global__ __launch_bounds__(kThreads) void decode_generic_kernel(DecodeArgs a) 
     for (int idx = tid; idx < kHeads * kTile; idx += kThreads) {
       const int hh = idx / kTile, tt = idx % kTile;
       float s = -INFINITY;
-      if (hh < nh && tt < n_t && ok_s[tt]) {
+      if (hh < nh && tt < n_t && ok_s[tt] && t0 + tt < lim_s[hh]) {
         const int64_t kb = kbase_s[tt];
         float dot = 0.f;
         for (int d = 0; d < dk; ++d) dot = fmaf(q_s[hh * dk + d], E::load(kc, kb + d), dot);
@@ -154,12 +173,17 @@ __global__ __launch_bounds__(kThreads) void decode_generic_kernel(DecodeArgs a) 
   for (int k = 0; k < kAcc; ++k) {
     const int idx = tid + k * kThreads;
     const int hh = idx / dv, d = idx % dv;
-    if (hh < nh) a.part_out[(out_row + h0 + hh) * dv + d] = acc[k] / l_s[hh] * out_mul;
+    if (hh < nh) a.part_out[out_row(hh) * dv + d] = l_s[hh] > 0.f ? acc[k] / l_s[hh] * out_mul : 0.f;
   }
-  if (tid < nh) a.part_lse[out_row + h0 + tid] = m_s[tid] + logf(l_s[tid]);
+  // a column may see none of this partition's tokens: lse -inf
+  if (tid < nh) a.part_lse[out_row(tid)] = l_s[tid] > 0.f ? m_s[tid] + logf(l_s[tid]) : -INFINITY;
 }
 
 }  // namespace
+
+int generic_column_chunks(const DecodeArgs& a) {
+  return (a.max_q * (a.hq / a.hkv) + kHeads - 1) / kHeads;
+}
 
 static const void* generic_kernel(int dtype, int kv_dtype) {
   if (kv_dtype == kFP8)
@@ -180,9 +204,7 @@ int generic_workgroups_per_cu(int dtype, int kv_dtype) {
 }
 
 hipError_t launch_decode_generic(const DecodeArgs& a, hipStream_t st) {
-  const int g = a.hq / a.hkv;
-  const int chunks = (g + kHeads - 1) / kHeads;
-  const dim3 grid(a.max_parts, a.n_seqs * a.n_shards, a.hkv * chunks);
+  const dim3 grid(a.max_parts, a.n_seqs * a.n_shards, a.hkv * generic_column_chunks(a));
   if (a.kv_dtype == kFP8) {
     if (a.dtype == kF32)
       hipLaunchKernelGGL((decode_generic_kernel<kF32, kFP8>), grid, dim3(kThreads), 0, st, a);

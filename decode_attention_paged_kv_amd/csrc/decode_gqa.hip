@@ -9,8 +9,10 @@
 // soroban.highreso.jp, DCP mechanism section).
 //
 // How it maps onto gfx950:
-//  * One workgroup = one (partition, sequence x shard, KV head, group of <= 16 query
-//    heads); its NW waves split the partition's 16-token sub-tiles into contiguous
+//  * One workgroup = one (partition, sequence x shard, KV head, 16 columns); a column
+//    is a query head of the KV head's group, or, with several new tokens per sequence,
+//    a (new token, query head) pair -- then each column also has its own causal end
+//    (the new token sees the tokens up to its own position).  Its NW waves split the partition's 16-token sub-tiles into contiguous
 //    ranges and merge their (max, sum, output) through LDS at the end.  Each K/V byte
 //    is read by exactly one wave, so K/V go straight from HBM into registers (no LDS
 //    staging: there is no reuse to stage for).
@@ -145,39 +147,58 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeArgs a) {
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int col = lane & 15;   // key row (A operand) / head (B operand, results)
+  const int col = lane & 15;   // key row (A operand) / column (B operand, results)
   const int grp = lane >> 4;   // k-slot group
   const int p = blockIdx.x;
   const int b = blockIdx.y / a.n_shards;
   const int r = blockIdx.y % a.n_shards;
   const int g = a.hq / a.hkv;
-  const int chunks = (g + 15) >> 4;
+  // Columns of the products are (new token, query head of this KV head) pairs, token
+  // major; a workgroup takes 16 of them.  One new token per sequence: the heads.
+  const int row0 = a.query_start ? a.query_start[b] : b;         // q row of its first new token
+  const int nq = a.query_start ? a.query_start[b + 1] - row0 : 1;
+  const int chunks = (a.max_q * g + 15) >> 4;
   const int kvh = blockIdx.z / chunks;
-  const int chunk = blockIdx.z % chunks;
-  const int h0 = kvh * g + chunk * 16;
-  const int nh = min(16, g - chunk * 16);
+  const int c0 = (blockIdx.z % chunks) * 16;
+  const int ncol = min(16, nq * g - c0);         // valid columns here
   const int bs = a.bs;
 
   const int L = a.context_lens[b];
   const int Lr = L > 0 ? shard_len(L, a.n_shards, a.interleave, r) : 0;
   const int T = a.part_tokens;
-  if (p == 0 && threadIdx.x == 0 && (Lr + T - 1) / T > a.max_parts) raise_flag(a.flag, kErrCapacity);
+  // several new tokens: more than the context holds, or rows outside the arrays, is an
+  // error (flagged, rows left unwritten); one per sequence: an empty context is allowed
+  const bool bad = a.query_start && (nq > L || nq > a.max_q || row0 < 0 || row0 + nq > a.n_rows);
+  if (p == 0 && threadIdx.x == 0 && blockIdx.z == 0 && ((Lr + T - 1) / T > a.max_parts || bad))
+    raise_flag(a.flag, kErrCapacity);
+  if (ncol <= 0 || bad) return;  // no rows here (or bad input)
   const int t_begin = p * T;
-  const int t_end = min(t_begin + T, Lr);
-  const int64_t out_row = ((int64_t(b) * a.n_shards + r) * a.max_parts + p) * a.hq + h0;
+  // output row of column cc (< ncol), and how many of the shard's tokens it may see
+  auto out_row = [&](int cc) -> int64_t {
+    const int qi = (c0 + cc) / g, h = (c0 + cc) - qi * g;
+    return ((int64_t(row0 + qi) * a.n_shards + r) * a.max_parts + p) * a.hq + kvh * g + h;
+  };
+  auto visible = [&](int cc) -> int {
+    return visible_on_shard(L - nq + (c0 + cc) / g, a.n_shards, a.interleave, r);
+  };
+  // the last column sees the most: the workgroup's tokens end there
+  const int t_end = min(min(t_begin + T, Lr), visible(ncol - 1));
   if (t_begin >= t_end) {  // empty partition: lse = -inf, output rows left unwritten
-    if (threadIdx.x < nh) a.part_lse[out_row + threadIdx.x] = -INFINITY;
+    if (threadIdx.x < ncol) a.part_lse[out_row(threadIdx.x)] = -INFINITY;
     return;
   }
+  const int lim = min(t_end, visible(min(col, ncol - 1)));   // this lane's column's end
 
-  // query operand: lane (head col, group grp) holds q[h0+col][32j + 8grp .. +7] (bf16
-  // cache) or q[h0+col][grp*D/4 + 8j .. +7] (E4M3 cache), the order of the key operand
+  // query operand: lane (column col, group grp) holds q[row][head][32j + 8grp .. +7]
+  // (bf16 cache) or [grp*D/4 + 8j .. +7] (E4M3 cache), the order of the key operand
   bf16x8_t qop[KJ];
   {
-    const uint16_t* qrow = q + (int64_t(b) * a.hq + h0 + col) * D + (F8 ? grp * (D / 4) : 8 * grp);
+    const int qi = (c0 + col) / g, h = (c0 + col) - qi * g;
+    const uint16_t* qrow = q + (int64_t(row0 + qi) * a.hq + kvh * g + h) * D +
+                           (F8 ? grp * (D / 4) : 8 * grp);
 #pragma unroll
     for (int j = 0; j < KJ; ++j) {
-      if (col < nh)
+      if (col < ncol)
         qop[j] = *reinterpret_cast<const bf16x8_t*>(qrow + (F8 ? 8 * j : 32 * j));
       else
         qop[j] = bf16x8_t{};
@@ -288,7 +309,7 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int tok = st.tok0[t] + 4 * grp + i;
-        const bool ok = st.tok0[t] >= 0 && tok < t_end;
+        const bool ok = st.tok0[t] >= 0 && tok < lim;
         sc[t][i] = ok ? acc[i] : -INFINITY;
       }
     }
@@ -301,7 +322,7 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeArgs a) {
     mt = xor_max(mt);
     const float alpha = (mt == -INFINITY) ? 1.f : exp2f((m - mt) * c);
     m = mt;
-    const float mc = mt * c;
+    const float mc = (mt == -INFINITY) ? 0.f : mt * c;   // a column that has seen nothing yet
     float pv[SUBS][4];
     float psum = 0.f;
 #pragma unroll
@@ -389,7 +410,7 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) o_s[wave][16 * n + 4 * grp + i][col] = o[n][i];
   __syncthreads();
-  for (int idx = threadIdx.x; idx < nh * D; idx += 64 * NW) {
+  for (int idx = threadIdx.x; idx < ncol * D; idx += 64 * NW) {
     const int hh = idx / D, d = idx % D;
     float M = -INFINITY;
 #pragma unroll
@@ -402,8 +423,10 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeArgs a) {
       Ls = fmaf(f, l_s[w2][hh], Ls);
       acc = fmaf(f, o_s[w2][d][hh], acc);
     }
-    a.part_out[(out_row + hh) * D + d] = acc / Ls * value_scale;
-    if (d == 0) a.part_lse[out_row + hh] = (M * c + log2f(Ls)) * kLn2;
+    const int64_t orow = out_row(hh);
+    const bool seen = Ls > 0.f;       // a column may see none of this partition's tokens
+    a.part_out[orow * D + d] = seen ? acc / Ls * value_scale : 0.f;
+    if (d == 0) a.part_lse[orow] = seen ? (M * c + log2f(Ls)) * kLn2 : -INFINITY;
   }
 }
 
@@ -413,6 +436,8 @@ bool gqa_supported(const DecodeArgs& a) {
   return a.dtype == kBF16 && (a.kv_dtype == kBF16 || a.kv_dtype == kFP8) && a.v_cache != nullptr &&
          a.dk == a.dv && (a.dk == 64 || a.dk == 128) && a.bs % 16 == 0;
 }
+
+int gqa_column_chunks(const DecodeArgs& a) { return (a.max_q * (a.hq / a.hkv) + 15) / 16; }
 
 #ifndef PA_GQA_WAVES
 #define PA_GQA_WAVES 8
@@ -454,9 +479,7 @@ int gqa_workgroups_per_cu(int dk, int kv_dtype) {
 }
 
 hipError_t launch_decode_gqa(const DecodeArgs& a, hipStream_t st) {
-  const int g = a.hq / a.hkv;
-  const int chunks = (g + 15) / 16;
-  const dim3 grid(a.max_parts, a.n_seqs * a.n_shards, a.hkv * chunks);
+  const dim3 grid(a.max_parts, a.n_seqs * a.n_shards, a.hkv * gqa_column_chunks(a));
   void* args[] = {const_cast<DecodeArgs*>(&a)};
   return hipLaunchKernel(gqa_kernel_for(a.dk, a.kv_dtype), grid, dim3(64 * waves_of(a.kv_dtype)),
                          args, 0, st);

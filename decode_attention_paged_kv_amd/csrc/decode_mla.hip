@@ -724,7 +724,8 @@ void decode_mla_kernel(DecodeArgs a) {
 }  // namespace
 
 bool mla_supported(const DecodeArgs& a) {
-  return a.dtype == kBF16 && a.kv_dtype == kBF16 && a.v_cache == nullptr && a.dk == DK && a.dv == DV &&
+  return a.dtype == kBF16 && a.kv_dtype == kBF16 && a.query_start == nullptr && a.v_cache == nullptr &&
+         a.dk == DK && a.dv == DV &&
          a.hq == HEADS * a.hkv && a.bs % TT == 0;
 }
 

@@ -10,10 +10,9 @@ hipError_t dispatch_decode(const DecodeArgs& a, hipStream_t st) {
 }
 
 KernelChoice choose_kernel(const DecodeArgs& a) {
-  const int g = a.hq / a.hkv;
-  if (gqa_supported(a)) return {a.hkv * ((g + 15) / 16), gqa_workgroups_per_cu(a.dk, a.kv_dtype), false};
+  if (gqa_supported(a)) return {a.hkv * gqa_column_chunks(a), gqa_workgroups_per_cu(a.dk, a.kv_dtype), false};
   if (mla_supported(a)) return {a.hkv, mla_workgroups_per_cu(), true};
-  return {a.hkv * ((g + 15) / 16), generic_workgroups_per_cu(a.dtype, a.kv_dtype), false};
+  return {a.hkv * generic_column_chunks(a), generic_workgroups_per_cu(a.dtype, a.kv_dtype), false};
 }
 
 }  // namespace pa

@@ -38,6 +38,40 @@ __global__ void slot_mapping_kernel(const int32_t* __restrict__ bt, const int32_
   slots[b] = slot;
 }
 
+// Slots of several new tokens per sequence: new token i of the last n sits at global
+// position L - n + i and is placed like any token (rows of the packed query order).
+// More new tokens than context tokens: the slots are -1 and the flag is raised; rows
+// outside [0, n_rows) are never written (flag raised).
+__global__ void slot_mapping_multi_kernel(const int32_t* __restrict__ bt,
+                                          const int32_t* __restrict__ lens,
+                                          const int32_t* __restrict__ qstart, int n_seqs, int S,
+                                          int I, int bs, int max_blocks, int64_t n_blocks,
+                                          int n_rows, int64_t* __restrict__ slots, int* flag) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= n_seqs) return;
+  const int L = lens[b];
+  const int row0 = qstart[b];
+  const int n = qstart[b + 1] - row0;
+  if (row0 < 0 || n < 0 || row0 + n > n_rows) {
+    raise_flag(flag, kErrCapacity);
+    return;
+  }
+  const bool bad = n > L;
+  if (bad) raise_flag(flag, kErrCapacity);
+  for (int i = 0; i < n; ++i) {
+    int64_t slot = -1;
+    if (!bad) {
+      const int pos = L - n + i;
+      const int r = shard_of(pos, S, I);
+      const int t = local_index(pos, S, I);
+      const int32_t* row = bt + (int64_t(b) * S + r) * max_blocks;
+      const int64_t phys = table_block(row, t / bs, max_blocks, n_blocks, flag);
+      if (phys >= 0) slot = phys * bs + t % bs;
+    }
+    slots[row0 + i] = slot;
+  }
+}
+
 template <typename RAW>
 __global__ void kv_append_kernel(const RAW* __restrict__ k_new, const RAW* __restrict__ v_new,
                                  RAW* __restrict__ k_cache, RAW* __restrict__ v_cache,
@@ -200,6 +234,17 @@ hipError_t launch_slot_mapping(const int32_t* bt, const int32_t* lens, int n_seq
   const int blocks = (n_seqs + threads - 1) / threads;
   hipLaunchKernelGGL(slot_mapping_kernel, dim3(blocks), dim3(threads), 0, st, bt, lens, n_seqs, S,
                      I, bs, max_blocks, n_blocks, slots, flag);
+  return hipGetLastError();
+}
+
+hipError_t launch_slot_mapping_multi(const int32_t* bt, const int32_t* lens, const int32_t* qstart,
+                                     int n_seqs, int S, int I, int bs, int max_blocks,
+                                     int64_t n_blocks, int n_rows, int64_t* slots, int* flag,
+                                     hipStream_t st) {
+  const int threads = 256;
+  const int blocks = (n_seqs + threads - 1) / threads;
+  hipLaunchKernelGGL(slot_mapping_multi_kernel, dim3(blocks), dim3(threads), 0, st, bt, lens, qstart,
+                     n_seqs, S, I, bs, max_blocks, n_blocks, n_rows, slots, flag);
   return hipGetLastError();
 }
 

@@ -346,6 +346,9 @@ int check_decode(const char* fn, const void* q, const void* k_cache, const void*
   a.kv_dtype = dtype;
   a.k_scale = a.v_scale = nullptr;
   a.n_scales = 0;
+  a.query_start = nullptr;
+  a.max_q = 1;
+  a.n_rows = n_seqs;
   *out = a;
   return PA_OK;
 }
@@ -394,6 +397,70 @@ int pa_decode_fp8(const void* q, const uint8_t* k_cache, const uint8_t* v_cache,
   a.v_scale = v_scale;
   a.n_scales = n_scales;
   return hip_status(pa::dispatch_decode(a, (hipStream_t)stream), "pa_decode_fp8 launch");
+}
+
+int pa_slot_mapping_multi(const int32_t* block_table, const int32_t* context_lens,
+                          const int32_t* query_start, int32_t n_seqs, int32_t n_rows,
+                          int32_t n_shards, int32_t interleave, int32_t block_size,
+                          int32_t max_blocks_per_shard, int64_t n_blocks, int64_t* slot_mapping,
+                          int32_t* err_flag, void* stream) {
+  REQUIRE(block_table && context_lens && query_start && slot_mapping, PA_ERR_NULL,
+          "pa_slot_mapping_multi: block_table, context_lens, query_start and slot_mapping must "
+          "be non-NULL");
+  REQUIRE(n_seqs >= 0 && n_rows >= 0, PA_ERR_SHAPE, "n_seqs=%d and n_rows=%d must be >= 0", n_seqs,
+          n_rows);
+  if (int rc = check_placement(n_shards, interleave, block_size)) return rc;
+  REQUIRE(max_blocks_per_shard >= 1 && n_blocks >= 1, PA_ERR_SHAPE,
+          "max_blocks_per_shard=%d and n_blocks=%lld must be >= 1", max_blocks_per_shard,
+          (long long)n_blocks);
+  if (n_seqs == 0) return ok();
+  return hip_status(pa::launch_slot_mapping_multi(block_table, context_lens, query_start, n_seqs,
+                                                  n_shards, interleave, block_size,
+                                                  max_blocks_per_shard, n_blocks, n_rows,
+                                                  slot_mapping, err_flag, (hipStream_t)stream),
+                    "pa_slot_mapping_multi launch");
+}
+
+int pa_decode_multi(const void* q, int32_t q_dtype, const int32_t* query_start, int32_t n_rows,
+                    int32_t max_q_len, const void* k_cache, const void* v_cache, int32_t kv_dtype,
+                    const float* k_scale, const float* v_scale, int32_t n_scales,
+                    const int32_t* block_table, const int32_t* context_lens, int32_t n_seqs,
+                    int32_t n_q_heads, int32_t n_kv_heads, int32_t dk, int32_t dv,
+                    int32_t block_size, int64_t n_blocks, int32_t max_blocks_per_shard,
+                    int32_t n_shards, int32_t interleave, int32_t partition_tokens,
+                    int32_t max_partitions, float scale, float* part_out, float* part_lse,
+                    int32_t* err_flag, void* stream) {
+  pa::DecodeArgs a;
+  if (int rc = check_decode("pa_decode_multi", q, k_cache, v_cache, block_table, context_lens,
+                            n_seqs, n_q_heads, n_kv_heads, dk, dv, block_size, n_blocks,
+                            max_blocks_per_shard, n_shards, interleave, partition_tokens,
+                            max_partitions, scale, q_dtype, part_out, part_lse, err_flag, &a))
+    return rc;
+  REQUIRE(query_start != nullptr, PA_ERR_NULL, "pa_decode_multi: query_start must be non-NULL");
+  REQUIRE(n_rows >= 0 && max_q_len >= 1, PA_ERR_SHAPE, "n_rows=%d must be >= 0 and max_q_len=%d >= 1",
+          n_rows, max_q_len);
+  REQUIRE(kv_dtype == q_dtype || kv_dtype == PA_FP8_E4M3, PA_ERR_UNSUPPORTED,
+          "kv_dtype=%d must equal q_dtype=%d or be PA_FP8_E4M3", kv_dtype, q_dtype);
+  if (kv_dtype == PA_FP8_E4M3) {
+    REQUIRE(k_scale && (v_cache == nullptr || v_scale), PA_ERR_NULL,
+            "pa_decode_multi: an E4M3 cache needs k_scale (and v_scale with a value cache)");
+    REQUIRE(n_scales == 1 || n_scales == n_kv_heads, PA_ERR_SHAPE,
+            "n_scales=%d must be 1 or n_kv_heads=%d", n_scales, n_kv_heads);
+  }
+  const int64_t g = n_q_heads / n_kv_heads;
+  REQUIRE(int64_t(n_kv_heads) * ((int64_t(max_q_len) * g + 15) / 16) <= 65535, PA_ERR_SHAPE,
+          "n_kv_heads * ceil(max_q_len * n_q_heads / n_kv_heads / 16) exceeds 65535");
+  if (n_seqs == 0 || n_rows == 0) return ok();
+  a.query_start = query_start;
+  a.max_q = max_q_len;
+  a.n_rows = n_rows;
+  if (kv_dtype == PA_FP8_E4M3) {
+    a.kv_dtype = PA_FP8_E4M3;
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
+    a.n_scales = n_scales;
+  }
+  return hip_status(pa::dispatch_decode(a, (hipStream_t)stream), "pa_decode_multi launch");
 }
 
 int pa_merge_lse(const float* part_out, const float* part_lse, int32_t n_seqs, int32_t n_parts,

@@ -37,6 +37,13 @@ __host__ __device__ inline int local_index(int i, int S, int I) {
   return (i / (I * S)) * I + i % I;
 }
 
+// Several new tokens per sequence: the one at global position `pos` attends over
+// positions 0..pos (causal among the new tokens), which on shard r are the first
+// shard_len(pos + 1) local tokens (a shard keeps global order).
+__host__ __device__ inline int visible_on_shard(int pos, int S, int I, int r) {
+  return pos >= 0 ? shard_len(pos + 1, S, I, r) : 0;
+}
+
 // ---------------------------------------------------------------- error flag
 // Device-detected data errors.  Stored with an ordinary vector atomic.
 enum : int { kErrBlockId = 1, kErrCapacity = 2, kErrSlot = 4 };

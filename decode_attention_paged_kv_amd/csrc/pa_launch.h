@@ -25,11 +25,20 @@ struct DecodeArgs {
   const float* k_scale;    // kFP8: value = code * scale, per KV head (n_scales ==
   const float* v_scale;    //   hkv) or per tensor (n_scales == 1); NULL otherwise
   int n_scales;
+  // several new tokens per sequence: q rows query_start[b] .. query_start[b+1]-1 are
+  // sequence b's last tokens, each attending causally; NULL: one row per sequence.
+  const int32_t* query_start;
+  int max_q;               // grid bound on new tokens per sequence (1 when query_start NULL)
+  int n_rows;              // q rows (n_seqs when query_start NULL)
 };
 
 hipError_t launch_slot_mapping(const int32_t* bt, const int32_t* lens, int n_seqs, int S, int I,
                                int bs, int max_blocks, int64_t n_blocks, int64_t* slots, int* flag,
                                hipStream_t st);
+hipError_t launch_slot_mapping_multi(const int32_t* bt, const int32_t* lens, const int32_t* qstart,
+                                     int n_seqs, int S, int I, int bs, int max_blocks,
+                                     int64_t n_blocks, int n_rows, int64_t* slots, int* flag,
+                                     hipStream_t st);
 hipError_t launch_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                             const int64_t* slots, int n_tokens, int hkv, int dk, int dv, int bs,
                             int64_t n_blocks, int dtype, int* flag, hipStream_t st);
@@ -47,6 +56,8 @@ hipError_t launch_gather(const void* k_cache, const void* v_cache, const int32_t
                          hipStream_t st);
 hipError_t launch_decode_generic(const DecodeArgs& a, hipStream_t st);
 bool gqa_supported(const DecodeArgs& a);
+int gqa_column_chunks(const DecodeArgs& a);     // workgroups per (partition, pair, KV head)
+int generic_column_chunks(const DecodeArgs& a);
 hipError_t launch_decode_gqa(const DecodeArgs& a, hipStream_t st);
 bool mla_supported(const DecodeArgs& a);
 hipError_t launch_decode_mla(const DecodeArgs& a, hipStream_t st);

@@ -75,3 +75,70 @@ class DecodeStep:
         self.attend(q, k_cache, v_cache, block_table, context_lens, k_scale, v_scale)
         self.merge()
         return self.out, self.lse
+
+
+class MultiDecodeStep:
+    """One step with several new tokens per sequence, each attending causally (the
+    ``_multi`` entry points): routes and appends every new token's K/V, attends, and
+    merges per row.  Sized for ``n_rows`` new tokens in total and at most
+    ``max_q_len`` per sequence."""
+
+    def __init__(self, n_seqs, n_rows, max_q_len, n_q_heads, n_kv_heads, dk, dv, block_size,
+                 max_context_len, n_shards=1, interleave=1, partition_tokens=0, scale=None,
+                 device="cuda", out_dtype=torch.float32, context_lens_host=None,
+                 kv_dtype=torch.bfloat16, latent=False):
+        self.n_seqs, self.n_rows, self.max_q = n_seqs, n_rows, max_q_len
+        self.hq, self.hkv, self.dk, self.dv = n_q_heads, n_kv_heads, dk, dv
+        self.block_size, self.n_shards, self.interleave = block_size, n_shards, interleave
+        if not partition_tokens and context_lens_host is not None:
+            # the kernels treat (new token, head) pairs as columns: as many heads per KV head
+            partition_tokens = L.pa_choose_partition_tokens(context_lens_host, n_q_heads * max_q_len,
+                                                            n_kv_heads, dk, dv, block_size, kv_dtype,
+                                                            latent, n_shards, interleave)
+        if not partition_tokens:
+            partition_tokens = L.pa_default_partition_tokens(n_seqs, n_kv_heads, max_context_len,
+                                                             n_shards, interleave, block_size)
+        self.partition_tokens = partition_tokens
+        self.max_partitions = max(1, L.pa_max_partitions(max_context_len, n_shards, interleave,
+                                                         partition_tokens))
+        self.scale = float(torch.tensor(scale if scale is not None else dk ** -0.5,
+                                        dtype=torch.float32))
+        dev = torch.device(device)
+        P = self.max_partitions
+        self.slot_mapping = torch.empty(n_rows, dtype=torch.int64, device=dev)
+        self.part_out = torch.empty(n_rows, n_shards, P, n_q_heads, dv, dtype=torch.float32, device=dev)
+        self.part_lse = torch.empty(n_rows, n_shards, P, n_q_heads, dtype=torch.float32, device=dev)
+        self.out = torch.empty(n_rows, n_q_heads, dv, dtype=out_dtype, device=dev)
+        self.lse = torch.empty(n_rows, n_q_heads, dtype=torch.float32, device=dev)
+        self.err_flag = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def route(self, block_table, context_lens, query_start, n_blocks):
+        L.pa_slot_mapping_multi(block_table, context_lens, query_start, self.n_shards,
+                                self.interleave, self.block_size, n_blocks, self.slot_mapping,
+                                self.err_flag)
+
+    def append(self, k_new, v_new, k_cache, v_cache, k_scale=None, v_scale=None):
+        if k_cache.dtype == torch.uint8:
+            L.pa_kv_append_fp8(k_new, v_new, k_cache, v_cache, k_scale, v_scale, self.slot_mapping,
+                               self.err_flag)
+        else:
+            L.pa_kv_append(k_new, v_new, k_cache, v_cache, self.slot_mapping, self.err_flag)
+
+    def attend(self, q, query_start, k_cache, v_cache, block_table, context_lens, k_scale=None,
+               v_scale=None):
+        L.pa_decode_multi(q, query_start, self.max_q, k_cache, v_cache, block_table, context_lens,
+                          self.n_shards, self.interleave, self.partition_tokens,
+                          self.max_partitions, self.scale, self.part_out, self.part_lse,
+                          k_scale=k_scale, v_scale=v_scale, dv=self.dv, err_flag=self.err_flag)
+
+    def merge(self):
+        L.pa_merge_lse(self.part_out, self.part_lse, self.out, self.lse)
+
+    def __call__(self, q, query_start, k_new, v_new, k_cache, v_cache, block_table, context_lens,
+                 k_scale=None, v_scale=None):
+        """The whole step; returns ``(out, lse)`` per row (views of this object's buffers)."""
+        self.route(block_table, context_lens, query_start, k_cache.shape[0])
+        self.append(k_new, v_new, k_cache, v_cache, k_scale, v_scale)
+        self.attend(q, query_start, k_cache, v_cache, block_table, context_lens, k_scale, v_scale)
+        self.merge()
+        return self.out, self.lse

@@ -17,6 +17,10 @@
  *        own tokens and returns an output plus its softmax LSE; the partial outputs
  *        are reweighted with the LSEs and summed (DCP mechanism section); the decode
  *        backend must return the LSE (DCP configuration section).
+ *  [AGX] agentlenshq.com/ja/blogs/5a6c5ce5-d812-4d7e-b52c-cb4a97581aac, "vLLM AgentX
+ *        release": long prompts split by a per-step token threshold (execution-plane
+ *        section) and a speculative-verification kernel path (open-source kernel
+ *        contributions section), both steps with several new tokens per sequence.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -182,6 +186,55 @@ int pa_decode_fp8(const void* q, const uint8_t* k_cache, const uint8_t* v_cache,
                   int32_t n_shards, int32_t interleave, int32_t partition_tokens,
                   int32_t max_partitions, float scale, int32_t q_dtype, float* part_out,
                   float* part_lse, int32_t* err_flag, void* stream);
+
+/*
+ * Several new tokens per sequence (multi-query decode).  A step may carry more than
+ * one new token of a sequence -- a prompt continued in chunks ([KVB], failure-mode
+ * paragraph on chunked prefill; [AGX], execution-plane section) or speculative tokens
+ * to verify ([AGX], open-source kernel contributions section) -- and each follows the
+ * decode rule of [KVB] ("Why does writing one token at a time duplicate work?"): it
+ * attends over every earlier token and itself.  The n_b new tokens of sequence b are
+ * the last n_b of its context (context_lens[b] counts them): new token i sits at
+ * global position L - n_b + i and attends over positions 0 .. L - n_b + i (causal
+ * among the new tokens).
+ *   query_start  DEVICE int32 [n_seqs + 1], non-decreasing, query_start[0] = 0,
+ *                query_start[n_seqs] = n_rows: rows query_start[b] .. query_start[b+1]-1
+ *                of the packed arrays below are sequence b's new tokens in order.  A
+ *                sequence whose rows fall outside [0, n_rows), or with more new tokens
+ *                than context tokens (or than max_q_len), sets *err_flag and is skipped
+ *                (its rows are not written).
+ */
+
+/*
+ * pa_slot_mapping_multi -- the cache slot of every new token (slot_mapping int64
+ * [n_rows], row order), by the same placement rule as pa_slot_mapping.  The new rows
+ * then go to pa_kv_append (or pa_kv_append_fp8) with n_tokens = n_rows.
+ */
+int pa_slot_mapping_multi(const int32_t* block_table, const int32_t* context_lens,
+                          const int32_t* query_start, int32_t n_seqs, int32_t n_rows,
+                          int32_t n_shards, int32_t interleave, int32_t block_size,
+                          int32_t max_blocks_per_shard, int64_t n_blocks, int64_t* slot_mapping,
+                          int32_t* err_flag, void* stream);
+
+/*
+ * pa_decode_multi -- pa_decode with several new tokens per sequence, each attending
+ * causally.  q [n_rows][n_q_heads][dk] of q_dtype; max_q_len: a bound on every
+ * sequence's new tokens (it sizes the launch).  kv_dtype is q_dtype, or PA_FP8_E4M3
+ * with k_scale/v_scale/n_scales as in pa_decode_fp8 (else those are ignored).
+ *   part_out float32 [n_rows][n_shards][Pmax][n_q_heads][dv], part_lse float32
+ *   [n_rows][n_shards][Pmax][n_q_heads]: as in pa_decode, per row; a partition holding
+ *   none of the tokens a row may see has lse -inf.  pa_merge_lse with n_seqs = n_rows
+ *   finishes the step.
+ */
+int pa_decode_multi(const void* q, int32_t q_dtype, const int32_t* query_start, int32_t n_rows,
+                    int32_t max_q_len, const void* k_cache, const void* v_cache, int32_t kv_dtype,
+                    const float* k_scale, const float* v_scale, int32_t n_scales,
+                    const int32_t* block_table, const int32_t* context_lens, int32_t n_seqs,
+                    int32_t n_q_heads, int32_t n_kv_heads, int32_t dk, int32_t dv,
+                    int32_t block_size, int64_t n_blocks, int32_t max_blocks_per_shard,
+                    int32_t n_shards, int32_t interleave, int32_t partition_tokens,
+                    int32_t max_partitions, float scale, float* part_out, float* part_lse,
+                    int32_t* err_flag, void* stream);
 
 /*
  * pa_merge_lse -- combine the partials of each (sequence, head) into the attention

@@ -20,6 +20,9 @@ Sources (web pages; every function cites the page and section it follows):
   "Why does writing one token at a time duplicate work?" (the query is compared
   with all earlier keys and the values are weighted by the result; cached rows
   never change), and "How KV-cache memory limits concurrency" (bytes per token).
+* [AGX]  agentlenshq.com/ja/blogs/5a6c5ce5-d812-4d7e-b52c-cb4a97581aac -- "vLLM AgentX
+  release".  Sections used: execution plane (long prompts split by a per-step token
+  threshold) and open-source kernel contributions (a speculative-verification path).
 * [PA]   ai-compass.weeybrid.co.jp/algorizm/paged-attention/ -- "What is
   PagedAttention?".  Sections "A block table separates logical order from
   physical placement", "Reusing blocks freed when a request ends" (worked

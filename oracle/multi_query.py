@@ -7,10 +7,10 @@ decode step follows: the new token's query is compared with the keys of every
 token before it and of itself, and the values are weighted by the result; stored
 rows never change.  A step may carry more than one new token of a sequence -- the
 continuation of a long prompt split into chunks ([KVB], failure-mode paragraph on
-chunked prefill; the long-prefill token threshold of the inference-optimisation
-page) or the verification of speculative tokens (that page's list of kernel
-contributions) -- and the same rule then applies to each of them, which is the
-causal mask among the new tokens.
+chunked prefill; [AGX], execution-plane section: a per-step long-prefill token
+threshold) or the verification of speculative tokens ([AGX], open-source kernel
+contributions section) -- and the same rule then applies to each of them, which is
+the causal mask among the new tokens.
 
 Readings taken here:
 * the ``n_b`` new tokens of sequence ``b`` are the last ``n_b`` of its context;

@@ -26,6 +26,7 @@ import torch
 
 import workloads as wl
 from oracle import fp8_kv as f8
+from oracle import multi_query as mq
 from oracle import paged_attention as pa
 
 TOL = {wl.F32: dict(out=1e-5, lse=1e-5), wl.BF16: dict(out=5e-3, lse=1e-3)}
@@ -57,6 +58,16 @@ def run_library(w, T, partition_tokens=None, out_dtype=torch.float32):
     import decode_attention_paged_kv_amd as P
 
     Tp = partition_tokens or w.partition_tokens or 0
+    if w.multi:
+        step = P.MultiDecodeStep(w.n_seqs, w.n_rows, max(1, int(w.q_lens.max())), w.n_q_heads,
+                                 w.n_kv_heads, w.dk, w.dv, w.block_size, int(w.context_lens.max()),
+                                 w.n_shards, w.interleave, Tp, w.scale_f32, device=T["q"].device,
+                                 out_dtype=out_dtype, context_lens_host=w.context_lens,
+                                 kv_dtype=T["k_cache"].dtype, latent=w.latent)
+        step(T["q"], T["query_start"], T["k_new"], T["v_new"], T["k_cache"], T["v_cache"],
+             T["block_table"], T["context_lens"], T.get("k_scale"), T.get("v_scale"))
+        torch.cuda.synchronize()
+        return step
     step = P.DecodeStep(w.n_seqs, w.n_q_heads, w.n_kv_heads, w.dk, w.dv, w.block_size,
                         int(w.context_lens.max()), w.n_shards, w.interleave, Tp, w.scale_f32,
                         device=T["q"].device, out_dtype=out_dtype,
@@ -95,8 +106,25 @@ def compare_outputs(name, dtype, o, lse, o_ref, lse_ref, rel_l2=REL_L2, out_tol=
     assert rel <= rel_l2, f"{name}: output relative L2 {rel:.3g} > {rel_l2}"
 
 
-def oracle_step(w, H, block_table, context_lens, Tp, Pmax):
-    """The oracle's step on numpy inputs ``H`` (E4M3 caches through ``fp8_kv``)."""
+def oracle_step(w, H, block_table, context_lens, Tp, Pmax, query_start=None):
+    """The oracle's step on numpy inputs ``H`` (E4M3 caches through ``fp8_kv``; several
+    new tokens per sequence through ``multi_query``, with ``query_start``)."""
+    if w.multi:
+        slots = mq.slot_mapping_multi(block_table, context_lens, query_start, w.n_shards,
+                                      w.interleave, w.block_size)
+        if w.cache_dtype == wl.FP8:
+            kc, vc = f8.kv_append(H["k_cache"], H["v_cache"], H["k_new"], H["v_new"], slots,
+                                  w.block_size, H["k_scale"], H["v_scale"])
+            kd, vd = f8.dequantize_cache(kc, vc, H["k_scale"], H["v_scale"])
+        else:
+            kc, vc = pa.kv_append(H["k_cache"], H["v_cache"], H["k_new"], H["v_new"], slots,
+                                  w.block_size)
+            kd, vd = kc, vc
+        o, lse, part_o, part_lse = mq.decode_multi(H["q"], query_start, kd, vd, block_table,
+                                                   context_lens, w.n_shards, w.interleave,
+                                                   w.block_size, Tp, Pmax, w.scale_f32, w.dv)
+        return dict(slots=slots, k_cache=kc, v_cache=vc, o=o, lse=lse, part_o=part_o,
+                    part_lse=part_lse)
     if w.cache_dtype == wl.FP8:
         return f8.decode_step(H["q"], H["k_new"], H["v_new"], H["k_cache"], H["v_cache"],
                               H["k_scale"], H["v_scale"], block_table, context_lens, w.n_shards,
@@ -122,7 +150,7 @@ def check_small(w, partition_tokens=None, fill="normal", rel_l2=REL_L2, seed=Non
     T = {k: (None if v is None else v.to(dev)) for k, v in Tc.items()}
     step = run_library(w, T, partition_tokens)
     Tp, Pmax = step.partition_tokens, step.max_partitions
-    ref = oracle_step(w, H, w.block_table, w.context_lens, Tp, Pmax)
+    ref = oracle_step(w, H, w.block_table, w.context_lens, Tp, Pmax, w.query_start)
     kdt = T["k_cache"].dtype
     assert int(step.err_flag.item()) == 0, f"{w.name}: device error flag {int(step.err_flag.item())}"
     assert np.array_equal(to_np(step.slot_mapping), ref["slots"]), f"{w.name}: slot mapping"
@@ -167,7 +195,12 @@ def check_large(w, sample_seqs, partition_tokens=None, fill="normal", rel_l2=REL
     v_before = None if T["v_cache"] is None else T["v_cache"].clone()
     step = run_library(w, T, partition_tokens)
     assert int(step.err_flag.item()) == 0, f"{w.name}: device error flag"
-    slots_ref = pa.slot_mapping(w.block_table, w.context_lens, w.n_shards, w.interleave, w.block_size)
+    if w.multi:
+        slots_ref = mq.slot_mapping_multi(w.block_table, w.context_lens, w.query_start, w.n_shards,
+                                          w.interleave, w.block_size)
+    else:
+        slots_ref = pa.slot_mapping(w.block_table, w.context_lens, w.n_shards, w.interleave,
+                                    w.block_size)
     assert np.array_equal(to_np(step.slot_mapping), slots_ref), f"{w.name}: slot mapping"
     # append: compare slot-major views on the device
     bs = w.block_size
@@ -208,12 +241,14 @@ def check_large(w, sample_seqs, partition_tokens=None, fill="normal", rel_l2=REL
         idx = torch.from_numpy(ids).to(dev)
         kc = to_np(k_before.index_select(0, idx))
         vc = None if v_before is None else to_np(v_before.index_select(0, idx))
-        kn = to_np(T["k_new"][b:b + 1])
-        vn = None if T["v_new"] is None else to_np(T["v_new"][b:b + 1])
-        qb = to_np(T["q"][b:b + 1])
+        rows = slice(int(w.query_start[b]), int(w.query_start[b + 1]))   # this sequence's q rows
+        kn = to_np(T["k_new"][rows])
+        vn = None if T["v_new"] is None else to_np(T["v_new"][rows])
+        qb = to_np(T["q"][rows])
         Hb = dict(q=qb, k_new=kn, v_new=vn, k_cache=kc, v_cache=vc,
                   k_scale=to_np(T.get("k_scale")), v_scale=to_np(T.get("v_scale")))
-        ref = oracle_step(w, Hb, bt_b.astype(np.int32), w.context_lens[b:b + 1], Tp, Pmax)
+        qs_b = np.array([0, rows.stop - rows.start], np.int32)
+        ref = oracle_step(w, Hb, bt_b.astype(np.int32), w.context_lens[b:b + 1], Tp, Pmax, qs_b)
         # the gather of each shard, bit for bit
         for r in range(w.n_shards):
             Lr = P.pa_shard_length(L, w.n_shards, w.interleave, r)
@@ -225,11 +260,11 @@ def check_large(w, sample_seqs, partition_tokens=None, fill="normal", rel_l2=REL
                                      w.interleave, bs, w.dv)
             assert bits_equal(to_np(kg)[:Lr], kr) and bits_equal(to_np(vg)[:Lr], vr), \
                 f"{w.name}: gather seq {b} shard {r}"
-        compare_outputs(f"{w.name} seq {b} partials", w.dtype, to_np(step.part_out[b:b + 1]),
-                        to_np(step.part_lse[b:b + 1]), ref["part_o"], ref["part_lse"], rel_l2,
+        compare_outputs(f"{w.name} seq {b} partials", w.dtype, to_np(step.part_out[rows]),
+                        to_np(step.part_lse[rows]), ref["part_o"], ref["part_lse"], rel_l2,
                         partials=True)
-        compare_outputs(f"{w.name} seq {b} merged", w.dtype, to_np(step.out[b:b + 1]),
-                        to_np(step.lse[b:b + 1]), ref["o"], ref["lse"], rel_l2)
+        compare_outputs(f"{w.name} seq {b} merged", w.dtype, to_np(step.out[rows]),
+                        to_np(step.lse[rows]), ref["o"], ref["lse"], rel_l2)
     torch.cuda.synchronize()
     assert int(step.err_flag.item()) == 0
     return step

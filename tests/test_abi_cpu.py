@@ -132,3 +132,34 @@ def test_fp8_entry_points_reject_bad_arguments():
     assert dec(n=0) == 0
     assert P.pa_choose_partition_tokens(np.array([1000], np.int32), 8, 2, 64, 64, 16,
                                         __import__("torch").uint8, False) % 16 == 0
+
+
+def test_multi_entry_points_reject_bad_arguments():
+    vp = ctypes.c_void_p(0x1000)
+    sm = P.lib.pa_slot_mapping_multi
+    # bt, lens, qstart, n_seqs, n_rows, S, I, bs, mb, nb, slots, flag, stream
+    assert sm(vp, vp, None, 1, 1, 1, 1, 16, 4, 8, vp, None, None) == -1
+    assert sm(vp, vp, vp, 1, -1, 1, 1, 16, 4, 8, vp, None, None) == -2
+    assert sm(vp, vp, vp, 1, 1, 0, 1, 16, 4, 8, vp, None, None) == -2
+    assert sm(vp, vp, vp, 0, 0, 1, 1, 16, 4, 8, vp, None, None) == 0
+    dm = P.lib.pa_decode_multi
+
+    def dec(**over):
+        a = dict(q=vp, qdt=1, qs=vp, rows=4, maxq=2, k=vp, v=vp, kvdt=1, ks=None, vs=None, ns=0,
+                 bt=vp, lens=vp, n=2, hq=8, hkv=2, dk=128, dv=128, bs=16, nb=8, mb=4, S=1, I=1,
+                 T=16, P=4, scale=0.1)
+        a.update(over)
+        return dm(a["q"], a["qdt"], a["qs"], a["rows"], a["maxq"], a["k"], a["v"], a["kvdt"], a["ks"],
+                  a["vs"], a["ns"], a["bt"], a["lens"], a["n"], a["hq"], a["hkv"], a["dk"], a["dv"],
+                  a["bs"], a["nb"], a["mb"], a["S"], a["I"], a["T"], a["P"], a["scale"], vp, vp, None,
+                  None)
+
+    assert dec(qs=None) == -1
+    assert dec(maxq=0) == -2
+    assert dec(rows=-1) == -2
+    assert dec(kvdt=0) == -3                          # f32 cache with bf16 queries
+    assert dec(kvdt=2) == -1                          # E4M3 cache without scales
+    assert dec(kvdt=2, ks=vp, vs=vp, ns=3) == -2
+    assert dec(maxq=1 << 20) == -2                    # launch grid too large
+    assert dec(rows=0) == 0
+    assert dec(n=0) == 0

@@ -1,0 +1,72 @@
+"""Several new tokens per sequence (causal among them) on the GPU against the
+oracle's ``multi_query``: slots and appended rows bit for bit, every partition's
+output and LSE and the merged rows, on small workloads over the MFMA kernel
+(bf16, head 64/128, E4M3 cache, DCP shards) and the generic one (fp32, odd
+shapes, the latent cache), a whole sequence of new tokens (causal attention over
+all of it), and the speculative-verification workload at full size."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from gpu_harness import check_large, check_small, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import decode_attention_paged_kv_amd  # noqa: F401  (fails loudly if the library is missing)
+
+
+# name, lens, q_lens, hq, hkv, dk, dv, bs, dtype, S, I, T, latent, kv_dtype
+SMALL = [
+    ("mq_gqa128", [1, 17, 300, 1000], [1, 4, 7, 3], 32, 8, 128, 128, 16, wl.BF16, 1, 1, 64, False, ""),
+    ("mq_gqa_dcp", [900, 131], [5, 2], 64, 8, 128, 128, 16, wl.BF16, 4, 16, 64, False, ""),
+    ("mq_gqa64_long_q", [70, 9, 400], [2, 0, 16], 16, 2, 64, 64, 32, wl.BF16, 1, 1, 64, False, ""),
+    ("mq_gqa_fp8", [33, 520], [4, 4], 32, 8, 128, 128, 16, wl.BF16, 1, 1, 128, False, wl.FP8),
+    ("mq_generic_f32", [30, 7, 99], [3, 1, 5], 6, 3, 40, 24, 8, wl.F32, 2, 3, 16, False, ""),
+    ("mq_latent", [70, 200], [2, 3], 16, 1, 576, 512, 64, wl.BF16, 1, 1, 128, True, ""),
+    ("mq_whole_sequence", [40, 77], [40, 77], 8, 2, 128, 128, 16, wl.BF16, 1, 1, 32, False, ""),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_multi_small(case):
+    name, lens, q_lens, hq, hkv, dk, dv, bs, dt, S, I, T, latent, kv = case
+    w = wl.small(name, lens, hq, hkv, dk, dv, bs, dt, n_shards=S, interleave=I, partition_tokens=T,
+                 latent=latent, seed=sum(map(ord, name)) % 1000, kv_dtype=kv, q_lens=q_lens)
+    rel = 4e-3 if (latent and dt == wl.BF16) else 1e-4
+    check_small(w, rel_l2=rel)
+
+
+def test_multi_speculative_long():
+    """The long-context batch with 4 new tokens per sequence, at full size."""
+    w = wl.speculative(q_len=4)
+    order = np.argsort(w.context_lens)
+    check_large(w, [int(order[0]), int(order[-1])])
+
+
+def test_multi_error_flag_on_too_many_new_tokens():
+    """A sequence with more new tokens than context tokens is flagged and skipped; the
+    others are computed."""
+    import decode_attention_paged_kv_amd as P
+
+    say("[multi-error] q_len > context")
+    w = wl.small("mq_bad", [20, 50], 8, 2, 128, 128, 16, wl.BF16, partition_tokens=32, seed=5,
+                 q_lens=[2, 3])
+    dev = torch.device("cuda")
+    T = wl.make_tensors(w, dev)
+    lens = T["context_lens"].clone()
+    lens[0] = 1                                  # 2 new tokens, 1 context token
+    step = P.MultiDecodeStep(w.n_seqs, w.n_rows, 3, w.n_q_heads, w.n_kv_heads, w.dk, w.dv,
+                             w.block_size, 50, partition_tokens=32, device=dev)
+    step.part_lse.fill_(123.0)
+    step(T["q"], T["query_start"], T["k_new"], T["v_new"], T["k_cache"], T["v_cache"],
+         T["block_table"], lens)
+    torch.cuda.synchronize()
+    assert int(step.err_flag.item()) != 0
+    assert torch.all(step.part_lse[:2] == 123.0)          # the bad sequence's rows untouched
+    assert not torch.any(step.part_lse[2:] == 123.0)      # the good one's rows all written
