@@ -5,7 +5,7 @@ kv append, the partitioned attention (pa_decode) and the LSE merge.  Inputs are
 seeded synthetic tensors already resident in HBM.  Prints ONE JSON line.
 
   python bench.py [--steps K] [--warmup W]
-                  [--config long|dcp1|dcp16|batch|latent|tiny|long_fp8|dcp1_fp8|dcp16_fp8]
+                  [--config long|dcp1|dcp16|batch|latent|tiny|long_fp8|dcp1_fp8|dcp16_fp8|spec4]
                   [--no-cpu-baseline] [--secondary]
 
 The default workload is the long-context step (8 sequences, log-normal lengths
@@ -45,6 +45,7 @@ def make_workload(name):
         "long_fp8": lambda: wl.with_fp8_cache(wl.long(partition_tokens=0)),
         "dcp1_fp8": lambda: wl.with_fp8_cache(wl.dcp(interleave=1)),
         "dcp16_fp8": lambda: wl.with_fp8_cache(wl.dcp(interleave=16)),
+        "spec4": lambda: wl.speculative(q_len=4),
     }[name]()
 
 
@@ -67,6 +68,9 @@ DESCRIBE = {
                 "d 128, bf16 q, block 16, S=4 interleaved shards, I=1",
     "dcp16_fp8": "DCP emulation with an E4M3 KV cache: 1 seq of 200000 tokens, 64 q / 8 kv heads, "
                  "d 128, bf16 q, block 16, S=4 interleaved shards, I=16",
+    "spec4": "speculative verification on the long-context batch: 8 seqs, L log-normal (median 142K), "
+             "4 new tokens per sequence attending causally, 32 q / 8 kv heads, d 128, bf16, block 16, "
+             "partition size chosen by pa_choose_partition_tokens",
 }
 
 
@@ -104,9 +108,20 @@ def time_gpu(w, T, step, steps, warmup):
     import torch
 
     ks, vs = T.get("k_scale"), T.get("v_scale")
-    args = (T["q"], T["k_new"], T["v_new"], T["k_cache"], T["v_cache"], T["block_table"],
-            T["context_lens"], ks, vs)
     nb = T["k_cache"].shape[0]
+    if w.multi:
+        qs = T["query_start"]
+        args = (T["q"], qs, T["k_new"], T["v_new"], T["k_cache"], T["v_cache"], T["block_table"],
+                T["context_lens"], ks, vs)
+        route = lambda: step.route(T["block_table"], T["context_lens"], qs, nb)
+        attend = lambda: step.attend(T["q"], qs, T["k_cache"], T["v_cache"], T["block_table"],
+                                     T["context_lens"], ks, vs)
+    else:
+        args = (T["q"], T["k_new"], T["v_new"], T["k_cache"], T["v_cache"], T["block_table"],
+                T["context_lens"], ks, vs)
+        route = lambda: step.route(T["block_table"], T["context_lens"], nb)
+        attend = lambda: step.attend(T["q"], T["k_cache"], T["v_cache"], T["block_table"],
+                                     T["context_lens"], ks, vs)
     for _ in range(warmup):
         step(*args)
     torch.cuda.synchronize()
@@ -117,10 +132,10 @@ def time_gpu(w, T, step, steps, warmup):
     wall0 = time.perf_counter()
     t0.record()
     for i in range(steps):
-        step.route(T["block_table"], T["context_lens"], nb)
+        route()
         step.append(T["k_new"], T["v_new"], T["k_cache"], T["v_cache"], ks, vs)
         ev[i][0].record()
-        step.attend(T["q"], T["k_cache"], T["v_cache"], T["block_table"], T["context_lens"], ks, vs)
+        attend()
         ev[i][1].record()
         step.merge()
     t1.record()
@@ -166,7 +181,16 @@ def cpu_baseline(w, T, budget_s=12.0):
         t = time.perf_counter()
         qn, kn = host(T["q"][b:b + 1]), host(T["k_new"][b:b + 1])
         vn = None if T["v_new"] is None else host(T["v_new"][b:b + 1])
-        if w.cache_dtype == "fp8":
+        if w.multi:
+            from oracle import multi_query as mq
+
+            rows = slice(int(w.query_start[b]), int(w.query_start[b + 1]))
+            qs_b = np.array([0, rows.stop - rows.start], np.int32)
+            vm = None if T["v_new"] is None else host(T["v_new"][rows])
+            mq.decode_step_multi(host(T["q"][rows]), qs_b, host(T["k_new"][rows]), vm, kc, vc, bt,
+                                 w.context_lens[b:b + 1], w.n_shards, w.interleave, w.block_size,
+                                 Tp, max(pmax, 1), w.scale_f32, w.dv)
+        elif w.cache_dtype == "fp8":
             f8.decode_step(qn, kn, vn, kc, vc, host(T["k_scale"]), host(T.get("v_scale")), bt,
                            w.context_lens[b:b + 1], w.n_shards, w.interleave, w.block_size, Tp,
                            max(pmax, 1), w.scale_f32, w.dv)
@@ -197,11 +221,18 @@ def run_config(name, steps, warmup, with_cpu, partition_tokens=0):
         w.partition_tokens = partition_tokens
     dev = torch.device("cuda", 0)
     T = wl.make_tensors(w, dev)
-    step = P.DecodeStep(w.n_seqs, w.n_q_heads, w.n_kv_heads, w.dk, w.dv, w.block_size,
-                        int(w.context_lens.max()), w.n_shards, w.interleave,
-                        w.partition_tokens, w.scale_f32, device=dev,
-                        context_lens_host=w.context_lens, kv_dtype=T["k_cache"].dtype,
-                        latent=w.latent)
+    if w.multi:
+        step = P.MultiDecodeStep(w.n_seqs, w.n_rows, int(w.q_lens.max()), w.n_q_heads, w.n_kv_heads,
+                                 w.dk, w.dv, w.block_size, int(w.context_lens.max()), w.n_shards,
+                                 w.interleave, w.partition_tokens, w.scale_f32, device=dev,
+                                 context_lens_host=w.context_lens, kv_dtype=T["k_cache"].dtype,
+                                 latent=w.latent)
+    else:
+        step = P.DecodeStep(w.n_seqs, w.n_q_heads, w.n_kv_heads, w.dk, w.dv, w.block_size,
+                            int(w.context_lens.max()), w.n_shards, w.interleave,
+                            w.partition_tokens, w.scale_f32, device=dev,
+                            context_lens_host=w.context_lens, kv_dtype=T["k_cache"].dtype,
+                            latent=w.latent)
     if not w.partition_tokens:
         w.partition_tokens = step.partition_tokens
     cpu = cpu_baseline(w, T) if with_cpu else None
@@ -213,8 +244,10 @@ def run_config(name, steps, warmup, with_cpu, partition_tokens=0):
     dec_ms = t["decode_ms_mean"]
     achieved = kv_bytes / (dec_ms * 1e-3) / 1e9
     tokens = int(np.sum(w.context_lens.astype(np.int64)))
+    new_tokens = w.n_rows
     res = dict(w=w, step=step, kv_bytes=kv_bytes, ms_per_step=ms, decode_ms=dec_ms,
                tokens_per_s_decode=tokens / (dec_ms * 1e-3),
+               new_tokens_per_s=new_tokens / (ms * 1e-3),
                value=kv_bytes / (ms * 1e-3) / 1e9, seq_steps=w.n_seqs / (ms * 1e-3),
                achieved=achieved, timing=t, cpu=cpu)
     if w.latent:
@@ -292,6 +325,7 @@ def main():
         "seq_steps_per_s": round(r["seq_steps"], 2),
         "decode_ms": round(r["decode_ms"], 5),
         "kv_tokens_per_s_decode": round(r["tokens_per_s_decode"], 1),
+        "new_tokens_per_s": round(r["new_tokens_per_s"], 1),
         "roofline": {"bound": "hbm", "achieved": round(r["achieved"], 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(r["achieved"] / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "kernel": "pa_decode",
@@ -303,7 +337,8 @@ def main():
         line["roofline"]["mfma_frac"] = round(r["tflops"] / MFMA_BF16_TFLOPS, 4)
     if a.secondary:
         sec = {}
-        for name in ("dcp1", "dcp16", "batch", "latent", "tiny", "long_fp8", "dcp1_fp8", "dcp16_fp8"):
+        for name in ("dcp1", "dcp16", "batch", "latent", "tiny", "long_fp8", "dcp1_fp8", "dcp16_fp8",
+                     "spec4"):
             if name == a.config:
                 continue
             s = run_config(name, a.steps, a.warmup, False)
@@ -311,6 +346,7 @@ def main():
                          "hbm_frac_decode": round(s["achieved"] / HBM_PEAK_GBS, 4),
                          "ms_per_step": round(s["ms_per_step"], 5), "decode_ms": round(s["decode_ms"], 5),
                          "kv_tokens_per_s_decode": round(s["tokens_per_s_decode"], 1),
+                         "new_tokens_per_s": round(s["new_tokens_per_s"], 1),
                          "seq_steps_per_s": round(s["seq_steps"], 2)}
             if "tflops" in s:
                 sec[name]["mfma_tflops"] = round(s["tflops"], 2)

@@ -119,6 +119,7 @@ int32_t pa_choose_partition_tokens(const int32_t* context_lens_host, int32_t n_s
   a.bs = block_size;
   a.dtype = dtype == PA_FP8_E4M3 ? PA_BF16 : dtype;  // E4M3 cache: bf16 queries
   a.kv_dtype = dtype;
+  a.max_q = 1;  // (new token, head) columns: callers with several new tokens scale n_q_heads
   a.v_cache = latent ? nullptr : static_cast<const void*>(&a);  // only its NULL-ness matters
   const pa::KernelChoice kc = pa::choose_kernel(a);
   int cus = 0, xccs = 0, dev = 0;

@@ -163,3 +163,17 @@ def test_multi_entry_points_reject_bad_arguments():
     assert dec(maxq=1 << 20) == -2                    # launch grid too large
     assert dec(rows=0) == 0
     assert dec(n=0) == 0
+
+
+def test_chooser_picks_long_partitions_for_long_contexts():
+    """Long contexts spread over every compute unit in partitions of thousands of tokens,
+    not a block or two (the per-partition cost would dominate)."""
+    import torch
+
+    import workloads as wl
+
+    for w, hq in ((wl.dcp(1), 64), (wl.long(), 32), (wl.speculative(), 32 * 4)):
+        for kv in (torch.bfloat16, torch.uint8):
+            T = P.pa_choose_partition_tokens(w.context_lens, hq, w.n_kv_heads, w.dk, w.dv,
+                                             w.block_size, kv, False, w.n_shards, w.interleave)
+            assert 1024 <= T <= 16384, (w.name, kv, T)
