@@ -52,6 +52,10 @@
 #include "pa_common.h"
 #include "pa_launch.h"
 
+#ifndef PA_GQA_MIN_WAVES_FP8
+#define PA_GQA_MIN_WAVES_FP8 2
+#endif
+
 namespace pa {
 namespace {
 
@@ -67,14 +71,36 @@ __device__ inline f32x4_t mfma16x16x32(bf16x8_t a, bf16x8_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// Reductions over lanes l, l^16, l^32, l^48 (the four lanes of one column).  A row swap
+// (v_permlane16_swap / v_permlane32_swap, both operands the same value) leaves each lane
+// holding its own value and its partner's (lane ^ 16, lane ^ 32), so one vector
+// instruction and one max/add replace each exchange through the LDS crossbar.
 __device__ inline float xor_max(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16));
-  return fmaxf(v, __shfl_xor(v, 32));
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// 2^x for the softmax weights: the transcendental unit's instruction alone (raw), or the
+// library call, which adds a fix-up for results below 2^-126 (irrelevant next to the
+// running maximum's weight of 1; -inf gives 0 either way).
+#ifndef PA_GQA_RAW_EXP
+#define PA_GQA_RAW_EXP 0
+#endif
+__device__ inline float exp2_w(float x) {
+#if PA_GQA_RAW_EXP
+  return __builtin_amdgcn_exp2f(x);
+#else
+  return exp2f(x);
+#endif
 }
 
 __device__ inline float xor_sum(float v) {
-  v += __shfl_xor(v, 16);
-  return v + __shfl_xor(v, 32);
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 // Keep the bf16 halves of a 32-bit word whose tokens are valid.
@@ -133,8 +159,11 @@ struct Step {
   int sub[SUBS];
 };
 
+// At least two waves per SIMD (registers capped at 256): each wave's step of loads in
+// flight is what hides the HBM latency.
 template <int D, int NW, int SUBS, int KT>
-__global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(KT == kFP8 ? PA_GQA_MIN_WAVES_FP8 : 2))) void decode_gqa_kernel(
+    DecodeArgs a) {
   using TileT = Tile<D, SUBS, KT>;
   using raw = typename Elem<KT>::raw;
   constexpr bool F8 = TileT::F8;
@@ -298,21 +327,25 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeArgs a) {
   // one step: scores of the sub-tiles, then after_scores() (the key registers are free),
   // softmax and the output product, then after_output() (the value registers are free)
   auto compute = [&](TileT& tl, const StepT& st, auto&& after_scores, auto&& after_output) {
+    // the sub-tiles' score chains are interleaved (k-step outer), so consecutive MFMAs
+    // never wait on each other; absent sub-tiles hold whatever block 0 holds and are
+    // masked below
     float sc[SUBS][4];
+    f32x4_t acc[SUBS];
 #pragma unroll
-    for (int t = 0; t < SUBS; ++t) {
-      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-      if (st.tok0[t] >= 0) {
+    for (int t = 0; t < SUBS; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int j = 0; j < KJ; ++j) acc = mfma16x16x32(tl.key(t, j), qop[j], acc);
-      }
+    for (int j = 0; j < KJ; ++j)
+#pragma unroll
+      for (int t = 0; t < SUBS; ++t) acc[t] = mfma16x16x32(tl.key(t, j), qop[j], acc[t]);
+#pragma unroll
+    for (int t = 0; t < SUBS; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int tok = st.tok0[t] + 4 * grp + i;
         const bool ok = st.tok0[t] >= 0 && tok < lim;
-        sc[t][i] = ok ? acc[i] : -INFINITY;
+        sc[t][i] = ok ? acc[t][i] : -INFINITY;
       }
-    }
     after_scores();
     float mt = m;
 #pragma unroll
@@ -320,7 +353,7 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) mt = fmaxf(mt, sc[t][i]);
     mt = xor_max(mt);
-    const float alpha = (mt == -INFINITY) ? 1.f : exp2f((m - mt) * c);
+    const float alpha = (mt == -INFINITY) ? 1.f : exp2_w((m - mt) * c);
     m = mt;
     const float mc = (mt == -INFINITY) ? 0.f : mt * c;   // a column that has seen nothing yet
     float pv[SUBS][4];
@@ -329,7 +362,7 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeArgs a) {
     for (int t = 0; t < SUBS; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        pv[t][i] = exp2f(fmaf(sc[t][i], c, -mc));
+        pv[t][i] = exp2_w(fmaf(sc[t][i], c, -mc));
         psum += pv[t][i];
       }
     lsum = fmaf(lsum, alpha, psum);
@@ -446,7 +479,7 @@ int gqa_column_chunks(const DecodeArgs& a) { return (a.max_q * (a.hq / a.hkv) + 
 #define PA_GQA_SUBS 2
 #endif
 #ifndef PA_GQA_SUBS_FP8
-#define PA_GQA_SUBS_FP8 4   // an E4M3 sub-tile has half the bytes: twice as many in flight
+#define PA_GQA_SUBS_FP8 2   // measured: as fast as four sub-tiles and lighter on registers
 #endif
 #ifndef PA_GQA_WAVES_FP8
 #define PA_GQA_WAVES_FP8 4  // measured: the E4M3 kernel runs faster as smaller workgroups
