@@ -143,8 +143,21 @@ def time_gpu(w, T, step, steps, warmup):
     wall = time.perf_counter() - wall0
     total_ms = t0.elapsed_time(t1)
     dec = sorted(a.elapsed_time(b) for a, b in ev)
-    return dict(total_ms=total_ms, wall_s=wall, decode_ms_mean=sum(dec) / len(dec),
-                decode_ms_median=dec[len(dec) // 2], decode_ms_min=dec[0])
+    res = dict(total_ms=total_ms, wall_s=wall, decode_ms_mean=sum(dec) / len(dec),
+               decode_ms_median=dec[len(dec) // 2], decode_ms_min=dec[0])
+    # After the timed region: the same step recorded once as a HIP graph and replayed
+    # K times (reported separately; it removes the host's per-launch cost).
+    graph = step.capture(*args)
+    torch.cuda.synchronize()
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g0.record()
+    for _ in range(steps):
+        graph.replay()
+    g1.record()
+    torch.cuda.synchronize()
+    res["graph_ms_per_step"] = g0.elapsed_time(g1) / steps
+    del graph
+    return res
 
 
 def cpu_baseline(w, T, budget_s=12.0):
@@ -326,6 +339,7 @@ def main():
         "decode_ms": round(r["decode_ms"], 5),
         "kv_tokens_per_s_decode": round(r["tokens_per_s_decode"], 1),
         "new_tokens_per_s": round(r["new_tokens_per_s"], 1),
+        "graph_ms_per_step": round(r["timing"]["graph_ms_per_step"], 5),
         "roofline": {"bound": "hbm", "achieved": round(r["achieved"], 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(r["achieved"] / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "kernel": "pa_decode",
@@ -347,6 +361,7 @@ def main():
                          "ms_per_step": round(s["ms_per_step"], 5), "decode_ms": round(s["decode_ms"], 5),
                          "kv_tokens_per_s_decode": round(s["tokens_per_s_decode"], 1),
                          "new_tokens_per_s": round(s["new_tokens_per_s"], 1),
+                         "graph_ms_per_step": round(s["timing"]["graph_ms_per_step"], 5),
                          "seq_steps_per_s": round(s["seq_steps"], 2)}
             if "tflops" in s:
                 sec[name]["mfma_tflops"] = round(s["tflops"], 2)

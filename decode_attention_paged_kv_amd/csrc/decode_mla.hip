@@ -79,7 +79,20 @@ constexpr int NBUF = 3;                             // tile buffers
 constexpr int KSTEPS = DK / 16;                     // 36 k-steps of the score product
 constexpr int MT = DV / 32;                         // 16 value-column tiles
 constexpr int TBL = 256;                            // block-table entries staged in LDS
-constexpr int QL = 12;                              // query k-steps kept in LDS (rest in registers)
+#ifndef PA_MLA_QL
+#define PA_MLA_QL 12
+#endif
+#ifndef PA_MLA_KA
+#define PA_MLA_KA 3
+#endif
+#ifndef PA_MLA_VA
+#define PA_MLA_VA 2
+#endif
+#ifndef PA_MLA_COPY_STRIDE
+#define PA_MLA_COPY_STRIDE 4   // MFMA shadows between the tile copies of a wave
+#endif
+constexpr int QL = PA_MLA_QL;                       // query k-steps kept in LDS (rest in registers)
+static_assert(QL >= 0 && QL <= 36 && PA_MLA_KA >= 1 && PA_MLA_VA >= 1, "read-ahead and query split");
 static_assert(TILE_SLOTS % (64 * NW) == 0, "tile copies must split evenly over the waves");
 static_assert(ROW_CHUNKS % 8 == 0, "the swizzle permutes aligned groups of 8 chunks");
 
@@ -174,6 +187,8 @@ void decode_mla_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) char kt[NBUF * TILE_BYTES];
   __shared__ __attribute__((aligned(16))) uint16_t q_s[QL * 2 * HEADS * 8];   // [ks][k-group][head][8]
   __shared__ int32_t tbl_s[TBL];   // block-table entries of the partition, TBL at a time
+  static_assert(NBUF * TILE_BYTES + QL * 2 * HEADS * 8 * 2 + TBL * 4 + 2 * NW * 4 <= 160 * 1024,
+                "the tiles, the query part and the table must fit the compute unit's 160 KiB of LDS");
   __shared__ __attribute__((aligned(16))) int ovf_s[2][NW];   // [tile parity][wave]: overflow seen
 
   const int tid = threadIdx.x;
@@ -415,7 +430,7 @@ void decode_mla_kernel(DecodeArgs a) {
       kb[j] = tile + ka[j];
       asm volatile("" : "+v"(kb[j]));
     }
-    constexpr int KA = 3;
+    constexpr int KA = PA_MLA_KA;   // k-steps of read-ahead
     bf16x8_t kop[KA + 1], qlo[KA + 1];
     auto kread = [&](int ks) {
       return *reinterpret_cast<const lds_bf16x8_t*>(kb[ks & 3] + 128 * (ks >> 2));
@@ -474,7 +489,7 @@ void decode_mla_kernel(DecodeArgs a) {
         vb[h][par] = tile + va[h][par];
         asm volatile("" : "+v"(vb[h][par]));
       }
-    constexpr int VA = 2, NV = 2 * MT;
+    constexpr int VA = PA_MLA_VA, NV = 2 * MT;
     bf16x8_t vop[VA + 1];
     auto vread = [&](int n) {   // operand n = kv * MT + m
       const int kv = n / MT, m = n % MT;
@@ -606,17 +621,24 @@ void decode_mla_kernel(DecodeArgs a) {
       Copy cp{};
       f32x16_t s_next = s_cur;
       if (has_next) {
-        // slot ks: the copy of tile i+2 every fourth MFMA (ks = 1, 5, .., 33), softmax
-        // steps in the other slots, in order
+        // slot ks: the copy of tile i+2 in every CS-th MFMA shadow from ks = 1 (early in
+        // the iteration, so the copies have the most time to land before the next
+        // iteration waits for them), softmax steps in the other slots, in order
+        constexpr int CS = PA_MLA_COPY_STRIDE;
+        static_assert(CS >= 2 && 1 + CS * (COPIES - 1) < KSTEPS &&
+                          KSTEPS - COPIES >= kFirstSteps, "copy slots and softmax steps");
         scores(tile_ptr(i + 1), s_next, [&](int ks) {
-          if ((ks & 3) == 1) {
-            const int k = ks >> 2;
+          const bool copy_slot = ks >= 1 && (ks - 1) % CS == 0 && (ks - 1) / CS < COPIES;
+          if (copy_slot) {
+            const int k = (ks - 1) / CS;
             if (copy_next) {
               if (k == 0) cp = finish_tile(i + 2, entry);
               copy_piece(cp, k);
             }
           } else {
-            const int step = ks - (ks + 2) / 4;   // index among the non-copy slots
+            // index among the non-copy slots
+            const int copies_before = ks < 1 ? 0 : (ks - 1) / CS + 1 < COPIES ? (ks - 1) / CS + 1 : COPIES;
+            const int step = ks - copies_before;
             if (step < kFirstSteps) softmax_piece(step);
           }
         });

@@ -76,6 +76,27 @@ class DecodeStep:
         self.merge()
         return self.out, self.lse
 
+    def capture(self, *args, **kwargs):
+        """Record the whole step (the same arguments as a call) as a HIP graph and return
+        it; ``graph.replay()`` then reruns the four launches on whatever the argument
+        tensors hold at that time.  The library allocates nothing and issues no memset,
+        so the recorded launches are the step itself."""
+        return capture_graph(lambda: self(*args, **kwargs))
+
+
+def capture_graph(fn):
+    """Run ``fn`` once to warm up, then record it into a ``torch.cuda.CUDAGraph`` (on a
+    side stream, as graph capture requires)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fn()
+    return graph
+
 
 class MultiDecodeStep:
     """One step with several new tokens per sequence, each attending causally (the
@@ -142,3 +163,7 @@ class MultiDecodeStep:
         self.attend(q, query_start, k_cache, v_cache, block_table, context_lens, k_scale, v_scale)
         self.merge()
         return self.out, self.lse
+
+    def capture(self, *args, **kwargs):
+        """The whole step recorded as a HIP graph (see ``DecodeStep.capture``)."""
+        return capture_graph(lambda: self(*args, **kwargs))
