@@ -485,26 +485,39 @@ int gqa_column_chunks(const DecodeArgs& a) { return (a.max_q * (a.hq / a.hkv) + 
 #define PA_GQA_WAVES_FP8 4  // measured: the E4M3 kernel runs faster as smaller workgroups
 #endif
 
-namespace {
-constexpr int waves_of(int kv_dtype) { return kv_dtype == kFP8 ? PA_GQA_WAVES_FP8 : PA_GQA_WAVES; }
+#ifndef PA_GQA_SHORT_TOKENS
+#define PA_GQA_SHORT_TOKENS 512   // partitions this short (or several new tokens) use 4 waves
+#endif
 
-template <int D, int KT>
+namespace {
+template <int D, int NW, int KT>
 const void* gqa_kernel() {
-  constexpr int NW = waves_of(KT);
   constexpr int SUBS = KT == kFP8 ? PA_GQA_SUBS_FP8 : PA_GQA_SUBS;
   return (const void*)decode_gqa_kernel<D, NW, SUBS, KT>;
 }
 
-const void* gqa_kernel_for(int dk, int kv_dtype) {
-  if (kv_dtype == kFP8) return dk == 128 ? gqa_kernel<128, kFP8>() : gqa_kernel<64, kFP8>();
-  return dk == 128 ? gqa_kernel<128, kBF16>() : gqa_kernel<64, kBF16>();
+// Waves per workgroup.  Measured: long single-token partitions run best with 8 waves
+// (one workgroup per compute unit, each wave a long contiguous range); short partitions
+// and several new tokens per sequence (more, shorter workgroups) with 4; the E4M3 cache
+// with 4.
+int gqa_waves(const DecodeArgs& a) {
+  if (a.kv_dtype == kFP8) return PA_GQA_WAVES_FP8;
+  return (a.max_q > 1 || a.part_tokens <= PA_GQA_SHORT_TOKENS) ? 4 : PA_GQA_WAVES;
+}
+
+const void* gqa_kernel_for(const DecodeArgs& a) {
+  const bool d128 = a.dk == 128;
+  if (a.kv_dtype == kFP8)
+    return d128 ? gqa_kernel<128, PA_GQA_WAVES_FP8, kFP8>() : gqa_kernel<64, PA_GQA_WAVES_FP8, kFP8>();
+  if (gqa_waves(a) == 4) return d128 ? gqa_kernel<128, 4, kBF16>() : gqa_kernel<64, 4, kBF16>();
+  return d128 ? gqa_kernel<128, PA_GQA_WAVES, kBF16>() : gqa_kernel<64, PA_GQA_WAVES, kBF16>();
 }
 }  // namespace
 
-int gqa_workgroups_per_cu(int dk, int kv_dtype) {
+int gqa_workgroups_per_cu(const DecodeArgs& a) {
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gqa_kernel_for(dk, kv_dtype),
-                                                   64 * waves_of(kv_dtype), 0) != hipSuccess) {
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gqa_kernel_for(a), 64 * gqa_waves(a), 0) !=
+      hipSuccess) {
     (void)hipGetLastError();
     return 0;
   }
@@ -514,8 +527,7 @@ int gqa_workgroups_per_cu(int dk, int kv_dtype) {
 hipError_t launch_decode_gqa(const DecodeArgs& a, hipStream_t st) {
   const dim3 grid(a.max_parts, a.n_seqs * a.n_shards, a.hkv * gqa_column_chunks(a));
   void* args[] = {const_cast<DecodeArgs*>(&a)};
-  return hipLaunchKernel(gqa_kernel_for(a.dk, a.kv_dtype), grid, dim3(64 * waves_of(a.kv_dtype)),
-                         args, 0, st);
+  return hipLaunchKernel(gqa_kernel_for(a), grid, dim3(64 * gqa_waves(a)), args, 0, st);
 }
 
 }  // namespace pa

@@ -121,6 +121,18 @@ int32_t pa_choose_partition_tokens(const int32_t* context_lens_host, int32_t n_s
   a.kv_dtype = dtype;
   a.max_q = 1;  // (new token, head) columns: callers with several new tokens scale n_q_heads
   a.v_cache = latent ? nullptr : static_cast<const void*>(&a);  // only its NULL-ness matters
+  std::vector<int32_t> shard_len_v(size_t(n_seqs) * n_shards);
+  int32_t longest = 0;
+  for (int b = 0; b < n_seqs; ++b)
+    for (int r = 0; r < n_shards; ++r) {
+      const int32_t Lr = pa::shard_len(std::max(context_lens_host[b], 0), n_shards, interleave, r);
+      shard_len_v[size_t(b) * n_shards + r] = Lr;
+      longest = std::max(longest, Lr);
+    }
+  if (longest == 0) return block_size;
+  // the kernel variant can depend on the partition size; partitions as long as the
+  // longest shard stand for the sizes the scan below can pick (short contexts stay short)
+  a.part_tokens = longest;
   const pa::KernelChoice kc = pa::choose_kernel(a);
   int cus = 0, xccs = 0, dev = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
@@ -143,15 +155,6 @@ int32_t pa_choose_partition_tokens(const int32_t* context_lens_host, int32_t n_s
   const int64_t partial_bytes = int64_t(n_q_heads / n_kv_heads) * dv * 4 * 2;
   const int64_t token_bytes = int64_t(latent ? dk : dk + dv) * elem_bytes(dtype);
   const int64_t overhead = 128 + partial_bytes / (token_bytes > 0 ? token_bytes : 1);
-  std::vector<int32_t> shard_len_v(size_t(n_seqs) * n_shards);
-  int32_t longest = 0;
-  for (int b = 0; b < n_seqs; ++b)
-    for (int r = 0; r < n_shards; ++r) {
-      const int32_t Lr = pa::shard_len(std::max(context_lens_host[b], 0), n_shards, interleave, r);
-      shard_len_v[size_t(b) * n_shards + r] = Lr;
-      longest = std::max(longest, Lr);
-    }
-  if (longest == 0) return block_size;
   const int64_t Y = int64_t(n_seqs) * n_shards, Z = kc.units_per_partition;
   const int32_t max_m = (longest + block_size - 1) / block_size;
   // every multiple of the block size while the scan stays cheap, else a coarser grid

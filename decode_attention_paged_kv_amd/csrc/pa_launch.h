@@ -61,7 +61,7 @@ int generic_column_chunks(const DecodeArgs& a);
 hipError_t launch_decode_gqa(const DecodeArgs& a, hipStream_t st);
 bool mla_supported(const DecodeArgs& a);
 hipError_t launch_decode_mla(const DecodeArgs& a, hipStream_t st);
-int gqa_workgroups_per_cu(int dk, int kv_dtype);
+int gqa_workgroups_per_cu(const DecodeArgs& a);
 int mla_workgroups_per_cu();
 int generic_workgroups_per_cu(int dtype, int kv_dtype);
 hipError_t launch_merge(const float* part_out, const float* part_lse, int n_seqs, int n_parts,
