@@ -78,6 +78,7 @@ SMALL = [
     ("f8_generic_f32q", [1, 50, 130], 6, 3, 40, 24, 8, wl.F32, 1, 1, 32, False, True),
     ("f8_generic_bf16q", [3, 90], 5, 1, 96, 80, 16, wl.BF16, 2, 3, 32, False, False),
     ("f8_latent", [65, 300], 16, 1, 576, 512, 64, wl.BF16, 1, 1, 128, True, True),
+    ("f8_empty_and_one", [0, 1, 17], 8, 2, 128, 128, 16, wl.BF16, 1, 1, 16, False, True),
 ]
 
 
@@ -100,3 +101,20 @@ def test_fp8_long():
 def test_fp8_dcp():
     w = wl.with_fp8_cache(wl.dcp(16))
     check_large(w, [0])
+
+
+def test_fp8_block_copy():
+    """pa_copy_blocks moves E4M3 codes bit for bit."""
+    import decode_attention_paged_kv_amd as P
+    from oracle import paged_attention as pa
+
+    g = torch.Generator().manual_seed(3)
+    k = torch.randint(0, 256, (20, 8, 16, 128), dtype=torch.uint8, generator=g)
+    v = torch.randint(0, 256, (20, 8, 128, 16), dtype=torch.uint8, generator=g)
+    pairs = [(2, 5), (2, 6), (19, 0)]
+    k_ref, v_ref = pa.copy_blocks(k.numpy(), v.numpy(), pairs)
+    dev = torch.device("cuda")
+    kd, vd = k.to(dev), v.to(dev)
+    P.pa_copy_blocks(kd, vd, torch.tensor(pairs, dtype=torch.int64, device=dev))
+    torch.cuda.synchronize()
+    assert bits_equal(to_np(kd), k_ref) and bits_equal(to_np(vd), v_ref)

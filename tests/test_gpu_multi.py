@@ -30,6 +30,8 @@ SMALL = [
     ("mq_generic_f32", [30, 7, 99], [3, 1, 5], 6, 3, 40, 24, 8, wl.F32, 2, 3, 16, False, ""),
     ("mq_latent", [70, 200], [2, 3], 16, 1, 576, 512, 64, wl.BF16, 1, 1, 128, True, ""),
     ("mq_whole_sequence", [40, 77], [40, 77], 8, 2, 128, 128, 16, wl.BF16, 1, 1, 32, False, ""),
+    ("mq_latent_fp8_empty", [70, 0, 9], [3, 0, 9], 16, 1, 576, 512, 64, wl.BF16, 1, 1, 64, True, wl.FP8),
+    ("mq_dcp_fp8_d64", [200, 45], [6, 1], 16, 4, 64, 64, 16, wl.BF16, 3, 2, 32, False, wl.FP8),
 ]
 
 
@@ -40,6 +42,28 @@ def test_multi_small(case):
                  latent=latent, seed=sum(map(ord, name)) % 1000, kv_dtype=kv, q_lens=q_lens)
     rel = 4e-3 if (latent and dt == wl.BF16) else 1e-4
     check_small(w, rel_l2=rel)
+
+
+def test_multi_grid_bound_above_need():
+    """max_q_len larger than any sequence's new tokens: the extra column chunks find no
+    rows and exit; the result equals the tight bound's bit for bit."""
+    import decode_attention_paged_kv_amd as P
+
+    say("[multi] loose max_q_len")
+    w = wl.small("mq_loose", [300, 70], 32, 8, 128, 128, 16, wl.BF16, partition_tokens=64, seed=9,
+                 q_lens=[2, 1])
+    dev = torch.device("cuda")
+    outs = []
+    for max_q in (2, 9):
+        T = wl.make_tensors(w, dev)
+        step = P.MultiDecodeStep(w.n_seqs, w.n_rows, max_q, w.n_q_heads, w.n_kv_heads, w.dk, w.dv,
+                                 w.block_size, 300, partition_tokens=64, scale=w.scale_f32, device=dev)
+        step(T["q"], T["query_start"], T["k_new"], T["v_new"], T["k_cache"], T["v_cache"],
+             T["block_table"], T["context_lens"])
+        torch.cuda.synchronize()
+        assert int(step.err_flag.item()) == 0
+        outs.append((step.out.clone(), step.lse.clone()))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
 
 
 def test_multi_speculative_long():
