@@ -55,9 +55,6 @@
 #ifndef PA_GQA_MIN_WAVES_FP8
 #define PA_GQA_MIN_WAVES_FP8 2
 #endif
-#ifndef PA_GQA_MIN_WAVES
-#define PA_GQA_MIN_WAVES 2
-#endif
 
 namespace pa {
 namespace {
@@ -165,7 +162,7 @@ struct Step {
 // At least two waves per SIMD (registers capped at 256): each wave's step of loads in
 // flight is what hides the HBM latency.
 template <int D, int NW, int SUBS, int KT>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(KT == kFP8 ? PA_GQA_MIN_WAVES_FP8 : PA_GQA_MIN_WAVES))) void decode_gqa_kernel(
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(KT == kFP8 ? PA_GQA_MIN_WAVES_FP8 : 2))) void decode_gqa_kernel(
     DecodeArgs a) {
   using TileT = Tile<D, SUBS, KT>;
   using raw = typename Elem<KT>::raw;
