@@ -63,6 +63,19 @@ typedef __bf16 bf16x8_t __attribute__((__vector_size__(8 * sizeof(__bf16))));
 typedef __bf16 bf16x2_t __attribute__((__vector_size__(2 * sizeof(__bf16))));
 typedef float f32x4_t __attribute__((__vector_size__(4 * sizeof(float))));
 typedef uint32_t u32x4_t __attribute__((__vector_size__(4 * sizeof(uint32_t))));
+typedef uint32_t u32x2_t __attribute__((__vector_size__(2 * sizeof(uint32_t))));
+
+// Value loads use the non-temporal policy (`nt`): the cache is read once per step, and on
+// this GPU `nt` streams random 2-16 KiB chunks from HBM ~11 % faster.  It pays only where
+// one load instruction covers whole 128-byte lines, as a value load does (16 d rows x all
+// tokens of the sub-tile, contiguous).  A key load covers half of each token's line (the
+// other half comes with the next instruction), and under `nt` the long-context decode
+// measured 5 % slower with key loads included, 5 % faster without them.
+__device__ inline uint2 load_nt(const uint2* p) {
+  const u32x2_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+  return uint2{x[0], x[1]};
+}
+__device__ inline uint32_t load_nt(const uint32_t* p) { return __builtin_nontemporal_load(p); }
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -307,7 +320,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(KT == k
       const raw* vp = vc + st.base[t] + int64_t(col) * bs + st.sub[t] + 4 * grp;
 #pragma unroll
       for (int n = 0; n < NT; ++n)
-        tl.v[t][n] = *reinterpret_cast<const typename TileT::VWord*>(vp + int64_t(16 * n) * bs);
+        tl.v[t][n] = load_nt(reinterpret_cast<const typename TileT::VWord*>(vp + int64_t(16 * n) * bs));
     }
   };
 

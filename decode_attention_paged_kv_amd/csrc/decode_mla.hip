@@ -113,11 +113,13 @@ __device__ inline void lds_barrier() {
 
 // 16-byte asynchronous copy HBM -> LDS (global_load_lds_dwordx4): lane i copies 16 B
 // from base + off_i; the 64 lanes' data land at consecutive 16-byte slots starting at
-// LDS byte address `lds_addr` (wave-uniform, passed in M0).  Issued through asm so the
+// LDS byte address `lds_addr` (wave-uniform, passed in M0).  The cache is read once per
+// step, so the copies use the non-temporal policy (`nt`), which streams random chunks
+// from HBM faster on this GPU.  Issued through asm so the
 // compiler does not attach its own conservative waits to later LDS reads; the kernel
 // waits for these copies explicitly with vmcnt before the barrier that publishes a tile.
 __device__ inline void copy16_to_lds(const char* base, uint32_t off, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
                :
                : "v"(off), "s"(base), "s"(lds_addr)
                : "memory", "m0");
@@ -350,7 +352,7 @@ void decode_mla_kernel(DecodeArgs a) {
       copy16_to_lds(cp.src, full_off[k], dst);
     } else {   // partial tile (a separate asm statement, so the two are not merged)
       const uint32_t off = slot_offset(k, cp.rows);
-      asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 ; partial tile"
+      asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt ; partial tile"
                    :
                    : "v"(off), "s"(cp.src), "s"(dst)
                    : "memory", "m0");
