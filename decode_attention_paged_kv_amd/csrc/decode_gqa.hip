@@ -63,19 +63,14 @@ typedef __bf16 bf16x8_t __attribute__((__vector_size__(8 * sizeof(__bf16))));
 typedef __bf16 bf16x2_t __attribute__((__vector_size__(2 * sizeof(__bf16))));
 typedef float f32x4_t __attribute__((__vector_size__(4 * sizeof(float))));
 typedef uint32_t u32x4_t __attribute__((__vector_size__(4 * sizeof(uint32_t))));
-typedef uint32_t u32x2_t __attribute__((__vector_size__(2 * sizeof(uint32_t))));
 
 // Value loads use the non-temporal policy (`nt`): the cache is read once per step, and on
 // this GPU `nt` streams random 2-16 KiB chunks from HBM ~11 % faster.  It pays only where
-// one load instruction covers whole 128-byte lines, as a value load does (16 d rows x all
+// one load instruction covers whole 128-byte lines, as a value load does (d rows x all
 // tokens of the sub-tile, contiguous).  A key load covers half of each token's line (the
 // other half comes with the next instruction), and under `nt` the long-context decode
 // measured 5 % slower with key loads included, 5 % faster without them.
-__device__ inline uint2 load_nt(const uint2* p) {
-  const u32x2_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
-  return uint2{x[0], x[1]};
-}
-__device__ inline uint32_t load_nt(const uint32_t* p) { return __builtin_nontemporal_load(p); }
+__device__ inline u32x4_t load_nt(const u32x4_t* p) { return __builtin_nontemporal_load(p); }
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -136,9 +131,11 @@ struct Tile {
   // bf16: one 16-byte word per score MFMA; E4M3: the lane's D/4 key bytes
   static constexpr int KW = F8 ? D / 64 : KJ;
   u32x4_t k[SUBS][KW];
-  // 4 tokens of one d row: 8 bytes (bf16) or 4 (E4M3)
-  using VWord = typename std::conditional<F8, uint32_t, uint2>::type;
-  VWord v[SUBS][NT];
+  // Values: each lane loads 16 bytes of a d row, so one load instruction reads 1 KiB of
+  // whole d rows (contiguous when a block holds 16 tokens); the bytes are then handed to
+  // the lanes whose operand needs them (value_pairs, value_words).  bf16: group q covers output tiles 2q, 2q+1; E4M3: tiles 4q .. 4q+3.
+  static constexpr int NV = F8 ? NT / 4 : NT / 2;
+  u32x4_t v[SUBS][NV];
 
   // key operand of score MFMA j of sub-tile t
   __device__ inline bf16x8_t key(int t, int j) const {
@@ -153,12 +150,38 @@ struct Tile {
       return __builtin_bit_cast(bf16x8_t, k[t][j]);
     }
   }
-  // 4 tokens of d row 16n + col of sub-tile t, as bf16
-  __device__ inline uint2 value(int t, int n) const {
-    if constexpr (F8) {
-      return uint2{e4m3x2_to_bf16x2<false>(v[t][n]), e4m3x2_to_bf16x2<true>(v[t][n])};
-    } else {
-      return v[t][n];
+  // bf16: w[n] = tokens 4 grp .. 4 grp + 3 of d row 16n + col of sub-tile t (the lane's
+  // operand words for output tile n).  Lane row 2a + b loaded tokens 8b .. 8b + 7 of d row
+  // 16(2q + a) + col.  Lane row g needs, for tile 2q + h, dwords 2(g & 1) and 2(g & 1) + 1
+  // of lane row 2h + (g >> 1): the bits (a, b, dword pair) must become (b, pair, h), which
+  // a 16-lane swap (row bit b <-> register bit) and then a 32-lane swap (row bit a <->
+  // register bit) do for each dword of the pair.
+  __device__ inline void value_pairs(int t, uint2 (&w)[NT]) const {
+#pragma unroll
+    for (int q = 0; q < NV; ++q) {
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const auto a = __builtin_amdgcn_permlane16_swap(v[t][q][k], v[t][q][2 + k], false, false);
+        const auto b = __builtin_amdgcn_permlane32_swap(a[0], a[1], false, false);
+        if (k == 0) { w[2 * q].x = b[0]; w[2 * q + 1].x = b[1]; }
+        else { w[2 * q].y = b[0]; w[2 * q + 1].y = b[1]; }
+      }
+    }
+  }
+  // E4M3: w[n] = the 4 codes (tokens 4 grp .. 4 grp + 3) of d row 16n + col of sub-tile
+  // t.  For group q the four 16-lane rows hold a 4 x 4 block of dwords (row h: d row
+  // 16(4q + h) + col, dword g: tokens 4g .. 4g + 3); transposing it across the rows, by
+  // 32-lane swaps and then 16-lane swaps, leaves row g with dword g of every row.
+  __device__ inline void value_words(int t, uint32_t (&w)[NT]) const {
+#pragma unroll
+    for (int q = 0; q < NV; ++q) {
+      uint32_t r0 = v[t][q][0], r1 = v[t][q][1], r2 = v[t][q][2], r3 = v[t][q][3];
+      const auto a = __builtin_amdgcn_permlane32_swap(r0, r2, false, false);
+      const auto b = __builtin_amdgcn_permlane32_swap(r1, r3, false, false);
+      r0 = a[0], r2 = a[1], r1 = b[0], r3 = b[1];
+      const auto c = __builtin_amdgcn_permlane16_swap(r0, r1, false, false);
+      const auto d = __builtin_amdgcn_permlane16_swap(r2, r3, false, false);
+      w[4 * q + 0] = c[0], w[4 * q + 1] = c[1], w[4 * q + 2] = d[0], w[4 * q + 3] = d[1];
     }
   }
 };
@@ -317,10 +340,20 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(KT == k
   auto load_v = [&](TileT& tl, const StepT& st) {
 #pragma unroll
     for (int t = 0; t < SUBS; ++t) {
-      const raw* vp = vc + st.base[t] + int64_t(col) * bs + st.sub[t] + 4 * grp;
+      // 16 bytes per lane rather than the 4 (E4M3) or 8 (bf16) its operand takes: loads
+      // of 256 or 512 bytes per instruction measured slower (E4M3: 0.455 vs 0.378 ms on
+      // the long-context batch; bf16: 0.744 vs 0.717 ms)
+      if constexpr (F8) {
+        const raw* vp = vc + st.base[t] + int64_t(16 * grp + col) * bs + st.sub[t];
 #pragma unroll
-      for (int n = 0; n < NT; ++n)
-        tl.v[t][n] = load_nt(reinterpret_cast<const typename TileT::VWord*>(vp + int64_t(16 * n) * bs));
+        for (int q = 0; q < TileT::NV; ++q)
+          tl.v[t][q] = load_nt(reinterpret_cast<const u32x4_t*>(vp + int64_t(64 * q) * bs));
+      } else {
+        const raw* vp = vc + st.base[t] + int64_t(16 * (grp >> 1) + col) * bs + st.sub[t] + 8 * (grp & 1);
+#pragma unroll
+        for (int q = 0; q < TileT::NV; ++q)
+          tl.v[t][q] = load_nt(reinterpret_cast<const u32x4_t*>(vp + int64_t(32 * q) * bs));
+      }
     }
   };
 
@@ -404,9 +437,25 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(KT == k
           phi[4 * t + i] = h;
           plo[4 * t + i] = (__bf16)(pv[t2 + t][i] - (float)h);
         }
+      uint32_t wa[NT], wb[NT];
+      uint2 pa[NT], pb[NT];
+      if constexpr (F8) {
+        tl.value_words(t2, wa);
+        tl.value_words(t2 + 1, wb);
+      } else {
+        tl.value_pairs(t2, pa);
+        tl.value_pairs(t2 + 1, pb);
+      }
 #pragma unroll
       for (int n = 0; n < NT; ++n) {
-        uint2 va = tl.value(t2, n), vb = tl.value(t2 + 1, n);
+        uint2 va, vb;
+        if constexpr (F8) {
+          va = uint2{e4m3x2_to_bf16x2<false>(wa[n]), e4m3x2_to_bf16x2<true>(wa[n])};
+          vb = uint2{e4m3x2_to_bf16x2<false>(wb[n]), e4m3x2_to_bf16x2<true>(wb[n])};
+        } else {
+          va = pa[n];
+          vb = pb[n];
+        }
         if (!__all(full)) {
           va.x = keep(va.x, ok[t2][0], ok[t2][1]);
           va.y = keep(va.y, ok[t2][2], ok[t2][3]);
