@@ -7,7 +7,8 @@
 // Parts with lse_p = -inf are empty and skipped (no -inf - -inf is ever formed); their
 // part_out rows are never read.
 //
-// One workgroup per (sequence, head).
+// One workgroup per (sequence, head) and column block; one wave per (sequence, head)
+// when there are at most 16 parts.
 #include <math.h>
 
 #include "pa_common.h"
@@ -140,6 +141,91 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const float* __restrict
   if (lse_out && threadIdx.x == 0 && blockIdx.y == 0) lse_out[int64_t(b) * hq + h] = total;
 }
 
+// Few parts (at most 16): one wave per (sequence, head), no LDS and no barrier, so the
+// dependent steps are one lse load, the cross-lane reductions and one round of output
+// loads.  Lane p holds part p's lse; the max and the sum of weights are cross-lane
+// reductions; then the wave walks the non-empty parts (a uniform loop, each weight read
+// from its lane) with VEC columns per lane and eight parts' loads in flight at once.
+constexpr int kSmallParts = 16;   // measured: with ~50 parts per row it is slower
+constexpr int kInFlight = 8;      // parts whose loads are issued together
+
+__device__ inline float wave_max(float v) {
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ inline float wave_sum(float v) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+template <int VEC>
+__global__ __launch_bounds__(256) void merge_small_kernel(const float* __restrict__ part_out,
+                                                          const float* __restrict__ part_lse,
+                                                          int n_rows, int n_parts, int hq, int dv,
+                                                          void* out, int out_dtype, float* lse_out) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= n_rows) return;   // the whole wave
+  const int lane = threadIdx.x & 63;
+  const int b = row / hq, h = row - (row / hq) * hq;
+  const float* lse_p = part_lse + int64_t(b) * n_parts * hq + h;        // stride hq
+  const float* o_p = part_out + (int64_t(b) * n_parts * hq + h) * dv;   // stride hq*dv
+  const int64_t stride = int64_t(hq) * dv;
+
+  const float x = lane < n_parts ? lse_p[int64_t(lane) * hq] : -INFINITY;
+  const float m = wave_max(x);
+  float total = -INFINITY, w = 0.f;
+  if (m != -INFINITY) {
+    total = m + logf(wave_sum(x != -INFINITY ? expf(x - m) : 0.f));
+    if (x != -INFINITY) w = expf(x - total);
+  }
+  const uint64_t live = __ballot(w != 0.f);
+
+  const int64_t orow = int64_t(row) * dv;
+  for (int c = lane * VEC; c < dv; c += 64 * VEC) {
+    float acc[VEC];
+#pragma unroll
+    for (int k = 0; k < VEC; ++k) acc[k] = 0.f;
+    uint64_t todo = live;
+    while (todo) {
+      // up to kInFlight parts at once: their loads are independent
+      int ps[kInFlight];
+      float ws[kInFlight];
+#pragma unroll
+      for (int u = 0; u < kInFlight; ++u) {
+        ps[u] = todo ? __builtin_ctzll(todo) : -1;
+        if (todo) todo &= todo - 1;
+        // ps[u] is wave-uniform and readlane ignores the exec mask, so the broadcast also
+        // works in the lanes that have left the column loop
+        ws[u] = ps[u] >= 0 ? __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(w), ps[u])) : 0.f;
+      }
+      float v[kInFlight][VEC];
+#pragma unroll
+      for (int u = 0; u < kInFlight; ++u) {
+        const float* sp = o_p + int64_t(ps[u] >= 0 ? ps[u] : ps[0]) * stride + c;
+        if constexpr (VEC == 4) {
+          const float4 t = *reinterpret_cast<const float4*>(sp);
+          v[u][0] = t.x, v[u][1 % VEC] = t.y, v[u][2 % VEC] = t.z, v[u][3 % VEC] = t.w;
+        } else {
+#pragma unroll
+          for (int k = 0; k < VEC; ++k) v[u][k] = sp[k];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kInFlight; ++u)
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) acc[k] = fmaf(ws[u], v[u][k], acc[k]);
+    }
+#pragma unroll
+    for (int k = 0; k < VEC; ++k) {
+      if (out_dtype == kF32)
+        static_cast<float*>(out)[orow + c + k] = acc[k];
+      else
+        static_cast<uint16_t*>(out)[orow + c + k] = f32_to_bf16_bits(acc[k]);
+    }
+  }
+  if (lse_out && lane == 0) lse_out[row] = total;
+}
+
 }  // namespace
 
 hipError_t launch_merge(const float* part_out, const float* part_lse, int n_seqs, int n_parts,
@@ -148,6 +234,17 @@ hipError_t launch_merge(const float* part_out, const float* part_lse, int n_seqs
   // (sequence, head) rows to spread over the GPU; otherwise wide (at most 128 column
   // groups per workgroup), so each workgroup has enough work.
   const int vec = dv % 4 == 0 ? 4 : 1;
+  if (n_parts <= kSmallParts) {
+    const int rows = n_seqs * hq;
+    const dim3 g((rows + 3) / 4);
+    if (vec == 4)
+      hipLaunchKernelGGL(merge_small_kernel<4>, g, dim3(256), 0, st, part_out, part_lse, rows,
+                         n_parts, hq, dv, out, out_dtype, lse);
+    else
+      hipLaunchKernelGGL(merge_small_kernel<1>, g, dim3(256), 0, st, part_out, part_lse, rows,
+                         n_parts, hq, dv, out, out_dtype, lse);
+    return hipGetLastError();
+  }
   int cb = 128 * vec;
   if (int64_t(n_seqs) * hq < 1024) cb = 8 * vec;
   if (cb > dv) cb = dv;
