@@ -115,13 +115,17 @@ def time_gpu(w, T, step, steps, warmup, settle_s=SETTLE_S):
         qs = T["query_start"]
         args = (T["q"], qs, T["k_new"], T["v_new"], T["k_cache"], T["v_cache"], T["block_table"],
                 T["context_lens"], ks, vs)
-        route = lambda: step.route(T["block_table"], T["context_lens"], qs, nb)
+        def prepare():   # routing, then the append
+            step.route(T["block_table"], T["context_lens"], qs, nb)
+            step.append(T["k_new"], T["v_new"], T["k_cache"], T["v_cache"], ks, vs)
         attend = lambda: step.attend(T["q"], qs, T["k_cache"], T["v_cache"], T["block_table"],
                                      T["context_lens"], ks, vs)
     else:
         args = (T["q"], T["k_new"], T["v_new"], T["k_cache"], T["v_cache"], T["block_table"],
                 T["context_lens"], ks, vs)
-        route = lambda: step.route(T["block_table"], T["context_lens"], nb)
+        def prepare():   # routing and append in one launch
+            step.route_append(T["k_new"], T["v_new"], T["k_cache"], T["v_cache"], T["block_table"],
+                              T["context_lens"], ks, vs)
         attend = lambda: step.attend(T["q"], T["k_cache"], T["v_cache"], T["block_table"],
                                      T["context_lens"], ks, vs)
     for _ in range(warmup):
@@ -143,8 +147,7 @@ def time_gpu(w, T, step, steps, warmup, settle_s=SETTLE_S):
     wall0 = time.perf_counter()
     t0.record()
     for i in range(steps):
-        route()
-        step.append(T["k_new"], T["v_new"], T["k_cache"], T["v_cache"], ks, vs)
+        prepare()
         ev[i][0].record()
         attend()
         ev[i][1].record()
@@ -181,8 +184,7 @@ def time_gpu(w, T, step, steps, warmup, settle_s=SETTLE_S):
         sink.add_(flush.sum())
         a, b, c, d = (torch.cuda.Event(enable_timing=True) for _ in range(4))
         a.record()
-        route()
-        step.append(T["k_new"], T["v_new"], T["k_cache"], T["v_cache"], ks, vs)
+        prepare()
         b.record()
         attend()
         c.record()

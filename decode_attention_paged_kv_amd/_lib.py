@@ -46,6 +46,8 @@ _SIGS = {
     "pa_decode_multi": [_p, _i32, _p, _i32, _i32, _p, _p, _i32, _p, _p, _i32, _p, _p, _i32, _i32, _i32,
                         _i32, _i32, _i32, _i64, _i32, _i32, _i32, _i32, _i32, _f32, _p, _p, _p, _p],
     "pa_copy_blocks": [_p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i64, _i32, _p, _p],
+    "pa_kv_append_routed": [_p, _p, _i32, _p, _p, _i32, _p, _p, _i32, _p, _p, _i32, _i32, _i32, _i32,
+                            _i32, _i64, _i32, _i32, _i32, _p, _p, _p],
     "pa_pool_add": [_p, _i64, _i64],
     "pa_pool_append": [_p, _i64, _i64, _p, _i32, _p],
     "pa_pool_fork": [_p, _i64, _i64],
@@ -241,6 +243,42 @@ def pa_kv_append_fp8(k_new, v_new, k_cache, v_cache, k_scale, v_scale, slot_mapp
     _check(lib.pa_kv_append_fp8(_ptr(k_new), _ptr(v_new), _dtype_code(k_new), _ptr(k_cache),
                                 _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), ns, _ptr(slot_mapping),
                                 n, hkv, dk, dv, bs, nb, _ptr(err_flag), _stream(k_cache)))
+
+
+def pa_kv_append_routed(k_new, v_new, k_cache, v_cache, block_table, context_lens, n_shards,
+                        interleave, k_scale=None, v_scale=None, slot_mapping=None, err_flag=None):
+    """Routing and append in one launch (one new token per sequence); ``slot_mapping``
+    (int64 [n_seqs], optional) receives the slots.  A uint8 cache holds E4M3 codes and
+    takes its scales."""
+    _need(k_new, None, 3, "k_new")
+    _need(k_cache, None, 4, "k_cache")
+    _need(v_new, k_new.dtype, 3, "v_new")
+    _need(v_cache, k_cache.dtype, 4, "v_cache")
+    _need(block_table, torch.int32, 3, "block_table")
+    _need(context_lens, torch.int32, 1, "context_lens")
+    _need(slot_mapping, torch.int64, 1, "slot_mapping")
+    _need(err_flag, torch.int32, None, "err_flag")
+    n, hkv, dk = k_new.shape
+    nb, hkv2, bs, dk2 = k_cache.shape
+    dv = 0 if v_new is None else v_new.shape[2]
+    if hkv2 != hkv or dk2 != dk or context_lens.shape[0] != n or block_table.shape[0] != n:
+        raise ValueError("k_new / k_cache / block_table / context_lens shapes disagree")
+    if block_table.shape[1] != n_shards:
+        raise ValueError(f"block_table must be [n_seqs][{n_shards}][max_blocks]")
+    if slot_mapping is not None and slot_mapping.shape[0] != n:
+        raise ValueError("slot_mapping must be [n_seqs]")
+    if v_cache is not None and tuple(v_cache.shape) != (nb, hkv, dv, bs):
+        raise ValueError("v_cache must be [n_blocks][n_kv_heads][dv][block_size]")
+    ns = 0
+    if k_cache.dtype == torch.uint8:
+        ns = _scales(k_scale, v_scale, hkv, v_cache is None)
+    elif k_cache.dtype != k_new.dtype:
+        raise TypeError("k_new must have the cache's element type (or the cache be uint8 codes)")
+    _check(lib.pa_kv_append_routed(_ptr(k_new), _ptr(v_new), _dtype_code(k_new), _ptr(k_cache),
+                                   _ptr(v_cache), _dtype_code(k_cache, cache=True), _ptr(k_scale),
+                                   _ptr(v_scale), ns, _ptr(block_table), _ptr(context_lens), n, hkv,
+                                   dk, dv, bs, nb, block_table.shape[2], n_shards, interleave,
+                                   _ptr(slot_mapping), _ptr(err_flag), _stream(k_cache)))
 
 
 def pa_decode_fp8(q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens, n_shards,

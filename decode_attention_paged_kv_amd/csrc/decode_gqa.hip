@@ -12,18 +12,23 @@
 //  * One workgroup = one (partition, sequence x shard, KV head, 16 columns); a column
 //    is a query head of the KV head's group, or, with several new tokens per sequence,
 //    a (new token, query head) pair -- then each column also has its own causal end
-//    (the new token sees the tokens up to its own position).  Its NW waves split the partition's 16-token sub-tiles into contiguous
-//    ranges and merge their (max, sum, output) through LDS at the end.  Each K/V byte
-//    is read by exactly one wave, so K/V go straight from HBM into registers (no LDS
-//    staging: there is no reuse to stage for).
+//    (the new token sees the tokens up to its own position).  Its NW waves split the
+//    partition's 16-token sub-tiles into contiguous ranges and merge their (max, sum,
+//    output) through LDS at the end.  Each K/V byte is read by exactly one wave, so K/V
+//    go straight from HBM into registers (no LDS staging: there is no reuse to stage
+//    for).
 //  * Scores S^T[token][head] = K (16 x D) . Q^T (D x 16) on v_mfma_f32_16x16x32_bf16:
 //    lane (row = lane % 16, group = lane / 16) supplies 8 consecutive head-dim values
 //    of key row `row` -- one 16-byte load per MFMA -- and the result leaves scores of
 //    tokens 4*group .. 4*group+3 for head lane % 16 in each lane.
 //  * Output O^T[d][head] += V^T (16 x 32 tokens) . P^T (32 tokens x 16 heads) on the
-//    same instruction.  The value cache stores each block as [d][token], so a lane's
-//    operand (4 tokens of one d row, per 16-token sub-tile) is one 8-byte load, and the
-//    weights P^T a lane needs are exactly the scores it already holds: no shuffles.
+//    same instruction.  The value cache stores each block as [d][token]; a lane's
+//    operand is 4 tokens of one d row per 16-token sub-tile, and the weights P^T it
+//    needs are exactly the scores it already holds (no shuffles for them).  Values are
+//    loaded 16 bytes per lane -- whole d rows, 1 KiB per load instruction -- and handed
+//    to the lanes whose operand needs them by lane-row swaps (Tile::value_pairs,
+//    Tile::value_words); narrower loads streamed measurably slower from HBM.  Value
+//    loads take the non-temporal cache policy, key loads the default one.
 //  * The softmax weights enter P.V as two bf16 terms, hi = bf16(p) and
 //    lo = bf16(p - hi), so they keep ~16 significant bits; K, V and q are used exactly.
 //  * Online softmax in base 2: scores stay raw, p = exp2(s*c - m*c) with

@@ -20,22 +20,26 @@
 namespace pa {
 namespace {
 
+// Slot of sequence b's new token, the last of its L context tokens (global position
+// L - 1): its shard and local index by the interleave rule, its block through that
+// shard's table row.  -1 for an empty sequence or an unusable table entry (flagged).
+__device__ inline int64_t new_token_slot(const int32_t* __restrict__ bt, int L, int b, int S, int I,
+                                         int bs, int max_blocks, int64_t n_blocks, int* flag) {
+  if (L <= 0) return -1;
+  const int i = L - 1;
+  const int r = shard_of(i, S, I);
+  const int t = local_index(i, S, I);
+  const int32_t* row = bt + (int64_t(b) * S + r) * max_blocks;
+  const int64_t phys = table_block(row, t / bs, max_blocks, n_blocks, flag);
+  return phys >= 0 ? phys * bs + t % bs : -1;
+}
+
 __global__ void slot_mapping_kernel(const int32_t* __restrict__ bt, const int32_t* __restrict__ lens,
                                     int n_seqs, int S, int I, int bs, int max_blocks,
                                     int64_t n_blocks, int64_t* __restrict__ slots, int* flag) {
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
   if (b >= n_seqs) return;
-  const int L = lens[b];
-  int64_t slot = -1;
-  if (L > 0) {
-    const int i = L - 1;
-    const int r = shard_of(i, S, I);
-    const int t = local_index(i, S, I);
-    const int32_t* row = bt + (int64_t(b) * S + r) * max_blocks;
-    const int64_t phys = table_block(row, t / bs, max_blocks, n_blocks, flag);
-    if (phys >= 0) slot = phys * bs + t % bs;
-  }
-  slots[b] = slot;
+  slots[b] = new_token_slot(bt, lens[b], b, S, I, bs, max_blocks, n_blocks, flag);
 }
 
 // Slots of several new tokens per sequence: new token i of the last n sits at global
@@ -72,6 +76,23 @@ __global__ void slot_mapping_multi_kernel(const int32_t* __restrict__ bt,
   }
 }
 
+// Row n, KV head h of the new keys/values into slot `slot` (a valid one), bit for bit.
+template <typename RAW>
+__device__ inline void append_row(const RAW* __restrict__ k_new, const RAW* __restrict__ v_new,
+                                  RAW* __restrict__ k_cache, RAW* __restrict__ v_cache, int n, int h,
+                                  int64_t slot, int hkv, int dk, int dv, int bs) {
+  const int64_t blk = slot / bs;
+  const int off = int(slot % bs);
+  const RAW* ks = k_new + (int64_t(n) * hkv + h) * dk;
+  RAW* kd = k_cache + ((blk * hkv + h) * bs + off) * dk;
+  for (int e = threadIdx.x; e < dk; e += blockDim.x) kd[e] = ks[e];
+  if (v_cache != nullptr) {
+    const RAW* vs = v_new + (int64_t(n) * hkv + h) * dv;
+    RAW* vd = v_cache + (blk * hkv + h) * int64_t(dv) * bs + off;
+    for (int d = threadIdx.x; d < dv; d += blockDim.x) vd[int64_t(d) * bs] = vs[d];
+  }
+}
+
 template <typename RAW>
 __global__ void kv_append_kernel(const RAW* __restrict__ k_new, const RAW* __restrict__ v_new,
                                  RAW* __restrict__ k_cache, RAW* __restrict__ v_cache,
@@ -85,40 +106,20 @@ __global__ void kv_append_kernel(const RAW* __restrict__ k_new, const RAW* __res
     if (threadIdx.x == 0) raise_flag(flag, kErrSlot);
     return;
   }
-  const int64_t blk = slot / bs;
-  const int off = int(slot % bs);
-  const RAW* ks = k_new + (int64_t(n) * hkv + h) * dk;
-  RAW* kd = k_cache + ((blk * hkv + h) * bs + off) * dk;
-  for (int e = threadIdx.x; e < dk; e += blockDim.x) kd[e] = ks[e];
-  if (v_cache != nullptr) {
-    const RAW* vs = v_new + (int64_t(n) * hkv + h) * dv;
-    RAW* vd = v_cache + (blk * hkv + h) * int64_t(dv) * bs + off;
-    for (int d = threadIdx.x; d < dv; d += blockDim.x) vd[int64_t(d) * bs] = vs[d];
-  }
+  append_row(k_new, v_new, k_cache, v_cache, n, h, slot, hkv, dk, dv, bs);
 }
 
 // E4M3 cache: each element of the new rows becomes the code of element / scale (the
 // scale of its KV head, or the tensor's), rounded as f32_to_e4m3 describes.  The
 // division is IEEE (correctly rounded), so the code is a function of the inputs alone.
 template <int DT>
-__global__ void kv_append_fp8_kernel(const void* __restrict__ k_new_, const void* __restrict__ v_new_,
-                                     uint8_t* __restrict__ k_cache, uint8_t* __restrict__ v_cache,
-                                     const float* __restrict__ k_scale,
-                                     const float* __restrict__ v_scale, int n_scales,
-                                     const int64_t* __restrict__ slots, int hkv, int dk, int dv,
-                                     int bs, int64_t n_blocks, int* flag) {
+__device__ inline void append_row_fp8(const typename Elem<DT>::raw* __restrict__ k_new,
+                                      const typename Elem<DT>::raw* __restrict__ v_new,
+                                      uint8_t* __restrict__ k_cache, uint8_t* __restrict__ v_cache,
+                                      const float* __restrict__ k_scale,
+                                      const float* __restrict__ v_scale, int n_scales, int n, int h,
+                                      int64_t slot, int hkv, int dk, int dv, int bs) {
   using E = Elem<DT>;
-  using raw = typename E::raw;
-  const raw* k_new = static_cast<const raw*>(k_new_);
-  const raw* v_new = static_cast<const raw*>(v_new_);
-  const int n = blockIdx.x;
-  const int h = blockIdx.y;
-  const int64_t slot = slots[n];
-  if (slot < 0) return;
-  if (slot >= n_blocks * bs) {
-    if (threadIdx.x == 0) raise_flag(flag, kErrSlot);
-    return;
-  }
   const int64_t blk = slot / bs;
   const int off = int(slot % bs);
   const int si = n_scales > 1 ? h : 0;
@@ -133,6 +134,63 @@ __global__ void kv_append_fp8_kernel(const void* __restrict__ k_new_, const void
     for (int d = threadIdx.x; d < dv; d += blockDim.x)
       vd[int64_t(d) * bs] = f32_to_e4m3(__fdiv_rn(E::load(v_new, vsrc + d), vs));
   }
+}
+
+template <int DT>
+__global__ void kv_append_fp8_kernel(const void* __restrict__ k_new_, const void* __restrict__ v_new_,
+                                     uint8_t* __restrict__ k_cache, uint8_t* __restrict__ v_cache,
+                                     const float* __restrict__ k_scale,
+                                     const float* __restrict__ v_scale, int n_scales,
+                                     const int64_t* __restrict__ slots, int hkv, int dk, int dv,
+                                     int bs, int64_t n_blocks, int* flag) {
+  using raw = typename Elem<DT>::raw;
+  const raw* k_new = static_cast<const raw*>(k_new_);
+  const raw* v_new = static_cast<const raw*>(v_new_);
+  const int n = blockIdx.x;
+  const int h = blockIdx.y;
+  const int64_t slot = slots[n];
+  if (slot < 0) return;
+  if (slot >= n_blocks * bs) {
+    if (threadIdx.x == 0) raise_flag(flag, kErrSlot);
+    return;
+  }
+  append_row_fp8<DT>(k_new, v_new, k_cache, v_cache, k_scale, v_scale, n_scales, n, h, slot, hkv,
+                     dk, dv, bs);
+}
+
+// One launch for a decode step's append: workgroup (b, h) finds sequence b's new-token
+// slot as slot_mapping_kernel does (optionally recording it) and writes that token's
+// rows of KV head h as kv_append_kernel / kv_append_fp8_kernel do.  F8: an E4M3 cache
+// (rows of element type DT quantised); otherwise a plain copy of DT rows.
+template <int DT, bool F8>
+__global__ void kv_append_routed_kernel(const void* __restrict__ k_new, const void* __restrict__ v_new,
+                                        void* __restrict__ k_cache, void* __restrict__ v_cache,
+                                        const float* __restrict__ k_scale,
+                                        const float* __restrict__ v_scale, int n_scales,
+                                        const int32_t* __restrict__ bt, const int32_t* __restrict__ lens,
+                                        int S, int I, int max_blocks, int hkv, int dk, int dv, int bs,
+                                        int64_t n_blocks, int64_t* __restrict__ slots_out, int* flag) {
+  const int b = blockIdx.x;
+  const int h = blockIdx.y;
+  __shared__ int64_t slot_s;
+  if (threadIdx.x == 0) {
+    // every KV head's workgroup resolves the slot; only head 0's reports table errors
+    const int64_t slot =
+        new_token_slot(bt, lens[b], b, S, I, bs, max_blocks, n_blocks, h == 0 ? flag : nullptr);
+    slot_s = slot;
+    if (h == 0 && slots_out != nullptr) slots_out[b] = slot;
+  }
+  __syncthreads();
+  const int64_t slot = slot_s;
+  if (slot < 0) return;
+  using raw = typename Elem<DT>::raw;
+  if constexpr (F8)
+    append_row_fp8<DT>(static_cast<const raw*>(k_new), static_cast<const raw*>(v_new),
+                       static_cast<uint8_t*>(k_cache), static_cast<uint8_t*>(v_cache), k_scale,
+                       v_scale, n_scales, b, h, slot, hkv, dk, dv, bs);
+  else
+    append_row(static_cast<const raw*>(k_new), static_cast<const raw*>(v_new),
+               static_cast<raw*>(k_cache), static_cast<raw*>(v_cache), b, h, slot, hkv, dk, dv, bs);
 }
 
 template <typename RAW>
@@ -261,6 +319,26 @@ hipError_t launch_kv_append(const void* k_new, const void* v_new, void* k_cache,
                        (const uint16_t*)k_new, (const uint16_t*)v_new, (uint16_t*)k_cache,
                        (uint16_t*)v_cache, slots, hkv, dk, dv, bs, n_blocks, flag);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_append_routed(const void* k_new, const void* v_new, int new_dtype,
+                                   void* k_cache, void* v_cache, int cache_dtype,
+                                   const float* k_scale, const float* v_scale, int n_scales,
+                                   const int32_t* bt, const int32_t* lens, int n_seqs, int S, int I,
+                                   int max_blocks, int hkv, int dk, int dv, int bs,
+                                   int64_t n_blocks, int64_t* slots_out, int* flag,
+                                   hipStream_t st) {
+  const dim3 grid(n_seqs, hkv);
+  const auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, grid, dim3(64), 0, st, k_new, v_new, k_cache, v_cache, k_scale,
+                       v_scale, n_scales, bt, lens, S, I, max_blocks, hkv, dk, dv, bs, n_blocks,
+                       slots_out, flag);
+  };
+  if (cache_dtype == kFP8)
+    new_dtype == kF32 ? go(kv_append_routed_kernel<kF32, true>) : go(kv_append_routed_kernel<kBF16, true>);
+  else
+    cache_dtype == kF32 ? go(kv_append_routed_kernel<kF32, false>) : go(kv_append_routed_kernel<kBF16, false>);
   return hipGetLastError();
 }
 

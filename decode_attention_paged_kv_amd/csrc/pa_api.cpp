@@ -309,6 +309,49 @@ int pa_kv_append_fp8(const void* k_new, const void* v_new, int32_t new_dtype, ui
                     "pa_kv_append_fp8 launch");
 }
 
+int pa_kv_append_routed(const void* k_new, const void* v_new, int32_t new_dtype, void* k_cache,
+                        void* v_cache, int32_t cache_dtype, const float* k_scale,
+                        const float* v_scale, int32_t n_scales, const int32_t* block_table,
+                        const int32_t* context_lens, int32_t n_seqs, int32_t n_kv_heads, int32_t dk,
+                        int32_t dv, int32_t block_size, int64_t n_blocks,
+                        int32_t max_blocks_per_shard, int32_t n_shards, int32_t interleave,
+                        int64_t* slot_mapping, int32_t* err_flag, void* stream) {
+  REQUIRE(k_new && k_cache && block_table && context_lens, PA_ERR_NULL,
+          "pa_kv_append_routed: k_new, k_cache, block_table and context_lens must be non-NULL");
+  REQUIRE((v_new == nullptr) == (v_cache == nullptr), PA_ERR_NULL,
+          "pa_kv_append_routed: v_new and v_cache must both be NULL (latent cache) or both non-NULL");
+  REQUIRE(valid_dtype(new_dtype), PA_ERR_UNSUPPORTED, "new_dtype=%d is not PA_F32 or PA_BF16",
+          new_dtype);
+  REQUIRE(valid_cache_dtype(cache_dtype), PA_ERR_UNSUPPORTED,
+          "cache_dtype=%d is not PA_F32, PA_BF16 or PA_FP8_E4M3", cache_dtype);
+  REQUIRE(cache_dtype == PA_FP8_E4M3 || cache_dtype == new_dtype, PA_ERR_UNSUPPORTED,
+          "new_dtype=%d must equal cache_dtype=%d (or the cache be PA_FP8_E4M3)", new_dtype,
+          cache_dtype);
+  if (cache_dtype == PA_FP8_E4M3) {
+    REQUIRE(k_scale && (v_cache == nullptr || v_scale), PA_ERR_NULL,
+            "pa_kv_append_routed: an E4M3 cache needs k_scale (and v_scale with a value cache)");
+    REQUIRE(n_scales == 1 || n_scales == n_kv_heads, PA_ERR_SHAPE,
+            "n_scales=%d must be 1 or n_kv_heads=%d", n_scales, n_kv_heads);
+  }
+  REQUIRE(n_seqs >= 0 && n_seqs <= (1 << 30), PA_ERR_SHAPE, "n_seqs=%d out of range", n_seqs);
+  REQUIRE(n_kv_heads >= 1 && n_kv_heads <= 65535, PA_ERR_SHAPE, "n_kv_heads=%d out of range", n_kv_heads);
+  REQUIRE(dk >= 1 && dk <= PA_MAX_HEAD_DIM, PA_ERR_UNSUPPORTED, "dk=%d must be in [1, %d]", dk, PA_MAX_HEAD_DIM);
+  REQUIRE(v_cache == nullptr || (dv >= 1 && dv <= PA_MAX_HEAD_DIM), PA_ERR_UNSUPPORTED,
+          "dv=%d must be in [1, %d]", dv, PA_MAX_HEAD_DIM);
+  if (int rc = check_placement(n_shards, interleave, block_size)) return rc;
+  REQUIRE(max_blocks_per_shard >= 1 && n_blocks >= 1, PA_ERR_SHAPE,
+          "max_blocks_per_shard=%d and n_blocks=%lld must be >= 1", max_blocks_per_shard,
+          (long long)n_blocks);
+  if (n_seqs == 0) return ok();
+  return hip_status(pa::launch_kv_append_routed(k_new, v_new, new_dtype, k_cache, v_cache,
+                                                cache_dtype, k_scale, v_scale, n_scales, block_table,
+                                                context_lens, n_seqs, n_shards, interleave,
+                                                max_blocks_per_shard, n_kv_heads, dk, dv, block_size,
+                                                n_blocks, slot_mapping, err_flag,
+                                                (hipStream_t)stream),
+                    "pa_kv_append_routed launch");
+}
+
 }  // extern "C"
 
 namespace {

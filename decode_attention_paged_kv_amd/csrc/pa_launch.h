@@ -47,6 +47,14 @@ hipError_t launch_kv_append_fp8(const void* k_new, const void* v_new, int new_dt
                                 const float* v_scale, int n_scales, const int64_t* slots,
                                 int n_tokens, int hkv, int dk, int dv, int bs, int64_t n_blocks,
                                 int* flag, hipStream_t st);
+// Routing and append in one launch (one new token per sequence); slots_out may be null.
+hipError_t launch_kv_append_routed(const void* k_new, const void* v_new, int new_dtype,
+                                   void* k_cache, void* v_cache, int cache_dtype,
+                                   const float* k_scale, const float* v_scale, int n_scales,
+                                   const int32_t* bt, const int32_t* lens, int n_seqs, int S, int I,
+                                   int max_blocks, int hkv, int dk, int dv, int bs,
+                                   int64_t n_blocks, int64_t* slots_out, int* flag,
+                                   hipStream_t st);
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int64_t* pairs, int n_pairs,
                               int64_t k_bytes, int64_t v_bytes, int64_t n_blocks, int* flag,
                               hipStream_t st);

@@ -1,7 +1,8 @@
 """One decode step on one stream: slot routing, kv append, attention, LSE merge.
 
 ``DecodeStep`` owns the step's output and scratch tensors (allocated once, with
-torch, for a maximum context length) and issues the four library calls.  A cache of
+torch, for a maximum context length) and issues the library calls: routing and append
+in one launch, then attention and merge.  A cache of
 ``torch.uint8`` holds E4M3 codes and takes its scales with each call (the ``_fp8``
 entry points).
 """
@@ -53,6 +54,14 @@ class DecodeStep:
         else:
             L.pa_kv_append(k_new, v_new, k_cache, v_cache, self.slot_mapping, self.err_flag)
 
+    def route_append(self, k_new, v_new, k_cache, v_cache, block_table, context_lens,
+                     k_scale=None, v_scale=None):
+        """route() and append() in one launch (``pa_kv_append_routed``); the slots still
+        land in ``slot_mapping``."""
+        L.pa_kv_append_routed(k_new, v_new, k_cache, v_cache, block_table, context_lens,
+                              self.n_shards, self.interleave, k_scale, v_scale, self.slot_mapping,
+                              self.err_flag)
+
     def attend(self, q, k_cache, v_cache, block_table, context_lens, k_scale=None, v_scale=None):
         if k_cache.dtype == torch.uint8:
             L.pa_decode_fp8(q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens,
@@ -70,15 +79,15 @@ class DecodeStep:
     def __call__(self, q, k_new, v_new, k_cache, v_cache, block_table, context_lens, k_scale=None,
                  v_scale=None):
         """The whole step; returns ``(out, lse)`` (views of this object's buffers)."""
-        self.route(block_table, context_lens, k_cache.shape[0])
-        self.append(k_new, v_new, k_cache, v_cache, k_scale, v_scale)
+        self.route_append(k_new, v_new, k_cache, v_cache, block_table, context_lens, k_scale,
+                          v_scale)
         self.attend(q, k_cache, v_cache, block_table, context_lens, k_scale, v_scale)
         self.merge()
         return self.out, self.lse
 
     def capture(self, *args, **kwargs):
         """Record the whole step (the same arguments as a call) as a HIP graph and return
-        it; ``graph.replay()`` then reruns the four launches on whatever the argument
+        it; ``graph.replay()`` then reruns the launches on whatever the argument
         tensors hold at that time.  The library allocates nothing and issues no memset,
         so the recorded launches are the step itself."""
         return capture_graph(lambda: self(*args, **kwargs))

@@ -144,6 +144,31 @@ int pa_kv_append_fp8(const void* k_new, const void* v_new, int32_t new_dtype, ui
                      int64_t n_blocks, int32_t* err_flag, void* stream);
 
 /*
+ * pa_kv_append_routed -- pa_slot_mapping and then the append (pa_kv_append, or
+ * pa_kv_append_fp8 for an E4M3 cache) in one launch, for a step with one new token per
+ * sequence: sequence b's new token (global position context_lens[b]-1) is routed to its
+ * shard, local index and block by the same rule, and its rows are stored exactly as the
+ * two calls would store them.  Saves a launch per decode step.
+ *   k_new, v_new: [n_seqs][n_kv_heads][dk|dv] of new_dtype (PA_F32 or PA_BF16); v_new
+ *   and v_cache NULL for the latent cache.
+ *   k_cache, v_cache: the paged cache of cache_dtype: PA_F32 or PA_BF16 (then equal to
+ *   new_dtype) or PA_FP8_E4M3 (then k_scale, v_scale, n_scales as in pa_kv_append_fp8;
+ *   otherwise they are ignored and may be NULL).
+ *   block_table, context_lens, n_shards, interleave, max_blocks_per_shard: as in
+ *   pa_slot_mapping.
+ *   slot_mapping (out, optional): int64 [n_seqs], the slots pa_slot_mapping would write;
+ *   NULL to skip.  An empty sequence or an invalid table entry appends nothing (the
+ *   latter sets *err_flag).
+ */
+int pa_kv_append_routed(const void* k_new, const void* v_new, int32_t new_dtype, void* k_cache,
+                        void* v_cache, int32_t cache_dtype, const float* k_scale,
+                        const float* v_scale, int32_t n_scales, const int32_t* block_table,
+                        const int32_t* context_lens, int32_t n_seqs, int32_t n_kv_heads, int32_t dk,
+                        int32_t dv, int32_t block_size, int64_t n_blocks,
+                        int32_t max_blocks_per_shard, int32_t n_shards, int32_t interleave,
+                        int64_t* slot_mapping, int32_t* err_flag, void* stream);
+
+/*
  * pa_decode -- attention of one query token per sequence over its paged K/V, split
  * into shards and partitions, each emitting an output and its LSE ([PA]: attention
  * follows the block table; [DCP]: local attention per shard returning output + LSE).

@@ -177,3 +177,34 @@ def test_chooser_picks_long_partitions_for_long_contexts():
             T = P.pa_choose_partition_tokens(w.context_lens, hq, w.n_kv_heads, w.dk, w.dv,
                                              w.block_size, kv, False, w.n_shards, w.interleave)
             assert 1024 <= T <= 16384, (w.name, kv, T)
+
+
+def test_routed_append_rejects_bad_arguments():
+    vp = ctypes.c_void_p(0x1000)
+    ap = P.lib.pa_kv_append_routed
+
+    def call(**over):
+        # k_new, v_new, new_dtype, k_cache, v_cache, cache_dtype, k_scale, v_scale, n_scales,
+        # block_table, context_lens, n_seqs, hkv, dk, dv, bs, nb, max_blocks, S, I, slots, flag
+        a = dict(kn=vp, vn=vp, nd=1, kc=vp, vc=vp, cd=1, ks=None, vs=None, ns=0, bt=vp, lens=vp, n=4,
+                 hkv=2, dk=64, dv=64, bs=16, nb=8, mb=4, S=1, I=1, slots=None, flag=None)
+        a.update(over)
+        return ap(*a.values(), None)
+
+    assert call(n=0) == 0                          # nothing to do
+    assert call(bt=None) == -1
+    assert call(lens=None) == -1
+    assert call(vn=None) == -1                     # v_new without v_cache
+    assert call(nd=0) == -3                        # rows f32, cache bf16
+    assert call(cd=7) == -3
+    assert call(nd=2, cd=2) == -3                  # E4M3 rows
+    assert call(cd=2) == -1                        # E4M3 cache without scales
+    assert call(cd=2, ks=vp, vs=vp, ns=3) == -2    # 3 scales for 2 KV heads
+    assert call(cd=2, ks=vp, vs=vp, ns=2, n=0) == 0
+    assert call(S=0) == -2
+    assert call(I=0) == -2
+    assert call(bs=0) == -3
+    assert call(mb=0) == -2
+    assert call(dk=0) == -3
+    assert call(n=-1) == -2
+    assert "n_seqs" in P.lib.pa_last_error().decode()
