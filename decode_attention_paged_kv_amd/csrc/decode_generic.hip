@@ -74,8 +74,10 @@ __global__ __launch_bounds__(kThreads) void decode_generic_kernel(DecodeArgs a) 
     return visible_on_shard(L - nq + (c0 + hh) / g, a.n_shards, a.interleave, r);
   };
   const int t_end = min(min(t_begin + T, Lr), visible(nh - 1));
-  if (t_begin >= t_end) {  // empty partition: lse = -inf, output rows left unwritten
+  if (t_begin >= t_end) {  // empty partition: lse = -inf; output rows 0 in partition 0 only
     if (tid < nh) a.part_lse[out_row(tid)] = -INFINITY;
+    if (p == 0)
+      for (int i = tid; i < nh * dv; i += blockDim.x) a.part_out[out_row(i / dv) * dv + i % dv] = 0.f;
     return;
   }
 

@@ -253,8 +253,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(KT == k
   };
   // the last column sees the most: the workgroup's tokens end there
   const int t_end = min(min(t_begin + T, Lr), visible(ncol - 1));
-  if (t_begin >= t_end) {  // empty partition: lse = -inf, output rows left unwritten
+  if (t_begin >= t_end) {  // empty partition: lse = -inf; output rows 0 in partition 0 only
     if (threadIdx.x < ncol) a.part_lse[out_row(threadIdx.x)] = -INFINITY;
+    if (p == 0)
+      for (int i = threadIdx.x; i < ncol * D; i += 64 * NW) a.part_out[out_row(i / D) * D + i % D] = 0.f;
     return;
   }
   const int lim = min(t_end, visible(min(col, ncol - 1)));   // this lane's column's end

@@ -736,12 +736,16 @@ void decode_mla_kernel(DecodeArgs a) {
   finish(o, m_ref, lsum);
   }
 
-  // partitions past a pair's last one: lse = -inf (their output rows are not written)
+  // partitions past a pair's last one: lse = -inf; their output rows are not written,
+  // except in partition 0 of a pair with no tokens, where they are 0
   for (int y = blockIdx.x; y < Y; y += gridDim.x) {
     const int n = parts_of(y);
     for (int p = n; p < a.max_parts; ++p)
       for (int i = tid; i < a.hq; i += 64 * NW)
         a.part_lse[(int64_t(y) * a.max_parts + p) * a.hq + i] = -INFINITY;
+    if (n == 0)
+      for (int64_t i = tid; i < int64_t(a.hq) * DV; i += 64 * NW)
+        a.part_out[int64_t(y) * a.max_parts * a.hq * DV + i] = 0.f;
   }
 }
 

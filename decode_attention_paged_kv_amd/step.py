@@ -39,8 +39,8 @@ class DecodeStep:
         self.slot_mapping = torch.empty(n_seqs, dtype=torch.int64, device=dev)
         self.part_out = torch.empty(n_seqs, n_shards, P, n_q_heads, dv, dtype=torch.float32, device=dev)
         self.part_lse = torch.empty(n_seqs, n_shards, P, n_q_heads, dtype=torch.float32, device=dev)
-        self.out = torch.empty(n_seqs, n_q_heads, dv, dtype=out_dtype, device=dev)
-        self.lse = torch.empty(n_seqs, n_q_heads, dtype=torch.float32, device=dev)
+        self.out, self.lse, self.direct = _outputs(self.part_out, self.part_lse, n_seqs, n_q_heads, dv,
+                                                   n_shards, P, out_dtype, dev)
         self.err_flag = torch.zeros(1, dtype=torch.int32, device=dev)
 
     def route(self, block_table, context_lens, n_blocks):
@@ -74,7 +74,8 @@ class DecodeStep:
                         self.part_out, self.part_lse, dv=self.dv, err_flag=self.err_flag)
 
     def merge(self):
-        L.pa_merge_lse(self.part_out, self.part_lse, self.out, self.lse)
+        if not self.direct:
+            L.pa_merge_lse(self.part_out, self.part_lse, self.out, self.lse)
 
     def __call__(self, q, k_new, v_new, k_cache, v_cache, block_table, context_lens, k_scale=None,
                  v_scale=None):
@@ -91,6 +92,17 @@ class DecodeStep:
         tensors hold at that time.  The library allocates nothing and issues no memset,
         so the recorded launches are the step itself."""
         return capture_graph(lambda: self(*args, **kwargs))
+
+
+def _outputs(part_out, part_lse, n_rows, hq, dv, n_shards, max_partitions, out_dtype, dev):
+    """The step's output and LSE buffers.  With one shard, one partition and float32
+    output they are views of the partials: the merge of a single part is the identity
+    (weight exp(lse - lse) = 1) and the decode writes zeros into partition 0 of an empty
+    sequence, so the merge launch is skipped (``direct``)."""
+    if n_shards == 1 and max_partitions == 1 and out_dtype == torch.float32:
+        return part_out.view(n_rows, hq, dv), part_lse.view(n_rows, hq), True
+    return (torch.empty(n_rows, hq, dv, dtype=out_dtype, device=dev),
+            torch.empty(n_rows, hq, dtype=torch.float32, device=dev), False)
 
 
 def capture_graph(fn):
@@ -138,8 +150,8 @@ class MultiDecodeStep:
         self.slot_mapping = torch.empty(n_rows, dtype=torch.int64, device=dev)
         self.part_out = torch.empty(n_rows, n_shards, P, n_q_heads, dv, dtype=torch.float32, device=dev)
         self.part_lse = torch.empty(n_rows, n_shards, P, n_q_heads, dtype=torch.float32, device=dev)
-        self.out = torch.empty(n_rows, n_q_heads, dv, dtype=out_dtype, device=dev)
-        self.lse = torch.empty(n_rows, n_q_heads, dtype=torch.float32, device=dev)
+        self.out, self.lse, self.direct = _outputs(self.part_out, self.part_lse, n_rows, n_q_heads, dv,
+                                                   n_shards, P, out_dtype, dev)
         self.err_flag = torch.zeros(1, dtype=torch.int32, device=dev)
 
     def route(self, block_table, context_lens, query_start, n_blocks):
@@ -162,7 +174,8 @@ class MultiDecodeStep:
                           k_scale=k_scale, v_scale=v_scale, dv=self.dv, err_flag=self.err_flag)
 
     def merge(self):
-        L.pa_merge_lse(self.part_out, self.part_lse, self.out, self.lse)
+        if not self.direct:
+            L.pa_merge_lse(self.part_out, self.part_lse, self.out, self.lse)
 
     def __call__(self, q, query_start, k_new, v_new, k_cache, v_cache, block_table, context_lens,
                  k_scale=None, v_scale=None):

@@ -182,7 +182,10 @@ int pa_kv_append_routed(const void* k_new, const void* v_new, int32_t new_dtype,
  *   scale      multiplies q.k before the softmax.
  *   part_out   float32 [n_seqs][n_shards][Pmax][n_q_heads][dv]: softmax-weighted mean
  *              of the partition's values.  Rows of an empty partition are NOT written
- *              (their weight in any merge is zero); pa_merge_lse never reads them.
+ *              (their weight in any merge is zero; pa_merge_lse never reads them),
+ *              except in partition 0 of a shard with no tokens, where they are 0 --
+ *              so with one shard and Pmax = 1 the partials already are what
+ *              pa_merge_lse would return (a single part has weight exactly 1).
  *   part_lse   float32 [n_seqs][n_shards][Pmax][n_q_heads]: natural log of the sum of
  *              exp(scale*q.k) over the partition; -inf for an empty partition.
  *   Unsupported: dk or dv outside [1, PA_MAX_HEAD_DIM], dv > 512, block_size outside
