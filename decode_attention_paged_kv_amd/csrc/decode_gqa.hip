@@ -65,7 +65,6 @@ namespace pa {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((__vector_size__(8 * sizeof(__bf16))));
-typedef __bf16 bf16x2_t __attribute__((__vector_size__(2 * sizeof(__bf16))));
 typedef float f32x4_t __attribute__((__vector_size__(4 * sizeof(float))));
 typedef uint32_t u32x4_t __attribute__((__vector_size__(4 * sizeof(uint32_t))));
 
@@ -95,19 +94,9 @@ __device__ inline float xor_max(float v) {
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
-// 2^x for the softmax weights: the transcendental unit's instruction alone (raw), or the
-// library call, which adds a fix-up for results below 2^-126 (irrelevant next to the
-// running maximum's weight of 1; -inf gives 0 either way).
-#ifndef PA_GQA_RAW_EXP
-#define PA_GQA_RAW_EXP 0
-#endif
-__device__ inline float exp2_w(float x) {
-#if PA_GQA_RAW_EXP
-  return __builtin_amdgcn_exp2f(x);
-#else
-  return exp2f(x);
-#endif
-}
+// 2^x for the softmax weights (the library call; the transcendental unit's instruction
+// alone measured no faster).
+__device__ inline float exp2_w(float x) { return exp2f(x); }
 
 __device__ inline float xor_sum(float v) {
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
