@@ -37,17 +37,20 @@ __global__ __launch_bounds__(kThreads) void decode_generic_kernel(DecodeArgs a) 
   const raw* kc = static_cast<const raw*>(a.k_cache);
   const raw* vc = static_cast<const raw*>(a.v_cache);
 
-  const int p = blockIdx.x;
-  const int b = blockIdx.y / a.n_shards;
-  const int r = blockIdx.y % a.n_shards;
+  // grid x = partition + max_parts * (sequence x shard): partition fastest, as a 3-D
+  // grid would order them, without a 65535 bound on the (sequence, shard) count
+  const int yy = blockIdx.x / a.max_parts;
+  const int p = blockIdx.x - yy * a.max_parts;
+  const int b = yy / a.n_shards;
+  const int r = yy % a.n_shards;
   const int g = a.hq / a.hkv;
   // columns: (new token, query head of this KV head) pairs, token major; kHeads of them
   // per workgroup (one new token per sequence: the heads)
   const int row0 = a.query_start ? a.query_start[b] : b;
   const int nq = a.query_start ? a.query_start[b + 1] - row0 : 1;
   const int chunks = (a.max_q * g + kHeads - 1) / kHeads;
-  const int kvh = blockIdx.z / chunks;
-  const int c0 = (blockIdx.z % chunks) * kHeads;
+  const int kvh = blockIdx.y / chunks;
+  const int c0 = (blockIdx.y % chunks) * kHeads;
   const int nh = min(kHeads, nq * g - c0);       // valid columns here
   const int tid = threadIdx.x;
   const int dk = a.dk, dv = a.dv, bs = a.bs;
@@ -58,7 +61,7 @@ __global__ __launch_bounds__(kThreads) void decode_generic_kernel(DecodeArgs a) 
   // several new tokens: more than the context holds, or rows outside the arrays, is an
   // error (flagged, rows left unwritten); one per sequence: an empty context is allowed
   const bool bad = a.query_start && (nq > L || nq > a.max_q || row0 < 0 || row0 + nq > a.n_rows);
-  if (p == 0 && tid == 0 && blockIdx.z == 0 && ((Lr + T - 1) / T > a.max_parts || bad))
+  if (p == 0 && tid == 0 && blockIdx.y == 0 && ((Lr + T - 1) / T > a.max_parts || bad))
     raise_flag(a.flag, kErrCapacity);
   if (nh <= 0 || bad) return;
   const int t_begin = p * T;
@@ -206,7 +209,7 @@ int generic_workgroups_per_cu(int dtype, int kv_dtype) {
 }
 
 hipError_t launch_decode_generic(const DecodeArgs& a, hipStream_t st) {
-  const dim3 grid(a.max_parts, a.n_seqs * a.n_shards, a.hkv * generic_column_chunks(a));
+  const dim3 grid(unsigned(int64_t(a.max_parts) * a.n_seqs * a.n_shards), a.hkv * generic_column_chunks(a));
   if (a.kv_dtype == kFP8) {
     if (a.dtype == kF32)
       hipLaunchKernelGGL((decode_generic_kernel<kF32, kFP8>), grid, dim3(kThreads), 0, st, a);

@@ -208,17 +208,20 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(KT == k
   const int wave = threadIdx.x >> 6;
   const int col = lane & 15;   // key row (A operand) / column (B operand, results)
   const int grp = lane >> 4;   // k-slot group
-  const int p = blockIdx.x;
-  const int b = blockIdx.y / a.n_shards;
-  const int r = blockIdx.y % a.n_shards;
+  // grid x = partition + max_parts * (sequence x shard): partition fastest, as a 3-D
+  // grid would order them, without a 65535 bound on the (sequence, shard) count
+  const int yy = blockIdx.x / a.max_parts;
+  const int p = blockIdx.x - yy * a.max_parts;
+  const int b = yy / a.n_shards;
+  const int r = yy % a.n_shards;
   const int g = a.hq / a.hkv;
   // Columns of the products are (new token, query head of this KV head) pairs, token
   // major; a workgroup takes 16 of them.  One new token per sequence: the heads.
   const int row0 = a.query_start ? a.query_start[b] : b;         // q row of its first new token
   const int nq = a.query_start ? a.query_start[b + 1] - row0 : 1;
   const int chunks = (a.max_q * g + 15) >> 4;
-  const int kvh = blockIdx.z / chunks;
-  const int c0 = (blockIdx.z % chunks) * 16;
+  const int kvh = blockIdx.y / chunks;
+  const int c0 = (blockIdx.y % chunks) * 16;
   const int ncol = min(16, nq * g - c0);         // valid columns here
   const int bs = a.bs;
 
@@ -228,7 +231,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(KT == k
   // several new tokens: more than the context holds, or rows outside the arrays, is an
   // error (flagged, rows left unwritten); one per sequence: an empty context is allowed
   const bool bad = a.query_start && (nq > L || nq > a.max_q || row0 < 0 || row0 + nq > a.n_rows);
-  if (p == 0 && threadIdx.x == 0 && blockIdx.z == 0 && ((Lr + T - 1) / T > a.max_parts || bad))
+  if (p == 0 && threadIdx.x == 0 && blockIdx.y == 0 && ((Lr + T - 1) / T > a.max_parts || bad))
     raise_flag(a.flag, kErrCapacity);
   if (ncol <= 0 || bad) return;  // no rows here (or bad input)
   const int t_begin = p * T;
@@ -583,7 +586,7 @@ int gqa_workgroups_per_cu(const DecodeArgs& a) {
 }
 
 hipError_t launch_decode_gqa(const DecodeArgs& a, hipStream_t st) {
-  const dim3 grid(a.max_parts, a.n_seqs * a.n_shards, a.hkv * gqa_column_chunks(a));
+  const dim3 grid(unsigned(int64_t(a.max_parts) * a.n_seqs * a.n_shards), a.hkv * gqa_column_chunks(a));
   void* args[] = {const_cast<DecodeArgs*>(&a)};
   return hipLaunchKernel(gqa_kernel_for(a), grid, dim3(64 * gqa_waves(a)), args, 0, st);
 }

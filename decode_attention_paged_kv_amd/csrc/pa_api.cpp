@@ -382,8 +382,9 @@ int check_decode(const char* fn, const void* q, const void* k_cache, const void*
           "partition_tokens=%d must be a positive multiple of block_size=%d", partition_tokens,
           block_size);
   REQUIRE(max_partitions >= 1, PA_ERR_BUFFER, "max_partitions=%d must be >= 1", max_partitions);
-  REQUIRE(int64_t(n_seqs) * n_shards <= 65535, PA_ERR_SHAPE,
-          "n_seqs*n_shards=%lld exceeds 65535", (long long)n_seqs * n_shards);
+  REQUIRE(int64_t(max_partitions) * n_seqs * n_shards <= 0x7fffffff, PA_ERR_SHAPE,
+          "max_partitions*n_seqs*n_shards=%lld exceeds 2^31-1",
+          (long long)max_partitions * n_seqs * n_shards);
   REQUIRE(n_kv_heads * ((n_q_heads / n_kv_heads + 15) / 16) <= 65535, PA_ERR_SHAPE,
           "too many heads");
   pa::DecodeArgs a{q,        k_cache,         v_cache,    block_table, context_lens, n_seqs,

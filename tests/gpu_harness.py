@@ -230,7 +230,8 @@ def check_large(w, sample_seqs, partition_tokens=None, fill="normal", rel_l2=REL
             newbits = torch.from_numpy(want).to(dev)
         else:
             newbits = new.reshape(new.shape[0], -1).view(A.dtype)
-        assert torch.equal(A[sl], newbits), f"{w.name}: appended rows differ"
+        valid = sl >= 0                  # empty sequences append nothing (slot -1)
+        assert torch.equal(A[sl[valid]], newbits[valid]), f"{w.name}: appended rows differ"
     del A, B
     Tp, Pmax = step.partition_tokens, step.max_partitions
     for b in sample_seqs:

@@ -208,3 +208,11 @@ def test_routed_append_rejects_bad_arguments():
     assert call(dk=0) == -3
     assert call(n=-1) == -2
     assert "n_seqs" in P.lib.pa_last_error().decode()
+
+
+def test_decode_rejects_a_grid_past_2_31():
+    vp = ctypes.c_void_p(0x1000)
+    # q, k, v, bt, lens, n, hq, hkv, dk, dv, bs, nb, mb, S, I, T, P, scale, dtype, po, pl, flag, stream
+    st = P.lib.pa_decode(vp, vp, vp, vp, vp, 1 << 20, 8, 2, 64, 64, 16, 8, 4, 64, 1, 16, 64, 0.125, 1,
+                         vp, vp, None, None)
+    assert st == -2 and "exceeds 2^31-1" in P.lib.pa_last_error().decode()

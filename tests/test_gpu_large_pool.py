@@ -8,12 +8,14 @@ the result, and the kernels reduce in logical order, so the whole step's output 
 LSE must agree bit for bit, the appended rows must land at the same place relative
 to the content, the poisoned part must be untouched, and the gather and block copy
 must move the same bytes.  Covered: the bf16 MFMA kernel, the E4M3 cache, the latent
-kernel and the generic one (fp32)."""
+kernel and the generic one (fp32).  Also a batch of more than 65,535 (sequence, shard)
+pairs, which the decode grids must take."""
+import numpy as np
 import pytest
 import torch
 
 import workloads as wl
-from gpu_harness import run_library, say
+from gpu_harness import check_large, run_library, say
 
 pytestmark = pytest.mark.gpu
 
@@ -120,3 +122,22 @@ def test_content_at_the_top_of_a_large_pool(case):
     assert torch.equal(_bits(kbig[0]), _bits(saved)) and torch.equal(_bits(kbig[top - 1]), _bits(saved))
     del kbig, vbig, T_big, T
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("kernel", ["gqa_bf16", "generic_f32"])
+def test_more_than_65535_sequence_shard_pairs(kernel):
+    """17,000 short sequences on 4 shards (68,000 (sequence, shard) pairs, past a 16-bit
+    grid dimension): routing for every sequence, the append over the whole pool, and
+    the attention of sampled sequences against the oracle; empty sequences among them."""
+    rng = np.random.default_rng(17)
+    lens = [int(x) for x in rng.integers(0, 48, 17_000)]
+    lens[:3] = [0, 1, 47]
+    if kernel == "gqa_bf16":
+        w = wl.small("many_seqs_bf16", lens, 8, 2, 64, 64, 16, wl.BF16, n_shards=4, interleave=2,
+                     partition_tokens=16, seed=31)
+    else:
+        w = wl.small("many_seqs_f32", lens, 4, 2, 40, 24, 8, wl.F32, n_shards=4, interleave=3,
+                     partition_tokens=8, seed=32)
+    assert w.n_seqs * w.n_shards > 65535
+    sample = [0, 1, 2] + [int(x) for x in rng.integers(3, w.n_seqs, 5)] + [w.n_seqs - 1]
+    check_large(w, sample)
