@@ -11,7 +11,8 @@ import pytest
 import torch
 
 import workloads as wl
-from gpu_harness import check_large, check_small, say
+from gpu_harness import check_large, check_small, run_library, say
+from oracle import paged_attention as pa
 
 pytestmark = pytest.mark.gpu
 
@@ -75,6 +76,49 @@ def test_mean_probe_full_size(make):
     misaddressed token moves it."""
     w = make()
     check_large(w, [int(np.argmax(w.context_lens))], fill="mean_probe")
+
+
+@pytest.mark.parametrize("make", [lambda: wl.long(), lambda: wl.dcp(interleave=16),
+                                  lambda: wl.dcp(interleave=1)], ids=["long", "dcp_I16", "dcp_I1"])
+def test_needle_full_size(make):
+    """One token per sequence, at a random earlier position, gets key alpha*u (u the
+    sequence's unit query, shared by all its heads; alpha*scale ~ 45 while every other
+    score stays below ~0.5), so its weight is all but 1 among up to 200,000 tokens: the
+    output must be that token's value row and the LSE its score.  Checks the block-table
+    read at that exact position, its shard and partition, and the merge, at full size."""
+    import decode_attention_paged_kv_amd as P  # noqa: F401
+
+    w = make()
+    say(f"[needle] {w.name} N={w.n_seqs} S={w.n_shards} I={w.interleave}")
+    dev = torch.device("cuda")
+    T = wl.make_tensors(w, dev)
+    rng = np.random.default_rng(123)
+    alpha = 512.0
+    g = w.n_q_heads // w.n_kv_heads
+    expect_o, expect_lse = [], []
+    for b in range(w.n_seqs):
+        L = int(w.context_lens[b])
+        i = int(rng.integers(0, L - 1))                      # an old token (not the new one)
+        _, _, phys, off = pa.token_home(w.block_table[b], i, w.n_shards, w.interleave, w.block_size)
+        u = torch.randn(w.dk, generator=torch.Generator().manual_seed(b), dtype=torch.float32)
+        u = (u / u.norm()).to(torch.bfloat16)
+        k = (u.float() * alpha).to(torch.bfloat16)
+        T["q"][b] = u.to(dev)                                # every head of the sequence
+        T["k_cache"][phys, :, off, :] = k.to(dev)            # every KV head
+        v = T["v_cache"][phys, :, :, off].float().cpu()      # [Hkv][dv]
+        s = float(np.float32(w.scale_f32)) * float((u.double() * k.double()).sum())
+        expect_o.append(v.repeat_interleave(g, dim=0))       # [Hq][dv]
+        expect_lse.append(s)
+    step = run_library(w, T)
+    assert int(step.err_flag.item()) == 0
+    out = step.out.float().cpu()
+    lse = step.lse.float().cpu()
+    for b in range(w.n_seqs):
+        d_o = (out[b] - expect_o[b]).abs().max().item()
+        d_l = (lse[b] - expect_lse[b]).abs().max().item()
+        say(f"  seq {b}: max|o - v_needle| = {d_o:.3g}, max|lse - s_needle| = {d_l:.3g}")
+        assert d_o < 1e-4, f"seq {b}: output is not the needle's value row"
+        assert d_l < 1e-3, f"seq {b}: lse is not the needle's score"
 
 
 # ------------------------------------------------------------------ shapes and edge cases
