@@ -79,13 +79,17 @@ def test_mean_probe_full_size(make):
 
 
 @pytest.mark.parametrize("make", [lambda: wl.long(), lambda: wl.dcp(interleave=16),
-                                  lambda: wl.dcp(interleave=1)], ids=["long", "dcp_I16", "dcp_I1"])
+                                  lambda: wl.dcp(interleave=1), lambda: wl.latent()],
+                         ids=["long", "dcp_I16", "dcp_I1", "latent"])
 def test_needle_full_size(make):
     """One token per sequence, at a random earlier position, gets key alpha*u (u the
-    sequence's unit query, shared by all its heads; alpha*scale ~ 45 while every other
-    score stays below ~0.5), so its weight is all but 1 among up to 200,000 tokens: the
-    output must be that token's value row and the LSE its score.  Checks the block-table
-    read at that exact position, its shard and partition, and the merge, at full size."""
+    sequence's unit query, shared by all its heads; alpha*scale ~ 45, or 50 for the
+    latent cache, while every other score stays below ~0.5), so its weight is all but 1
+    among up to 200,000 tokens: the output must be that token's value row and the LSE
+    its score.  Checks the block-table read at that exact position, its shard and
+    partition, and the merge, at full size.  In the latent kernel a needle outside the
+    first tile lies more than 64 log2 units above the reference max set by earlier
+    tokens, so the partition is redone against the exact max."""
     import decode_attention_paged_kv_amd as P  # noqa: F401
 
     w = make()
@@ -93,19 +97,23 @@ def test_needle_full_size(make):
     dev = torch.device("cuda")
     T = wl.make_tensors(w, dev)
     rng = np.random.default_rng(123)
-    alpha = 512.0
+    alpha = 50.0 / float(w.scale_f32) if w.latent else 512.0
     g = w.n_q_heads // w.n_kv_heads
     expect_o, expect_lse = [], []
     for b in range(w.n_seqs):
         L = int(w.context_lens[b])
-        i = int(rng.integers(0, L - 1))                      # an old token (not the new one)
+        lo = w.prefix_tokens if w.prefix_tokens else 0        # outside a shared prefix
+        i = int(rng.integers(lo, L - 1))                     # an old token (not the new one)
         _, _, phys, off = pa.token_home(w.block_table[b], i, w.n_shards, w.interleave, w.block_size)
         u = torch.randn(w.dk, generator=torch.Generator().manual_seed(b), dtype=torch.float32)
         u = (u / u.norm()).to(torch.bfloat16)
         k = (u.float() * alpha).to(torch.bfloat16)
         T["q"][b] = u.to(dev)                                # every head of the sequence
         T["k_cache"][phys, :, off, :] = k.to(dev)            # every KV head
-        v = T["v_cache"][phys, :, :, off].float().cpu()      # [Hkv][dv]
+        if w.latent:                                         # the value is the key's head
+            v = k[:w.dv].float()[None, :].repeat(w.n_kv_heads, 1)
+        else:
+            v = T["v_cache"][phys, :, :, off].float().cpu()  # [Hkv][dv]
         s = float(np.float32(w.scale_f32)) * float((u.double() * k.double()).sum())
         expect_o.append(v.repeat_interleave(g, dim=0))       # [Hq][dv]
         expect_lse.append(s)
@@ -116,8 +124,12 @@ def test_needle_full_size(make):
     for b in range(w.n_seqs):
         d_o = (out[b] - expect_o[b]).abs().max().item()
         d_l = (lse[b] - expect_lse[b]).abs().max().item()
-        say(f"  seq {b}: max|o - v_needle| = {d_o:.3g}, max|lse - s_needle| = {d_l:.3g}")
-        assert d_o < 1e-4, f"seq {b}: output is not the needle's value row"
+        # the latent kernel rounds each weight to bf16 for the output product (the sum of
+        # weights stays unrounded): the needle's weight, 1 within the rounding of its
+        # score, costs a relative ~3e-6 there; a misread row would be off by ~|v|
+        tol_o = 2.0 ** -8 * expect_o[b].abs().max().item() if w.latent else 1e-4
+        say(f"  seq {b}: max|o - v_needle| = {d_o:.3g} (tol {tol_o:.3g}), max|lse - s_needle| = {d_l:.3g}")
+        assert d_o < tol_o, f"seq {b}: output is not the needle's value row"
         assert d_l < 1e-3, f"seq {b}: lse is not the needle's score"
 
 
