@@ -7,8 +7,8 @@
 // Parts with lse_p = -inf are empty and skipped (no -inf - -inf is ever formed); their
 // part_out rows are never read.
 //
-// One workgroup per (sequence, head) and column block; one wave per (sequence, head)
-// when there are at most 16 parts.
+// One workgroup per (sequence, head) and column block; with at most 64 parts, one wave
+// per (sequence, head) and block of columns.
 #include <math.h>
 
 #include "pa_common.h"
@@ -141,13 +141,15 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const float* __restrict
   if (lse_out && threadIdx.x == 0 && blockIdx.y == 0) lse_out[int64_t(b) * hq + h] = total;
 }
 
-// Few parts (at most 16): one wave per (sequence, head), no LDS and no barrier, so the
-// dependent steps are one lse load, the cross-lane reductions and one round of output
-// loads.  Lane p holds part p's lse; the max and the sum of weights are cross-lane
-// reductions; then the wave walks the non-empty parts (a uniform loop, each weight read
-// from its lane) with VEC columns per lane and eight parts' loads in flight at once.
-constexpr int kSmallParts = 16;   // measured: with ~50 parts per row it is slower
-constexpr int kInFlight = 8;      // parts whose loads are issued together
+// Up to 64 parts: one wave per (sequence, head, block of columns), no LDS and no
+// barrier, so the dependent steps are one lse load, cross-lane reductions and rounds of
+// output loads.  Lane p holds part p's lse; the max and the sum of weights are
+// cross-lane reductions.  The lanes then form PG part groups x (64 / PG) column groups of
+// VEC columns: in a round, lane (pg, cg) reads parts p0 + pg + PG k, k < 8 (issued
+// together) of its columns, so a round covers 8 PG parts; the part groups' sums meet by
+// xor exchanges.  PG = 8: one round for up to 64 parts, narrow blocks (many waves when
+// rows are few); PG = 1: wide blocks, every lane's loads useful (many rows).
+constexpr int kWaveParts = 64;
 
 __device__ inline float wave_max(float v) {
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
@@ -158,13 +160,16 @@ __device__ inline float wave_sum(float v) {
   return v;
 }
 
-template <int VEC>
-__global__ __launch_bounds__(256) void merge_small_kernel(const float* __restrict__ part_out,
-                                                          const float* __restrict__ part_lse,
-                                                          int n_rows, int n_parts, int hq, int dv,
-                                                          void* out, int out_dtype, float* lse_out) {
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= n_rows) return;   // the whole wave
+template <int VEC, int PG>
+__global__ __launch_bounds__(256) void merge_wave_kernel(const float* __restrict__ part_out,
+                                                         const float* __restrict__ part_lse,
+                                                         int n_rows, int n_cblk, int n_parts, int hq,
+                                                         int dv, void* out, int out_dtype,
+                                                         float* lse_out) {
+  constexpr int CG = 64 / PG;   // column groups; a block has CG * VEC columns
+  const int64_t wid = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (wid >= int64_t(n_rows) * n_cblk) return;   // the whole wave
+  const int row = int(wid / n_cblk), cblk = int(wid - (wid / n_cblk) * n_cblk);
   const int lane = threadIdx.x & 63;
   const int b = row / hq, h = row - (row / hq) * hq;
   const float* lse_p = part_lse + int64_t(b) * n_parts * hq + h;        // stride hq
@@ -178,52 +183,61 @@ __global__ __launch_bounds__(256) void merge_small_kernel(const float* __restric
     total = m + logf(wave_sum(x != -INFINITY ? expf(x - m) : 0.f));
     if (x != -INFINITY) w = expf(x - total);
   }
-  const uint64_t live = __ballot(w != 0.f);
-
-  const int64_t orow = int64_t(row) * dv;
-  for (int c = lane * VEC; c < dv; c += 64 * VEC) {
-    float acc[VEC];
+  const int pg = lane / CG, cg = lane % CG;
+  const int c = cblk * CG * VEC + cg * VEC;
+  float acc[VEC];
 #pragma unroll
-    for (int k = 0; k < VEC; ++k) acc[k] = 0.f;
-    uint64_t todo = live;
-    while (todo) {
-      // up to kInFlight parts at once: their loads are independent
-      int ps[kInFlight];
-      float ws[kInFlight];
+  for (int j = 0; j < VEC; ++j) acc[j] = 0.f;
+  for (int p0 = 0; p0 < n_parts; p0 += 8 * PG) {   // uniform: every lane takes the shuffles
+    float wk[8], v[8][VEC];
 #pragma unroll
-      for (int u = 0; u < kInFlight; ++u) {
-        ps[u] = todo ? __builtin_ctzll(todo) : -1;
-        if (todo) todo &= todo - 1;
-        // ps[u] is wave-uniform and readlane ignores the exec mask, so the broadcast also
-        // works in the lanes that have left the column loop
-        ws[u] = ps[u] >= 0 ? __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(w), ps[u])) : 0.f;
-      }
-      float v[kInFlight][VEC];
-#pragma unroll
-      for (int u = 0; u < kInFlight; ++u) {
-        const float* sp = o_p + int64_t(ps[u] >= 0 ? ps[u] : ps[0]) * stride + c;
-        if constexpr (VEC == 4) {
-          const float4 t = *reinterpret_cast<const float4*>(sp);
-          v[u][0] = t.x, v[u][1 % VEC] = t.y, v[u][2 % VEC] = t.z, v[u][3 % VEC] = t.w;
-        } else {
-#pragma unroll
-          for (int k = 0; k < VEC; ++k) v[u][k] = sp[k];
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < kInFlight; ++u)
-#pragma unroll
-        for (int k = 0; k < VEC; ++k) acc[k] = fmaf(ws[u], v[u][k], acc[k]);
+    for (int k = 0; k < 8; ++k) {
+      const int p = p0 + pg + PG * k;
+      wk[k] = __shfl(w, p < 64 ? p : 0);
+      if (p >= n_parts) wk[k] = 0.f;
     }
 #pragma unroll
-    for (int k = 0; k < VEC; ++k) {
+    for (int k = 0; k < 8; ++k) {
+      // a part of weight 0 (empty, or past n_parts) is not read
+      const bool use = c < dv && wk[k] != 0.f;
+      const float* sp = o_p + int64_t(p0 + pg + PG * k) * stride + c;
+      if constexpr (VEC == 4) {
+        const float4 t = use ? *reinterpret_cast<const float4*>(sp) : float4{0.f, 0.f, 0.f, 0.f};
+        v[k][0] = t.x, v[k][1 % VEC] = t.y, v[k][2 % VEC] = t.z, v[k][3 % VEC] = t.w;
+      } else {
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) v[k][j] = use ? sp[j] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) acc[j] = fmaf(wk[k], v[k][j], acc[j]);
+  }
+#pragma unroll
+  for (int d = CG; d < 64; d <<= 1)
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) acc[j] += __shfl_xor(acc[j], d);
+  if (pg == 0 && c < dv) {
+    const int64_t orow = int64_t(row) * dv + c;
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) {
       if (out_dtype == kF32)
-        static_cast<float*>(out)[orow + c + k] = acc[k];
+        static_cast<float*>(out)[orow + j] = acc[j];
       else
-        static_cast<uint16_t*>(out)[orow + c + k] = f32_to_bf16_bits(acc[k]);
+        static_cast<uint16_t*>(out)[orow + j] = f32_to_bf16_bits(acc[j]);
     }
   }
-  if (lse_out && lane == 0) lse_out[row] = total;
+  if (lse_out && lane == 0 && cblk == 0) lse_out[row] = total;
+}
+
+template <int VEC, int PG>
+void launch_wave(const float* part_out, const float* part_lse, int rows, int n_parts, int hq, int dv,
+                 void* out, int out_dtype, float* lse, hipStream_t st) {
+  const int n_cblk = (dv + (64 / PG) * VEC - 1) / ((64 / PG) * VEC);
+  const dim3 g(unsigned((int64_t(rows) * n_cblk + 3) / 4));
+  hipLaunchKernelGGL((merge_wave_kernel<VEC, PG>), g, dim3(256), 0, st, part_out, part_lse, rows,
+                     n_cblk, n_parts, hq, dv, out, out_dtype, lse);
 }
 
 }  // namespace
@@ -234,15 +248,16 @@ hipError_t launch_merge(const float* part_out, const float* part_lse, int n_seqs
   // (sequence, head) rows to spread over the GPU; otherwise wide (at most 128 column
   // groups per workgroup), so each workgroup has enough work.
   const int vec = dv % 4 == 0 ? 4 : 1;
-  if (n_parts <= kSmallParts) {
+  if (n_parts <= kWaveParts) {
+    // narrow blocks (8 part groups) while they give fewer than ~16K waves, else wide ones
     const int rows = n_seqs * hq;
-    const dim3 g((rows + 3) / 4);
+    const bool narrow = int64_t(rows) * ((dv + 8 * vec - 1) / (8 * vec)) <= 16384;
     if (vec == 4)
-      hipLaunchKernelGGL(merge_small_kernel<4>, g, dim3(256), 0, st, part_out, part_lse, rows,
-                         n_parts, hq, dv, out, out_dtype, lse);
+      narrow ? launch_wave<4, 8>(part_out, part_lse, rows, n_parts, hq, dv, out, out_dtype, lse, st)
+             : launch_wave<4, 1>(part_out, part_lse, rows, n_parts, hq, dv, out, out_dtype, lse, st);
     else
-      hipLaunchKernelGGL(merge_small_kernel<1>, g, dim3(256), 0, st, part_out, part_lse, rows,
-                         n_parts, hq, dv, out, out_dtype, lse);
+      narrow ? launch_wave<1, 8>(part_out, part_lse, rows, n_parts, hq, dv, out, out_dtype, lse, st)
+             : launch_wave<1, 1>(part_out, part_lse, rows, n_parts, hq, dv, out, out_dtype, lse, st);
     return hipGetLastError();
   }
   int cb = 128 * vec;
