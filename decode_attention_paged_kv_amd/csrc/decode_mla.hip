@@ -93,6 +93,18 @@ constexpr int TBL = 256;                            // block-table entries stage
 #endif
 constexpr int QL = PA_MLA_QL;                       // query k-steps kept in LDS (rest in registers)
 static_assert(QL >= 0 && QL <= 36 && PA_MLA_KA >= 1 && PA_MLA_VA >= 1, "read-ahead and query split");
+// E4M3 cache: the codes are widened to bf16 on their way into the same LDS tile layout,
+// by all the workgroup's threads through registers, into two tile buffers; the LDS the
+// third buffer frees holds more of the query (fewer query registers).
+#ifndef PA_MLA_QL_FP8
+#define PA_MLA_QL_FP8 21
+#endif
+constexpr int NBUF_FP8 = 2;
+constexpr int QL_FP8 = PA_MLA_QL_FP8;
+constexpr int ROW_BYTES_FP8 = DK;                   // 576 codes per token row
+static_assert(QL_FP8 >= 0 && QL_FP8 <= 36 &&
+                  NBUF_FP8 * TILE_BYTES + QL_FP8 * 2 * HEADS * 8 * 2 + TBL * 4 + 2 * NW * 4 <= 160 * 1024,
+              "E4M3: two tiles, the query part and the table must fit 160 KiB of LDS");
 static_assert(TILE_SLOTS % (64 * NW) == 0, "tile copies must split evenly over the waves");
 static_assert(ROW_CHUNKS % 8 == 0, "the swizzle permutes aligned groups of 8 chunks");
 
@@ -181,15 +193,18 @@ __device__ inline f32x16_t to_agpr(f32x16_t v) {
 // Source of the copy of a tile whose block id is invalid (zero-initialised device memory).
 __device__ __attribute__((aligned(16))) char g_zero_tile[TILE_BYTES];
 
+template <bool F8>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_mla_kernel(DecodeArgs a) {
+  constexpr int NB = F8 ? NBUF_FP8 : NBUF;   // tile buffers
+  constexpr int QLk = F8 ? QL_FP8 : QL;      // query k-steps in LDS
   const uint16_t* __restrict__ q = static_cast<const uint16_t*>(a.q);
   const char* __restrict__ kc = static_cast<const char*>(a.k_cache);
 
-  __shared__ __attribute__((aligned(16))) char kt[NBUF * TILE_BYTES];
-  __shared__ __attribute__((aligned(16))) uint16_t q_s[QL * 2 * HEADS * 8];   // [ks][k-group][head][8]
+  __shared__ __attribute__((aligned(16))) char kt[NB * TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) uint16_t q_s[QLk * 2 * HEADS * 8];   // [ks][k-group][head][8]
   __shared__ int32_t tbl_s[TBL];   // block-table entries of the partition, TBL at a time
-  static_assert(NBUF * TILE_BYTES + QL * 2 * HEADS * 8 * 2 + TBL * 4 + 2 * NW * 4 <= 160 * 1024,
+  static_assert(NB * TILE_BYTES + QLk * 2 * HEADS * 8 * 2 + TBL * 4 + 2 * NW * 4 <= 160 * 1024,
                 "the tiles, the query part and the table must fit the compute unit's 160 KiB of LDS");
   __shared__ __attribute__((aligned(16))) int ovf_s[2][NW];   // [tile parity][wave]: overflow seen
 
@@ -302,7 +317,7 @@ void decode_mla_kernel(DecodeArgs a) {
   // out of the tile loop they would hold nine registers the loop needs.  In the last,
   // partial tile, rows past the partition end repeat its last row.
   const uint32_t kt_lds = lds_address(kt);
-  uint32_t bad = 0;   // bit (i % NBUF): tile i has an invalid block
+  uint32_t bad = 0;   // bit (i % NB): tile i has an invalid block
   struct Copy {
     const char* src;
     uint32_t dst;
@@ -318,7 +333,7 @@ void decode_mla_kernel(DecodeArgs a) {
     const char* src = phys >= 0
         ? kc + ((int64_t(phys) * a.hkv + kvh) * bs + (tok0 % bs)) * int64_t(ROW_BYTES)
         : g_zero_tile;
-    const uint32_t slot = uint32_t(i % NBUF);
+    const uint32_t slot = uint32_t(i % NB);
     bad = (bad & ~(1u << slot)) | (uint32_t(phys < 0) << slot);
     return Copy{uniform_ptr(src), kt_lds + slot * TILE_BYTES, phys < 0 ? TT : min(TT, t_end - tok0)};
   };
@@ -341,10 +356,12 @@ void decode_mla_kernel(DecodeArgs a) {
     return __umul24(row_src, uint32_t(ROW_BYTES)) + ((x ^ uint32_t(swz(t))) << 4);
   };
   uint32_t full_off[COPIES];
+  if constexpr (!F8) {
 #pragma unroll
-  for (int k = 0; k < COPIES; ++k) {
-    full_off[k] = slot_offset(k, TT);
-    asm volatile("" : "+v"(full_off[k]));
+    for (int k = 0; k < COPIES; ++k) {
+      full_off[k] = slot_offset(k, TT);
+      asm volatile("" : "+v"(full_off[k]));
+    }
   }
   auto copy_piece = [&](const Copy& cp, int k) {
     const uint32_t dst = cp.dst + uint32_t((k * NW + wave) * 64 * 16);
@@ -363,24 +380,24 @@ void decode_mla_kernel(DecodeArgs a) {
 #pragma unroll
     for (int k = 0; k < COPIES; ++k) copy_piece(cp, k);
   };
-  auto tile_valid = [&](int i) { return (bad >> (i % NBUF)) & 1 ? 0 : min(TT, t_end - (t_begin + i * TT)); };
+  auto tile_valid = [&](int i) { return (bad >> (i % NB)) & 1 ? 0 : min(TT, t_end - (t_begin + i * TT)); };
 
   // Query operand (B of the score product): lane (head 32w + r32, k-group c32) needs
   // q[head][16 ks + 8 c32 .. +7] for k-steps ks = 0..35.  The first QL k-steps of all
   // heads sit in LDS as [ks][k-group][head][8] (a wave's read is 1 KB of consecutive
   // 16-byte pieces), the rest in registers for the whole partition.
-  bf16x8_t qop[KSTEPS - QL];
+  bf16x8_t qop[KSTEPS - QLk];
   {
     const uint16_t* qb = q + (int64_t(b) * a.hq + h0) * DK;
-    for (int i = tid; i < QL * 2 * HEADS; i += 64 * NW) {   // 16-byte pieces
+    for (int i = tid; i < QLk * 2 * HEADS; i += 64 * NW) {   // 16-byte pieces
       const int ks = i / (2 * HEADS), g = (i / HEADS) % 2, hh = i % HEADS;
       *reinterpret_cast<uint4*>(q_s + 8 * i) =
           *reinterpret_cast<const uint4*>(qb + int64_t(hh) * DK + 16 * ks + 8 * g);
     }
     const uint16_t* qrow = q + (int64_t(b) * a.hq + h0 + HW * wave + r32) * DK + 8 * c32;
 #pragma unroll
-    for (int ks = QL; ks < KSTEPS; ++ks)
-      qop[ks - QL] = *reinterpret_cast<const bf16x8_t*>(qrow + 16 * ks);
+    for (int ks = QLk; ks < KSTEPS; ++ks)
+      qop[ks - QLk] = *reinterpret_cast<const bf16x8_t*>(qrow + 16 * ks);
   }
   const lds_char_t* qlds = (const lds_char_t*)q_s + (c32 * HEADS + HW * wave + r32) * 16;
   // settle every global load issued so far here, so that no wait for them is placed
@@ -416,9 +433,13 @@ void decode_mla_kernel(DecodeArgs a) {
     }
   }
 
-  const float c = a.scale * kLog2e;
+  // E4M3: the tile holds the codes' values; the key scale joins the score multiplier, and
+  // (the value being the key's first DV entries) the final division
+  float key_scale = 1.f;
+  if constexpr (F8) key_scale = a.k_scale[a.n_scales > 1 ? kvh : 0];
+  const float c = a.scale * key_scale * kLog2e;
   constexpr float kOverflow = 64.f;
-  auto tile_ptr = [&](int i) { return (const lds_char_t*)kt + (i % NBUF) * TILE_BYTES; };
+  auto tile_ptr = [&](int i) { return (const lds_char_t*)kt + (i % NB) * TILE_BYTES; };
 
   // The 36 score MFMAs of the tile at `tile` into s.  Key operands are read KA k-steps
   // ahead of their MFMA; the scheduling fences keep the order as written, so the reads
@@ -443,16 +464,16 @@ void decode_mla_kernel(DecodeArgs a) {
 #pragma unroll
     for (int ks = 0; ks < KA; ++ks) {
       kop[ks] = kread(ks);
-      if (ks < QL) qlo[ks] = qread(ks);
+      if (ks < QLk) qlo[ks] = qread(ks);
     }
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
       if (ks + KA < KSTEPS) {
         kop[(ks + KA) % (KA + 1)] = kread(ks + KA);
-        if (ks + KA < QL) qlo[(ks + KA) % (KA + 1)] = qread(ks + KA);
+        if (ks + KA < QLk) qlo[(ks + KA) % (KA + 1)] = qread(ks + KA);
       }
       const bf16x8_t kk = kop[ks % (KA + 1)];
-      const bf16x8_t qq = ks < QL ? qlo[ks % (KA + 1)] : qop[ks < QL ? 0 : ks - QL];
+      const bf16x8_t qq = ks < QLk ? qlo[ks % (KA + 1)] : qop[ks < QLk ? 0 : ks - QLk];
       if (ks == 0)
         s = mfma32_vgpr_first(kk, qq);
       else if (ks + 1 < KSTEPS)
@@ -676,21 +697,137 @@ void decode_mla_kernel(DecodeArgs a) {
       stage_table(tbl_base);
       __syncthreads();
     }
-    for (int i = 0; i < NBUF - 1 && i < n_tiles; ++i) issue_tile(i);
+    for (int i = 0; i < NB - 1 && i < n_tiles; ++i) issue_tile(i);
     for (int i = 0; i < n_tiles; ++i) {
-      const int ahead = min(NBUF - 2, n_tiles - 1 - i);
+      const int ahead = min(NB - 2, n_tiles - 1 - i);
       if (ahead >= 1) {
         PA_WAIT_VM(COPIES);
       } else {
         PA_WAIT_VM(0);
       }
       lds_barrier();
-      if (i + NBUF - 1 < n_tiles) issue_tile(i + NBUF - 1);
+      if (i + NB - 1 < n_tiles) issue_tile(i + NB - 1);
       f32x16_t s;
       scores(tile_ptr(i), s, no_filler);
       float sc[16];
       masked(s, tile_valid(i), sc);
       m_ref = fmaxf(m_ref, row_max(sc));
+    }
+    __syncthreads();
+  };
+
+  // ---- E4M3 cache: tiles staged through registers (two buffers, no copy in flight
+  // across a barrier).  Thread tid fills LDS slots s = tid + 256 k, k < COPIES: slot s is
+  // row s / 72, position s % 72 of the tile, which holds source chunk (s % 72) ^ swz(row)
+  // -- here 8 codes (8 bytes) of that row, widened to 8 bf16 (16 bytes, exact).  Rows past
+  // the partition end repeat its last row; a tile whose block id is invalid reads as
+  // zeros.  load_tile_f8 issues the loads (kept in registers), store_tile_f8 widens and
+  // writes them once the tile's buffer is free.
+  struct RawTile {
+    uint2 w[COPIES];
+  };
+  auto load_tile_f8 = [&](int i, int entry, RawTile& raw) {
+    int phys = __builtin_amdgcn_readfirstlane(entry);
+    if (phys < 0) {   // invalid block id (-2) or an entry past the row (-3)
+      if (tid == 0) raise_flag(a.flag, phys == -3 ? kErrCapacity : kErrBlockId);
+      phys = -1;
+    }
+    const int tok0 = t_begin + i * TT;
+    const uint32_t slot = uint32_t(i % NB);
+    bad = (bad & ~(1u << slot)) | (uint32_t(phys < 0) << slot);
+    const int rows = min(TT, t_end - tok0);
+    const char* src = kc + ((int64_t(max(phys, 0)) * a.hkv + kvh) * bs + (tok0 % bs)) * int64_t(ROW_BYTES_FP8);
+#pragma unroll
+    for (int k = 0; k < COPIES; ++k) {
+      const int s_ = tid + 64 * NW * k;
+      const int t = s_ / ROW_CHUNKS, x = s_ % ROW_CHUNKS;
+      const int chunk = x ^ swz(t);
+      raw.w[k] = phys >= 0
+          ? *reinterpret_cast<const uint2*>(src + min(t, rows - 1) * ROW_BYTES_FP8 + 8 * chunk)
+          : uint2{0u, 0u};
+    }
+  };
+  auto store_tile_f8 = [&](int i, const RawTile& raw) {
+    char* dst = kt + (i % NB) * TILE_BYTES;
+#pragma unroll
+    for (int k = 0; k < COPIES; ++k) {
+      const int s_ = tid + 64 * NW * k;
+      uint4 v;
+      v.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.w[k].x, 1.0f, false));
+      v.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.w[k].x, 1.0f, true));
+      v.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.w[k].y, 1.0f, false));
+      v.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.w[k].y, 1.0f, true));
+      *reinterpret_cast<uint4*>(dst + 16 * s_) = v;
+    }
+  };
+  auto restage_first = [&]() {
+    if (tbl_base != e_first) {
+      __syncthreads();
+      tbl_base = e_first;
+      stage_table(tbl_base);
+      __syncthreads();
+    }
+  };
+  // Accumulating pass: tile i+1's loads are issued before tile i's products and written
+  // after them; the softmax is the same as the bf16 path's (reference max fixed by the
+  // first tile with a valid token, overflow beyond kOverflow ends the pass).
+  auto pass_acc_f8 = [&](float& m_ref, f32x16_t (&o)[MT], float& lsum) -> bool {
+    restage_first();
+    RawTile raw;
+    load_tile_f8(0, table_entry(0), raw);
+    store_tile_f8(0, raw);
+    lds_barrier();
+    bool ok = true;
+    for (int i = 0; i < n_tiles; ++i) {
+      const bool has_next = i + 1 < n_tiles;
+      if (has_next) load_tile_f8(i + 1, table_entry(i + 1), raw);
+      f32x16_t s;
+      scores(tile_ptr(i), s, no_filler);
+      float sc[16];
+      masked(s, tile_valid(i), sc);
+      const float mx = row_max(sc);
+      if (m_ref == -INFINITY) m_ref = mx;   // first tile with a valid token of this head
+      const bool ovf = __any(mx != -INFINITY && (mx - m_ref) * c > kOverflow);
+      if (lane == 0) ovf_s[i & 1][wave] = ovf ? 1 : 0;
+      const float mc = (m_ref == -INFINITY) ? 0.f : m_ref * c;
+      float part = 0.f;
+      bf16x8_t pop[2];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float pe = __builtin_amdgcn_exp2f(fmaf(sc[e], c, -mc));
+        part += pe;
+        pop[e >> 3][e & 7] = (__bf16)pe;
+      }
+      outputs(tile_ptr(i), pop, o, no_filler);
+      lsum += part;
+      if (has_next) store_tile_f8(i + 1, raw);
+      // tile i+1 written by everyone, everyone done with tile i; the overflow flags seen
+      lds_barrier();
+      if (any_overflow(i & 1)) {
+        ok = false;
+        break;
+      }
+    }
+    __syncthreads();
+    return ok;
+  };
+  // Scores-only pass: m_ref becomes each head's exact max over the partition.
+  auto pass_max_f8 = [&](float& m_ref) {
+    restage_first();
+    RawTile raw;
+    load_tile_f8(0, table_entry(0), raw);
+    store_tile_f8(0, raw);
+    lds_barrier();
+    for (int i = 0; i < n_tiles; ++i) {
+      const bool has_next = i + 1 < n_tiles;
+      if (has_next) load_tile_f8(i + 1, table_entry(i + 1), raw);
+      f32x16_t s;
+      scores(tile_ptr(i), s, no_filler);
+      float sc[16];
+      masked(s, tile_valid(i), sc);
+      m_ref = fmaxf(m_ref, row_max(sc));
+      if (has_next) store_tile_f8(i + 1, raw);
+      lds_barrier();
     }
     __syncthreads();
   };
@@ -702,7 +839,7 @@ void decode_mla_kernel(DecodeArgs a) {
                    "+a"(o[6]), "+a"(o[7]), "+a"(o[8]), "+a"(o[9]), "+a"(o[10]), "+a"(o[11]),
                    "+a"(o[12]), "+a"(o[13]), "+a"(o[14]), "+a"(o[15]));
     const float lt = lsum + __shfl_xor(lsum, 32);
-    const float inv = 1.f / lt;
+    const float inv = (F8 ? key_scale : 1.f) / lt;
     const int hh = HW * wave + r32;
     float* orow = a.part_out + (out_row + hh) * DV + 4 * c32;
 #pragma unroll
@@ -728,9 +865,14 @@ void decode_mla_kernel(DecodeArgs a) {
   for (;;) {
     zero_tiles(o);
     lsum = 0.f;
-    if (pass_acc(m_ref, o, lsum)) break;
     float m_exact = -INFINITY;
-    pass_max(m_exact);
+    if constexpr (F8) {
+      if (pass_acc_f8(m_ref, o, lsum)) break;
+      pass_max_f8(m_exact);
+    } else {
+      if (pass_acc(m_ref, o, lsum)) break;
+      pass_max(m_exact);
+    }
     m_ref = m_exact;
   }
   finish(o, m_ref, lsum);
@@ -752,14 +894,16 @@ void decode_mla_kernel(DecodeArgs a) {
 }  // namespace
 
 bool mla_supported(const DecodeArgs& a) {
-  return a.dtype == kBF16 && a.kv_dtype == kBF16 && a.query_start == nullptr && a.v_cache == nullptr &&
+  return a.dtype == kBF16 && (a.kv_dtype == kBF16 || a.kv_dtype == kFP8) && a.query_start == nullptr &&
+         a.v_cache == nullptr &&
          a.dk == DK && a.dv == DV &&
          a.hq == HEADS * a.hkv && a.bs % TT == 0;
 }
 
-int mla_workgroups_per_cu() {
+int mla_workgroups_per_cu(int kv_dtype) {
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, (const void*)decode_mla_kernel, 64 * NW, 0) !=
+  const void* fn = kv_dtype == kFP8 ? (const void*)decode_mla_kernel<true> : (const void*)decode_mla_kernel<false>;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, 64 * NW, 0) !=
       hipSuccess) {
     (void)hipGetLastError();
     return 0;
@@ -770,12 +914,13 @@ int mla_workgroups_per_cu() {
 int mla_grid(const DecodeArgs& a) {
   // every workgroup resident: the CUs times the workgroups that fit on one, no more than
   // there can be units
-  static std::atomic<int> per_cu{0};
-  int wpc = per_cu.load(std::memory_order_relaxed);
+  static std::atomic<int> per_cu[2] = {{0}, {0}};
+  std::atomic<int>& slot = per_cu[a.kv_dtype == kFP8 ? 1 : 0];
+  int wpc = slot.load(std::memory_order_relaxed);
   if (wpc <= 0) {
-    wpc = mla_workgroups_per_cu();
+    wpc = mla_workgroups_per_cu(a.kv_dtype);
     if (wpc <= 0) wpc = 1;
-    per_cu.store(wpc, std::memory_order_relaxed);
+    slot.store(wpc, std::memory_order_relaxed);
   }
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
@@ -788,7 +933,10 @@ int mla_grid(const DecodeArgs& a) {
 }
 
 hipError_t launch_decode_mla(const DecodeArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(decode_mla_kernel, dim3(mla_grid(a)), dim3(64 * NW), 0, st, a);
+  if (a.kv_dtype == kFP8)
+    hipLaunchKernelGGL(decode_mla_kernel<true>, dim3(mla_grid(a)), dim3(64 * NW), 0, st, a);
+  else
+    hipLaunchKernelGGL(decode_mla_kernel<false>, dim3(mla_grid(a)), dim3(64 * NW), 0, st, a);
   return hipGetLastError();
 }
 

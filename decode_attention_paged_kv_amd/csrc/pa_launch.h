@@ -70,7 +70,7 @@ hipError_t launch_decode_gqa(const DecodeArgs& a, hipStream_t st);
 bool mla_supported(const DecodeArgs& a);
 hipError_t launch_decode_mla(const DecodeArgs& a, hipStream_t st);
 int gqa_workgroups_per_cu(const DecodeArgs& a);
-int mla_workgroups_per_cu();
+int mla_workgroups_per_cu(int kv_dtype);
 int generic_workgroups_per_cu(int dtype, int kv_dtype);
 hipError_t launch_merge(const float* part_out, const float* part_lse, int n_seqs, int n_parts,
                         int hq, int dv, void* out, int out_dtype, float* lse, hipStream_t st);

@@ -79,7 +79,12 @@ SMALL = [
     ("f8_generic_bf16q", [3, 90], 5, 1, 96, 80, 16, wl.BF16, 2, 3, 32, False, False),
     ("f8_latent", [65, 300], 16, 1, 576, 512, 64, wl.BF16, 1, 1, 128, True, True),
     ("f8_empty_and_one", [0, 1, 17], 8, 2, 128, 128, 16, wl.BF16, 1, 1, 16, False, True),
+    # 128 query heads on the latent cache: the matrix-core latent kernel
+    ("f8_latent128", [129, 200, 700, 1500], 128, 1, 576, 512, 64, wl.BF16, 1, 1, 256, True, True),
+    ("f8_latent128_edges", [0, 1, 65, 64], 128, 1, 576, 512, 64, wl.BF16, 1, 1, 64, True, False),
 ]
+# the latent kernel rounds each weight to bf16 once for the output product
+LATENT_REL_L2 = 4e-3
 
 
 @pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
@@ -88,7 +93,7 @@ def test_fp8_small(case):
     w = wl.small(name, lens, hq, hkv, dk, dv, bs, dt, n_shards=S, interleave=I,
                  partition_tokens=T, latent=latent, seed=sum(map(ord, name)) % 1000,
                  kv_dtype=wl.FP8, scale_per_head=per_head)
-    check_small(w)
+    check_small(w, rel_l2=LATENT_REL_L2 if (latent and hq == 128) else 1e-4)
 
 
 def test_fp8_long():
@@ -96,6 +101,30 @@ def test_fp8_long():
     w = wl.with_fp8_cache(wl.long(partition_tokens=0))
     order = np.argsort(w.context_lens)
     check_large(w, [int(order[0]), int(order[-1])])
+
+
+def test_fp8_latent():
+    """The latent batch (32 sequences, 4K-64K tokens, 128 heads, shared prefixes) with an
+    E4M3 cache, at full size."""
+    w = wl.with_fp8_cache(wl.latent())
+    order = np.argsort(w.context_lens)
+    check_large(w, [int(order[0]), int(order[-1])], rel_l2=LATENT_REL_L2)
+
+
+def test_fp8_latent_score_far_above_first_tile():
+    """E4M3 latent cache: each sequence's appended token carries a key whose score is
+    more than 64 log2 units above every other, so the partition holding it is redone
+    against the exact max.  The scale (1/8) keeps the spike's code exact (40 -> 320)."""
+    w = wl.small("f8_latent_spike", [150, 700], 128, 1, 576, 512, 64, wl.BF16, partition_tokens=512,
+                 latent=True, seed=11, kv_dtype=wl.FP8, scale_per_head=False)
+
+    def spike(T):
+        T["k_scale"].fill_(0.125)
+        T["q"][:, :, 0] += 30.0
+        T["k_new"][:, :, 0] = 40.0
+
+    step, ref = check_small(w, tweak=spike, rel_l2=LATENT_REL_L2)
+    assert ref["lse"].min() > 44.0
 
 
 def test_fp8_dcp():
