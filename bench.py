@@ -5,7 +5,7 @@ kv append, the partitioned attention (pa_decode) and the LSE merge.  Inputs are
 seeded synthetic tensors already resident in HBM.  Prints ONE JSON line.
 
   python bench.py [--steps K] [--warmup W]
-                  [--config long|dcp1|dcp16|batch|latent|latent_fp8|tiny|long_fp8|dcp1_fp8|dcp16_fp8|spec4]
+                  [--config long|dcp1|dcp16|batch|latent|latent_fp8|latent_spec2|tiny|long_fp8|dcp1_fp8|dcp16_fp8|spec4]
                   [--no-cpu-baseline] [--secondary]
 
 The default workload is the long-context step (8 sequences, log-normal lengths
@@ -48,6 +48,7 @@ def make_workload(name):
         "dcp1_fp8": lambda: wl.with_fp8_cache(wl.dcp(interleave=1)),
         "dcp16_fp8": lambda: wl.with_fp8_cache(wl.dcp(interleave=16)),
         "latent_fp8": lambda: wl.with_fp8_cache(wl.latent()),
+        "latent_spec2": lambda: wl.latent(q_len=2),
         "spec4": lambda: wl.speculative(q_len=4),
     }[name]()
 
@@ -74,6 +75,9 @@ DESCRIBE = {
     "latent_fp8": "latent (MLA-style) cache in E4M3 (one scale for the single kv head): 32 seqs, "
                   "L U[4096, 65536], 128 q heads, key 576 / value 512 (view), bf16 q, block 64, "
                   "2048-token prefixes shared by 4",
+    "latent_spec2": "speculative verification on the latent batch: 32 seqs, L U[4096, 65536], "
+                    "2 new tokens per sequence attending causally, 128 q heads on the 576-wide latent "
+                    "cache (value 512), bf16, block 64",
     "spec4": "speculative verification on the long-context batch: 8 seqs, L log-normal (median 142K), "
              "4 new tokens per sequence attending causally, 32 q / 8 kv heads, d 128, bf16, block 16, "
              "partition size chosen by pa_choose_partition_tokens",
@@ -449,7 +453,7 @@ def main():
     if a.secondary:
         sec = {}
         for name in ("dcp1", "dcp16", "batch", "latent", "tiny", "long_fp8", "dcp1_fp8", "dcp16_fp8",
-                     "latent_fp8", "spec4"):
+                     "latent_fp8", "latent_spec2", "spec4"):
             if name == a.config:
                 continue
             s = run_config(name, a.steps, a.warmup, False, settle_s=a.settle)

@@ -38,6 +38,8 @@ _SIGS = {
     "pa_max_partitions": [_i32, _i32, _i32, _i32],
     "pa_default_partition_tokens": [_i32, _i32, _i32, _i32, _i32, _i32],
     "pa_choose_partition_tokens": [_p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32],
+    "pa_choose_partition_tokens_multi": [_p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                         _i32],
     "pa_kv_append_fp8": [_p, _p, _i32, _p, _p, _p, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32, _i64,
                          _p, _p],
     "pa_decode_fp8": [_p, _p, _p, _p, _p, _i32, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i64, _i32,
@@ -141,6 +143,20 @@ def pa_choose_partition_tokens(context_lens_host, n_q_heads, n_kv_heads, dk, dv,
     return int(lib.pa_choose_partition_tokens(lens.ctypes.data_as(ctypes.c_void_p), int(lens.size),
                                               n_q_heads, n_kv_heads, dk, dv, block_size, code,
                                               int(bool(latent)), n_shards, interleave))
+
+
+def pa_choose_partition_tokens_multi(context_lens_host, max_q_len, n_q_heads, n_kv_heads, dk, dv,
+                                     block_size, dtype, latent, n_shards=1, interleave=1) -> int:
+    """As ``pa_choose_partition_tokens``, for ``pa_decode_multi`` with grid bound
+    ``max_q_len`` on new tokens per sequence (``n_q_heads`` unscaled)."""
+    import numpy as np
+
+    lens = np.ascontiguousarray(np.asarray(context_lens_host, dtype=np.int32))
+    code = {torch.float32: PA_F32, torch.bfloat16: PA_BF16, torch.uint8: PA_FP8_E4M3}[dtype]
+    return int(lib.pa_choose_partition_tokens_multi(lens.ctypes.data_as(ctypes.c_void_p),
+                                                    int(lens.size), max_q_len, n_q_heads, n_kv_heads,
+                                                    dk, dv, block_size, code, int(bool(latent)),
+                                                    n_shards, interleave))
 
 
 # ------------------------------------------------------------------ entry points

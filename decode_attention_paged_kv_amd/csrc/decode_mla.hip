@@ -244,11 +244,17 @@ void decode_mla_kernel(DecodeArgs a) {
     w_total = __builtin_amdgcn_readfirstlane(__shfl(w_incl, 63));
   };
   load_chunk();
+  // Several new tokens per sequence: each (pair, partition) slot holds max_q units per KV
+  // head, one per new token (units past a sequence's own count are skipped).
+  const int MQ = a.query_start ? a.max_q : 1;
 
   for (int unit = blockIdx.x;; unit += gridDim.x) {
-    // ---- resolve unit -> (pair y, partition p, KV head kvh); stop past the last pair
-    const int slot = unit / a.hkv;
-    const int kvh = unit - slot * a.hkv;
+    // ---- resolve unit -> (pair y, partition p, new token qi, KV head kvh); stop past the
+    // last pair
+    const int slot = unit / (a.hkv * MQ);
+    const int qk = unit - slot * (a.hkv * MQ);
+    const int qi = qk / a.hkv;
+    const int kvh = qk - qi * a.hkv;
     while (slot >= w_base + w_total && w_chunk < Y) {
       w_base += w_total;
       w_chunk += 64;
@@ -264,10 +270,30 @@ void decode_mla_kernel(DecodeArgs a) {
     const int r = y - b * a.n_shards;
     const int h0 = kvh * HEADS;
     const int L = a.context_lens[b];
-    const int Lr = shard_len(L, a.n_shards, a.interleave, r);
+    // q row of the unit and how many of the shard's tokens it sees: all of them, or for
+    // new token qi of nq (global position L - nq + qi) those at or before its position
+    int qr = b;
+    int Lq = shard_len(L, a.n_shards, a.interleave, r);
+    if (a.query_start) {
+      const int row0 = a.query_start[b];
+      const int nq = a.query_start[b + 1] - row0;
+      if (nq > L || nq > a.max_q || row0 < 0 || row0 + nq > a.n_rows) {   // rows left unwritten
+        if (tid == 0 && p == 0 && qi == 0 && kvh == 0) raise_flag(a.flag, kErrCapacity);
+        continue;
+      }
+      if (qi >= nq) continue;
+      qr = row0 + qi;
+      Lq = visible_on_shard(L - nq + qi, a.n_shards, a.interleave, r);
+    }
     const int t_begin = p * T;
-    const int t_end = min(t_begin + T, Lr);
-    const int64_t out_row = ((int64_t(b) * a.n_shards + r) * a.max_parts + p) * a.hq + h0;
+    const int t_end = min(t_begin + T, Lq);
+    const int64_t out_row = ((int64_t(qr) * a.n_shards + r) * a.max_parts + p) * a.hq + h0;
+    if (t_end <= t_begin) {   // a new token that sees none of the partition's tokens
+      for (int i = tid; i < HEADS; i += 64 * NW) a.part_lse[out_row + i] = -INFINITY;
+      if (p == 0)
+        for (int i = tid; i < HEADS * DV; i += 64 * NW) a.part_out[out_row * DV + i] = 0.f;
+      continue;
+    }
     __syncthreads();   // the previous unit is done with the LDS
 
   const int32_t* row = a.block_table + (int64_t(b) * a.n_shards + r) * a.max_blocks;
@@ -388,13 +414,13 @@ void decode_mla_kernel(DecodeArgs a) {
   // 16-byte pieces), the rest in registers for the whole partition.
   bf16x8_t qop[KSTEPS - QLk];
   {
-    const uint16_t* qb = q + (int64_t(b) * a.hq + h0) * DK;
+    const uint16_t* qb = q + (int64_t(qr) * a.hq + h0) * DK;
     for (int i = tid; i < QLk * 2 * HEADS; i += 64 * NW) {   // 16-byte pieces
       const int ks = i / (2 * HEADS), g = (i / HEADS) % 2, hh = i % HEADS;
       *reinterpret_cast<uint4*>(q_s + 8 * i) =
           *reinterpret_cast<const uint4*>(qb + int64_t(hh) * DK + 16 * ks + 8 * g);
     }
-    const uint16_t* qrow = q + (int64_t(b) * a.hq + h0 + HW * wave + r32) * DK + 8 * c32;
+    const uint16_t* qrow = q + (int64_t(qr) * a.hq + h0 + HW * wave + r32) * DK + 8 * c32;
 #pragma unroll
     for (int ks = QLk; ks < KSTEPS; ++ks)
       qop[ks - QLk] = *reinterpret_cast<const bf16x8_t*>(qrow + 16 * ks);
@@ -879,23 +905,32 @@ void decode_mla_kernel(DecodeArgs a) {
   }
 
   // partitions past a pair's last one: lse = -inf; their output rows are not written,
-  // except in partition 0 of a pair with no tokens, where they are 0
+  // except in partition 0 of a pair with no tokens, where they are 0 (for every q row of
+  // the sequence; none for rows of a sequence whose query_start is invalid)
   for (int y = blockIdx.x; y < Y; y += gridDim.x) {
     const int n = parts_of(y);
-    for (int p = n; p < a.max_parts; ++p)
-      for (int i = tid; i < a.hq; i += 64 * NW)
-        a.part_lse[(int64_t(y) * a.max_parts + p) * a.hq + i] = -INFINITY;
-    if (n == 0)
-      for (int64_t i = tid; i < int64_t(a.hq) * DV; i += 64 * NW)
-        a.part_out[int64_t(y) * a.max_parts * a.hq * DV + i] = 0.f;
+    const int b = y / a.n_shards;
+    const int r = y - b * a.n_shards;
+    int row0 = b, nq = 1;
+    if (a.query_start) {
+      row0 = a.query_start[b];
+      nq = a.query_start[b + 1] - row0;
+      if (nq > a.context_lens[b] || nq > a.max_q || row0 < 0 || row0 + nq > a.n_rows) nq = 0;
+    }
+    for (int qi = 0; qi < nq; ++qi) {
+      const int64_t base = (int64_t(row0 + qi) * a.n_shards + r) * a.max_parts;
+      for (int p = n; p < a.max_parts; ++p)
+        for (int i = tid; i < a.hq; i += 64 * NW) a.part_lse[(base + p) * a.hq + i] = -INFINITY;
+      if (n == 0)
+        for (int64_t i = tid; i < int64_t(a.hq) * DV; i += 64 * NW) a.part_out[base * a.hq * DV + i] = 0.f;
+    }
   }
 }
 
 }  // namespace
 
 bool mla_supported(const DecodeArgs& a) {
-  return a.dtype == kBF16 && (a.kv_dtype == kBF16 || a.kv_dtype == kFP8) && a.query_start == nullptr &&
-         a.v_cache == nullptr &&
+  return a.dtype == kBF16 && (a.kv_dtype == kBF16 || a.kv_dtype == kFP8) && a.v_cache == nullptr &&
          a.dk == DK && a.dv == DV &&
          a.hq == HEADS * a.hkv && a.bs % TT == 0;
 }
@@ -928,7 +963,8 @@ int mla_grid(const DecodeArgs& a) {
     (void)hipGetLastError();
     cus = 256;
   }
-  const int64_t units = int64_t(a.n_seqs) * a.n_shards * a.max_parts * a.hkv;
+  const int64_t units = int64_t(a.n_seqs) * a.n_shards * a.max_parts * a.hkv *
+                        (a.query_start ? a.max_q : 1);
   return int(std::max<int64_t>(1, std::min<int64_t>(int64_t(cus) * wpc, units)));
 }
 

@@ -102,10 +102,33 @@ int32_t pa_default_partition_tokens(int32_t n_seqs, int32_t n_kv_heads, int32_t 
   return T;
 }
 
+static int32_t choose_partition_tokens(const int32_t* context_lens_host, int32_t n_seqs,
+                                       int32_t max_q, int32_t n_q_heads, int32_t n_kv_heads,
+                                       int32_t dk, int32_t dv, int32_t block_size, int32_t dtype,
+                                       int32_t latent, int32_t n_shards, int32_t interleave);
+
 int32_t pa_choose_partition_tokens(const int32_t* context_lens_host, int32_t n_seqs,
                                    int32_t n_q_heads, int32_t n_kv_heads, int32_t dk, int32_t dv,
                                    int32_t block_size, int32_t dtype, int32_t latent,
                                    int32_t n_shards, int32_t interleave) {
+  return choose_partition_tokens(context_lens_host, n_seqs, 0, n_q_heads, n_kv_heads, dk, dv,
+                                 block_size, dtype, latent, n_shards, interleave);
+}
+
+int32_t pa_choose_partition_tokens_multi(const int32_t* context_lens_host, int32_t n_seqs,
+                                         int32_t max_q_len, int32_t n_q_heads, int32_t n_kv_heads,
+                                         int32_t dk, int32_t dv, int32_t block_size, int32_t dtype,
+                                         int32_t latent, int32_t n_shards, int32_t interleave) {
+  if (max_q_len < 1) return -1;
+  return choose_partition_tokens(context_lens_host, n_seqs, max_q_len, n_q_heads, n_kv_heads, dk,
+                                 dv, block_size, dtype, latent, n_shards, interleave);
+}
+
+// max_q == 0: pa_decode's launch (one new token, no query_start); else pa_decode_multi's
+static int32_t choose_partition_tokens(const int32_t* context_lens_host, int32_t n_seqs,
+                                       int32_t max_q, int32_t n_q_heads, int32_t n_kv_heads,
+                                       int32_t dk, int32_t dv, int32_t block_size, int32_t dtype,
+                                       int32_t latent, int32_t n_shards, int32_t interleave) {
   if (!context_lens_host || n_seqs < 1 || n_q_heads < 1 || n_kv_heads < 1 ||
       n_q_heads % n_kv_heads != 0 || block_size < 1 || block_size > PA_MAX_BLOCK_SIZE ||
       n_shards < 1 || interleave < 1 || int64_t(n_shards) * interleave > (int64_t(1) << 30) ||
@@ -119,7 +142,8 @@ int32_t pa_choose_partition_tokens(const int32_t* context_lens_host, int32_t n_s
   a.bs = block_size;
   a.dtype = dtype == PA_FP8_E4M3 ? PA_BF16 : dtype;  // E4M3 cache: bf16 queries
   a.kv_dtype = dtype;
-  a.max_q = 1;  // (new token, head) columns: callers with several new tokens scale n_q_heads
+  a.max_q = max_q > 0 ? max_q : 1;
+  a.query_start = max_q > 0 ? &a.n_seqs : nullptr;  // only its NULL-ness matters
   a.v_cache = latent ? nullptr : static_cast<const void*>(&a);  // only its NULL-ness matters
   std::vector<int32_t> shard_len_v(size_t(n_seqs) * n_shards);
   int32_t longest = 0;

@@ -133,10 +133,10 @@ class MultiDecodeStep:
         self.hq, self.hkv, self.dk, self.dv = n_q_heads, n_kv_heads, dk, dv
         self.block_size, self.n_shards, self.interleave = block_size, n_shards, interleave
         if not partition_tokens and context_lens_host is not None:
-            # the kernels treat (new token, head) pairs as columns: as many heads per KV head
-            partition_tokens = L.pa_choose_partition_tokens(context_lens_host, n_q_heads * max_q_len,
-                                                            n_kv_heads, dk, dv, block_size, kv_dtype,
-                                                            latent, n_shards, interleave)
+            partition_tokens = L.pa_choose_partition_tokens_multi(context_lens_host, max_q_len,
+                                                                  n_q_heads, n_kv_heads, dk, dv,
+                                                                  block_size, kv_dtype, latent,
+                                                                  n_shards, interleave)
         if not partition_tokens:
             partition_tokens = L.pa_default_partition_tokens(n_seqs, n_kv_heads, max_context_len,
                                                              n_shards, interleave, block_size)

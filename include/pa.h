@@ -381,6 +381,19 @@ int32_t pa_choose_partition_tokens(const int32_t* context_lens_host, int32_t n_s
                                    int32_t block_size, int32_t dtype, int32_t latent,
                                    int32_t n_shards, int32_t interleave);
 
+/*
+ * pa_choose_partition_tokens_multi -- the same choice for pa_decode_multi with
+ * max_q_len (>= 1) as its grid bound on new tokens per sequence: the model takes the
+ * launch pa_decode_multi makes (in the GQA and generic kernels the (new token, head)
+ * pairs of a KV head share workgroups; the latent kernel takes one unit of work per new
+ * token).  context_lens_host and the other arguments as in pa_choose_partition_tokens
+ * (n_q_heads unscaled).  Returns -1 on invalid arguments.
+ */
+int32_t pa_choose_partition_tokens_multi(const int32_t* context_lens_host, int32_t n_seqs,
+                                         int32_t max_q_len, int32_t n_q_heads, int32_t n_kv_heads,
+                                         int32_t dk, int32_t dv, int32_t block_size, int32_t dtype,
+                                         int32_t latent, int32_t n_shards, int32_t interleave);
+
 /* Message of the last failed call on this thread ("" if none). */
 const char* pa_last_error(void);
 

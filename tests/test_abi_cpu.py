@@ -105,6 +105,31 @@ def test_choose_partition_tokens():
     assert P.pa_choose_partition_tokens(lens, 6, 4, 64, 64, 4, torch.float32, False) == -1
 
 
+def test_choose_partition_tokens_multi():
+    """The multi-token chooser models pa_decode_multi's own launch: one new token gives
+    the single-token choice; on the latent shape two new tokens double the latent
+    kernel's units (the partition shrinks, never grows), where scaling the head count
+    instead would leave the latent kernel's model."""
+    import torch
+
+    import workloads as wl
+
+    for w in (wl.long(), wl.latent(), wl.small("x", [5, 900], 8, 2, 64, 64, 32, wl.BF16)):
+        args = (w.n_q_heads, w.n_kv_heads, w.dk, w.dv, w.block_size, torch.bfloat16, w.latent,
+                w.n_shards, w.interleave)
+        T1 = P.pa_choose_partition_tokens(w.context_lens, *args)
+        assert P.pa_choose_partition_tokens_multi(w.context_lens, 1, *args) == T1
+        T2 = P.pa_choose_partition_tokens_multi(w.context_lens, 2, *args)
+        assert T2 > 0 and T2 % w.block_size == 0
+        if w.latent:
+            assert T2 <= T1
+            scaled = P.pa_choose_partition_tokens(w.context_lens, 2 * w.n_q_heads, *args[1:])
+            assert T2 != scaled
+    lens = np.array([10], np.int32)
+    assert P.pa_choose_partition_tokens_multi(lens, 0, 4, 1, 64, 64, 4, torch.bfloat16, False) == -1
+    assert P.lib.pa_choose_partition_tokens_multi(None, 1, 2, 4, 1, 64, 64, 4, 0, 0, 1, 1) == -1
+
+
 def test_fp8_entry_points_reject_bad_arguments():
     vp = ctypes.c_void_p(0x1000)
     ap = P.lib.pa_kv_append_fp8

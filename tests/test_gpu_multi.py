@@ -32,6 +32,13 @@ SMALL = [
     ("mq_whole_sequence", [40, 77], [40, 77], 8, 2, 128, 128, 16, wl.BF16, 1, 1, 32, False, ""),
     ("mq_latent_fp8_empty", [70, 0, 9], [3, 0, 9], 16, 1, 576, 512, 64, wl.BF16, 1, 1, 64, True, wl.FP8),
     ("mq_dcp_fp8_d64", [200, 45], [6, 1], 16, 4, 64, 64, 16, wl.BF16, 3, 2, 32, False, wl.FP8),
+    # 128 query heads on the latent cache: the matrix-core latent kernel, one unit per new
+    # token -- ragged partitions; shards on which a new token sees none of a partition's
+    # tokens; an E4M3 cache with an empty sequence and one whose tokens are all new
+    ("mq_latent128", [129, 300, 700], [1, 4, 3], 128, 1, 576, 512, 64, wl.BF16, 1, 1, 128, True, ""),
+    ("mq_latent128_dcp", [300, 90], [5, 2], 128, 1, 576, 512, 64, wl.BF16, 3, 2, 64, True, ""),
+    ("mq_latent128_fp8", [70, 0, 9, 64], [3, 0, 9, 1], 128, 1, 576, 512, 64, wl.BF16, 1, 1, 64, True,
+     wl.FP8),
 ]
 
 
@@ -71,6 +78,14 @@ def test_multi_speculative_long():
     w = wl.speculative(q_len=4)
     order = np.argsort(w.context_lens)
     check_large(w, [int(order[0]), int(order[-1])])
+
+
+def test_multi_latent_speculative():
+    """The latent batch with 2 new tokens per sequence, at full size (the matrix-core
+    latent kernel, one unit per new token)."""
+    w = wl.latent(q_len=2)
+    order = np.argsort(w.context_lens)
+    check_large(w, [int(order[0]), int(order[-1])], rel_l2=4e-3)
 
 
 def test_multi_error_flag_on_too_many_new_tokens():

@@ -237,14 +237,18 @@ def dcp(interleave: int = 1, n_shards: int = 4, context_len: int = 200000, seed:
                          interleave=interleave, partition_tokens=partition_tokens, seed=seed))
 
 
-def latent(seed: int = 5, n_seqs: int = 32, lo: int = 4096, hi: int = 65536) -> Workload:
+def latent(seed: int = 5, n_seqs: int = 32, lo: int = 4096, hi: int = 65536,
+           q_len: int = 0) -> Workload:
     """Latent (MLA-style) cache: 32 sequences, 128 query heads on 1 KV head, key
     width 576 with the value the first 512 entries, context U[4,096, 65,536],
-    bf16, 64-token blocks; groups of 4 sequences share a 2,048-token prefix."""
+    bf16, 64-token blocks; groups of 4 sequences share a 2,048-token prefix.
+    ``q_len`` > 0: each sequence's last ``q_len`` tokens are new (speculative
+    verification, causal among themselves)."""
     rng = np.random.default_rng(seed)
     L = rng.integers(lo, hi + 1, n_seqs).astype(np.int32)
-    return plan(Workload("latent", 128, 1, 576, 512, 64, BF16, L, latent=True, prefix_group=4,
-                         prefix_tokens=2048, seed=seed))
+    return plan(Workload(f"latent_spec{q_len}" if q_len else "latent", 128, 1, 576, 512, 64, BF16, L,
+                         latent=True, prefix_group=4, prefix_tokens=2048, seed=seed,
+                         q_lens=np.full(L.size, q_len, np.int32) if q_len else None))
 
 
 def small(name: str, lens, hq: int, hkv: int, dk: int, dv: int, bs: int, dtype: str,
