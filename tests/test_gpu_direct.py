@@ -1,8 +1,8 @@
 """One shard and one partition per sequence: the step skips the merge and returns the
 partials themselves (a single part has weight exp(lse - lse) = 1, and the decode writes
 zeros into partition 0 of an empty sequence).  The outputs must equal what
-pa_merge_lse makes of the same partials, for the MFMA, generic and latent kernels and
-for several new tokens per sequence, with empty sequences among them; and the whole
+pa_merge_lse makes of the same partials, for the MFMA, generic and latent kernels (the
+latent one also with an E4M3 cache) and for several new tokens per sequence, with empty sequences among them; and the whole
 step is checked against the oracle (``check_small``)."""
 import pytest
 import torch
@@ -27,6 +27,10 @@ CASES = [
     ("generic_f32", [5, 0, 130], 6, 3, 40, 24, 8, wl.F32, 136, False, None, ""),
     ("latent", [0, 65, 300], 16, 1, 576, 512, 64, wl.BF16, 320, True, None, ""),
     ("multi", [0, 40, 77], 32, 8, 128, 128, 16, wl.BF16, 80, False, [0, 3, 5], ""),
+    # 128 heads on the latent cache: the matrix-core latent kernel
+    ("latent128", [0, 65, 300], 128, 1, 576, 512, 64, wl.BF16, 320, True, None, ""),
+    ("latent128_e4m3", [0, 65, 300], 128, 1, 576, 512, 64, wl.BF16, 320, True, None, wl.FP8),
+    ("latent128_multi", [0, 65, 300], 128, 1, 576, 512, 64, wl.BF16, 320, True, [0, 2, 3], ""),
 ]
 
 
