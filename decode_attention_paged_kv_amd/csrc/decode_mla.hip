@@ -42,6 +42,9 @@
 //    fills their rows with the partition's last row, and a tile whose block id is
 //    invalid is copied from a zero tile, so every value the weights meet is finite and a
 //    masked token adds exactly 0.
+// Fewer query heads per KV head (a tensor-parallel share of a latent model's heads) run
+// on the same 128-row products: rows past the real head count take a zero query and are
+// never written, since the kernel's time is set by its instruction stream, not its rows.
 // LDS tiles are unpadded and swizzled at 16-byte granularity: chunk c of token row t sits
 // at position c ^ g(t), g(t) = 4*bit1(t) + bits2..3(t), which spreads both the 32 rows of
 // a key-operand read and the 4 rows of a transposing read over distinct banks.
@@ -215,6 +218,9 @@ void decode_mla_kernel(DecodeArgs a) {
   const int bs = a.bs;
   const int T = a.part_tokens;
   const int Y = a.n_seqs * a.n_shards;   // (sequence, shard) pairs
+  // query heads per KV head (<= HEADS): the products always run on HEADS rows; rows past
+  // nh read a zero query and are never written
+  const int nh = a.hq / a.hkv;
 
   // Units of work are the non-empty (pair y, partition p, KV head) triples, numbered
   // densely in that order (KV head fastest); workgroup g takes units g, g + G, g + 2G, ..
@@ -268,7 +274,7 @@ void decode_mla_kernel(DecodeArgs a) {
     const int p = rel - (__builtin_amdgcn_readfirstlane(__shfl(w_incl - w_cnt, j)));
     const int b = y / a.n_shards;
     const int r = y - b * a.n_shards;
-    const int h0 = kvh * HEADS;
+    const int h0 = kvh * nh;
     const int L = a.context_lens[b];
     // q row of the unit and how many of the shard's tokens it sees: all of them, or for
     // new token qi of nq (global position L - nq + qi) those at or before its position
@@ -289,9 +295,9 @@ void decode_mla_kernel(DecodeArgs a) {
     const int t_end = min(t_begin + T, Lq);
     const int64_t out_row = ((int64_t(qr) * a.n_shards + r) * a.max_parts + p) * a.hq + h0;
     if (t_end <= t_begin) {   // a new token that sees none of the partition's tokens
-      for (int i = tid; i < HEADS; i += 64 * NW) a.part_lse[out_row + i] = -INFINITY;
+      for (int i = tid; i < nh; i += 64 * NW) a.part_lse[out_row + i] = -INFINITY;
       if (p == 0)
-        for (int i = tid; i < HEADS * DV; i += 64 * NW) a.part_out[out_row * DV + i] = 0.f;
+        for (int i = tid; i < nh * DV; i += 64 * NW) a.part_out[out_row * DV + i] = 0.f;
       continue;
     }
     __syncthreads();   // the previous unit is done with the LDS
@@ -418,12 +424,18 @@ void decode_mla_kernel(DecodeArgs a) {
     for (int i = tid; i < QLk * 2 * HEADS; i += 64 * NW) {   // 16-byte pieces
       const int ks = i / (2 * HEADS), g = (i / HEADS) % 2, hh = i % HEADS;
       *reinterpret_cast<uint4*>(q_s + 8 * i) =
-          *reinterpret_cast<const uint4*>(qb + int64_t(hh) * DK + 16 * ks + 8 * g);
+          hh < nh ? *reinterpret_cast<const uint4*>(qb + int64_t(hh) * DK + 16 * ks + 8 * g)
+                  : make_uint4(0, 0, 0, 0);
     }
-    const uint16_t* qrow = q + (int64_t(qr) * a.hq + h0 + HW * wave + r32) * DK + 8 * c32;
+    if (HW * wave + r32 < nh) {
+      const uint16_t* qrow = q + (int64_t(qr) * a.hq + h0 + HW * wave + r32) * DK + 8 * c32;
 #pragma unroll
-    for (int ks = QLk; ks < KSTEPS; ++ks)
-      qop[ks - QLk] = *reinterpret_cast<const bf16x8_t*>(qrow + 16 * ks);
+      for (int ks = QLk; ks < KSTEPS; ++ks)
+        qop[ks - QLk] = *reinterpret_cast<const bf16x8_t*>(qrow + 16 * ks);
+    } else {
+#pragma unroll
+      for (int ks = QLk; ks < KSTEPS; ++ks) qop[ks - QLk] = bf16x8_t{};
+    }
   }
   const lds_char_t* qlds = (const lds_char_t*)q_s + (c32 * HEADS + HW * wave + r32) * 16;
   // settle every global load issued so far here, so that no wait for them is placed
@@ -867,6 +879,7 @@ void decode_mla_kernel(DecodeArgs a) {
     const float lt = lsum + __shfl_xor(lsum, 32);
     const float inv = (F8 ? key_scale : 1.f) / lt;
     const int hh = HW * wave + r32;
+    if (hh >= nh) return;   // a padding row
     float* orow = a.part_out + (out_row + hh) * DV + 4 * c32;
 #pragma unroll
     for (int m = 0; m < MT; ++m)
@@ -931,8 +944,8 @@ void decode_mla_kernel(DecodeArgs a) {
 
 bool mla_supported(const DecodeArgs& a) {
   return a.dtype == kBF16 && (a.kv_dtype == kBF16 || a.kv_dtype == kFP8) && a.v_cache == nullptr &&
-         a.dk == DK && a.dv == DV &&
-         a.hq == HEADS * a.hkv && a.bs % TT == 0;
+         a.dk == DK && a.dv == DV && a.hkv > 0 && a.hq % a.hkv == 0 && a.hq / a.hkv <= HEADS &&
+         a.bs % TT == 0;
 }
 
 int mla_workgroups_per_cu(int kv_dtype) {

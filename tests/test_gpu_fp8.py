@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import workloads as wl
-from gpu_harness import bits_equal, check_large, check_small, say, to_np
+from gpu_harness import bits_equal, check_large, check_small, rel_l2_bar, say, to_np
 from oracle import fp8_kv as f8
 
 pytestmark = pytest.mark.gpu
@@ -93,7 +93,7 @@ def test_fp8_small(case):
     w = wl.small(name, lens, hq, hkv, dk, dv, bs, dt, n_shards=S, interleave=I,
                  partition_tokens=T, latent=latent, seed=sum(map(ord, name)) % 1000,
                  kv_dtype=wl.FP8, scale_per_head=per_head)
-    check_small(w, rel_l2=LATENT_REL_L2 if (latent and hq == 128) else 1e-4)
+    check_small(w, rel_l2=rel_l2_bar(w))
 
 
 def test_fp8_long():

@@ -4,6 +4,7 @@ Small workloads are compared whole: routing, append and gather bit for bit,
 every partition's output and LSE, and the merged result.  The full-size
 workloads run at their real sizes with the partition size the benchmark uses
 and are compared on sampled sequences (see ``gpu_harness.check_large``)."""
+import dataclasses
 import zlib
 
 import numpy as np
@@ -11,7 +12,7 @@ import pytest
 import torch
 
 import workloads as wl
-from gpu_harness import check_large, check_small, run_library, say
+from gpu_harness import check_large, check_small, rel_l2_bar, run_library, say
 from oracle import paged_attention as pa
 
 pytestmark = pytest.mark.gpu
@@ -66,6 +67,32 @@ def test_latent():
 
 
 LATENT_REL_L2 = 4e-3
+
+
+def test_latent_16_heads():
+    """The latent batch with 16 query heads (a tensor-parallel share of 128), at full size:
+    the latent kernel pads its products to 128 rows and writes only the real ones."""
+    w = dataclasses.replace(wl.latent(), n_q_heads=16, name="latent_h16")
+    order = np.argsort(w.context_lens)
+    check_large(w, [int(order[0]), int(order[-1])], rel_l2=LATENT_REL_L2)
+
+
+# name, lens, hq, hkv, S, I, T, kv dtype: fewer than 128 query heads per latent KV head
+FEWER_HEADS = [
+    ("latent_h16", [0, 1, 65, 700], 16, 1, 1, 1, 256, ""),
+    ("latent_h64_2kv", [300, 129], 128, 2, 1, 1, 128, ""),
+    ("latent_h32_e4m3", [70, 513], 32, 1, 1, 1, 128, wl.FP8),
+    ("latent_h16_dcp", [300, 90], 16, 1, 3, 2, 64, ""),
+    ("latent_h1", [33, 200], 1, 1, 1, 1, 64, ""),
+]
+
+
+@pytest.mark.parametrize("case", FEWER_HEADS, ids=[c[0] for c in FEWER_HEADS])
+def test_latent_fewer_heads(case):
+    name, lens, hq, hkv, S, I, T, kv = case
+    w = wl.small(name, lens, hq, hkv, 576, 512, 64, wl.BF16, n_shards=S, interleave=I,
+                 partition_tokens=T, latent=True, seed=sum(map(ord, name)) % 1000, kv_dtype=kv)
+    check_small(w, rel_l2=LATENT_REL_L2)
 
 
 # ------------------------------------------------------------------ exact probes at full size
@@ -157,7 +184,7 @@ def test_sweep(case):
     pg, pt = prefix or (1, 0)
     w = wl.small(name, lens, hq, hkv, dk, dv, bs, dt, n_shards=S, interleave=I,
                  partition_tokens=T, latent=latent, prefix_group=pg, prefix_tokens=pt, seed=zlib.crc32(name.encode()) % 1000)
-    check_small(w, rel_l2=LATENT_REL_L2 if (latent and hq >= 16 and dt == wl.BF16) else 1e-4)
+    check_small(w, rel_l2=rel_l2_bar(w))
 
 
 def test_partition_size_independence():
