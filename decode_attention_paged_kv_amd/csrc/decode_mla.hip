@@ -218,9 +218,11 @@ void decode_mla_kernel(DecodeArgs a) {
   const int bs = a.bs;
   const int T = a.part_tokens;
   const int Y = a.n_seqs * a.n_shards;   // (sequence, shard) pairs
-  // query heads per KV head (<= HEADS): the products always run on HEADS rows; rows past
-  // nh read a zero query and are never written
+  // query heads per KV head, taken HEADS at a time (NG groups, each a unit of its own):
+  // the products always run on HEADS rows; rows past a group's real count read a zero
+  // query and are never written
   const int nh = a.hq / a.hkv;
+  const int NG = (nh + HEADS - 1) / HEADS;
 
   // Units of work are the non-empty (pair y, partition p, KV head) triples, numbered
   // densely in that order (KV head fastest); workgroup g takes units g, g + G, g + 2G, ..
@@ -250,17 +252,21 @@ void decode_mla_kernel(DecodeArgs a) {
     w_total = __builtin_amdgcn_readfirstlane(__shfl(w_incl, 63));
   };
   load_chunk();
-  // Several new tokens per sequence: each (pair, partition) slot holds max_q units per KV
-  // head, one per new token (units past a sequence's own count are skipped).
+  // Several new tokens per sequence: each (pair, partition) slot holds max_q units per
+  // (head group, KV head), one per new token (units past a sequence's own count are
+  // skipped).
   const int MQ = a.query_start ? a.max_q : 1;
+  const int per_q = a.hkv * NG;
 
   for (int unit = blockIdx.x;; unit += gridDim.x) {
-    // ---- resolve unit -> (pair y, partition p, new token qi, KV head kvh); stop past the
-    // last pair
-    const int slot = unit / (a.hkv * MQ);
-    const int qk = unit - slot * (a.hkv * MQ);
-    const int qi = qk / a.hkv;
-    const int kvh = qk - qi * a.hkv;
+    // ---- resolve unit -> (pair y, partition p, new token qi, head group grp, KV head
+    // kvh); stop past the last pair
+    const int slot = unit / (per_q * MQ);
+    const int qk = unit - slot * (per_q * MQ);
+    const int qi = qk / per_q;
+    const int gk = qk - qi * per_q;
+    const int grp = gk / a.hkv;
+    const int kvh = gk - grp * a.hkv;
     while (slot >= w_base + w_total && w_chunk < Y) {
       w_base += w_total;
       w_chunk += 64;
@@ -274,7 +280,8 @@ void decode_mla_kernel(DecodeArgs a) {
     const int p = rel - (__builtin_amdgcn_readfirstlane(__shfl(w_incl - w_cnt, j)));
     const int b = y / a.n_shards;
     const int r = y - b * a.n_shards;
-    const int h0 = kvh * nh;
+    const int h0 = kvh * nh + grp * HEADS;   // the unit's first query head
+    const int nrow = min(HEADS, nh - grp * HEADS);   // its real rows
     const int L = a.context_lens[b];
     // q row of the unit and how many of the shard's tokens it sees: all of them, or for
     // new token qi of nq (global position L - nq + qi) those at or before its position
@@ -284,7 +291,7 @@ void decode_mla_kernel(DecodeArgs a) {
       const int row0 = a.query_start[b];
       const int nq = a.query_start[b + 1] - row0;
       if (nq > L || nq > a.max_q || row0 < 0 || row0 + nq > a.n_rows) {   // rows left unwritten
-        if (tid == 0 && p == 0 && qi == 0 && kvh == 0) raise_flag(a.flag, kErrCapacity);
+        if (tid == 0 && p == 0 && qi == 0 && grp == 0 && kvh == 0) raise_flag(a.flag, kErrCapacity);
         continue;
       }
       if (qi >= nq) continue;
@@ -295,9 +302,9 @@ void decode_mla_kernel(DecodeArgs a) {
     const int t_end = min(t_begin + T, Lq);
     const int64_t out_row = ((int64_t(qr) * a.n_shards + r) * a.max_parts + p) * a.hq + h0;
     if (t_end <= t_begin) {   // a new token that sees none of the partition's tokens
-      for (int i = tid; i < nh; i += 64 * NW) a.part_lse[out_row + i] = -INFINITY;
+      for (int i = tid; i < nrow; i += 64 * NW) a.part_lse[out_row + i] = -INFINITY;
       if (p == 0)
-        for (int i = tid; i < nh * DV; i += 64 * NW) a.part_out[out_row * DV + i] = 0.f;
+        for (int i = tid; i < nrow * DV; i += 64 * NW) a.part_out[out_row * DV + i] = 0.f;
       continue;
     }
     __syncthreads();   // the previous unit is done with the LDS
@@ -424,10 +431,10 @@ void decode_mla_kernel(DecodeArgs a) {
     for (int i = tid; i < QLk * 2 * HEADS; i += 64 * NW) {   // 16-byte pieces
       const int ks = i / (2 * HEADS), g = (i / HEADS) % 2, hh = i % HEADS;
       *reinterpret_cast<uint4*>(q_s + 8 * i) =
-          hh < nh ? *reinterpret_cast<const uint4*>(qb + int64_t(hh) * DK + 16 * ks + 8 * g)
+          hh < nrow ? *reinterpret_cast<const uint4*>(qb + int64_t(hh) * DK + 16 * ks + 8 * g)
                   : make_uint4(0, 0, 0, 0);
     }
-    if (HW * wave + r32 < nh) {
+    if (HW * wave + r32 < nrow) {
       const uint16_t* qrow = q + (int64_t(qr) * a.hq + h0 + HW * wave + r32) * DK + 8 * c32;
 #pragma unroll
       for (int ks = QLk; ks < KSTEPS; ++ks)
@@ -879,7 +886,7 @@ void decode_mla_kernel(DecodeArgs a) {
     const float lt = lsum + __shfl_xor(lsum, 32);
     const float inv = (F8 ? key_scale : 1.f) / lt;
     const int hh = HW * wave + r32;
-    if (hh >= nh) return;   // a padding row
+    if (hh >= nrow) return;   // a padding row
     float* orow = a.part_out + (out_row + hh) * DV + 4 * c32;
 #pragma unroll
     for (int m = 0; m < MT; ++m)
@@ -944,8 +951,11 @@ void decode_mla_kernel(DecodeArgs a) {
 
 bool mla_supported(const DecodeArgs& a) {
   return a.dtype == kBF16 && (a.kv_dtype == kBF16 || a.kv_dtype == kFP8) && a.v_cache == nullptr &&
-         a.dk == DK && a.dv == DV && a.hkv > 0 && a.hq % a.hkv == 0 && a.hq / a.hkv <= HEADS &&
-         a.bs % TT == 0;
+         a.dk == DK && a.dv == DV && a.hkv > 0 && a.hq % a.hkv == 0 && a.bs % TT == 0;
+}
+
+int mla_units_per_partition(const DecodeArgs& a) {
+  return a.hkv * (a.query_start ? a.max_q : 1) * ((a.hq / a.hkv + HEADS - 1) / HEADS);
 }
 
 int mla_workgroups_per_cu(int kv_dtype) {
@@ -976,8 +986,7 @@ int mla_grid(const DecodeArgs& a) {
     (void)hipGetLastError();
     cus = 256;
   }
-  const int64_t units = int64_t(a.n_seqs) * a.n_shards * a.max_parts * a.hkv *
-                        (a.query_start ? a.max_q : 1);
+  const int64_t units = int64_t(a.n_seqs) * a.n_shards * a.max_parts * mla_units_per_partition(a);
   return int(std::max<int64_t>(1, std::min<int64_t>(int64_t(cus) * wpc, units)));
 }
 

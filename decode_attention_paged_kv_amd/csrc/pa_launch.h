@@ -68,6 +68,7 @@ int gqa_column_chunks(const DecodeArgs& a);     // workgroups per (partition, pa
 int generic_column_chunks(const DecodeArgs& a);
 hipError_t launch_decode_gqa(const DecodeArgs& a, hipStream_t st);
 bool mla_supported(const DecodeArgs& a);
+int mla_units_per_partition(const DecodeArgs& a);   // (new token, head group, KV head) units
 hipError_t launch_decode_mla(const DecodeArgs& a, hipStream_t st);
 int gqa_workgroups_per_cu(const DecodeArgs& a);
 int mla_workgroups_per_cu(int kv_dtype);

@@ -39,6 +39,7 @@ SMALL = [
     ("mq_latent128_dcp", [300, 90], [5, 2], 128, 1, 576, 512, 64, wl.BF16, 3, 2, 64, True, ""),
     ("mq_latent128_fp8", [70, 0, 9, 64], [3, 0, 9, 1], 128, 1, 576, 512, 64, wl.BF16, 1, 1, 64, True,
      wl.FP8),
+    ("mq_latent192_dcp", [200, 77], [3, 2], 192, 1, 576, 512, 64, wl.BF16, 2, 1, 64, True, ""),
 ]
 
 

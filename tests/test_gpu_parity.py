@@ -84,6 +84,9 @@ FEWER_HEADS = [
     ("latent_h32_e4m3", [70, 513], 32, 1, 1, 1, 128, wl.FP8),
     ("latent_h16_dcp", [300, 90], 16, 1, 3, 2, 64, ""),
     ("latent_h1", [33, 200], 1, 1, 1, 1, 64, ""),
+    # more than 128 heads per KV head: units of 128 heads, the last one partial
+    ("latent_h160", [0, 129, 300], 160, 1, 1, 1, 128, ""),
+    ("latent_h256_2kv_e4m3", [65, 200], 512, 2, 1, 1, 64, wl.FP8),
 ]
 
 
