@@ -9,9 +9,10 @@
 // read), so both run on the matrix cores (v_mfma_f32_32x32x16_bf16).
 //
 // The grid holds as many workgroups as can be resident at once; each takes every G-th
-// unit of work -- a (partition, sequence x shard, KV head), numbered densely over the
-// non-empty ones -- with all 128 heads and four waves, one per SIMD.  Wave w owns heads 32w .. 32w+31 from end to end, so waves share
-// nothing but the key/value tiles:
+// unit of work -- a (partition, sequence x shard, new token, group of up to 128 query
+// heads, KV head), numbered densely over the non-empty partitions -- with its 128 head
+// rows and four waves, one per SIMD.  Wave w owns rows 32w .. 32w+31 from end to end,
+// so waves share nothing but the key/value tiles:
 //  * Tiles of 32 tokens (32 rows x 1152 B, contiguous inside a block) are copied HBM ->
 //    LDS with global_load_lds_dwordx4 (no registers involved) into a ring of three
 //    buffers.  The loop is software-pipelined by one tile: iteration i computes the
