@@ -87,7 +87,7 @@ constexpr int TBL = 256;                            // block-table entries stage
 #define PA_MLA_QL 12
 #endif
 #ifndef PA_MLA_KA
-#define PA_MLA_KA 3
+#define PA_MLA_KA 2
 #endif
 #ifndef PA_MLA_VA
 #define PA_MLA_VA 2
@@ -548,8 +548,8 @@ void decode_mla_kernel(DecodeArgs a) {
 
   // The 32 output MFMAs of tile `tile` with weights pop; value operands VA tiles ahead;
   // filler(n) issues in the shadow of MFMA n.
-  auto outputs = [&](const lds_char_t* tile, const bf16x8_t (&pop)[2], f32x16_t (&o)[MT],
-                     auto&& filler) {
+  auto outputs = [&](const lds_char_t* tile, const bf16x8_t (&pop)[2], const bf16x8_t (&plo)[2],
+                     f32x16_t (&o)[MT], auto&& filler) {
     const lds_char_t* vb[2][2];
 #pragma unroll
     for (int h = 0; h < 2; ++h)
@@ -575,6 +575,7 @@ void decode_mla_kernel(DecodeArgs a) {
     for (int n = 0; n < NV; ++n) {
       if (n + VA < NV) vop[(n + VA) % (VA + 1)] = vread(n + VA);
       mfma32_agpr_acc(o[n % MT], vop[n % (VA + 1)], pop[n / MT]);
+      mfma32_agpr_acc(o[n % MT], vop[n % (VA + 1)], plo[n / MT]);
       __builtin_amdgcn_sched_barrier(0);
       filler(n);
       __builtin_amdgcn_sched_barrier(0);
@@ -635,7 +636,7 @@ void decode_mla_kernel(DecodeArgs a) {
       const int valid = tile_valid(i);
       float sc[16], m0 = -INFINITY, m1 = -INFINITY, mx = -INFINITY, mxo = -INFINITY, mc = 0.f;
       float part = 0.f, pe[16];
-      bf16x8_t pop[2];
+      bf16x8_t pop[2], plo[2];
       // Softmax of tile i in small pieces, each a few VALU instructions (the shadow of one
       // MFMA): masks, row max, reference and overflow flag, weights, packing.  Steps 0..18
       // run among the score MFMAs of tile i+1, steps 19..29 among the first output MFMAs
@@ -680,8 +681,13 @@ void decode_mla_kernel(DecodeArgs a) {
         } else if (step == 17 || step == 18 || step == 27 || step == 28) {
           const int e0 = step < 19 ? 4 * (step - 17) : 8 + 4 * (step - 27);
 #pragma unroll
-          for (int e = e0; e < e0 + 4; ++e) pop[e >> 3][e & 7] = (__bf16)pe[e];
+          for (int e = e0; e < e0 + 4; ++e) {
+            const __bf16 hi = (__bf16)pe[e];
+            pop[e >> 3][e & 7] = hi;
+            plo[e >> 3][e & 7] = (__bf16)(pe[e] - (float)hi);
+          }
           pin(pop[e0 >> 3]);
+          pin(plo[e0 >> 3]);
         } else if (step == 29) {
           lsum += part;
         }
@@ -717,7 +723,7 @@ void decode_mla_kernel(DecodeArgs a) {
       }
       // one copy of the output MFMAs in the loop: a branch around them would join the
       // output tiles in a phi outside the AGPR file
-      outputs(tile_ptr(i), pop, o, [&](int n) {
+      outputs(tile_ptr(i), pop, plo, o, [&](int n) {
         if (n < 30 - kFirstSteps) softmax_piece(kFirstSteps + n);
       });
       s_cur = s_next;
@@ -837,14 +843,16 @@ void decode_mla_kernel(DecodeArgs a) {
       if (lane == 0) ovf_s[i & 1][wave] = ovf ? 1 : 0;
       const float mc = (m_ref == -INFINITY) ? 0.f : m_ref * c;
       float part = 0.f;
-      bf16x8_t pop[2];
+      bf16x8_t pop[2], plo[2];
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const float pe = __builtin_amdgcn_exp2f(fmaf(sc[e], c, -mc));
         part += pe;
-        pop[e >> 3][e & 7] = (__bf16)pe;
+        const __bf16 hi = (__bf16)pe;
+        pop[e >> 3][e & 7] = hi;
+        plo[e >> 3][e & 7] = (__bf16)(pe - (float)hi);
       }
-      outputs(tile_ptr(i), pop, o, no_filler);
+      outputs(tile_ptr(i), pop, plo, o, no_filler);
       lsum += part;
       if (has_next) store_tile_f8(i + 1, raw);
       // tile i+1 written by everyone, everyone done with tile i; the overflow flags seen

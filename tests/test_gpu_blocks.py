@@ -18,8 +18,6 @@ from oracle import paged_attention as pa
 
 pytestmark = pytest.mark.gpu
 
-LATENT_REL_L2 = 4e-3
-
 
 @pytest.fixture(autouse=True, scope="module")
 def _need_gpu():
@@ -159,8 +157,7 @@ def test_copy_on_write_decode_steps(dtype, hq, hkv, dk, dv, bs, latent):
         assert bits_equal(to_np(kd), k_ref), f"step {it}: k_cache"
         if v_ref is not None:
             assert bits_equal(to_np(vd), v_ref), f"step {it}: v_cache"
-        rel = LATENT_REL_L2 if latent and dtype == wl.BF16 else 1e-4
         compare_outputs(f"cow step {it}", dtype, to_np(step.out), to_np(step.lse), ref["o"],
-                        ref["lse"], rel)
+                        ref["lse"])
     assert n_copies == n_seqs - 1                # only the first write into the shared block copies
     assert max(pool.num_blocks(s) for s in range(n_seqs)) == max_blocks

@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import workloads as wl
-from gpu_harness import bits_equal, check_large, check_small, rel_l2_bar, say, to_np
+from gpu_harness import bits_equal, check_large, check_small, say, to_np
 from oracle import fp8_kv as f8
 
 pytestmark = pytest.mark.gpu
@@ -83,8 +83,6 @@ SMALL = [
     ("f8_latent128", [129, 200, 700, 1500], 128, 1, 576, 512, 64, wl.BF16, 1, 1, 256, True, True),
     ("f8_latent128_edges", [0, 1, 65, 64], 128, 1, 576, 512, 64, wl.BF16, 1, 1, 64, True, False),
 ]
-# the latent kernel rounds each weight to bf16 once for the output product
-LATENT_REL_L2 = 4e-3
 
 
 @pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
@@ -93,22 +91,20 @@ def test_fp8_small(case):
     w = wl.small(name, lens, hq, hkv, dk, dv, bs, dt, n_shards=S, interleave=I,
                  partition_tokens=T, latent=latent, seed=sum(map(ord, name)) % 1000,
                  kv_dtype=wl.FP8, scale_per_head=per_head)
-    check_small(w, rel_l2=rel_l2_bar(w))
+    check_small(w)
 
 
 def test_fp8_long():
     """8 sequences around 142K tokens, E4M3 cache, the benchmark's partition size."""
     w = wl.with_fp8_cache(wl.long(partition_tokens=0))
-    order = np.argsort(w.context_lens)
-    check_large(w, [int(order[0]), int(order[-1])])
+    check_large(w)
 
 
 def test_fp8_latent():
     """The latent batch (32 sequences, 4K-64K tokens, 128 heads, shared prefixes) with an
     E4M3 cache, at full size."""
     w = wl.with_fp8_cache(wl.latent())
-    order = np.argsort(w.context_lens)
-    check_large(w, [int(order[0]), int(order[-1])], rel_l2=LATENT_REL_L2)
+    check_large(w)
 
 
 def test_fp8_latent_score_far_above_first_tile():
@@ -123,7 +119,7 @@ def test_fp8_latent_score_far_above_first_tile():
         T["q"][:, :, 0] += 30.0
         T["k_new"][:, :, 0] = 40.0
 
-    step, ref = check_small(w, tweak=spike, rel_l2=LATENT_REL_L2)
+    step, ref = check_small(w, tweak=spike)
     assert ref["lse"].min() > 44.0
 
 

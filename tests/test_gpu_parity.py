@@ -3,7 +3,7 @@
 Small workloads are compared whole: routing, append and gather bit for bit,
 every partition's output and LSE, and the merged result.  The full-size
 workloads run at their real sizes with the partition size the benchmark uses
-and are compared on sampled sequences (see ``gpu_harness.check_large``)."""
+and every sequence is compared with the oracle (see ``gpu_harness.check_large``)."""
 import dataclasses
 import zlib
 
@@ -12,7 +12,7 @@ import pytest
 import torch
 
 import workloads as wl
-from gpu_harness import check_large, check_small, rel_l2_bar, run_library, say
+from gpu_harness import check_large, check_small, compare_outputs, run_library, say, to_np
 from oracle import paged_attention as pa
 
 pytestmark = pytest.mark.gpu
@@ -48,33 +48,77 @@ def test_batch():
 
 def test_long():
     """8 sequences, log-normal lengths around 142K, 4,096-token partitions."""
-    w = wl.long()
-    order = np.argsort(w.context_lens)
-    check_large(w, [int(order[0]), int(order[-1])])
+    check_large(wl.long())
 
 
 @pytest.mark.parametrize("I", [1, 16])
 def test_dcp(I):
     """One 200,000-token sequence in 4 interleaved shards."""
-    check_large(wl.dcp(interleave=I), [0])
+    check_large(wl.dcp(interleave=I))
+
+
+@pytest.mark.parametrize("I", [1, 16])
+def test_dcp_matches_unsharded(I):
+    """The 200,000-token sequence merged from 4 interleaved shards equals the same
+    sequence decoded unsharded (S = 1) on the GPU, and both equal the oracle ([DCP]
+    DCP mechanism section: the LSE-weighted merge of the ranks' partial outputs is the
+    attention over all tokens; its measuring section compares DCP size 1 with DCP
+    enabled).  The S = 1 cache is built from the sharded one through pa_gather_kv, in
+    global token order, into 12,500 fresh blocks."""
+    import decode_attention_paged_kv_amd as P
+
+    w = wl.dcp(interleave=I)
+    say(f"[dcp-vs-s1] I={I}")
+    dev = torch.device("cuda")
+    T = wl.make_tensors(w, dev)
+    sharded = run_library(w, T)                   # appends the new token, then decodes
+    assert int(sharded.err_flag.item()) == 0
+    L, S, bs = int(w.context_lens[0]), w.n_shards, w.block_size
+    # every token of the sequence, global order, from the appended sharded cache
+    K = torch.empty(L, w.n_kv_heads, w.dk, dtype=torch.bfloat16, device=dev)
+    V = torch.empty(L, w.n_kv_heads, w.dv, dtype=torch.bfloat16, device=dev)
+    for r in range(S):
+        Lr = P.pa_shard_length(L, S, I, r)
+        kg = torch.empty(Lr, w.n_kv_heads, w.dk, dtype=torch.bfloat16, device=dev)
+        vg = torch.empty(Lr, w.n_kv_heads, w.dv, dtype=torch.bfloat16, device=dev)
+        P.pa_gather_kv(T["k_cache"], T["v_cache"], T["block_table"], 0, r, L, S, I, kg, vg,
+                       sharded.err_flag)
+        ids = torch.from_numpy(pa.shard_members(L, S, I, r)).to(dev)
+        K[ids], V[ids] = kg, vg
+    nb = -(-L // bs)
+    k1 = torch.full((nb, w.n_kv_heads, bs, w.dk), float("nan"), dtype=torch.bfloat16, device=dev)
+    v1 = torch.full((nb, w.n_kv_heads, w.dv, bs), float("nan"), dtype=torch.bfloat16, device=dev)
+    t = torch.arange(L, device=dev)
+    k1[t // bs, :, t % bs, :] = K
+    v1[t // bs, :, :, t % bs] = V
+    bt1 = torch.arange(nb, dtype=torch.int32, device=dev).reshape(1, 1, nb)
+    one = P.DecodeStep(1, w.n_q_heads, w.n_kv_heads, w.dk, w.dv, bs, L, 1, 1, 0, w.scale_f32,
+                       device=dev, context_lens_host=w.context_lens)
+    one(T["q"], T["k_new"], T["v_new"], k1, v1, bt1, T["context_lens"])
+    torch.cuda.synchronize()
+    assert int(one.err_flag.item()) == 0
+    d_o = (one.out - sharded.out).abs().max().item()
+    d_l = (one.lse - sharded.lse).abs().max().item()
+    rel = ((one.out - sharded.out).double().norm() / one.out.double().norm()).item()
+    say(f"  S=4 vs S=1: max|do|={d_o:.3g} max|dlse|={d_l:.3g} rel_l2={rel:.3g}")
+    assert d_o <= 5e-3 and d_l <= 1e-3 and rel <= 1e-4
+    # both against the oracle, from host copies of the contiguous sequence
+    Kh, Vh = to_np(K), to_np(V)
+    o_ref, lse_ref = pa.attention(to_np(T["q"][0]), Kh, Vh, w.scale_f32)
+    for name, st in (("S=4 merged", sharded), ("S=1", one)):
+        compare_outputs(f"dcp I={I} {name}", wl.BF16, to_np(st.out)[0], to_np(st.lse)[0], o_ref,
+                        lse_ref)
 
 
 def test_latent():
     """128 query heads on one 576-wide latent head, shared 2,048-token prefixes."""
-    w = wl.latent()
-    order = np.argsort(w.context_lens)
-    check_large(w, [int(order[0]), int(order[-1])], rel_l2=LATENT_REL_L2)
-
-
-LATENT_REL_L2 = 4e-3
+    check_large(wl.latent())
 
 
 def test_latent_16_heads():
     """The latent batch with 16 query heads (a tensor-parallel share of 128), at full size:
     the latent kernel pads its products to 128 rows and writes only the real ones."""
-    w = dataclasses.replace(wl.latent(), n_q_heads=16, name="latent_h16")
-    order = np.argsort(w.context_lens)
-    check_large(w, [int(order[0]), int(order[-1])], rel_l2=LATENT_REL_L2)
+    check_large(dataclasses.replace(wl.latent(), n_q_heads=16, name="latent_h16"))
 
 
 # name, lens, hq, hkv, S, I, T, kv dtype: fewer than 128 query heads per latent KV head
@@ -95,17 +139,19 @@ def test_latent_fewer_heads(case):
     name, lens, hq, hkv, S, I, T, kv = case
     w = wl.small(name, lens, hq, hkv, 576, 512, 64, wl.BF16, n_shards=S, interleave=I,
                  partition_tokens=T, latent=True, seed=sum(map(ord, name)) % 1000, kv_dtype=kv)
-    check_small(w, rel_l2=LATENT_REL_L2)
+    check_small(w)
 
 
 # ------------------------------------------------------------------ exact probes at full size
-@pytest.mark.parametrize("make", [lambda: wl.dcp(interleave=16), lambda: wl.long()])
+@pytest.mark.parametrize("make", [lambda: wl.long(), lambda: wl.dcp(interleave=16),
+                                  lambda: wl.dcp(interleave=1), lambda: wl.latent()],
+                         ids=["long", "dcp_I16", "dcp_I1", "latent"])
 def test_mean_probe_full_size(make):
-    """q = 0: every weight is exactly 1/L, values are small integers, so the output
-    is the exact mean of each sequence's values -- any dropped, repeated or
-    misaddressed token moves it."""
-    w = make()
-    check_large(w, [int(np.argmax(w.context_lens))], fill="mean_probe")
+    """q = 0: every weight is exactly 1 (exp of a zero score, in any precision), values
+    are small integers, so every sum is exact and the output is the exact mean of each
+    sequence's values -- any dropped, repeated or misaddressed token moves it.  Every
+    sequence of the workload is compared."""
+    check_large(make(), fill="mean_probe")
 
 
 @pytest.mark.parametrize("make", [lambda: wl.long(), lambda: wl.dcp(interleave=16),
@@ -154,10 +200,9 @@ def test_needle_full_size(make):
     for b in range(w.n_seqs):
         d_o = (out[b] - expect_o[b]).abs().max().item()
         d_l = (lse[b] - expect_lse[b]).abs().max().item()
-        # the latent kernel rounds each weight to bf16 for the output product (the sum of
-        # weights stays unrounded): the needle's weight, 1 within the rounding of its
-        # score, costs a relative ~3e-6 there; a misread row would be off by ~|v|
-        tol_o = 2.0 ** -8 * expect_o[b].abs().max().item() if w.latent else 1e-4
+        # latent values reach ~150 (the needle's key is its value): the stated bf16 bar;
+        # elsewhere |v| ~ 1 and the bar is 1e-4.  A misread row would be off by ~|v|.
+        tol_o = 5e-3 if w.latent else 1e-4
         say(f"  seq {b}: max|o - v_needle| = {d_o:.3g} (tol {tol_o:.3g}), max|lse - s_needle| = {d_l:.3g}")
         assert d_o < tol_o, f"seq {b}: output is not the needle's value row"
         assert d_l < 1e-3, f"seq {b}: lse is not the needle's score"
@@ -187,7 +232,7 @@ def test_sweep(case):
     pg, pt = prefix or (1, 0)
     w = wl.small(name, lens, hq, hkv, dk, dv, bs, dt, n_shards=S, interleave=I,
                  partition_tokens=T, latent=latent, prefix_group=pg, prefix_tokens=pt, seed=zlib.crc32(name.encode()) % 1000)
-    check_small(w, rel_l2=rel_l2_bar(w))
+    check_small(w)
 
 
 def test_partition_size_independence():
@@ -293,7 +338,7 @@ def test_latent_score_far_above_first_tile():
         T["q"][:, :, 0] += 10.0
         T["k_new"][:, :, 0] = 200.0
 
-    step, ref = check_small(w, tweak=spike, rel_l2=LATENT_REL_L2)
+    step, ref = check_small(w, tweak=spike)
     # every head's spike is > 64 log2 units (44 nats) above the other scores (< ~5 nats)
     assert ref["lse"].min() > 50.0
 

@@ -11,7 +11,7 @@ import pytest
 import torch
 
 import workloads as wl
-from gpu_harness import check_small, rel_l2_bar
+from gpu_harness import check_small
 
 pytestmark = pytest.mark.gpu
 
@@ -75,4 +75,4 @@ def test_random_shape(i):
     w = wl.small(c["name"], c["lens"], c["hq"], c["hkv"], c["dk"], c["dv"], c["bs"], c["dt"],
                  n_shards=c["S"], interleave=c["I"], partition_tokens=c["T"], latent=c["latent"],
                  seed=100 + i, kv_dtype=c["kv"], scale_per_head=c["per_head"], q_lens=c["q_lens"])
-    check_small(w, rel_l2=rel_l2_bar(w))
+    check_small(w)
