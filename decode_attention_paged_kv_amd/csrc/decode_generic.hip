@@ -119,8 +119,8 @@ __global__ __launch_bounds__(kThreads) void decode_generic_kernel(DecodeArgs a) 
         if (phys >= 0) {
           ok = 1;
           const int off = t % bs;
-          kb = ((phys * a.hkv + kvh) * bs + off) * dk;
-          vb = vc ? (phys * a.hkv + kvh) * int64_t(dv) * bs + off : kb;
+          kb = key_row(phys, kvh, a.hkv, bs, off, dk);
+          vb = vc ? value_tile(phys, kvh, a.hkv, bs, dv) + off : kb;
         }
       }
       ok_s[tid] = ok;

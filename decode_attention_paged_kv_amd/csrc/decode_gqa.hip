@@ -279,22 +279,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(KT == k
 
   const int spb = bs >> 4;  // sub-tiles per block
   const int32_t* row = a.block_table + (int64_t(b) * a.n_shards + r) * a.max_blocks;
-  const int64_t kv_stride = int64_t(bs) * D;     // elements per (block, kv head)
   int tbl_base = -(1 << 30);
   int tbl = -1;
 
   auto block_of = [&](int e) -> int {            // e: logical block entry (wave-uniform)
     if (e - tbl_base >= 64 || e < tbl_base) {
       tbl_base = e;
-      const int ee = e + lane;
-      int v = -1;
-      if (ee < a.max_blocks) {
-        v = row[ee];
-        if (v < 0 || v >= a.n_blocks) v = -2;    // invalid id: reported when used
-      } else {
-        v = -3;                                  // beyond the table row
-      }
-      tbl = v;
+      tbl = table_entry(row, e + lane, a.max_blocks, a.n_blocks);   // errors reported when used
     }
     return __builtin_amdgcn_readlane(tbl, e - tbl_base);
   };
@@ -316,10 +307,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(KT == k
         const int phys = block_of(e);
         if (phys >= 0) {
           st.tok0[t] = u << 4;
-          st.base[t] = (int64_t(phys) * a.hkv + kvh) * kv_stride;
+          st.base[t] = key_row(phys, kvh, a.hkv, bs, 0, D);   // the value tile: the same offset
           st.sub[t] = (u - e * spb) << 4;
         } else if (lane == 0) {
-          raise_flag(a.flag, phys == -3 ? kErrCapacity : kErrBlockId);
+          raise_flag(a.flag, entry_error(phys));
         }
       }
     }

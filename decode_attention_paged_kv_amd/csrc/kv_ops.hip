@@ -84,11 +84,11 @@ __device__ inline void append_row(const RAW* __restrict__ k_new, const RAW* __re
   const int64_t blk = slot / bs;
   const int off = int(slot % bs);
   const RAW* ks = k_new + (int64_t(n) * hkv + h) * dk;
-  RAW* kd = k_cache + ((blk * hkv + h) * bs + off) * dk;
+  RAW* kd = k_cache + key_row(blk, h, hkv, bs, off, dk);
   for (int e = threadIdx.x; e < dk; e += blockDim.x) kd[e] = ks[e];
   if (v_cache != nullptr) {
     const RAW* vs = v_new + (int64_t(n) * hkv + h) * dv;
-    RAW* vd = v_cache + (blk * hkv + h) * int64_t(dv) * bs + off;
+    RAW* vd = v_cache + value_tile(blk, h, hkv, bs, dv) + off;
     for (int d = threadIdx.x; d < dv; d += blockDim.x) vd[int64_t(d) * bs] = vs[d];
   }
 }
@@ -125,12 +125,12 @@ __device__ inline void append_row_fp8(const typename Elem<DT>::raw* __restrict__
   const int si = n_scales > 1 ? h : 0;
   const float ks = k_scale[si];
   const int64_t ksrc = (int64_t(n) * hkv + h) * dk;
-  uint8_t* kd = k_cache + ((blk * hkv + h) * bs + off) * dk;
+  uint8_t* kd = k_cache + key_row(blk, h, hkv, bs, off, dk);
   for (int e = threadIdx.x; e < dk; e += blockDim.x) kd[e] = f32_to_e4m3(__fdiv_rn(E::load(k_new, ksrc + e), ks));
   if (v_cache != nullptr) {
     const float vs = v_scale[si];
     const int64_t vsrc = (int64_t(n) * hkv + h) * dv;
-    uint8_t* vd = v_cache + (blk * hkv + h) * int64_t(dv) * bs + off;
+    uint8_t* vd = v_cache + value_tile(blk, h, hkv, bs, dv) + off;
     for (int d = threadIdx.x; d < dv; d += blockDim.x)
       vd[int64_t(d) * bs] = f32_to_e4m3(__fdiv_rn(E::load(v_new, vsrc + d), vs));
   }
@@ -206,12 +206,12 @@ __global__ void gather_kernel(const RAW* __restrict__ k_cache, const RAW* __rest
   const int64_t phys = phys_s;
   if (phys < 0) return;
   const int off = t % bs;
-  const RAW* ks = k_cache + ((phys * hkv + h) * bs + off) * dk;
+  const RAW* ks = k_cache + key_row(phys, h, hkv, bs, off, dk);
   RAW* kd = k_out + (int64_t(t) * hkv + h) * dk;
   for (int e = threadIdx.x; e < dk; e += blockDim.x) kd[e] = ks[e];
   RAW* vd = v_out + (int64_t(t) * hkv + h) * dv;
   if (v_cache != nullptr) {
-    const RAW* vs = v_cache + (phys * hkv + h) * int64_t(dv) * bs + off;
+    const RAW* vs = v_cache + value_tile(phys, h, hkv, bs, dv) + off;
     for (int d = threadIdx.x; d < dv; d += blockDim.x) vd[d] = vs[int64_t(d) * bs];
   } else {
     for (int d = threadIdx.x; d < dv; d += blockDim.x) vd[d] = ks[d];

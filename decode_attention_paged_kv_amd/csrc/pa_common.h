@@ -52,20 +52,49 @@ __device__ inline void raise_flag(int* flag, int bits) {
   if (flag) atomicOr(flag, bits);
 }
 
+// ---------------------------------------------------------------- block-table addressing
+// The one address generator of the library: every kernel that reads or writes cache rows
+// through a block table (the decode kernels, the gather, the routed append) resolves an
+// entry with table_entry and forms the row's offset with key_row / value_tile.
+//
+// Entry j of a shard's table row: the physical block holding that shard's local tokens
+// j*block_size .. j*block_size+block_size-1, or kPastRow when j lies beyond the row, or
+// kBadId when the stored id is outside [0, n_blocks).
+enum : int { kBadId = -2, kPastRow = -3 };
+
+__device__ inline int table_entry(const int32_t* row, int j, int max_blocks, int64_t n_blocks) {
+  if (j < 0 || j >= max_blocks) return kPastRow;
+  const int v = row[j];
+  return (v < 0 || int64_t(v) >= n_blocks) ? kBadId : v;
+}
+
+// The error-flag bit an entry raises when used: 0 for a valid block id.
+__device__ inline int entry_error(int e) {
+  return e == kPastRow ? kErrCapacity : (e == kBadId ? kErrBlockId : 0);
+}
+
+// Element offset of the key row in slot `off` of physical block `phys`, KV head h, in a
+// cache laid out [n_blocks][hkv][bs][d] (a token's row contiguous).
+__device__ inline int64_t key_row(int64_t phys, int h, int hkv, int bs, int off, int d) {
+  return ((phys * hkv + h) * bs + off) * int64_t(d);
+}
+
+// Element offset of the value tile of physical block `phys`, KV head h, in a cache laid
+// out [n_blocks][hkv][dv][bs]: element (column c, slot off) sits at + c*bs + off.
+__device__ inline int64_t value_tile(int64_t phys, int h, int hkv, int bs, int dv) {
+  return (phys * hkv + h) * int64_t(dv) * bs;
+}
+
 // Physical block of logical entry j of a table row, or -1 (and the flag raised) when
 // the entry lies outside the row or holds an id outside [0, n_blocks).
 __device__ inline int64_t table_block(const int32_t* row, int j, int max_blocks, int64_t n_blocks,
                                       int* flag) {
-  if (j < 0 || j >= max_blocks) {
-    raise_flag(flag, kErrCapacity);
+  const int e = table_entry(row, j, max_blocks, n_blocks);
+  if (e < 0) {
+    raise_flag(flag, entry_error(e));
     return -1;
   }
-  const int64_t phys = row[j];
-  if (phys < 0 || phys >= n_blocks) {
-    raise_flag(flag, kErrBlockId);
-    return -1;
-  }
-  return phys;
+  return e;
 }
 
 // ---------------------------------------------------------------- element types
