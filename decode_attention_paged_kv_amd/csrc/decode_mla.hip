@@ -32,8 +32,11 @@
 //    score ever exceeds the reference by more than 64 (log2 units) the workgroup starts
 //    the partition over in two passes: the first finds each head's exact max, the second
 //    accumulates with weights <= 1.  Each lane holds 16 tokens of one head, so a tile's
-//    row max is one cross-lane exchange.  Weights enter the output product rounded to
-//    bf16 once; the normaliser (and so the LSE) sums them unrounded in fp32.
+//    row max is one cross-lane exchange; it is taken only on the tile that sets the
+//    reference, and a weight above 2^64 shows as the lane's weight sum exceeding 2^64.
+//    Weights enter the output product as a bf16 pair -- the weight rounded to bf16 and
+//    the rounded remainder, two MFMAs on the same value operand -- which carries ~16
+//    significant bits; the normaliser (and so the LSE) sums them unrounded in fp32.
 //  * Output: O^T[value column][head] += V^T . P^T, 16 column tiles of 32 x 32.  The
 //    score accumulator's layout is exactly the layout of the P^T operand (same token
 //    order on both operands), so weights never leave registers; the V^T operand (8
@@ -67,6 +70,20 @@ typedef short s16x8_t __attribute__((__vector_size__(8 * sizeof(short))));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 typedef __attribute__((address_space(3))) bf16x8_t lds_bf16x8_t;
 typedef __attribute__((address_space(3))) char lds_char_t;
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Weights a, b as bf16 pairs: hi = (bf16(a), bf16(b)), lo = (bf16(a - hi_a), bf16(b - hi_b)),
+// round to nearest even, two weights per conversion; hi + lo carries ~16 significant bits.
+struct Bf16Pairs {
+  uint32_t hi, lo;
+};
+__device__ inline Bf16Pairs split_pair(float a, float b) {
+  const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+  const float ha = __uint_as_float(h << 16), hb = __uint_as_float(h & 0xffff0000u);
+  return {h, __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a - ha, b - hb}, bf16x2_t))};
+}
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -484,7 +501,6 @@ void decode_mla_kernel(DecodeArgs a) {
   float key_scale = 1.f;
   if constexpr (F8) key_scale = a.k_scale[a.n_scales > 1 ? kvh : 0];
   const float c = a.scale * key_scale * kLog2e;
-  constexpr float kOverflow = 64.f;
   auto tile_ptr = [&](int i) { return (const lds_char_t*)kt + (i % NB) * TILE_BYTES; };
 
   // The 36 score MFMAs of the tile at `tile` into s.  Key operands are read KA k-steps
@@ -548,7 +564,7 @@ void decode_mla_kernel(DecodeArgs a) {
 
   // The 32 output MFMAs of tile `tile` with weights pop; value operands VA tiles ahead;
   // filler(n) issues in the shadow of MFMA n.
-  auto outputs = [&](const lds_char_t* tile, const bf16x8_t (&pop)[2], const bf16x8_t (&plo)[2],
+  auto outputs = [&](const lds_char_t* tile, const u32x4_t (&pop)[2], const u32x4_t (&plo)[2],
                      f32x16_t (&o)[MT], auto&& filler) {
     const lds_char_t* vb[2][2];
 #pragma unroll
@@ -574,8 +590,8 @@ void decode_mla_kernel(DecodeArgs a) {
 #pragma unroll
     for (int n = 0; n < NV; ++n) {
       if (n + VA < NV) vop[(n + VA) % (VA + 1)] = vread(n + VA);
-      mfma32_agpr_acc(o[n % MT], vop[n % (VA + 1)], pop[n / MT]);
-      mfma32_agpr_acc(o[n % MT], vop[n % (VA + 1)], plo[n / MT]);
+      mfma32_agpr_acc(o[n % MT], vop[n % (VA + 1)], __builtin_bit_cast(bf16x8_t, pop[n / MT]));
+      mfma32_agpr_acc(o[n % MT], vop[n % (VA + 1)], __builtin_bit_cast(bf16x8_t, plo[n / MT]));
       __builtin_amdgcn_sched_barrier(0);
       filler(n);
       __builtin_amdgcn_sched_barrier(0);
@@ -601,8 +617,8 @@ void decode_mla_kernel(DecodeArgs a) {
   // softmax of tile i; then tile i's output MFMAs.  Buffers: tile i (output), tile i+1
   // (scores), tile i+2 (in flight).  A head whose m_ref is still -inf takes the max of
   // its first tile with a valid token; the pass stops (returns false) as soon as a score
-  // exceeds m_ref by more than kOverflow (never, when m_ref is already the exact max).
-  auto pass_acc = [&](float& m_ref, f32x16_t (&o)[MT], float& lsum) -> bool {
+  // exceeds m_ref by more than 64 log2 units (never, when m_ref is already the exact max).
+  auto pass_acc = [&](float& m_ref, bool& have_ref, f32x16_t (&o)[MT], float& lsum) -> bool {
     if (tbl_base != e_first) {
       PA_WAIT_VM(0);
       __syncthreads();
@@ -634,62 +650,77 @@ void decode_mla_kernel(DecodeArgs a) {
       const bool copy_next = i + 2 < n_tiles;
       const int entry = copy_next ? table_entry(i + 2) : 0;
       const int valid = tile_valid(i);
-      float sc[16], m0 = -INFINITY, m1 = -INFINITY, mx = -INFINITY, mxo = -INFINITY, mc = 0.f;
+      // the reference is set by the first tile with a valid token (the same for every row)
+      const bool set_ref = !have_ref && valid > 0;
+      float m0 = -INFINITY, m1 = -INFINITY, mx = -INFINITY, mxo = -INFINITY, mc = 0.f;
       float part = 0.f, pe[16];
-      bf16x8_t pop[2], plo[2];
+      u32x4_t pop[2], plo[2];
       // Softmax of tile i in small pieces, each a few VALU instructions (the shadow of one
-      // MFMA): masks, row max, reference and overflow flag, weights, packing.  Steps 0..18
-      // run among the score MFMAs of tile i+1, steps 19..29 among the first output MFMAs
-      // of tile i (whose second k-step needs the second weight operand only from MFMA 16).
+      // MFMA): masks (partial tiles), row max (the reference tile), weights, packing, the
+      // overflow flag.  Steps 0..18 run among the score MFMAs of tile i+1, steps 19..29
+      // among the first output MFMAs of tile i (whose second k-step needs the second
+      // weight operand only from MFMA 16).
       auto softmax_piece = [&](int step) {
         if (step < 4) {
-          int lim = valid - 4 * c32;
-          pin(lim);
+          if (valid < TT) {
+            int lim = valid - 4 * c32;
+            pin(lim);
 #pragma unroll
-          for (int e = 4 * step; e < 4 * step + 4; ++e) {
-            float v = s_cur[e];
-            pin(v);
-            sc[e] = 8 * (e >> 2) + (e & 3) < lim ? v : -INFINITY;
-            pin(sc[e]);
+            for (int e = 4 * step; e < 4 * step + 4; ++e) {
+              float v = s_cur[e];
+              pin(v);
+              s_cur[e] = 8 * (e >> 2) + (e & 3) < lim ? v : -INFINITY;
+            }
           }
         } else if (step == 4) {
+          if (set_ref) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) m0 = fmaxf(m0, sc[e]);
-          pin(m0);
+            for (int e = 0; e < 8; ++e) m0 = fmaxf(m0, s_cur[e]);
+            pin(m0);
+          }
         } else if (step == 5) {
+          if (set_ref) {
 #pragma unroll
-          for (int e = 8; e < 16; ++e) m1 = fmaxf(m1, sc[e]);
-          pin(m1);
+            for (int e = 8; e < 16; ++e) m1 = fmaxf(m1, s_cur[e]);
+            pin(m1);
+          }
         } else if (step == 6) {
-          mx = fmaxf(m0, m1);
-          mxo = __shfl_xor(mx, 32);
-          pin(mxo);
+          if (set_ref) {
+            mx = fmaxf(m0, m1);
+            mxo = __shfl_xor(mx, 32);
+            pin(mxo);
+          }
         } else if (step == 8) {
-          mx = fmaxf(mx, mxo);
-          if (m_ref == -INFINITY) m_ref = mx;   // first tile with a valid token of this head
-          const bool ovf = __any(mx != -INFINITY && (mx - m_ref) * c > kOverflow);
-          if (lane == 0) ovf_s[i & 1][wave] = ovf ? 1 : 0;
-          mc = (m_ref == -INFINITY) ? 0.f : m_ref * c;
+          if (set_ref) {
+            m_ref = fmaxf(mx, mxo);
+            have_ref = true;
+          }
+          mc = have_ref ? m_ref * c : 0.f;
           pin(mc);
           pin(m_ref);
         } else if ((step >= 9 && step < 17) || (step >= 19 && step < 27)) {
           const int e = step < 17 ? step - 9 : step - 11;
-          pe[e] = __builtin_amdgcn_exp2f(fmaf(sc[e], c, -mc));
+          pe[e] = __builtin_amdgcn_exp2f(fmaf(s_cur[e], c, -mc));
           part += pe[e];
           pin(pe[e]);
           pin(part);
         } else if (step == 17 || step == 18 || step == 27 || step == 28) {
           const int e0 = step < 19 ? 4 * (step - 17) : 8 + 4 * (step - 27);
-#pragma unroll
-          for (int e = e0; e < e0 + 4; ++e) {
-            const __bf16 hi = (__bf16)pe[e];
-            pop[e >> 3][e & 7] = hi;
-            plo[e >> 3][e & 7] = (__bf16)(pe[e] - (float)hi);
-          }
-          pin(pop[e0 >> 3]);
-          pin(plo[e0 >> 3]);
+          const int kv = e0 >> 3, q = (e0 & 7) >> 1;
+          const Bf16Pairs w0 = split_pair(pe[e0], pe[e0 + 1]);
+          const Bf16Pairs w1 = split_pair(pe[e0 + 2], pe[e0 + 3]);
+          pop[kv][q] = w0.hi;
+          plo[kv][q] = w0.lo;
+          pop[kv][q + 1] = w1.hi;
+          plo[kv][q + 1] = w1.lo;
+          pin(pop[kv]);
+          pin(plo[kv]);
         } else if (step == 29) {
           lsum += part;
+          // a weight above 2^64 (a score more than 64 log2 units above the reference)
+          // makes the lane's sum exceed 2^64
+          const bool ovf = __any(part > 0x1p64f);
+          if (lane == 0) ovf_s[i & 1][wave] = ovf ? 1 : 0;
         }
       };
       constexpr int kFirstSteps = 19;   // steps among the score MFMAs
@@ -822,8 +853,8 @@ void decode_mla_kernel(DecodeArgs a) {
   };
   // Accumulating pass: tile i+1's loads are issued before tile i's products and written
   // after them; the softmax is the same as the bf16 path's (reference max fixed by the
-  // first tile with a valid token, overflow beyond kOverflow ends the pass).
-  auto pass_acc_f8 = [&](float& m_ref, f32x16_t (&o)[MT], float& lsum) -> bool {
+  // first tile with a valid token, a weight beyond 2^64 ends the pass).
+  auto pass_acc_f8 = [&](float& m_ref, bool& have_ref, f32x16_t (&o)[MT], float& lsum) -> bool {
     restage_first();
     RawTile raw;
     load_tile_f8(0, table_entry(0), raw);
@@ -835,22 +866,33 @@ void decode_mla_kernel(DecodeArgs a) {
       if (has_next) load_tile_f8(i + 1, table_entry(i + 1), raw);
       f32x16_t s;
       scores(tile_ptr(i), s, no_filler);
+      const int valid = tile_valid(i);
       float sc[16];
-      masked(s, tile_valid(i), sc);
-      const float mx = row_max(sc);
-      if (m_ref == -INFINITY) m_ref = mx;   // first tile with a valid token of this head
-      const bool ovf = __any(mx != -INFINITY && (mx - m_ref) * c > kOverflow);
-      if (lane == 0) ovf_s[i & 1][wave] = ovf ? 1 : 0;
-      const float mc = (m_ref == -INFINITY) ? 0.f : m_ref * c;
-      float part = 0.f;
-      bf16x8_t pop[2], plo[2];
+      if (valid < TT) {
+        masked(s, valid, sc);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sc[e] = s[e];
+      }
+      if (!have_ref && valid > 0) {   // the first tile with a valid token sets the reference
+        m_ref = row_max(sc);
+        have_ref = true;
+      }
+      const float mc = have_ref ? m_ref * c : 0.f;
+      float part = 0.f, pe[16];
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const float pe = __builtin_amdgcn_exp2f(fmaf(sc[e], c, -mc));
-        part += pe;
-        const __bf16 hi = (__bf16)pe;
-        pop[e >> 3][e & 7] = hi;
-        plo[e >> 3][e & 7] = (__bf16)(pe - (float)hi);
+        pe[e] = __builtin_amdgcn_exp2f(fmaf(sc[e], c, -mc));
+        part += pe[e];
+      }
+      const bool ovf = __any(part > 0x1p64f);   // a weight above 2^64
+      if (lane == 0) ovf_s[i & 1][wave] = ovf ? 1 : 0;
+      u32x4_t pop[2], plo[2];
+#pragma unroll
+      for (int e = 0; e < 16; e += 2) {
+        const Bf16Pairs w = split_pair(pe[e], pe[e + 1]);
+        pop[e >> 3][(e & 7) >> 1] = w.hi;
+        plo[e >> 3][(e & 7) >> 1] = w.lo;
       }
       outputs(tile_ptr(i), pop, plo, o, no_filler);
       lsum += part;
@@ -914,6 +956,7 @@ void decode_mla_kernel(DecodeArgs a) {
 
   f32x16_t o[MT];   // O^T tiles: [32-column tile]; lane holds head r32
   float m_ref = -INFINITY;   // reference max (raw score) of head r32 of this wave
+  bool have_ref = false;     // set by the first tile with a valid token (every row at once)
   float lsum;                // this lane's share of the sum of weights
   // The accumulating pass runs once, or -- after a score far above the first tile's
   // max -- a second time against each head's exact max, found by a scores-only pass.
@@ -922,13 +965,14 @@ void decode_mla_kernel(DecodeArgs a) {
     lsum = 0.f;
     float m_exact = -INFINITY;
     if constexpr (F8) {
-      if (pass_acc_f8(m_ref, o, lsum)) break;
+      if (pass_acc_f8(m_ref, have_ref, o, lsum)) break;
       pass_max_f8(m_exact);
     } else {
-      if (pass_acc(m_ref, o, lsum)) break;
+      if (pass_acc(m_ref, have_ref, o, lsum)) break;
       pass_max(m_exact);
     }
     m_ref = m_exact;
+    have_ref = true;
   }
   finish(o, m_ref, lsum);
   }
