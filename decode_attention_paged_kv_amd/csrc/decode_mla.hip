@@ -15,12 +15,14 @@
 // so waves share nothing but the key/value tiles:
 //  * Tiles of 32 tokens (32 rows x 1152 B, contiguous inside a block) are copied HBM ->
 //    LDS with global_load_lds_dwordx4 (no registers involved) into a ring of three
-//    buffers.  The loop is software-pipelined by one tile: iteration i computes the
-//    scores of tile i+1 and, between those MFMAs, issues the copy of tile i+2 and the
-//    softmax of tile i; then the output MFMAs of tile i.  One barrier per tile both
-//    publishes a landed tile and frees the buffer of the tile before it.  A single wave
-//    per SIMD keeps the matrix core busy only with work placed in the shadow of its own
-//    MFMAs, hence this interleaving.
+//    buffers.  Iteration i computes tile i's scores, softmax and output; the copies of
+//    tile i+2 issue in the shadow of its score MFMAs, into the buffer tile i-1 has left,
+//    so two tiles are in flight while one is computed.  The weights of the value
+//    product's first k-step are computed between the two products (with the first value
+//    reads in flight), those of the second k-step in the shadow of the first k-step's
+//    output MFMAs.  One barrier per tile both publishes a landed tile and frees the
+//    buffer of the tile before it.  A single wave per SIMD keeps the matrix core busy
+//    only with work placed in the shadow of its own MFMAs, hence this interleaving.
 //  * Scores: S^T[token][head] = K_tile . Q^T over 36 k-steps.  24 k-steps of the wave's
 //    32 query rows live in registers for the whole partition, 12 in LDS; the key operand
 //    is one 16-byte LDS read per lane per MFMA.
@@ -96,7 +98,10 @@ constexpr int ROW_CHUNKS = ROW_BYTES / 16;          // 72 chunks of 16 B per row
 constexpr int TILE_SLOTS = TT * ROW_CHUNKS;         // 2304
 constexpr int TILE_BYTES = TILE_SLOTS * 16;         // 36864
 constexpr int COPIES = TILE_SLOTS / (64 * NW);      // copies per wave per tile (9)
-constexpr int NBUF = 3;                             // tile buffers
+#ifndef PA_MLA_NBUF
+#define PA_MLA_NBUF 3
+#endif
+constexpr int NBUF = PA_MLA_NBUF;                   // tile buffers
 constexpr int KSTEPS = DK / 16;                     // 36 k-steps of the score product
 constexpr int MT = DV / 32;                         // 16 value-column tiles
 constexpr int TBL = 256;                            // block-table entries staged in LDS
@@ -229,6 +234,10 @@ void decode_mla_kernel(DecodeArgs a) {
                 "the tiles, the query part and the table must fit the compute unit's 160 KiB of LDS");
   __shared__ __attribute__((aligned(16))) int ovf_s[2][NW];   // [tile parity][wave]: overflow seen
 
+  // the zero tile's address, taken once: inside the tile loop its load from the constant
+  // table would wait for every LDS read in flight
+  const char* zero_tile = g_zero_tile;
+  asm volatile("" : "+s"(zero_tile));
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -332,22 +341,13 @@ void decode_mla_kernel(DecodeArgs a) {
 
   // Block-table entries of the partition are staged in LDS, TBL at a time, so a tile's
   // block id is an LDS read, not a global load that would wait behind the copies in
-  // flight.  Entry e of the row is tbl_s[e - tbl_base]; ids outside [0, n_blocks) or
-  // entries past the row read as -1 (flag raised by the tile that uses them).
+  // flight.  Entry e of the row is tbl_s[e - tbl_base], as table_entry reads it: ids
+  // outside [0, n_blocks) and entries past the row are negative codes (flag raised by the
+  // tile that uses them).
   const int e_first = t_begin / bs;
   int tbl_base = e_first;
   auto stage_table = [&](int base) {
-    for (int j = tid; j < TBL; j += 64 * NW) {
-      const int e = base + j;
-      int v;
-      if (e < a.max_blocks) {
-        v = row[e];
-        if (v < 0 || v >= a.n_blocks) v = -2;
-      } else {
-        v = -3;
-      }
-      tbl_s[j] = v;
-    }
+    for (int j = tid; j < TBL; j += 64 * NW) tbl_s[j] = table_entry(row, base + j, a.max_blocks, a.n_blocks);
   };
   stage_table(tbl_base);
   __syncthreads();
@@ -355,7 +355,7 @@ void decode_mla_kernel(DecodeArgs a) {
   // Block-table entry of tile i as read from LDS (restaging first if the entry lies in
   // another chunk of the table); finish_tile turns it into the wave-uniform block id.
   // Split so that the LDS read can be issued early and its latency hidden.
-  auto table_entry = [&](int i) -> int {
+  auto tile_entry = [&](int i) -> int {
     const int e = (t_begin + i * TT) / bs;
     if (e - tbl_base >= TBL || e < tbl_base) {   // other chunk of the table (long partitions)
       PA_WAIT_VM(0);
@@ -382,19 +382,18 @@ void decode_mla_kernel(DecodeArgs a) {
   };
   auto finish_tile = [&](int i, int entry) -> Copy {
     int phys = __builtin_amdgcn_readfirstlane(entry);
-    if (phys < 0) {   // invalid block id (-2) or an entry past the row (-3)
-      if (tid == 0) raise_flag(a.flag, phys == -3 ? kErrCapacity : kErrBlockId);
+    if (phys < 0) {   // invalid block id or an entry past the row
+      if (tid == 0) raise_flag(a.flag, entry_error(phys));
       phys = -1;
     }
     const int tok0 = t_begin + i * TT;
-    const char* src = phys >= 0
-        ? kc + ((int64_t(phys) * a.hkv + kvh) * bs + (tok0 % bs)) * int64_t(ROW_BYTES)
-        : g_zero_tile;
+    const char* src = phys >= 0 ? kc + key_row(phys, kvh, a.hkv, bs, tok0 % bs, ROW_BYTES) : zero_tile;
     const uint32_t slot = uint32_t(i % NB);
     bad = (bad & ~(1u << slot)) | (uint32_t(phys < 0) << slot);
-    return Copy{uniform_ptr(src), kt_lds + slot * TILE_BYTES, phys < 0 ? TT : min(TT, t_end - tok0)};
+    const int rows = __builtin_amdgcn_readfirstlane(phys < 0 ? TT : min(TT, t_end - tok0));
+    return Copy{uniform_ptr(src), kt_lds + slot * TILE_BYTES, rows};
   };
-  auto begin_tile = [&](int i) -> Copy { return finish_tile(i, table_entry(i)); };
+  auto begin_tile = [&](int i) -> Copy { return finish_tile(i, tile_entry(i)); };
   // Slot s = (k NW + w) 64 + lane = s0 + 256 k: with s0 = 72 t0 + x0 and 256 = 3*72 + 40,
   // row t = t0 + 3k + q and chunk x = y - 72 q for y = x0 + 40k, q = floor(y / 72) =
   // (57 y) >> 12 (exact for y < 392; here y <= 71 + 40*8).  Offsets of a full tile are
@@ -421,14 +420,17 @@ void decode_mla_kernel(DecodeArgs a) {
     }
   }
   auto copy_piece = [&](const Copy& cp, int k) {
-    const uint32_t dst = cp.dst + uint32_t((k * NW + wave) * 64 * 16);
+    // the operands are wave-uniform; reading them from the first lane makes that plain to
+    // the compiler wherever the copies are inlined
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(cp.dst + uint32_t((k * NW + wave) * 64 * 16));
+    const char* src = uniform_ptr(cp.src);
     if (cp.rows == TT) {
-      copy16_to_lds(cp.src, full_off[k], dst);
+      copy16_to_lds(src, full_off[k], dst);
     } else {   // partial tile (a separate asm statement, so the two are not merged)
       const uint32_t off = slot_offset(k, cp.rows);
       asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt ; partial tile"
                    :
-                   : "v"(off), "s"(cp.src), "s"(dst)
+                   : "v"(off), "s"(src), "s"(dst)
                    : "memory", "m0");
     }
   };
@@ -562,34 +564,42 @@ void decode_mla_kernel(DecodeArgs a) {
     return fmaxf(mx, __shfl_xor(mx, 32));
   };
 
-  // The 32 output MFMAs of tile `tile` with weights pop; value operands VA tiles ahead;
-  // filler(n) issues in the shadow of MFMA n.
-  auto outputs = [&](const lds_char_t* tile, const u32x4_t (&pop)[2], const u32x4_t (&plo)[2],
-                     f32x16_t (&o)[MT], auto&& filler) {
-    const lds_char_t* vb[2][2];
+  // The output product of one tile: 32 value operands (operand n = kv * MT + m), each
+  // taken by two MFMAs (weights rounded to bf16, then their remainders).  Value operands
+  // are read VA operands ahead: vstart issues the first VA reads (so their latency can
+  // hide under other work), outputs the rest; filler(n) issues in the shadow of operand
+  // n's MFMAs.
+  constexpr int VA = PA_MLA_VA, NV = 2 * MT;
+  struct VBase {
+    const lds_char_t* p[2][2];   // [h][mt parity]
+  };
+  auto vread = [&](const VBase& vb, int n) {
+    const int kv = n / MT, m = n % MT;
+    const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4_t*)(vb.p[0][m & 1] + 64 * m + 16 * ROW_BYTES * kv));
+    const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4_t*)(vb.p[1][m & 1] + 64 * m + 16 * ROW_BYTES * kv));
+    const s16x8_t cat = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8_t, cat);
+  };
+  auto vstart = [&](const lds_char_t* tile, bf16x8_t (&vop)[VA + 1]) -> VBase {
+    VBase vb;
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int par = 0; par < 2; ++par) {
-        vb[h][par] = tile + va[h][par];
-        asm volatile("" : "+v"(vb[h][par]));
+        vb.p[h][par] = tile + va[h][par];
+        asm volatile("" : "+v"(vb.p[h][par]));
       }
-    constexpr int VA = PA_MLA_VA, NV = 2 * MT;
-    bf16x8_t vop[VA + 1];
-    auto vread = [&](int n) {   // operand n = kv * MT + m
-      const int kv = n / MT, m = n % MT;
-      const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_s16x4_t*)(vb[0][m & 1] + 64 * m + 16 * ROW_BYTES * kv));
-      const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_s16x4_t*)(vb[1][m & 1] + 64 * m + 16 * ROW_BYTES * kv));
-      const s16x8_t cat = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      return __builtin_bit_cast(bf16x8_t, cat);
-    };
 #pragma unroll
-    for (int n = 0; n < VA; ++n) vop[n] = vread(n);
+    for (int n = 0; n < VA; ++n) vop[n] = vread(vb, n);
+    return vb;
+  };
+  auto outputs = [&](const VBase& vb, bf16x8_t (&vop)[VA + 1], const u32x4_t (&pop)[2],
+                     const u32x4_t (&plo)[2], f32x16_t (&o)[MT], auto&& filler) {
 #pragma unroll
     for (int n = 0; n < NV; ++n) {
-      if (n + VA < NV) vop[(n + VA) % (VA + 1)] = vread(n + VA);
+      if (n + VA < NV) vop[(n + VA) % (VA + 1)] = vread(vb, n + VA);
       mfma32_agpr_acc(o[n % MT], vop[n % (VA + 1)], __builtin_bit_cast(bf16x8_t, pop[n / MT]));
       mfma32_agpr_acc(o[n % MT], vop[n % (VA + 1)], __builtin_bit_cast(bf16x8_t, plo[n / MT]));
       __builtin_amdgcn_sched_barrier(0);
@@ -597,7 +607,12 @@ void decode_mla_kernel(DecodeArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-
+  auto outputs_all = [&](const lds_char_t* tile, const u32x4_t (&pop)[2], const u32x4_t (&plo)[2],
+                         f32x16_t (&o)[MT]) {
+    bf16x8_t vop[VA + 1];
+    const VBase vb = vstart(tile, vop);
+    outputs(vb, vop, pop, plo, o, no_filler);
+  };
   auto zero_tiles = [&](f32x16_t (&o)[MT]) {
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
@@ -612,12 +627,15 @@ void decode_mla_kernel(DecodeArgs a) {
     return (f.x | f.y | f.z | f.w) != 0;
   };
 
-  // Accumulating pass, software-pipelined by one tile: iteration i computes the scores
-  // of tile i+1 and, in the shadow of those MFMAs, issues the copy of tile i+2 and the
-  // softmax of tile i; then tile i's output MFMAs.  Buffers: tile i (output), tile i+1
-  // (scores), tile i+2 (in flight).  A head whose m_ref is still -inf takes the max of
-  // its first tile with a valid token; the pass stops (returns false) as soon as a score
-  // exceeds m_ref by more than 64 log2 units (never, when m_ref is already the exact max).
+  // Accumulating pass.  Iteration i computes tile i's scores, softmax and output.  The
+  // copies of tile i+2 issue in the shadow of its score MFMAs, into the buffer tile i-1
+  // has left (three buffers: tile i computed, tiles i+1 and i+2 in flight), so each copy
+  // has more than an iteration to land.  The weights of the value product's first k-step
+  // (tokens 0..15 of the tile) are computed between the two products, with the first
+  // value reads in flight; those of the second k-step in the shadow of the first k-step's
+  // output MFMAs.  A head whose m_ref is still -inf takes the max of its first tile with a
+  // valid token; the pass stops (returns false) as soon as a score exceeds m_ref by more
+  // than 64 log2 units (never, when m_ref is already the exact max).
   auto pass_acc = [&](float& m_ref, bool& have_ref, f32x16_t (&o)[MT], float& lsum) -> bool {
     if (tbl_base != e_first) {
       PA_WAIT_VM(0);
@@ -626,140 +644,103 @@ void decode_mla_kernel(DecodeArgs a) {
       stage_table(tbl_base);
       __syncthreads();
     }
-    issue_tile(0);
-    if (n_tiles > 1) {
-      issue_tile(1);
-      PA_WAIT_VM(COPIES);
-    } else {
-      PA_WAIT_VM(0);
-    }
-    lds_barrier();
-    f32x16_t s_cur;
-    scores(tile_ptr(0), s_cur, no_filler);
-
+    constexpr int AHEAD = NB - 1;   // tiles copied ahead of the one computed
+    for (int i = 0; i < AHEAD && i < n_tiles; ++i) issue_tile(i);
+    float mc = have_ref ? m_ref * c : 0.f;
     bool ok = true;
     for (int i = 0; i < n_tiles; ++i) {
-      const bool has_next = i + 1 < n_tiles;
-      if (has_next) PA_WAIT_VM(0);   // tile i+1 landed (the only copies in flight)
-      // everyone's copies of tile i+1 are in, everyone is done with tile i-1 (whose buffer
+      // tile i landed; the copies of the tiles after it may still be in flight
+      const int later = min(AHEAD - 1, n_tiles - 1 - i);
+      if (later >= 2) {
+        PA_WAIT_VM(2 * COPIES);
+      } else if (later == 1) {
+        PA_WAIT_VM(COPIES);
+      } else {
+        PA_WAIT_VM(0);
+      }
+      // everyone's copies of tile i are in, everyone is done with tile i-1 (whose buffer
       // tile i+2 takes), and tile i-1's overflow flags are visible
       lds_barrier();
       // LDS reads consumed later, so their latency hides under the MFMAs: tile i-1's
       // overflow flags (checked at the end of the iteration) and tile i+2's table entry
       const int4 flags = *reinterpret_cast<const int4*>(&ovf_s[(i + 1) & 1][0]);
-      const bool copy_next = i + 2 < n_tiles;
-      const int entry = copy_next ? table_entry(i + 2) : 0;
+      const bool copy_next = i + AHEAD < n_tiles;
+      const int entry = copy_next ? tile_entry(i + AHEAD) : 0;
+      f32x16_t s;
+      Copy cp{};
+      // copy k of tile i+AHEAD in the shadow of score MFMA 1 + CS k
+      constexpr int CS = PA_MLA_COPY_STRIDE;
+      static_assert(CS >= 1 && 1 + CS * (COPIES - 1) < KSTEPS, "copy slots");
+      scores(tile_ptr(i), s, [&](int ks) {
+        if (copy_next && ks >= 1 && (ks - 1) % CS == 0 && (ks - 1) / CS < COPIES) {
+          const int k = (ks - 1) / CS;
+          if (k == 0) cp = finish_tile(i + AHEAD, entry);
+          copy_piece(cp, k);
+        }
+      });
+      bf16x8_t vop[VA + 1];
+      const VBase vb = vstart(tile_ptr(i), vop);
+      // Softmax: lane holds head r32, tokens 8 (e / 4) + 4 c32 + e % 4 of the tile;
+      // elements 0..7 are the first k-step's weights, 8..15 the second's.
       const int valid = tile_valid(i);
-      // the reference is set by the first tile with a valid token (the same for every row)
-      const bool set_ref = !have_ref && valid > 0;
-      float m0 = -INFINITY, m1 = -INFINITY, mx = -INFINITY, mxo = -INFINITY, mc = 0.f;
+      if (valid < TT) {   // the partition's last tile, or an invalid block
+        const int lim = valid - 4 * c32;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s[e] = 8 * (e >> 2) + (e & 3) < lim ? s[e] : -INFINITY;
+      }
+      if (!have_ref && valid > 0) {   // the first tile with a valid token sets the reference
+        float mx = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[e]);
+        m_ref = fmaxf(mx, __shfl_xor(mx, 32));
+        have_ref = true;
+        mc = m_ref * c;
+      }
       float part = 0.f, pe[16];
       u32x4_t pop[2], plo[2];
-      // Softmax of tile i in small pieces, each a few VALU instructions (the shadow of one
-      // MFMA): masks (partial tiles), row max (the reference tile), weights, packing, the
-      // overflow flag.  Steps 0..18 run among the score MFMAs of tile i+1, steps 19..29
-      // among the first output MFMAs of tile i (whose second k-step needs the second
-      // weight operand only from MFMA 16).
-      auto softmax_piece = [&](int step) {
-        if (step < 4) {
-          if (valid < TT) {
-            int lim = valid - 4 * c32;
-            pin(lim);
 #pragma unroll
-            for (int e = 4 * step; e < 4 * step + 4; ++e) {
-              float v = s_cur[e];
-              pin(v);
-              s_cur[e] = 8 * (e >> 2) + (e & 3) < lim ? v : -INFINITY;
-            }
-          }
-        } else if (step == 4) {
-          if (set_ref) {
+      for (int e = 0; e < 8; ++e) {
+        pe[e] = __builtin_amdgcn_exp2f(fmaf(s[e], c, -mc));
+        part += pe[e];
+      }
 #pragma unroll
-            for (int e = 0; e < 8; ++e) m0 = fmaxf(m0, s_cur[e]);
-            pin(m0);
-          }
-        } else if (step == 5) {
-          if (set_ref) {
+      for (int qq = 0; qq < 4; ++qq) {
+        const Bf16Pairs w = split_pair(pe[2 * qq], pe[2 * qq + 1]);
+        pop[0][qq] = w.hi;
+        plo[0][qq] = w.lo;
+      }
+      // the second k-step's weights, two per output operand (each two MFMAs long), then
+      // the overflow flag: a weight above 2^64 (a score more than 64 log2 units above the
+      // reference) makes the lane's sum exceed 2^64
+      outputs(vb, vop, pop, plo, o, [&](int n) {
+        if (n < 4) {
 #pragma unroll
-            for (int e = 8; e < 16; ++e) m1 = fmaxf(m1, s_cur[e]);
-            pin(m1);
+          for (int e = 8 + 2 * n; e < 10 + 2 * n; ++e) {
+            float v = s[e];
+            pin(v);
+            pe[e] = __builtin_amdgcn_exp2f(fmaf(v, c, -mc));
+            part += pe[e];
+            pin(pe[e]);
           }
-        } else if (step == 6) {
-          if (set_ref) {
-            mx = fmaxf(m0, m1);
-            mxo = __shfl_xor(mx, 32);
-            pin(mxo);
-          }
-        } else if (step == 8) {
-          if (set_ref) {
-            m_ref = fmaxf(mx, mxo);
-            have_ref = true;
-          }
-          mc = have_ref ? m_ref * c : 0.f;
-          pin(mc);
-          pin(m_ref);
-        } else if ((step >= 9 && step < 17) || (step >= 19 && step < 27)) {
-          const int e = step < 17 ? step - 9 : step - 11;
-          pe[e] = __builtin_amdgcn_exp2f(fmaf(s_cur[e], c, -mc));
-          part += pe[e];
-          pin(pe[e]);
           pin(part);
-        } else if (step == 17 || step == 18 || step == 27 || step == 28) {
-          const int e0 = step < 19 ? 4 * (step - 17) : 8 + 4 * (step - 27);
-          const int kv = e0 >> 3, q = (e0 & 7) >> 1;
-          const Bf16Pairs w0 = split_pair(pe[e0], pe[e0 + 1]);
-          const Bf16Pairs w1 = split_pair(pe[e0 + 2], pe[e0 + 3]);
-          pop[kv][q] = w0.hi;
-          plo[kv][q] = w0.lo;
-          pop[kv][q + 1] = w1.hi;
-          plo[kv][q + 1] = w1.lo;
-          pin(pop[kv]);
-          pin(plo[kv]);
-        } else if (step == 29) {
+        } else if (n < 6) {
+#pragma unroll
+          for (int qq = 2 * (n - 4); qq < 2 * (n - 4) + 2; ++qq) {
+            const Bf16Pairs w = split_pair(pe[8 + 2 * qq], pe[9 + 2 * qq]);
+            pop[1][qq] = w.hi;
+            plo[1][qq] = w.lo;
+          }
+          pin(pop[1]);
+          pin(plo[1]);
+        } else if (n == 6) {
           lsum += part;
-          // a weight above 2^64 (a score more than 64 log2 units above the reference)
-          // makes the lane's sum exceed 2^64
           const bool ovf = __any(part > 0x1p64f);
           if (lane == 0) ovf_s[i & 1][wave] = ovf ? 1 : 0;
         }
-      };
-      constexpr int kFirstSteps = 19;   // steps among the score MFMAs
-      Copy cp{};
-      f32x16_t s_next = s_cur;
-      if (has_next) {
-        // slot ks: the copy of tile i+2 in every CS-th MFMA shadow from ks = 1 (early in
-        // the iteration, so the copies have the most time to land before the next
-        // iteration waits for them), softmax steps in the other slots, in order
-        constexpr int CS = PA_MLA_COPY_STRIDE;
-        static_assert(CS >= 2 && 1 + CS * (COPIES - 1) < KSTEPS &&
-                          KSTEPS - COPIES >= kFirstSteps, "copy slots and softmax steps");
-        scores(tile_ptr(i + 1), s_next, [&](int ks) {
-          const bool copy_slot = ks >= 1 && (ks - 1) % CS == 0 && (ks - 1) / CS < COPIES;
-          if (copy_slot) {
-            const int k = (ks - 1) / CS;
-            if (copy_next) {
-              if (k == 0) cp = finish_tile(i + 2, entry);
-              copy_piece(cp, k);
-            }
-          } else {
-            // index among the non-copy slots
-            const int copies_before = ks < 1 ? 0 : (ks - 1) / CS + 1 < COPIES ? (ks - 1) / CS + 1 : COPIES;
-            const int step = ks - copies_before;
-            if (step < kFirstSteps) softmax_piece(step);
-          }
-        });
-      } else {
-#pragma unroll
-        for (int step = 0; step < kFirstSteps; ++step) softmax_piece(step);
-      }
-      // one copy of the output MFMAs in the loop: a branch around them would join the
-      // output tiles in a phi outside the AGPR file
-      outputs(tile_ptr(i), pop, plo, o, [&](int n) {
-        if (n < 30 - kFirstSteps) softmax_piece(kFirstSteps + n);
       });
-      s_cur = s_next;
       if (i > 0 && (flags.x | flags.y | flags.z | flags.w) != 0) {   // tile i-1 overflowed
         ok = false;
+        PA_WAIT_VM(0);   // tile i+1's and i+2's copies, before the buffers are reused
         break;
       }
     }
@@ -770,7 +751,6 @@ void decode_mla_kernel(DecodeArgs a) {
     __syncthreads();
     return ok;
   };
-
   // Scores-only pass: m_ref becomes each head's exact max over the partition.
   auto pass_max = [&](float& m_ref) {
     if (tbl_base != e_first) {
@@ -811,15 +791,15 @@ void decode_mla_kernel(DecodeArgs a) {
   };
   auto load_tile_f8 = [&](int i, int entry, RawTile& raw) {
     int phys = __builtin_amdgcn_readfirstlane(entry);
-    if (phys < 0) {   // invalid block id (-2) or an entry past the row (-3)
-      if (tid == 0) raise_flag(a.flag, phys == -3 ? kErrCapacity : kErrBlockId);
+    if (phys < 0) {   // invalid block id or an entry past the row
+      if (tid == 0) raise_flag(a.flag, entry_error(phys));
       phys = -1;
     }
     const int tok0 = t_begin + i * TT;
     const uint32_t slot = uint32_t(i % NB);
     bad = (bad & ~(1u << slot)) | (uint32_t(phys < 0) << slot);
     const int rows = min(TT, t_end - tok0);
-    const char* src = kc + ((int64_t(max(phys, 0)) * a.hkv + kvh) * bs + (tok0 % bs)) * int64_t(ROW_BYTES_FP8);
+    const char* src = kc + key_row(max(phys, 0), kvh, a.hkv, bs, tok0 % bs, ROW_BYTES_FP8);
 #pragma unroll
     for (int k = 0; k < COPIES; ++k) {
       const int s_ = tid + 64 * NW * k;
@@ -857,13 +837,13 @@ void decode_mla_kernel(DecodeArgs a) {
   auto pass_acc_f8 = [&](float& m_ref, bool& have_ref, f32x16_t (&o)[MT], float& lsum) -> bool {
     restage_first();
     RawTile raw;
-    load_tile_f8(0, table_entry(0), raw);
+    load_tile_f8(0, tile_entry(0), raw);
     store_tile_f8(0, raw);
     lds_barrier();
     bool ok = true;
     for (int i = 0; i < n_tiles; ++i) {
       const bool has_next = i + 1 < n_tiles;
-      if (has_next) load_tile_f8(i + 1, table_entry(i + 1), raw);
+      if (has_next) load_tile_f8(i + 1, tile_entry(i + 1), raw);
       f32x16_t s;
       scores(tile_ptr(i), s, no_filler);
       const int valid = tile_valid(i);
@@ -894,7 +874,7 @@ void decode_mla_kernel(DecodeArgs a) {
         pop[e >> 3][(e & 7) >> 1] = w.hi;
         plo[e >> 3][(e & 7) >> 1] = w.lo;
       }
-      outputs(tile_ptr(i), pop, plo, o, no_filler);
+      outputs_all(tile_ptr(i), pop, plo, o);
       lsum += part;
       if (has_next) store_tile_f8(i + 1, raw);
       // tile i+1 written by everyone, everyone done with tile i; the overflow flags seen
@@ -911,12 +891,12 @@ void decode_mla_kernel(DecodeArgs a) {
   auto pass_max_f8 = [&](float& m_ref) {
     restage_first();
     RawTile raw;
-    load_tile_f8(0, table_entry(0), raw);
+    load_tile_f8(0, tile_entry(0), raw);
     store_tile_f8(0, raw);
     lds_barrier();
     for (int i = 0; i < n_tiles; ++i) {
       const bool has_next = i + 1 < n_tiles;
-      if (has_next) load_tile_f8(i + 1, table_entry(i + 1), raw);
+      if (has_next) load_tile_f8(i + 1, tile_entry(i + 1), raw);
       f32x16_t s;
       scores(tile_ptr(i), s, no_filler);
       float sc[16];
