@@ -5,11 +5,15 @@ kv append, the partitioned attention (pa_decode) and the LSE merge.  Inputs are
 seeded synthetic tensors already resident in HBM.  Prints ONE JSON line.
 
   python bench.py [--steps K] [--warmup W]
-                  [--config long|dcp1|dcp16|batch|latent|latent_fp8|latent_spec2|tiny|long_fp8|dcp1_fp8|dcp16_fp8|spec4]
-                  [--no-cpu-baseline] [--secondary]
+                  [--config long|dcp1|dcp16|dcp_s1|batch|latent|latent_fp8|latent_spec2|tiny|long_fp8|dcp1_fp8|dcp16_fp8|spec4]
+                  [--no-cpu-baseline] [--no-secondary] [--next] [--cpu-budget S]
 
 The default workload is the long-context step (8 sequences, log-normal lengths
 around 142K tokens), the configuration the HBM-roofline target is stated for.
+The other synthetic workloads (tiny, batch, DCP I=1 and I=16, the same 200K
+sequence unsharded, latent) follow under ``secondary``, each with its own rates,
+decode roofline and oracle baseline; ``--next`` adds the E4M3 and multi-token
+workloads.
 ``value`` is KV-read GB/s over the whole step (algorithmic bytes: every stored
 K and V element of every sequence read once per step; one byte per element for the
 ``_fp8`` configurations, whose cache holds E4M3 codes).  ``roofline`` prices the
@@ -41,6 +45,7 @@ def make_workload(name):
         "long": lambda: wl.long(),
         "dcp1": lambda: wl.dcp(interleave=1),
         "dcp16": lambda: wl.dcp(interleave=16),
+        "dcp_s1": lambda: wl.dcp(interleave=1, n_shards=1),
         "batch": lambda: wl.batch(),
         "latent": lambda: wl.latent(),
         "tiny": lambda: wl.tiny(),
@@ -60,6 +65,8 @@ DESCRIBE = {
             "S=4 interleaved shards, I=1, partition size chosen by pa_choose_partition_tokens",
     "dcp16": "DCP emulation: 1 seq of 200000 tokens, 64 q / 8 kv heads, d 128, bf16, block 16, "
              "S=4 interleaved shards, I=16, partition size chosen by pa_choose_partition_tokens",
+    "dcp_s1": "DCP reference: the same 200000-token sequence unsharded (S=1), 64 q / 8 kv heads, d 128, "
+              "bf16, block 16, partition size chosen by pa_choose_partition_tokens",
     "batch": "continuous-batching step: 64 seqs, L = U[8,32] + U[16,96], 32 q / 8 kv heads, d 128, "
              "bf16, block 16",
     "latent": "latent (MLA-style) cache: 32 seqs, L U[4096, 65536], 128 q heads on 1 kv head, "
@@ -317,7 +324,12 @@ def cpu_baseline(w, T, budget_s=12.0):
     return res
 
 
-def run_config(name, steps, warmup, with_cpu, partition_tokens=0, settle_s=SETTLE_S):
+# Workloads timed after the headline by default, and those ``--next`` adds.
+SECONDARY = ("tiny", "batch", "dcp1", "dcp16", "dcp_s1", "latent")
+NEXT = ("long_fp8", "dcp1_fp8", "dcp16_fp8", "latent_fp8", "latent_spec2", "spec4")
+
+
+def run_config(name, steps, warmup, with_cpu, partition_tokens=0, settle_s=SETTLE_S, cpu_budget=12.0):
     import numpy as np
     import torch
 
@@ -343,7 +355,7 @@ def run_config(name, steps, warmup, with_cpu, partition_tokens=0, settle_s=SETTL
                             latent=w.latent)
     if not w.partition_tokens:
         w.partition_tokens = step.partition_tokens
-    cpu = cpu_baseline(w, T) if with_cpu else None
+    cpu = cpu_baseline(w, T, cpu_budget) if with_cpu else None
     t = time_gpu(w, T, step, steps, warmup, settle_s)
     assert int(step.err_flag.item()) == 0, "device error flag set"
     assert torch.isfinite(step.out).all(), "non-finite output"
@@ -395,8 +407,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--settle", type=float, default=SETTLE_S,
                     help="seconds of further untimed steps after the warm-up, for the clocks to settle")
-    ap.add_argument("--secondary", action="store_true",
-                    help="also time the other workloads (reported under 'secondary')")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="time only the --config workload (no 'secondary' block)")
+    ap.add_argument("--next", action="store_true",
+                    help="also time the E4M3 and multi-token workloads under 'secondary'")
+    ap.add_argument("--cpu-budget", type=float, default=12.0,
+                    help="seconds of oracle time per workload for cpu_baseline (secondary: half)")
     ap.add_argument("--partition-tokens", type=int, default=0,
                     help="override the workload's partition size (tokens)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -410,7 +426,8 @@ def main():
     if a.calibrate_copy:
         print(json.dumps(calibrate_copy(a.steps)), flush=True)
         return
-    r = run_config(a.config, a.steps, a.warmup, not a.no_cpu_baseline, a.partition_tokens, a.settle)
+    r = run_config(a.config, a.steps, a.warmup, not a.no_cpu_baseline, a.partition_tokens, a.settle,
+                   a.cpu_budget)
     w = r["w"]
     traffic = measured_traffic(a.config, r["kv_bytes"])
     line = {
@@ -450,24 +467,44 @@ def main():
     if "tflops" in r:
         line["roofline"]["mfma_tflops"] = round(r["tflops"], 2)
         line["roofline"]["mfma_frac"] = round(r["tflops"] / MFMA_BF16_TFLOPS, 4)
-    if a.secondary:
+    if not a.no_secondary:
+        import torch
+
+        del r
+        torch.cuda.empty_cache()
         sec = {}
-        for name in ("dcp1", "dcp16", "batch", "latent", "tiny", "long_fp8", "dcp1_fp8", "dcp16_fp8",
-                     "latent_fp8", "latent_spec2", "spec4"):
+        names = SECONDARY + (NEXT if a.next else ())
+        for name in names:
             if name == a.config:
                 continue
-            s = run_config(name, a.steps, a.warmup, False, settle_s=a.settle)
-            sec[name] = {"kv_GBs_step": round(s["value"], 2), "kv_GBs_decode": round(s["achieved"], 2),
-                         "hbm_frac_decode": round(s["achieved"] / HBM_PEAK_GBS, 4),
-                         "ms_per_step": round(s["ms_per_step"], 5), "decode_ms": round(s["decode_ms"], 5),
-                         "kv_tokens_per_s_decode": round(s["tokens_per_s_decode"], 1),
-                         "new_tokens_per_s": round(s["new_tokens_per_s"], 1),
-                         "graph_ms_per_step": round(s["timing"]["graph_ms_per_step"], 5),
-                         "timing": timing_fields(s["timing"]),
-                         "seq_steps_per_s": round(s["seq_steps"], 2)}
+            with_cpu = not a.no_cpu_baseline and name in SECONDARY
+            s = run_config(name, a.steps, a.warmup, with_cpu, settle_s=a.settle, cpu_budget=a.cpu_budget / 2)
+            sw = s["w"]
+            sec[name] = {
+                "workload": DESCRIBE[name],
+                "kv_GBs_step": round(s["value"], 2),
+                "seq_steps_per_s": round(s["seq_steps"], 2),
+                "ms_per_step": round(s["ms_per_step"], 5),
+                "decode_ms": round(s["decode_ms"], 5),
+                "kv_tokens_per_s_decode": round(s["tokens_per_s_decode"], 1),
+                "new_tokens_per_s": round(s["new_tokens_per_s"], 1),
+                "graph_ms_per_step": round(s["timing"]["graph_ms_per_step"], 5),
+                "partition_tokens": s["step"].partition_tokens,
+                "kv_bytes_per_step": s["kv_bytes"],
+                "dtype": "f32" if sw.dtype == "f32" else "bf16",
+                "timing": timing_fields(s["timing"]),
+                "roofline": {"bound": "hbm", "achieved": round(s["achieved"], 2), "peak": HBM_PEAK_GBS,
+                             "unit": "GB/s", "frac": round(s["achieved"] / HBM_PEAK_GBS, 4),
+                             "traffic": measured_traffic(name, s["kv_bytes"]), "kernel": "pa_decode",
+                             "algorithmic_bytes_per_launch": s["kv_bytes"]},
+                "cpu_baseline": s["cpu"],
+            }
             if "tflops" in s:
-                sec[name]["mfma_tflops"] = round(s["tflops"], 2)
+                sec[name]["roofline"]["mfma_tflops"] = round(s["tflops"], 2)
+                sec[name]["roofline"]["mfma_frac"] = round(s["tflops"] / MFMA_BF16_TFLOPS, 4)
             del s
+            torch.cuda.empty_cache()
+            print(f"bench.py: {name} done", file=sys.stderr, flush=True)
         line["secondary"] = sec
     print(json.dumps(line), flush=True)
 
