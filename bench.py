@@ -1,8 +1,11 @@
 """Benchmark of one decode step of paged attention on one MI355X.
 
 A step is the whole hot path on one stream: slot routing of the new tokens,
-kv append, the partitioned attention (pa_decode) and the LSE merge.  Inputs are
-seeded synthetic tensors already resident in HBM.  Prints ONE JSON line.
+kv append and the partitioned attention (one launch, pa_decode_step: the workgroup
+whose partition holds a sequence's new token stores it first), then the LSE merge
+(skipped when every sequence is one partition).  Several new tokens per sequence:
+routing, append, attention and merge as separate launches.  Inputs are seeded
+synthetic tensors already resident in HBM.  Prints ONE JSON line.
 
   python bench.py [--steps K] [--warmup W]
                   [--config long|dcp1|dcp16|dcp_s1|batch|latent|latent_fp8|latent_spec2|tiny|long_fp8|dcp1_fp8|dcp16_fp8|spec4]
@@ -17,8 +20,9 @@ workloads.
 ``value`` is KV-read GB/s over the whole step (algorithmic bytes: every stored
 K and V element of every sequence read once per step; one byte per element for the
 ``_fp8`` configurations, whose cache holds E4M3 codes).  ``roofline`` prices the
-decode kernel alone: the same algorithmic bytes over its average launch time,
-measured with HIP events around each launch inside the timed region.
+decode kernel alone (with the append it performs): the same algorithmic bytes over
+its average launch time, measured with HIP events around each launch inside the
+timed region.
 """
 from __future__ import annotations
 
@@ -138,11 +142,9 @@ def time_gpu(w, T, step, steps, warmup, settle_s=SETTLE_S):
     else:
         args = (T["q"], T["k_new"], T["v_new"], T["k_cache"], T["v_cache"], T["block_table"],
                 T["context_lens"], ks, vs)
-        def prepare():   # routing and append in one launch
-            step.route_append(T["k_new"], T["v_new"], T["k_cache"], T["v_cache"], T["block_table"],
-                              T["context_lens"], ks, vs)
-        attend = lambda: step.attend(T["q"], T["k_cache"], T["v_cache"], T["block_table"],
-                                     T["context_lens"], ks, vs)
+        def prepare():   # routing and append happen inside the decode launch (pa_decode_step)
+            pass
+        attend = lambda: step.append_attend(*args)
     for _ in range(warmup):
         step(*args)
     torch.cuda.synchronize()

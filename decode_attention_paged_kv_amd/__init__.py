@@ -11,7 +11,7 @@ from ._lib import (  # noqa: F401
     ERR_BLOCK_ID, ERR_CAPACITY, ERR_SLOT, LIB_PATH, PA_BF16, PA_F32, PA_FP8_E4M3, BlockPool,
     PaError, PoolExhausted, lib, pa_choose_partition_tokens, pa_choose_partition_tokens_multi,
     pa_copy_blocks, pa_decode,
-    pa_decode_fp8, pa_decode_multi, pa_default_partition_tokens, pa_gather_kv, pa_kv_append,
+    pa_decode_fp8, pa_decode_multi, pa_decode_step, pa_default_partition_tokens, pa_gather_kv, pa_kv_append,
     pa_kv_append_fp8, pa_kv_append_routed, pa_max_partitions, pa_merge_lse, pa_shard_length,
     pa_slot_mapping, pa_slot_mapping_multi,
 )

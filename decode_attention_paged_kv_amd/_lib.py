@@ -50,6 +50,8 @@ _SIGS = {
     "pa_copy_blocks": [_p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i64, _i32, _p, _p],
     "pa_kv_append_routed": [_p, _p, _i32, _p, _p, _i32, _p, _p, _i32, _p, _p, _i32, _i32, _i32, _i32,
                             _i32, _i64, _i32, _i32, _i32, _p, _p, _p],
+    "pa_decode_step": [_p, _p, _p, _i32, _p, _p, _i32, _p, _p, _i32, _p, _p, _i32, _i32, _i32, _i32,
+                       _i32, _i32, _i64, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _p, _p, _p, _p, _p],
     "pa_pool_add": [_p, _i64, _i64],
     "pa_pool_append": [_p, _i64, _i64, _p, _i32, _p],
     "pa_pool_fork": [_p, _i64, _i64],
@@ -329,6 +331,57 @@ def pa_decode_fp8(q, k_cache, v_cache, k_scale, v_scale, block_table, context_le
                              block_table.shape[2], n_shards, interleave, partition_tokens,
                              max_partitions, float(scale), _dtype_code(q), _ptr(part_out),
                              _ptr(part_lse), _ptr(err_flag), _stream(q)))
+
+
+def pa_decode_step(q, k_new, v_new, k_cache, v_cache, block_table, context_lens, n_shards,
+                   interleave, partition_tokens, max_partitions, scale, part_out, part_lse,
+                   k_scale=None, v_scale=None, slot_mapping=None, dv=None, err_flag=None):
+    """Append of the new tokens and the attention in one call (``pa_decode_step``): the
+    effect of ``pa_kv_append_routed`` then ``pa_decode`` (``pa_decode_fp8`` for a uint8
+    cache of E4M3 codes, which takes its scales)."""
+    _need(q, None, 3, "q")
+    _need(k_new, None, 3, "k_new")
+    _need(v_new, k_new.dtype, 3, "v_new")
+    _need(k_cache, None, 4, "k_cache")
+    _need(v_cache, k_cache.dtype, 4, "v_cache")
+    _need(block_table, torch.int32, 3, "block_table")
+    _need(context_lens, torch.int32, 1, "context_lens")
+    _need(part_out, torch.float32, 5, "part_out")
+    _need(part_lse, torch.float32, 4, "part_lse")
+    _need(slot_mapping, torch.int64, 1, "slot_mapping")
+    _need(err_flag, torch.int32, None, "err_flag")
+    n, hq, dk = q.shape
+    nb, hkv, bs, dk2 = k_cache.shape
+    if dv is None:
+        dv = v_cache.shape[2] if v_cache is not None else dk
+    if dk2 != dk:
+        raise ValueError("q and k_cache head sizes differ")
+    if tuple(k_new.shape) != (n, hkv, dk):
+        raise ValueError(f"k_new must be {(n, hkv, dk)}")
+    if (v_new is None) != (v_cache is None) or (v_new is not None and tuple(v_new.shape) != (n, hkv, dv)):
+        raise ValueError(f"v_new must be {(n, hkv, dv)} with a value cache, None without one")
+    if v_cache is not None and tuple(v_cache.shape) != (nb, hkv, dv, bs):
+        raise ValueError("v_cache must be [n_blocks][n_kv_heads][dv][block_size]")
+    if tuple(part_out.shape) != (n, n_shards, max_partitions, hq, dv):
+        raise ValueError(f"part_out must be {(n, n_shards, max_partitions, hq, dv)}")
+    if tuple(part_lse.shape) != (n, n_shards, max_partitions, hq):
+        raise ValueError(f"part_lse must be {(n, n_shards, max_partitions, hq)}")
+    if block_table.shape[0] != n or block_table.shape[1] != n_shards or context_lens.shape[0] != n:
+        raise ValueError("block_table / context_lens shapes disagree with q")
+    if slot_mapping is not None and slot_mapping.shape[0] != n:
+        raise ValueError("slot_mapping must be [n_seqs]")
+    ns = 0
+    if k_cache.dtype == torch.uint8:
+        ns = _scales(k_scale, v_scale, hkv, v_cache is None)
+    elif k_cache.dtype != q.dtype or k_new.dtype != q.dtype:
+        raise TypeError("q, k_new and the cache must share an element type (or the cache be uint8 codes)")
+    _check(lib.pa_decode_step(_ptr(q), _ptr(k_new), _ptr(v_new), _dtype_code(k_new), _ptr(k_cache),
+                              _ptr(v_cache), _dtype_code(k_cache, cache=True), _ptr(k_scale),
+                              _ptr(v_scale), ns, _ptr(block_table), _ptr(context_lens), n, hq, hkv,
+                              dk, dv, bs, nb, block_table.shape[2], n_shards, interleave,
+                              partition_tokens, max_partitions, float(scale), _dtype_code(q),
+                              _ptr(slot_mapping), _ptr(part_out), _ptr(part_lse), _ptr(err_flag),
+                              _stream(q)))
 
 
 def pa_slot_mapping_multi(block_table, context_lens, query_start, n_shards, interleave, block_size,

@@ -17,6 +17,7 @@
 // scale is folded into the score multiplier and the value scale applied to the output.
 #include <math.h>
 
+#include "pa_append.h"
 #include "pa_common.h"
 #include "pa_launch.h"
 
@@ -54,6 +55,8 @@ __global__ __launch_bounds__(kThreads) void decode_generic_kernel(DecodeArgs a) 
   const int nh = min(kHeads, nq * g - c0);       // valid columns here
   const int tid = threadIdx.x;
   const int dk = a.dk, dv = a.dv, bs = a.bs;
+  // the step's append, when this launch performs it: before any read of the cache
+  if (c0 == 0) fused_append(a, b, r, p, kvh);
 
   const int L = a.context_lens[b];
   const int Lr = L > 0 ? shard_len(L, a.n_shards, a.interleave, r) : 0;

@@ -54,6 +54,7 @@
 
 #include <type_traits>
 
+#include "pa_append.h"
 #include "pa_common.h"
 #include "pa_launch.h"
 
@@ -224,6 +225,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(KT == k
   const int c0 = (blockIdx.y % chunks) * 16;
   const int ncol = min(16, nq * g - c0);         // valid columns here
   const int bs = a.bs;
+  // the step's append, when this launch performs it: before any read of the cache
+  if (c0 == 0) fused_append(a, b, r, p, kvh);
 
   const int L = a.context_lens[b];
   const int Lr = L > 0 ? shard_len(L, a.n_shards, a.interleave, r) : 0;

@@ -59,6 +59,7 @@
 #include <algorithm>
 #include <atomic>
 
+#include "pa_append.h"
 #include "pa_common.h"
 #include "pa_launch.h"
 
@@ -335,6 +336,8 @@ void decode_mla_kernel(DecodeArgs a) {
       continue;
     }
     __syncthreads();   // the previous unit is done with the LDS
+    // the step's append, when this launch performs it: before any read of the cache
+    if (qi == 0 && grp == 0) fused_append(a, b, r, p, kvh);
 
   const int32_t* row = a.block_table + (int64_t(b) * a.n_shards + r) * a.max_blocks;
   const int n_tiles = (t_end - t_begin + TT - 1) / TT;
@@ -970,6 +973,8 @@ void decode_mla_kernel(DecodeArgs a) {
       nq = a.query_start[b + 1] - row0;
       if (nq > a.context_lens[b] || nq > a.max_q || row0 < 0 || row0 + nq > a.n_rows) nq = 0;
     }
+    // a fused append's slot of a sequence with no tokens (no unit records it)
+    if (a.k_new && a.slots_out && r == 0 && tid == 0 && a.context_lens[b] <= 0) a.slots_out[b] = -1;
     for (int qi = 0; qi < nq; ++qi) {
       const int64_t base = (int64_t(row0 + qi) * a.n_shards + r) * a.max_parts;
       for (int p = n; p < a.max_parts; ++p)

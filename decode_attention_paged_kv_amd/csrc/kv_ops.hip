@@ -14,25 +14,12 @@
 // PagedAttention?", section "Sharing common blocks and copy-on-write").
 #include <algorithm>
 
+#include "pa_append.h"
 #include "pa_common.h"
 #include "pa_launch.h"
 
 namespace pa {
 namespace {
-
-// Slot of sequence b's new token, the last of its L context tokens (global position
-// L - 1): its shard and local index by the interleave rule, its block through that
-// shard's table row.  -1 for an empty sequence or an unusable table entry (flagged).
-__device__ inline int64_t new_token_slot(const int32_t* __restrict__ bt, int L, int b, int S, int I,
-                                         int bs, int max_blocks, int64_t n_blocks, int* flag) {
-  if (L <= 0) return -1;
-  const int i = L - 1;
-  const int r = shard_of(i, S, I);
-  const int t = local_index(i, S, I);
-  const int32_t* row = bt + (int64_t(b) * S + r) * max_blocks;
-  const int64_t phys = table_block(row, t / bs, max_blocks, n_blocks, flag);
-  return phys >= 0 ? phys * bs + t % bs : -1;
-}
 
 __global__ void slot_mapping_kernel(const int32_t* __restrict__ bt, const int32_t* __restrict__ lens,
                                     int n_seqs, int S, int I, int bs, int max_blocks,
@@ -76,23 +63,6 @@ __global__ void slot_mapping_multi_kernel(const int32_t* __restrict__ bt,
   }
 }
 
-// Row n, KV head h of the new keys/values into slot `slot` (a valid one), bit for bit.
-template <typename RAW>
-__device__ inline void append_row(const RAW* __restrict__ k_new, const RAW* __restrict__ v_new,
-                                  RAW* __restrict__ k_cache, RAW* __restrict__ v_cache, int n, int h,
-                                  int64_t slot, int hkv, int dk, int dv, int bs) {
-  const int64_t blk = slot / bs;
-  const int off = int(slot % bs);
-  const RAW* ks = k_new + (int64_t(n) * hkv + h) * dk;
-  RAW* kd = k_cache + key_row(blk, h, hkv, bs, off, dk);
-  for (int e = threadIdx.x; e < dk; e += blockDim.x) kd[e] = ks[e];
-  if (v_cache != nullptr) {
-    const RAW* vs = v_new + (int64_t(n) * hkv + h) * dv;
-    RAW* vd = v_cache + value_tile(blk, h, hkv, bs, dv) + off;
-    for (int d = threadIdx.x; d < dv; d += blockDim.x) vd[int64_t(d) * bs] = vs[d];
-  }
-}
-
 template <typename RAW>
 __global__ void kv_append_kernel(const RAW* __restrict__ k_new, const RAW* __restrict__ v_new,
                                  RAW* __restrict__ k_cache, RAW* __restrict__ v_cache,
@@ -107,33 +77,6 @@ __global__ void kv_append_kernel(const RAW* __restrict__ k_new, const RAW* __res
     return;
   }
   append_row(k_new, v_new, k_cache, v_cache, n, h, slot, hkv, dk, dv, bs);
-}
-
-// E4M3 cache: each element of the new rows becomes the code of element / scale (the
-// scale of its KV head, or the tensor's), rounded as f32_to_e4m3 describes.  The
-// division is IEEE (correctly rounded), so the code is a function of the inputs alone.
-template <int DT>
-__device__ inline void append_row_fp8(const typename Elem<DT>::raw* __restrict__ k_new,
-                                      const typename Elem<DT>::raw* __restrict__ v_new,
-                                      uint8_t* __restrict__ k_cache, uint8_t* __restrict__ v_cache,
-                                      const float* __restrict__ k_scale,
-                                      const float* __restrict__ v_scale, int n_scales, int n, int h,
-                                      int64_t slot, int hkv, int dk, int dv, int bs) {
-  using E = Elem<DT>;
-  const int64_t blk = slot / bs;
-  const int off = int(slot % bs);
-  const int si = n_scales > 1 ? h : 0;
-  const float ks = k_scale[si];
-  const int64_t ksrc = (int64_t(n) * hkv + h) * dk;
-  uint8_t* kd = k_cache + key_row(blk, h, hkv, bs, off, dk);
-  for (int e = threadIdx.x; e < dk; e += blockDim.x) kd[e] = f32_to_e4m3(__fdiv_rn(E::load(k_new, ksrc + e), ks));
-  if (v_cache != nullptr) {
-    const float vs = v_scale[si];
-    const int64_t vsrc = (int64_t(n) * hkv + h) * dv;
-    uint8_t* vd = v_cache + value_tile(blk, h, hkv, bs, dv) + off;
-    for (int d = threadIdx.x; d < dv; d += blockDim.x)
-      vd[int64_t(d) * bs] = f32_to_e4m3(__fdiv_rn(E::load(v_new, vsrc + d), vs));
-  }
 }
 
 template <int DT>

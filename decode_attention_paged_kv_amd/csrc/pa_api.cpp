@@ -421,6 +421,9 @@ int check_decode(const char* fn, const void* q, const void* k_cache, const void*
   a.query_start = nullptr;
   a.max_q = 1;
   a.n_rows = n_seqs;
+  a.k_new = a.v_new = nullptr;
+  a.new_dtype = dtype;
+  a.slots_out = nullptr;
   *out = a;
   return PA_OK;
 }
@@ -469,6 +472,49 @@ int pa_decode_fp8(const void* q, const uint8_t* k_cache, const uint8_t* v_cache,
   a.v_scale = v_scale;
   a.n_scales = n_scales;
   return hip_status(pa::dispatch_decode(a, (hipStream_t)stream), "pa_decode_fp8 launch");
+}
+
+int pa_decode_step(const void* q, const void* k_new, const void* v_new, int32_t new_dtype,
+                   void* k_cache, void* v_cache, int32_t cache_dtype, const float* k_scale,
+                   const float* v_scale, int32_t n_scales, const int32_t* block_table,
+                   const int32_t* context_lens, int32_t n_seqs, int32_t n_q_heads,
+                   int32_t n_kv_heads, int32_t dk, int32_t dv, int32_t block_size, int64_t n_blocks,
+                   int32_t max_blocks_per_shard, int32_t n_shards, int32_t interleave,
+                   int32_t partition_tokens, int32_t max_partitions, float scale, int32_t q_dtype,
+                   int64_t* slot_mapping, float* part_out, float* part_lse, int32_t* err_flag,
+                   void* stream) {
+  pa::DecodeArgs a;
+  if (int rc = check_decode("pa_decode_step", q, k_cache, v_cache, block_table, context_lens,
+                            n_seqs, n_q_heads, n_kv_heads, dk, dv, block_size, n_blocks,
+                            max_blocks_per_shard, n_shards, interleave, partition_tokens,
+                            max_partitions, scale, q_dtype, part_out, part_lse, err_flag, &a))
+    return rc;
+  REQUIRE(k_new && (v_new == nullptr) == (v_cache == nullptr), PA_ERR_NULL,
+          "pa_decode_step: k_new must be non-NULL, v_new NULL exactly when v_cache is");
+  REQUIRE(valid_dtype(new_dtype), PA_ERR_UNSUPPORTED, "new_dtype=%d is not PA_F32 or PA_BF16",
+          new_dtype);
+  REQUIRE(valid_cache_dtype(cache_dtype), PA_ERR_UNSUPPORTED,
+          "cache_dtype=%d is not PA_F32, PA_BF16 or PA_FP8_E4M3", cache_dtype);
+  if (cache_dtype == PA_FP8_E4M3) {
+    REQUIRE(k_scale && (v_cache == nullptr || v_scale), PA_ERR_NULL,
+            "pa_decode_step: an E4M3 cache needs k_scale (and v_scale with a value cache)");
+    REQUIRE(n_scales == 1 || n_scales == n_kv_heads, PA_ERR_SHAPE,
+            "n_scales=%d must be 1 or n_kv_heads=%d", n_scales, n_kv_heads);
+    a.kv_dtype = PA_FP8_E4M3;
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
+    a.n_scales = n_scales;
+  } else {
+    REQUIRE(cache_dtype == q_dtype && new_dtype == q_dtype, PA_ERR_UNSUPPORTED,
+            "new_dtype=%d and cache_dtype=%d must equal q_dtype=%d (or the cache be PA_FP8_E4M3)",
+            new_dtype, cache_dtype, q_dtype);
+  }
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.new_dtype = new_dtype;
+  a.slots_out = slot_mapping;
+  if (n_seqs == 0) return ok();
+  return hip_status(pa::dispatch_decode(a, (hipStream_t)stream), "pa_decode_step launch");
 }
 
 int pa_slot_mapping_multi(const int32_t* block_table, const int32_t* context_lens,

@@ -30,6 +30,14 @@ struct DecodeArgs {
   const int32_t* query_start;
   int max_q;               // grid bound on new tokens per sequence (1 when query_start NULL)
   int n_rows;              // q rows (n_seqs when query_start NULL)
+  // The step's append, done by the decode launch (fused_append in pa_append.h): row b of
+  // k_new/v_new (element type new_dtype) is sequence b's new token, stored into its slot
+  // before it is read; its slot goes to slots_out[b] when that is non-NULL.  k_new NULL:
+  // no append.
+  const void* k_new;
+  const void* v_new;
+  int new_dtype;
+  int64_t* slots_out;
 };
 
 hipError_t launch_slot_mapping(const int32_t* bt, const int32_t* lens, int n_seqs, int S, int I,

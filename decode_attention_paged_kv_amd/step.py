@@ -1,8 +1,8 @@
 """One decode step on one stream: slot routing, kv append, attention, LSE merge.
 
 ``DecodeStep`` owns the step's output and scratch tensors (allocated once, with
-torch, for a maximum context length) and issues the library calls: routing and append
-in one launch, then attention and merge.  A cache of
+torch, for a maximum context length) and issues the library calls: routing, append and
+attention in one call (``pa_decode_step``), then the merge.  A cache of
 ``torch.uint8`` holds E4M3 codes and takes its scales with each call (the ``_fp8``
 entry points).
 """
@@ -77,12 +77,22 @@ class DecodeStep:
         if not self.direct:
             L.pa_merge_lse(self.part_out, self.part_lse, self.out, self.lse)
 
+    def append_attend(self, q, k_new, v_new, k_cache, v_cache, block_table, context_lens,
+                      k_scale=None, v_scale=None):
+        """route_append() then attend() in one call (``pa_decode_step``): one launch where
+        the kernel can store the new rows itself; the slots land in ``slot_mapping``."""
+        L.pa_decode_step(q, k_new, v_new, k_cache, v_cache, block_table, context_lens,
+                         self.n_shards, self.interleave, self.partition_tokens,
+                         self.max_partitions, self.scale, self.part_out, self.part_lse,
+                         k_scale=k_scale, v_scale=v_scale, slot_mapping=self.slot_mapping,
+                         dv=self.dv, err_flag=self.err_flag)
+
     def __call__(self, q, k_new, v_new, k_cache, v_cache, block_table, context_lens, k_scale=None,
                  v_scale=None):
-        """The whole step; returns ``(out, lse)`` (views of this object's buffers)."""
-        self.route_append(k_new, v_new, k_cache, v_cache, block_table, context_lens, k_scale,
-                          v_scale)
-        self.attend(q, k_cache, v_cache, block_table, context_lens, k_scale, v_scale)
+        """The whole step; returns ``(out, lse)`` (views of this object's buffers).  One
+        launch with a single partition per sequence, else two (the merge)."""
+        self.append_attend(q, k_new, v_new, k_cache, v_cache, block_table, context_lens, k_scale,
+                           v_scale)
         self.merge()
         return self.out, self.lse
 

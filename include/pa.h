@@ -199,6 +199,41 @@ int pa_decode(const void* q, const void* k_cache, const void* v_cache,
               float* part_out, float* part_lse, int32_t* err_flag, void* stream);
 
 /*
+ * pa_decode_step -- a decode step's append and attention in one call: the effect of
+ * pa_kv_append_routed (one new token per sequence, the last of its context_lens[b]
+ * tokens) followed by pa_decode / pa_decode_fp8 on the same stream, with the same
+ * results -- the cache then holds the new rows bit for bit (E4M3: the same codes), and
+ * the outputs are those of the decode over the appended cache.  A decode step stores
+ * the new token's rows, then attends over everything stored ([KVB] "KV キャッシュは何を
+ * 保持するのか?"); here the workgroup whose partition holds a sequence's new token stores
+ * its rows before reading them, so the step is one launch.  When one partition of a KV
+ * head is read by several workgroups (more than 16 query heads per KV head outside the
+ * latent kernel, more than 128 on it) the append is a launch of its own first.
+ *   k_new, v_new  [n_seqs][n_kv_heads][dk | dv] of new_dtype: the cache's element type,
+ *              or PA_F32 / PA_BF16 rows quantised into an E4M3 cache; v_new NULL exactly
+ *              when v_cache is (latent cache).
+ *   k_cache, v_cache  the cache of cache_dtype, written (the new tokens' slots) and read.
+ *   k_scale, v_scale, n_scales  as in pa_decode_fp8 when cache_dtype is PA_FP8_E4M3,
+ *              otherwise ignored (may be NULL / 0).
+ *   q_dtype    element type of q; equal to cache_dtype and new_dtype unless the cache is
+ *              PA_FP8_E4M3.
+ *   slot_mapping (out, optional)  int64 [n_seqs]: as in pa_kv_append_routed.
+ *   The block receiving a new token must be private to its sequence (copy-on-write keeps
+ *   a block that is written private), since other sequences' workgroups run meanwhile.
+ *   Other arguments and the outputs: as in pa_decode.  Errors: as pa_kv_append_routed and
+ *   pa_decode report them; nothing is launched on a rejected call.
+ */
+int pa_decode_step(const void* q, const void* k_new, const void* v_new, int32_t new_dtype,
+                   void* k_cache, void* v_cache, int32_t cache_dtype, const float* k_scale,
+                   const float* v_scale, int32_t n_scales, const int32_t* block_table,
+                   const int32_t* context_lens, int32_t n_seqs, int32_t n_q_heads,
+                   int32_t n_kv_heads, int32_t dk, int32_t dv, int32_t block_size, int64_t n_blocks,
+                   int32_t max_blocks_per_shard, int32_t n_shards, int32_t interleave,
+                   int32_t partition_tokens, int32_t max_partitions, float scale, int32_t q_dtype,
+                   int64_t* slot_mapping, float* part_out, float* part_lse, int32_t* err_flag,
+                   void* stream);
+
+/*
  * pa_decode_fp8 -- pa_decode over an E4M3 cache written by pa_kv_append_fp8: every
  * stored key (value) element is taken as value(code) * k_scale[h] (v_scale[h]; index 0
  * when n_scales == 1), for KV head h; the latent cache (v_cache == NULL) takes the

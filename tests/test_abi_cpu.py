@@ -241,3 +241,35 @@ def test_decode_rejects_a_grid_past_2_31():
     st = P.lib.pa_decode(vp, vp, vp, vp, vp, 1 << 20, 8, 2, 64, 64, 16, 8, 4, 64, 1, 16, 64, 0.125, 1,
                          vp, vp, None, None)
     assert st == -2 and "exceeds 2^31-1" in P.lib.pa_last_error().decode()
+
+
+def test_decode_step_rejects_bad_arguments():
+    vp = ctypes.c_void_p(0x1000)
+    ds = P.lib.pa_decode_step
+
+    def call(**over):
+        # q, k_new, v_new, new_dtype, k_cache, v_cache, cache_dtype, k_scale, v_scale, n_scales,
+        # block_table, context_lens, n_seqs, hq, hkv, dk, dv, bs, nb, max_blocks, S, I, T, Pmax,
+        # scale, q_dtype, slots, part_out, part_lse, flag
+        a = dict(q=vp, kn=vp, vn=vp, nd=1, kc=vp, vc=vp, cd=1, ks=None, vs=None, ns=0, bt=vp, lens=vp,
+                 n=4, hq=8, hkv=2, dk=64, dv=64, bs=16, nb=8, mb=4, S=1, I=1, T=64, P=4, scale=0.125,
+                 qd=1, slots=None, po=vp, pl=vp, flag=None)
+        a.update(over)
+        return ds(*a.values(), None)
+
+    assert call(n=0) == 0                          # nothing to do
+    assert call(kn=None) == -1
+    assert call(vn=None) == -1                     # v_new without v_cache
+    assert call(q=None) == -1
+    assert call(po=None) == -1
+    assert call(nd=0) == -3                        # rows f32, cache and q bf16
+    assert call(cd=0) == -3                        # cache f32, q bf16
+    assert call(cd=7) == -3
+    assert call(nd=2) == -3                        # E4M3 rows
+    assert call(cd=2) == -1                        # E4M3 cache without scales
+    assert call(cd=2, ks=vp, vs=vp, ns=3) == -2    # 3 scales for 2 KV heads
+    assert call(cd=2, ks=vp, vs=vp, ns=2, n=0) == 0
+    assert call(T=24) == -2                        # not a multiple of the block size
+    assert call(S=0) == -2
+    assert call(n=-1) == -2
+    assert "n_seqs" in P.lib.pa_last_error().decode()

@@ -1,0 +1,137 @@
+"""pa_decode_step (the step's append and attention in one call) on the GPU.
+
+Held bit for bit to the same step as two calls, pa_kv_append_routed then pa_decode (or
+pa_decode_fp8): every byte of both caches, the slots, and every partial output and LSE
+(the decode reads the same cache, so the results must be identical, not merely close).
+The two-call path is itself held to the oracle by the routed-append and decode parity
+tests.  Cases cover each decode kernel with the append fused (GQA bf16, the generic
+kernel in fp32, E4M3, DCP shards with interleave, the latent kernel) and the shapes that
+keep the append a launch of its own (more than 16 query heads per KV head; more than 128
+on the latent kernel), with empty, one-token and multi-partition sequences."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from gpu_harness import say, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import decode_attention_paged_kv_amd  # noqa: F401  (fails loudly if the library is missing)
+
+
+# name, lens, hq, hkv, dk, dv, bs, dtype, S, I, latent, kv dtype, partition tokens
+CASES = [
+    ("gqa_bf16", [1, 17, 300, 0, 1000], 32, 8, 128, 128, 16, wl.BF16, 1, 1, False, "", 64),
+    ("gqa_g32_unfused", [5, 260, 0, 77], 64, 2, 128, 128, 16, wl.BF16, 1, 1, False, "", 128),
+    ("generic_f32_dcp", [0, 1, 5, 130, 77], 6, 3, 40, 24, 8, wl.F32, 3, 2, False, "", 16),
+    ("gqa_dcp16", [900, 31, 16, 0], 64, 8, 128, 128, 16, wl.BF16, 4, 16, False, "", 96),
+    ("gqa_e4m3", [33, 520, 0, 1], 32, 8, 128, 128, 16, wl.BF16, 1, 1, False, wl.FP8, 128),
+    ("latent", [65, 300, 1, 0, 2000], 16, 1, 576, 512, 64, wl.BF16, 1, 1, True, "", 256),
+    ("latent_e4m3", [70, 0, 9, 700], 16, 1, 576, 512, 64, wl.BF16, 1, 1, True, wl.FP8, 256),
+    ("latent_256h_unfused", [70, 640], 256, 1, 576, 512, 64, wl.BF16, 1, 1, True, "", 256),
+]
+
+
+def _bits(t):
+    return None if t is None else t.contiguous().view(torch.uint8)
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_decode_step_equals_append_then_decode(case):
+    import decode_attention_paged_kv_amd as P
+
+    name, lens, hq, hkv, dk, dv, bs, dt, S, I, latent, kv, T_part = case
+    say(f"[decode step] {name}")
+    w = wl.small(name, lens, hq, hkv, dk, dv, bs, dt, n_shards=S, interleave=I, latent=latent,
+                 partition_tokens=T_part, seed=sum(map(ord, name)) % 1000, kv_dtype=kv)
+    dev = torch.device("cuda")
+    T = wl.make_tensors(w, dev)
+    ks, vs = T.get("k_scale"), T.get("v_scale")
+    fp8 = T["k_cache"].dtype == torch.uint8
+    n = w.n_seqs
+    Pmax = max(1, P.pa_max_partitions(int(max(lens)), S, I, T_part))
+    scale = float(w.scale_f32)
+
+    def buffers():
+        po = torch.full((n, S, Pmax, hq, dv), float("nan"), dtype=torch.float32, device=dev)
+        pl = torch.full((n, S, Pmax, hq), float("nan"), dtype=torch.float32, device=dev)
+        slots = torch.full((n,), 12345, dtype=torch.int64, device=dev)
+        flag = torch.zeros(1, dtype=torch.int32, device=dev)
+        return po, pl, slots, flag
+
+    # two calls
+    k2 = T["k_cache"].clone()
+    v2 = None if T["v_cache"] is None else T["v_cache"].clone()
+    po2, pl2, slots2, flag2 = buffers()
+    P.pa_kv_append_routed(T["k_new"], T["v_new"], k2, v2, T["block_table"], T["context_lens"], S, I,
+                          ks, vs, slots2, flag2)
+    if fp8:
+        P.pa_decode_fp8(T["q"], k2, v2, ks, vs, T["block_table"], T["context_lens"], S, I, T_part, Pmax,
+                        scale, po2, pl2, dv=dv, err_flag=flag2)
+    else:
+        P.pa_decode(T["q"], k2, v2, T["block_table"], T["context_lens"], S, I, T_part, Pmax, scale, po2,
+                    pl2, dv=dv, err_flag=flag2)
+
+    # one call
+    k1 = T["k_cache"].clone()
+    v1 = None if T["v_cache"] is None else T["v_cache"].clone()
+    po1, pl1, slots1, flag1 = buffers()
+    P.pa_decode_step(T["q"], T["k_new"], T["v_new"], k1, v1, T["block_table"], T["context_lens"], S, I,
+                     T_part, Pmax, scale, po1, pl1, k_scale=ks, v_scale=vs, slot_mapping=slots1, dv=dv,
+                     err_flag=flag1)
+    torch.cuda.synchronize()
+
+    assert int(flag1.item()) == 0 and int(flag2.item()) == 0
+    assert np.array_equal(to_np(slots1), to_np(slots2)), "slots differ"
+    assert torch.equal(_bits(k1), _bits(k2)), "key cache differs"
+    if v1 is not None:
+        assert torch.equal(_bits(v1), _bits(v2)), "value cache differs"
+    assert torch.equal(_bits(pl1), _bits(pl2)), "partial LSEs differ"
+    assert torch.equal(_bits(po1), _bits(po2)), "partial outputs differ"
+
+
+def test_decode_step_object_and_graph():
+    """DecodeStep's call (pa_decode_step, then the merge when there are several parts)
+    equals the step made of separate calls; its captured graph replays it exactly,
+    with eager work in between, several times."""
+    import decode_attention_paged_kv_amd as P
+
+    say("[decode step] DecodeStep and graph")
+    w = wl.small("step_obj", [300, 70, 1, 0, 900], 32, 8, 128, 128, 16, wl.BF16, partition_tokens=128,
+                 seed=11)
+    dev = torch.device("cuda")
+    T = wl.make_tensors(w, dev)
+    Lmax = int(w.context_lens.max())
+    mk = lambda: P.DecodeStep(w.n_seqs, 32, 8, 128, 128, 16, Lmax, partition_tokens=128,
+                              scale=float(w.scale_f32), device=dev)
+    ref = mk()
+    k2, v2 = T["k_cache"].clone(), T["v_cache"].clone()
+    ref.route_append(T["k_new"], T["v_new"], k2, v2, T["block_table"], T["context_lens"])
+    ref.attend(T["q"], k2, v2, T["block_table"], T["context_lens"])
+    ref.merge()
+    step = mk()
+    k1, v1 = T["k_cache"].clone(), T["v_cache"].clone()
+    out, lse = step(T["q"], T["k_new"], T["v_new"], k1, v1, T["block_table"], T["context_lens"])
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(k1), _bits(k2)) and torch.equal(_bits(v1), _bits(v2))
+    assert torch.equal(step.slot_mapping, ref.slot_mapping)
+    assert torch.equal(_bits(out), _bits(ref.out)) and torch.equal(_bits(lse), _bits(ref.lse))
+
+    k3, v3 = T["k_cache"].clone(), T["v_cache"].clone()
+    g = step.capture(T["q"], T["k_new"], T["v_new"], k3, v3, T["block_table"], T["context_lens"])
+    for rep in range(3):
+        step.out.zero_()
+        k3.copy_(T["k_cache"])
+        v3.copy_(T["v_cache"])
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(k3), _bits(k2)) and torch.equal(_bits(v3), _bits(v2)), rep
+        assert torch.equal(_bits(step.out), _bits(ref.out)), rep
+        assert torch.equal(_bits(step.lse), _bits(ref.lse)), rep
