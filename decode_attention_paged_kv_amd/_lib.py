@@ -18,6 +18,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("PAGEDATTN_LIB", os.path.join(_HERE, "libpagedattn.so"))
 
 PA_F32, PA_BF16, PA_FP8_E4M3 = 0, 1, 2
+PA_ERR_BUFFER = -4
+PA_STATIC_SCRATCH_BYTES = 64 << 20   # include/pa.h: pa_decode_step_static's partials array
 ERR_BLOCK_ID, ERR_CAPACITY, ERR_SLOT = 1, 2, 4
 
 if not os.path.exists(LIB_PATH):
@@ -52,6 +54,9 @@ _SIGS = {
                             _i32, _i64, _i32, _i32, _i32, _p, _p, _p],
     "pa_decode_step": [_p, _p, _p, _i32, _p, _p, _i32, _p, _p, _i32, _p, _p, _i32, _i32, _i32, _i32,
                        _i32, _i32, _i64, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _p, _p, _p, _p, _p],
+    "pa_decode_step_static": [_p, _p, _p, _i32, _p, _p, _i32, _p, _p, _i32, _p, _p, _i32, _i32, _i32,
+                              _i32, _i32, _i32, _i64, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _p, _p,
+                              _i32, _p, _p, _p],
     "pa_pool_add": [_p, _i64, _i64],
     "pa_pool_append": [_p, _i64, _i64, _p, _i32, _p],
     "pa_pool_fork": [_p, _i64, _i64],

@@ -517,6 +517,51 @@ int pa_decode_step(const void* q, const void* k_new, const void* v_new, int32_t 
   return hip_status(pa::dispatch_decode(a, (hipStream_t)stream), "pa_decode_step launch");
 }
 
+int pa_decode_step_static(const void* q, const void* k_new, const void* v_new, int32_t new_dtype,
+                          void* k_cache, void* v_cache, int32_t cache_dtype, const float* k_scale,
+                          const float* v_scale, int32_t n_scales, const int32_t* block_table,
+                          const int32_t* context_lens, int32_t n_seqs, int32_t n_q_heads,
+                          int32_t n_kv_heads, int32_t dk, int32_t dv, int32_t block_size,
+                          int64_t n_blocks, int32_t max_blocks_per_shard, int32_t n_shards,
+                          int32_t interleave, int32_t partition_tokens, int32_t max_partitions,
+                          float scale, int32_t q_dtype, int64_t* slot_mapping, void* out,
+                          int32_t out_dtype, float* lse, int32_t* err_flag, void* stream) {
+  // the checks the two calls below would make after the first has launched, and the size
+  REQUIRE(out && lse, PA_ERR_NULL, "pa_decode_step_static: out and lse must be non-NULL");
+  REQUIRE(valid_dtype(out_dtype), PA_ERR_UNSUPPORTED, "out_dtype=%d is not PA_F32 or PA_BF16",
+          out_dtype);
+  REQUIRE(n_seqs >= 0 && n_q_heads >= 1 && n_shards >= 1 && max_partitions >= 1 && dv >= 1,
+          PA_ERR_SHAPE, "n_seqs=%d, n_q_heads=%d, n_shards=%d, max_partitions=%d, dv=%d out of range",
+          n_seqs, n_q_heads, n_shards, max_partitions, dv);
+  REQUIRE(int64_t(n_seqs) * n_q_heads <= 0x7fffffff, PA_ERR_SHAPE, "n_seqs*n_q_heads too large");
+  auto round256 = [](uint64_t x) { return (x + 255) / 256 * 256; };
+  const uint64_t rows = uint64_t(n_seqs) * uint64_t(n_shards) * uint64_t(max_partitions) * uint64_t(n_q_heads);
+  const uint64_t out_bytes = round256(rows * uint64_t(dv) * 4);
+  const uint64_t lse_bytes = round256(rows * 4);
+  REQUIRE(out_bytes + lse_bytes <= pa::kStaticScratchBytes, PA_ERR_BUFFER,
+          "pa_decode_step_static: the partials need %llu bytes, more than the %llu of the "
+          "library's array", (unsigned long long)(out_bytes + lse_bytes),
+          (unsigned long long)pa::kStaticScratchBytes);
+  const bool direct = n_shards == 1 && max_partitions == 1 && out_dtype == PA_F32;
+  float* po = static_cast<float*>(out);
+  float* pl = lse;
+  if (!direct && n_seqs > 0) {
+    char* base = nullptr;
+    const hipError_t e = pa::static_scratch(&base);
+    if (e != hipSuccess) return hip_status(e, "pa_decode_step_static: address of the partials array");
+    po = reinterpret_cast<float*>(base);
+    pl = reinterpret_cast<float*>(base + out_bytes);
+  }
+  const int rc = pa_decode_step(q, k_new, v_new, new_dtype, k_cache, v_cache, cache_dtype, k_scale,
+                                v_scale, n_scales, block_table, context_lens, n_seqs, n_q_heads,
+                                n_kv_heads, dk, dv, block_size, n_blocks, max_blocks_per_shard,
+                                n_shards, interleave, partition_tokens, max_partitions, scale,
+                                q_dtype, slot_mapping, po, pl, err_flag, stream);
+  if (rc != PA_OK || direct || n_seqs == 0) return rc;
+  return pa_merge_lse(po, pl, n_seqs, n_shards * max_partitions, n_q_heads, dv, out, out_dtype, lse,
+                      stream);
+}
+
 int pa_slot_mapping_multi(const int32_t* block_table, const int32_t* context_lens,
                           const int32_t* query_start, int32_t n_seqs, int32_t n_rows,
                           int32_t n_shards, int32_t interleave, int32_t block_size,

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "pa.h"
+
 namespace pa {
 
 struct DecodeArgs {
@@ -39,6 +41,11 @@ struct DecodeArgs {
   int new_dtype;
   int64_t* slots_out;
 };
+
+// The library's fixed partials array on the current device (step_static.hip): its device
+// address, taken once per device; kStaticScratchBytes is its size.
+constexpr size_t kStaticScratchBytes = PA_STATIC_SCRATCH_BYTES;
+hipError_t static_scratch(char** out);
 
 hipError_t launch_slot_mapping(const int32_t* bt, const int32_t* lens, int n_seqs, int S, int I,
                                int bs, int max_blocks, int64_t n_blocks, int64_t* slots, int* flag,

@@ -234,6 +234,35 @@ int pa_decode_step(const void* q, const void* k_new, const void* v_new, int32_t 
                    void* stream);
 
 /*
+ * pa_decode_step_static -- pa_decode_step followed by pa_merge_lse, allocating nothing:
+ * for callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc).  The partial outputs and LSEs, which
+ * the two calls take from the caller, live here in a fixed device array of the library,
+ * PA_STATIC_SCRATCH_BYTES on each GPU, held from the library's load until the process
+ * ends.  No allocator is called.
+ *   out   [n_seqs][n_q_heads][dv] of out_dtype (PA_F32 or PA_BF16) and lse float32
+ *         [n_seqs][n_q_heads]: as pa_merge_lse writes them (with one shard, one partition
+ *         slot and out_dtype PA_F32 the decode writes them itself, one launch in all).
+ *   Other arguments: as in pa_decode_step.
+ *   The partials take n_seqs*n_shards*max_partitions*n_q_heads*(dv + 1)*4 bytes (output
+ *   and LSE parts each rounded up to 256); a call needing more than
+ *   PA_STATIC_SCRATCH_BYTES returns PA_ERR_BUFFER and launches nothing.
+ *   Every call on one GPU shares that GPU's array, which keeps the last call's contents
+ *   (nothing in it needs to start at zero): calls that overlap on one GPU -- from several
+ *   streams or host threads -- race, and the caller must order them.
+ */
+#define PA_STATIC_SCRATCH_BYTES (64u << 20)
+int pa_decode_step_static(const void* q, const void* k_new, const void* v_new, int32_t new_dtype,
+                          void* k_cache, void* v_cache, int32_t cache_dtype, const float* k_scale,
+                          const float* v_scale, int32_t n_scales, const int32_t* block_table,
+                          const int32_t* context_lens, int32_t n_seqs, int32_t n_q_heads,
+                          int32_t n_kv_heads, int32_t dk, int32_t dv, int32_t block_size,
+                          int64_t n_blocks, int32_t max_blocks_per_shard, int32_t n_shards,
+                          int32_t interleave, int32_t partition_tokens, int32_t max_partitions,
+                          float scale, int32_t q_dtype, int64_t* slot_mapping, void* out,
+                          int32_t out_dtype, float* lse, int32_t* err_flag, void* stream);
+
+/*
  * pa_decode_fp8 -- pa_decode over an E4M3 cache written by pa_kv_append_fp8: every
  * stored key (value) element is taken as value(code) * k_scale[h] (v_scale[h]; index 0
  * when n_scales == 1), for KV head h; the latent cache (v_cache == NULL) takes the
