@@ -286,7 +286,17 @@ void decode_mla_kernel(DecodeArgs a) {
   const int MQ = a.query_start ? a.max_q : 1;
   const int per_q = a.hkv * NG;
 
-  for (int unit = blockIdx.x;; unit += gridDim.x) {
+  // Workgroup b runs on XCD b mod 8 (the dispatcher deals workgroups out round-robin);
+  // each XCD has an L2 of its own.  Numbering the workgroups XCD by XCD -- first unit
+  // (b mod 8) * (G / 8) + b / 8 -- puts units that follow one another on one XCD, at the
+  // same time: the new tokens of one partition (consecutive units) then read each tile
+  // once from HBM and again from that XCD's L2.  The same units, dealt to other
+  // workgroups: the per-workgroup loads are unchanged.
+  constexpr int kXcds = 8;
+  const int G = gridDim.x;
+  const int first = G % kXcds == 0 ? int(blockIdx.x % kXcds) * (G / kXcds) + int(blockIdx.x / kXcds)
+                                   : int(blockIdx.x);
+  for (int unit = first;; unit += G) {
     // ---- resolve unit -> (pair y, partition p, new token qi, head group grp, KV head
     // kvh); stop past the last pair
     const int slot = unit / (per_q * MQ);
