@@ -97,9 +97,9 @@ DESCRIBE = {
 
 # Source files that make up each decode kernel: a committed counter summary stays valid
 # while these are unchanged.
-KERNEL_FILES = {"decode_gqa_kernel": ["decode_gqa.hip", "pa_common.h", "pa_launch.h"],
-                "decode_mla_kernel": ["decode_mla.hip", "pa_common.h", "pa_launch.h"],
-                "decode_generic_kernel": ["decode_generic.hip", "pa_common.h", "pa_launch.h"]}
+KERNEL_FILES = {"decode_gqa_kernel": ["decode_gqa.hip", "pa_append.h", "pa_common.h", "pa_launch.h"],
+                "decode_mla_kernel": ["decode_mla.hip", "pa_append.h", "pa_common.h", "pa_launch.h"],
+                "decode_generic_kernel": ["decode_generic.hip", "pa_append.h", "pa_common.h", "pa_launch.h"]}
 
 
 def kernel_source_hash(kernel):
