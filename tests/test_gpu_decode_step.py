@@ -135,3 +135,59 @@ def test_decode_step_object_and_graph():
         assert torch.equal(_bits(k3), _bits(k2)) and torch.equal(_bits(v3), _bits(v2)), rep
         assert torch.equal(_bits(step.out), _bits(ref.out)), rep
         assert torch.equal(_bits(step.lse), _bits(ref.lse)), rep
+
+
+@pytest.mark.parametrize("latent", [False, True], ids=["gqa", "latent"])
+def test_decode_step_with_an_invalid_new_token_block(latent):
+    """A sequence whose new token's table entry is invalid: the flag is raised, nothing is
+    stored for it, its slot is -1 -- as in the two-call path -- and the other sequences
+    append and attend as usual (caches, slots and outputs equal to the two-call path)."""
+    import decode_attention_paged_kv_amd as P
+    from oracle import paged_attention as pa
+
+    if latent:
+        w = wl.small("step_bad_latent", [300, 70, 900], 16, 1, 576, 512, 64, wl.BF16, latent=True,
+                     partition_tokens=256, seed=31)
+    else:
+        w = wl.small("step_bad_gqa", [300, 70, 900, 5], 32, 8, 128, 128, 16, wl.BF16,
+                     partition_tokens=128, seed=32)
+    say(f"[decode step] invalid block, {w.name}")
+    dev = torch.device("cuda")
+    T = wl.make_tensors(w, dev)
+    n, hq, dv, bs = w.n_seqs, w.n_q_heads, w.dv, w.block_size
+    nb = T["k_cache"].shape[0]
+    T_part = w.partition_tokens
+    Pmax = max(1, P.pa_max_partitions(int(w.context_lens.max()), 1, 1, T_part))
+    b_bad = 2
+    L_bad = int(w.context_lens[b_bad])
+    bt = T["block_table"].clone()
+    loc = int(pa.shard_lengths(L_bad, 1, 1)[0]) - 1
+    bt[b_bad, 0, loc // bs] = nb + 7
+    scale = float(w.scale_f32)
+
+    def run(fused):
+        k = T["k_cache"].clone()
+        v = None if T["v_cache"] is None else T["v_cache"].clone()
+        po = torch.full((n, 1, Pmax, hq, dv), float("nan"), dtype=torch.float32, device=dev)
+        pl = torch.full((n, 1, Pmax, hq), float("nan"), dtype=torch.float32, device=dev)
+        slots = torch.full((n,), 12345, dtype=torch.int64, device=dev)
+        flag = torch.zeros(1, dtype=torch.int32, device=dev)
+        if fused:
+            P.pa_decode_step(T["q"], T["k_new"], T["v_new"], k, v, bt, T["context_lens"], 1, 1, T_part, Pmax,
+                             scale, po, pl, slot_mapping=slots, dv=dv, err_flag=flag)
+        else:
+            P.pa_kv_append_routed(T["k_new"], T["v_new"], k, v, bt, T["context_lens"], 1, 1, None, None, slots,
+                                  flag)
+            P.pa_decode(T["q"], k, v, bt, T["context_lens"], 1, 1, T_part, Pmax, scale, po, pl, dv=dv,
+                        err_flag=flag)
+        torch.cuda.synchronize()
+        return k, v, po, pl, slots, int(flag.item())
+
+    k1, v1, po1, pl1, s1, f1 = run(True)
+    k2, v2, po2, pl2, s2, f2 = run(False)
+    assert f1 == f2 and f1 & P.ERR_BLOCK_ID, (f1, f2)
+    assert int(s1[b_bad].item()) == -1 and torch.equal(s1, s2)
+    assert torch.equal(_bits(k1), _bits(k2))
+    if v1 is not None:
+        assert torch.equal(_bits(v1), _bits(v2))
+    assert torch.equal(_bits(pl1), _bits(pl2)) and torch.equal(_bits(po1), _bits(po2))

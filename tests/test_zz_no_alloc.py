@@ -3,7 +3,9 @@ library's fixed device array) against the entry points it stands in for: pa_deco
 with caller-allocated partials, then pa_merge_lse.  Same kernels on the same inputs, so
 the outputs, LSEs, slots and caches must be identical bit for bit.  Two calls in a row,
 the second smaller (the array keeps the first call's contents), then a call whose
-partials would not fit, which must fail with PA_ERR_BUFFER and launch nothing."""
+partials would not fit, which must fail with PA_ERR_BUFFER and launch nothing; and the
+call recorded into a HIP graph (its use case), replayed several times with eager work in
+between, each replay equal to the eager call."""
 import numpy as np
 import pytest
 import torch
@@ -102,3 +104,47 @@ def test_static_step_matches_the_allocating_entry_points_twice():
     assert torch.equal(k.view(torch.int16), T["k_cache"].view(torch.int16))   # NaN-poisoned slots:
     assert torch.equal(v.view(torch.int16), T["v_cache"].view(torch.int16))   # compare the bits
     assert bool((out == 7.0).all()) and bool((lse == 7.0).all()) and bool((slots == 5).all())
+
+
+def test_static_step_under_graph_capture():
+    import decode_attention_paged_kv_amd as P
+
+    say("[no-alloc step] graph capture")
+    w = wl.small("static_graph", [700, 20, 1300, 0, 64], 32, 8, 128, 128, 16, wl.BF16, partition_tokens=128,
+                 seed=23)
+    dev = torch.device("cuda")
+    T = wl.make_tensors(w, dev)
+    n = w.n_seqs
+    Pmax = max(1, P.pa_max_partitions(int(w.context_lens.max()), 1, 1, 128))
+    k, v = T["k_cache"].clone(), T["v_cache"].clone()
+    out = torch.empty(n, 32, w.dv, dtype=torch.float32, device=dev)
+    lse = torch.empty(n, 32, dtype=torch.float32, device=dev)
+    slots = torch.empty(n, dtype=torch.int64, device=dev)
+    flag = torch.zeros(1, dtype=torch.int32, device=dev)
+    assert _static_call(T, w, k, v, 128, Pmax, out, lse, slots, flag) == 0
+    torch.cuda.synchronize()
+    out_ref, lse_ref, k_ref, v_ref = out.clone(), lse.clone(), k.clone(), v.clone()
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        k.copy_(T["k_cache"])
+        v.copy_(T["v_cache"])
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=side):
+            assert _static_call(T, w, k, v, 128, Pmax, out, lse, slots, flag) == 0
+    torch.cuda.current_stream().wait_stream(side)
+    for rep in range(3):
+        out.zero_()
+        lse.zero_()
+        k.copy_(T["k_cache"])
+        v.copy_(T["v_cache"])
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert int(flag.item()) == 0
+        assert torch.equal(out.view(torch.int32), out_ref.view(torch.int32)), rep
+        assert torch.equal(lse.view(torch.int32), lse_ref.view(torch.int32)), rep
+        assert torch.equal(k.view(torch.int16), k_ref.view(torch.int16)), rep
+        assert torch.equal(v.view(torch.int16), v_ref.view(torch.int16)), rep
