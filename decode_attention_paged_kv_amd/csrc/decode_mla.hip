@@ -23,8 +23,10 @@
 //    output MFMAs.  One barrier per tile both publishes a landed tile and frees the
 //    buffer of the tile before it.  A single wave per SIMD keeps the matrix core busy
 //    only with work placed in the shadow of its own MFMAs, hence this interleaving.
-//  * Scores: S^T[token][head] = K_tile . Q^T over 36 k-steps.  24 k-steps of the wave's
-//    32 query rows live in registers for the whole partition, 12 in LDS; the key operand
+//  * Scores: S^T[token][head] = K_tile . Q^T over 36 k-steps.  33 k-steps of the wave's
+//    32 query rows live in registers for the whole partition, 3 in LDS (the score phase's
+//    LDS reads are what its time rests on; fewer query reads there measured ~2 % faster
+//    than 12 in LDS); the key operand
 //    is one 16-byte LDS read per lane per MFMA.
 //  * Softmax in base 2 against a reference max per head that is fixed by the first tile
 //    holding a valid token of the partition and never moved: later weights may exceed 1
@@ -107,7 +109,7 @@ constexpr int KSTEPS = DK / 16;                     // 36 k-steps of the score p
 constexpr int MT = DV / 32;                         // 16 value-column tiles
 constexpr int TBL = 256;                            // block-table entries staged in LDS
 #ifndef PA_MLA_QL
-#define PA_MLA_QL 12
+#define PA_MLA_QL 3
 #endif
 #ifndef PA_MLA_KA
 #define PA_MLA_KA 2
