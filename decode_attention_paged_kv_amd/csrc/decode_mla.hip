@@ -372,7 +372,7 @@ void decode_mla_kernel(DecodeArgs a) {
   // Split so that the LDS read can be issued early and its latency hidden.
   auto tile_entry = [&](int i) -> int {
     const int e = (t_begin + i * TT) / bs;
-    if (e - tbl_base >= TBL || e < tbl_base) {   // other chunk of the table (long partitions)
+    if (__builtin_expect(e - tbl_base >= TBL || e < tbl_base, 0)) {   // other chunk of the table (long partitions)
       PA_WAIT_VM(0);
       __syncthreads();
       tbl_base = e;
@@ -397,7 +397,7 @@ void decode_mla_kernel(DecodeArgs a) {
   };
   auto finish_tile = [&](int i, int entry) -> Copy {
     int phys = __builtin_amdgcn_readfirstlane(entry);
-    if (phys < 0) {   // invalid block id or an entry past the row
+    if (__builtin_expect(phys < 0, 0)) {   // invalid block id or an entry past the row
       if (tid == 0) raise_flag(a.flag, entry_error(phys));
       phys = -1;
     }
@@ -662,73 +662,32 @@ void decode_mla_kernel(DecodeArgs a) {
     constexpr int AHEAD = NB - 1;   // tiles copied ahead of the one computed
     for (int i = 0; i < AHEAD && i < n_tiles; ++i) issue_tile(i);
     float mc = have_ref ? m_ref * c : 0.f;
-    bool ok = true;
-    for (int i = 0; i < n_tiles; ++i) {
-      // tile i landed; the copies of the tiles after it may still be in flight
-      const int later = min(AHEAD - 1, n_tiles - 1 - i);
-      if (later >= 2) {
-        PA_WAIT_VM(2 * COPIES);
-      } else if (later == 1) {
-        PA_WAIT_VM(COPIES);
-      } else {
-        PA_WAIT_VM(0);
-      }
-      // everyone's copies of tile i are in, everyone is done with tile i-1 (whose buffer
-      // tile i+2 takes), and tile i-1's overflow flags are visible
-      lds_barrier();
-      // LDS reads consumed later, so their latency hides under the MFMAs: tile i-1's
-      // overflow flags (checked at the end of the iteration) and tile i+2's table entry
-      const int4 flags = *reinterpret_cast<const int4*>(&ovf_s[(i + 1) & 1][0]);
-      const bool copy_next = i + AHEAD < n_tiles;
-      const int entry = copy_next ? tile_entry(i + AHEAD) : 0;
-      f32x16_t s;
-      Copy cp{};
-      // copy k of tile i+AHEAD in the shadow of score MFMA 1 + CS k
-      constexpr int CS = PA_MLA_COPY_STRIDE;
-      static_assert(CS >= 1 && 1 + CS * (COPIES - 1) < KSTEPS, "copy slots");
-      scores(tile_ptr(i), s, [&](int ks) {
-        if (copy_next && ks >= 1 && (ks - 1) % CS == 0 && (ks - 1) / CS < COPIES) {
-          const int k = (ks - 1) / CS;
-          if (k == 0) cp = finish_tile(i + AHEAD, entry);
-          copy_piece(cp, k);
-        }
-      });
-      bf16x8_t vop[VA + 1];
-      const VBase vb = vstart(tile_ptr(i), vop);
-      // Softmax: lane holds head r32, tokens 8 (e / 4) + 4 c32 + e % 4 of the tile;
-      // elements 0..7 are the first k-step's weights, 8..15 the second's.
-      const int valid = tile_valid(i);
-      if (valid < TT) {   // the partition's last tile, or an invalid block
-        const int lim = valid - 4 * c32;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) s[e] = 8 * (e >> 2) + (e & 3) < lim ? s[e] : -INFINITY;
-      }
-      if (!have_ref && valid > 0) {   // the first tile with a valid token sets the reference
-        float mx = -INFINITY;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[e]);
-        m_ref = fmaxf(mx, __shfl_xor(mx, 32));
-        have_ref = true;
-        mc = m_ref * c;
-      }
+    // copy k of tile i+AHEAD in the shadow of score MFMA 1 + CS k
+    constexpr int CS = PA_MLA_COPY_STRIDE;
+    static_assert(CS >= 1 && 1 + CS * (COPIES - 1) < KSTEPS, "copy slots");
+    auto copy_slot = [](int ks) { return ks >= 1 && (ks - 1) % CS == 0 && (ks - 1) / CS < COPIES; };
+
+    // Weights and output product of tile i from its scores s.  Softmax: lane holds head
+    // r32, tokens 8 (e / 4) + 4 c32 + e % 4 of the tile; elements 0..7 are the first
+    // k-step's weights (computed here, with the first value reads in flight), 8..15 the
+    // second's (in the shadow of the first output MFMAs), then the overflow flag: a
+    // weight above 2^64 (a score more than 64 log2 units above the reference) makes the
+    // lane's sum exceed 2^64.
+    auto weigh_and_output = [&](int i, const f32x16_t& s, const VBase& vb, bf16x8_t (&vop)[VA + 1]) {
       float part = 0.f, pe[16];
       u32x4_t pop[2], plo[2];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        pe[e] = __builtin_amdgcn_exp2f(fmaf(s[e], c, -mc));
-        part += pe[e];
-      }
+      for (int e = 0; e < 8; ++e) pe[e] = __builtin_amdgcn_exp2f(fmaf(s[e], c, -mc));
 #pragma unroll
       for (int qq = 0; qq < 4; ++qq) {
         const Bf16Pairs w = split_pair(pe[2 * qq], pe[2 * qq + 1]);
         pop[0][qq] = w.hi;
         plo[0][qq] = w.lo;
       }
-      // the second k-step's weights, two per output operand (each two MFMAs long), then
-      // the overflow flag: a weight above 2^64 (a score more than 64 log2 units above the
-      // reference) makes the lane's sum exceed 2^64
+      // (the first weights join the sum in the shadow of the output MFMAs too)
       outputs(vb, vop, pop, plo, o, [&](int n) {
         if (n < 4) {
+          part += pe[2 * n] + pe[2 * n + 1];
 #pragma unroll
           for (int e = 8 + 2 * n; e < 10 + 2 * n; ++e) {
             float v = s[e];
@@ -753,11 +712,101 @@ void decode_mla_kernel(DecodeArgs a) {
           if (lane == 0) ovf_s[i & 1][wave] = ovf ? 1 : 0;
         }
       });
-      if (i > 0 && (flags.x | flags.y | flags.z | flags.w) != 0) {   // tile i-1 overflowed
-        ok = false;
+    };
+
+    // The common iteration runs straight-line code (a taken branch costs a wave with no
+    // other wave on its SIMD tens of cycles): tiles i .. i+AHEAD all full, tile i's block
+    // valid, the reference set, and every block of the partition in the staged chunk of
+    // the table.  Other iterations (the partition's first and last tiles, invalid blocks,
+    // table restaging) take the general path for their first half.  Tile i+AHEAD's block
+    // and first row are stepped along instead of divided out.
+    const bool table_fits = (t_end - 1) / bs - e_first < TBL;
+    auto fast_ok = [&](int i) {
+      return have_ref && table_fits && (i + AHEAD + 1) * TT <= t_end - t_begin && !((bad >> (i % NB)) & 1);
+    };
+    int nblk = (t_begin + AHEAD * TT) / bs;
+    int nrow = t_begin + AHEAD * TT - nblk * bs;
+    bool ok = true;
+    for (int i = 0; i < n_tiles; ++i) {
+      f32x16_t s;
+      Copy cp{};
+      int4 flags;
+      if (__builtin_expect(fast_ok(i), 1)) {
+        PA_WAIT_VM(COPIES);   // tile i landed, tile i+1's copies may be in flight
+        // everyone's copies of tile i are in, everyone is done with tile i-1 (whose buffer
+        // tile i+2 takes), and tile i-1's overflow flags are visible
+        lds_barrier();
+        // LDS reads consumed later, so their latency hides under the MFMAs: tile i-1's
+        // overflow flags (checked at the end of the iteration) and tile i+2's table entry
+        flags = *reinterpret_cast<const int4*>(&ovf_s[(i + 1) & 1][0]);
+        const int entry = tbl_s[nblk - tbl_base];
+        scores(tile_ptr(i), s, [&](int ks) {
+          if (copy_slot(ks)) {
+            const int k = (ks - 1) / CS;
+            if (k == 0) {
+              int phys = __builtin_amdgcn_readfirstlane(entry);
+              if (__builtin_expect(phys < 0, 0)) {   // invalid block id
+                if (tid == 0) raise_flag(a.flag, entry_error(phys));
+                phys = -1;
+              }
+              const char* src = phys >= 0 ? kc + key_row(phys, kvh, a.hkv, bs, nrow, ROW_BYTES) : zero_tile;
+              const uint32_t slot = uint32_t((i + AHEAD) % NB);
+              bad = (bad & ~(1u << slot)) | (uint32_t(phys < 0) << slot);
+              cp = Copy{uniform_ptr(src), kt_lds + slot * TILE_BYTES, TT};
+            }
+            copy16_to_lds(uniform_ptr(cp.src), full_off[k],
+                          __builtin_amdgcn_readfirstlane(cp.dst + uint32_t((k * NW + wave) * 64 * 16)));
+          }
+        });
+      } else {
+        // tile i landed; the copies of the tiles after it may still be in flight
+        const int later = min(AHEAD - 1, n_tiles - 1 - i);
+        if (later >= 2) {
+          PA_WAIT_VM(2 * COPIES);
+        } else if (later == 1) {
+          PA_WAIT_VM(COPIES);
+        } else {
+          PA_WAIT_VM(0);
+        }
+        lds_barrier();
+        flags = *reinterpret_cast<const int4*>(&ovf_s[(i + 1) & 1][0]);
+        const bool copy_next = i + AHEAD < n_tiles;
+        const int entry = copy_next ? tile_entry(i + AHEAD) : 0;
+        scores(tile_ptr(i), s, [&](int ks) {
+          if (copy_next && copy_slot(ks)) {
+            const int k = (ks - 1) / CS;
+            if (k == 0) cp = finish_tile(i + AHEAD, entry);
+            copy_piece(cp, k);
+          }
+        });
+        const int valid = tile_valid(i);
+        if (valid < TT) {   // the partition's last tile, or an invalid block
+          const int lim = valid - 4 * c32;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) s[e] = 8 * (e >> 2) + (e & 3) < lim ? s[e] : -INFINITY;
+        }
+        if (!have_ref && valid > 0) {   // the first tile with a valid token sets the reference
+          float mx = -INFINITY;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[e]);
+          m_ref = fmaxf(mx, __shfl_xor(mx, 32));
+          have_ref = true;
+          mc = m_ref * c;
+        }
+      }
+      bf16x8_t vop[VA + 1];
+      const VBase vb = vstart(tile_ptr(i), vop);
+      __builtin_amdgcn_sched_barrier(0);   // the first value reads go out before the weights
+      weigh_and_output(i, s, vb, vop);
+      if (__builtin_expect(i > 0 && (flags.x | flags.y | flags.z | flags.w) != 0, 0)) {
+        ok = false;   // tile i-1 overflowed
         PA_WAIT_VM(0);   // tile i+1's and i+2's copies, before the buffers are reused
         break;
       }
+      nrow += TT;
+      const bool wrap = nrow == bs;
+      nblk += wrap ? 1 : 0;
+      nrow = wrap ? 0 : nrow;
     }
     if (ok) {   // the last tile's flags: no later iteration reads them
       lds_barrier();
