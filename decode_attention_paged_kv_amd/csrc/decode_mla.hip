@@ -200,8 +200,12 @@ __device__ inline f32x16_t mfma32_vgpr_first(bf16x8_t a, bf16x8_t b) {
   asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
   return d;
 }
+// The score chain's accumulating MFMAs carry no wait states: their operands are LDS
+// reads (waited for with lgkmcnt) and query registers loaded before the tile loop, never
+// a value a VALU instruction has just written (tests/test_isa_hazards.py checks the
+// compiled code for that).
 __device__ inline void mfma32_vgpr_acc(f32x16_t& d, bf16x8_t a, bf16x8_t b) {
-  asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
 }
 __device__ inline void mfma32_vgpr_last(f32x16_t& d, bf16x8_t a, bf16x8_t b) {
   asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 4"
@@ -221,6 +225,24 @@ __device__ inline f32x16_t to_agpr(f32x16_t v) {
 
 // Source of the copy of a tile whose block id is invalid (zero-initialised device memory).
 __device__ __attribute__((aligned(16))) char g_zero_tile[TILE_BYTES];
+
+// Progress of the units that share their tiles with a partner (the new tokens of one
+// partition, side by side on one XCD): slot u % kProgressSlots holds (u & 0xffff) << 16 |
+// tile.  Only a hint: a stale or shared slot makes a unit wait less or not at all, never
+// changes a result, and every wait is bounded.
+constexpr int kProgressSlots = 4096;
+__device__ uint32_t g_progress[kProgressSlots];
+constexpr int kSyncEvery = 8;    // tiles between progress checks
+constexpr int kSyncDrift = 2;    // tiles a unit may run ahead of its partner
+constexpr int kSyncSpins = 80;   // bound of a wait (each spin sleeps ~256 cycles)
+
+// A progress slot read from L2 past the scalar cache (glc), waited for with lgkmcnt so that
+// the tile copies in flight (counted by vmcnt) are not waited for.
+__device__ inline uint32_t load_progress(const uint32_t* p) {
+  uint32_t v;
+  asm volatile("s_load_dword %0, %1, 0x0 glc\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+  return v;
+}
 
 template <bool F8>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -327,6 +349,7 @@ void decode_mla_kernel(DecodeArgs a) {
     // new token qi of nq (global position L - nq + qi) those at or before its position
     int qr = b;
     int Lq = shard_len(L, a.n_shards, a.interleave, r);
+    int partner = -1;   // unit sharing this one's tiles, kept in step with it
     if (a.query_start) {
       const int row0 = a.query_start[b];
       const int nq = a.query_start[b + 1] - row0;
@@ -337,6 +360,15 @@ void decode_mla_kernel(DecodeArgs a) {
       if (qi >= nq) continue;
       qr = row0 + qi;
       Lq = visible_on_shard(L - nq + qi, a.n_shards, a.interleave, r);
+      // the unit of new token qi ^ 1 reads the same tiles; with the XCD-wise numbering it
+      // runs at the same time on the same XCD when it falls in the same block of G / 8
+      // units -- then the two keep within a few tiles of each other, so that the second
+      // read of each tile is an L2 hit
+      const int qp = qi ^ 1;
+      if (qp < nq && G % kXcds == 0) {
+        const int pu = unit + (qp - qi) * per_q;
+        if (pu / (G / kXcds) == unit / (G / kXcds)) partner = pu;
+      }
     }
     const int t_begin = p * T;
     const int t_end = min(t_begin + T, Lq);
@@ -628,6 +660,55 @@ void decode_mla_kernel(DecodeArgs a) {
     const VBase vb = vstart(tile, vop);
     outputs(vb, vop, pop, plo, o, no_filler);
   };
+  // Weights and output product of tile i from its scores s.  Softmax: lane holds head
+  // r32, tokens 8 (e / 4) + 4 c32 + e % 4 of the tile; elements 0..7 are the first
+  // k-step's weights (computed here, with the first value reads in flight), 8..15 the
+  // second's (in the shadow of the first output MFMAs), then the overflow flag: a
+  // weight above 2^64 (a score more than 64 log2 units above the reference) makes the
+  // lane's sum exceed 2^64.  extra(n) is more of the caller's work for the shadow of
+  // operand n's MFMAs.
+  auto weigh_and_output = [&](int i, const f32x16_t& s, const VBase& vb, bf16x8_t (&vop)[VA + 1], float mc,
+                              f32x16_t (&o)[MT], float& lsum, auto&& extra) {
+    float part = 0.f, pe[16];
+    u32x4_t pop[2], plo[2];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pe[e] = __builtin_amdgcn_exp2f(fmaf(s[e], c, -mc));
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      const Bf16Pairs w = split_pair(pe[2 * qq], pe[2 * qq + 1]);
+      pop[0][qq] = w.hi;
+      plo[0][qq] = w.lo;
+    }
+    // (the first weights join the sum in the shadow of the output MFMAs too)
+    outputs(vb, vop, pop, plo, o, [&](int n) {
+      if (n < 4) {
+        part += pe[2 * n] + pe[2 * n + 1];
+#pragma unroll
+        for (int e = 8 + 2 * n; e < 10 + 2 * n; ++e) {
+          float v = s[e];
+          pin(v);
+          pe[e] = __builtin_amdgcn_exp2f(fmaf(v, c, -mc));
+          part += pe[e];
+          pin(pe[e]);
+        }
+        pin(part);
+      } else if (n < 6) {
+#pragma unroll
+        for (int qq = 2 * (n - 4); qq < 2 * (n - 4) + 2; ++qq) {
+          const Bf16Pairs w = split_pair(pe[8 + 2 * qq], pe[9 + 2 * qq]);
+          pop[1][qq] = w.hi;
+          plo[1][qq] = w.lo;
+        }
+        pin(pop[1]);
+        pin(plo[1]);
+      } else if (n == 6) {
+        lsum += part;
+        const bool ovf = __any(part > 0x1p64f);
+        if (lane == 0) ovf_s[i & 1][wave] = ovf ? 1 : 0;
+      }
+      extra(n);
+    });
+  };
   auto zero_tiles = [&](f32x16_t (&o)[MT]) {
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
@@ -667,53 +748,6 @@ void decode_mla_kernel(DecodeArgs a) {
     static_assert(CS >= 1 && 1 + CS * (COPIES - 1) < KSTEPS, "copy slots");
     auto copy_slot = [](int ks) { return ks >= 1 && (ks - 1) % CS == 0 && (ks - 1) / CS < COPIES; };
 
-    // Weights and output product of tile i from its scores s.  Softmax: lane holds head
-    // r32, tokens 8 (e / 4) + 4 c32 + e % 4 of the tile; elements 0..7 are the first
-    // k-step's weights (computed here, with the first value reads in flight), 8..15 the
-    // second's (in the shadow of the first output MFMAs), then the overflow flag: a
-    // weight above 2^64 (a score more than 64 log2 units above the reference) makes the
-    // lane's sum exceed 2^64.
-    auto weigh_and_output = [&](int i, const f32x16_t& s, const VBase& vb, bf16x8_t (&vop)[VA + 1]) {
-      float part = 0.f, pe[16];
-      u32x4_t pop[2], plo[2];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pe[e] = __builtin_amdgcn_exp2f(fmaf(s[e], c, -mc));
-#pragma unroll
-      for (int qq = 0; qq < 4; ++qq) {
-        const Bf16Pairs w = split_pair(pe[2 * qq], pe[2 * qq + 1]);
-        pop[0][qq] = w.hi;
-        plo[0][qq] = w.lo;
-      }
-      // (the first weights join the sum in the shadow of the output MFMAs too)
-      outputs(vb, vop, pop, plo, o, [&](int n) {
-        if (n < 4) {
-          part += pe[2 * n] + pe[2 * n + 1];
-#pragma unroll
-          for (int e = 8 + 2 * n; e < 10 + 2 * n; ++e) {
-            float v = s[e];
-            pin(v);
-            pe[e] = __builtin_amdgcn_exp2f(fmaf(v, c, -mc));
-            part += pe[e];
-            pin(pe[e]);
-          }
-          pin(part);
-        } else if (n < 6) {
-#pragma unroll
-          for (int qq = 2 * (n - 4); qq < 2 * (n - 4) + 2; ++qq) {
-            const Bf16Pairs w = split_pair(pe[8 + 2 * qq], pe[9 + 2 * qq]);
-            pop[1][qq] = w.hi;
-            plo[1][qq] = w.lo;
-          }
-          pin(pop[1]);
-          pin(plo[1]);
-        } else if (n == 6) {
-          lsum += part;
-          const bool ovf = __any(part > 0x1p64f);
-          if (lane == 0) ovf_s[i & 1][wave] = ovf ? 1 : 0;
-        }
-      });
-    };
-
     // The common iteration runs straight-line code (a taken branch costs a wave with no
     // other wave on its SIMD tens of cycles): tiles i .. i+AHEAD all full, tile i's block
     // valid, the reference set, and every block of the partition in the staged chunk of
@@ -722,7 +756,29 @@ void decode_mla_kernel(DecodeArgs a) {
     // and first row are stepped along instead of divided out.
     const bool table_fits = (t_end - 1) / bs - e_first < TBL;
     auto fast_ok = [&](int i) {
-      return have_ref && table_fits && (i + AHEAD + 1) * TT <= t_end - t_begin && !((bad >> (i % NB)) & 1);
+      return have_ref && table_fits && (i + AHEAD + 1) * TT <= t_end - t_begin && !((bad >> (i % NB)) & 1) &&
+             (partner < 0 || i % kSyncEvery != 0);
+    };
+    // Every kSyncEvery tiles of a unit with a partner: publish the tile reached, and let
+    // wave 0 wait (the others wait at the barrier that follows) while the partner is more
+    // than kSyncDrift tiles behind -- at most kSyncSpins short sleeps, after which the
+    // unit stops waiting for it.
+    auto pair_wait = [&](int i) {
+      if (wave != 0) return;
+      if (lane == 0)
+        __hip_atomic_store(&g_progress[unit % kProgressSlots], (uint32_t(unit & 0xffff) << 16) | uint32_t(i & 0xffff),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint32_t* slot_p = reinterpret_cast<const uint32_t*>(
+          uniform_ptr(reinterpret_cast<const char*>(&g_progress[partner % kProgressSlots])));
+      int spins = 0;
+#pragma unroll 1
+      for (; spins < kSyncSpins; ++spins) {
+        const uint32_t v = load_progress(slot_p);
+        const int at = (v >> 16) == (uint32_t(partner) & 0xffffu) ? int(v & 0xffffu) : -1;
+        if (at >= i - kSyncDrift) break;
+        __builtin_amdgcn_s_sleep(4);
+      }
+      if (spins == kSyncSpins) partner = -1;
     };
     int nblk = (t_begin + AHEAD * TT) / bs;
     int nrow = t_begin + AHEAD * TT - nblk * bs;
@@ -759,6 +815,7 @@ void decode_mla_kernel(DecodeArgs a) {
           }
         });
       } else {
+        if (partner >= 0 && i % kSyncEvery == 0) pair_wait(i);
         // tile i landed; the copies of the tiles after it may still be in flight
         const int later = min(AHEAD - 1, n_tiles - 1 - i);
         if (later >= 2) {
@@ -797,7 +854,7 @@ void decode_mla_kernel(DecodeArgs a) {
       bf16x8_t vop[VA + 1];
       const VBase vb = vstart(tile_ptr(i), vop);
       __builtin_amdgcn_sched_barrier(0);   // the first value reads go out before the weights
-      weigh_and_output(i, s, vb, vop);
+      weigh_and_output(i, s, vb, vop, mc, o, lsum, [](int) {});
       if (__builtin_expect(i > 0 && (flags.x | flags.y | flags.z | flags.w) != 0, 0)) {
         ok = false;   // tile i-1 overflowed
         PA_WAIT_VM(0);   // tile i+1's and i+2's copies, before the buffers are reused
@@ -874,18 +931,20 @@ void decode_mla_kernel(DecodeArgs a) {
           : uint2{0u, 0u};
     }
   };
-  auto store_tile_f8 = [&](int i, const RawTile& raw) {
+  // widens piece k of a tile's codes into tile i's buffer (16 bytes per thread)
+  auto store_piece_f8 = [&](int i, const RawTile& raw, int k) {
     char* dst = kt + (i % NB) * TILE_BYTES;
+    const int s_ = tid + 64 * NW * k;
+    uint4 v;
+    v.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.w[k].x, 1.0f, false));
+    v.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.w[k].x, 1.0f, true));
+    v.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.w[k].y, 1.0f, false));
+    v.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.w[k].y, 1.0f, true));
+    *reinterpret_cast<uint4*>(dst + 16 * s_) = v;
+  };
+  auto store_tile_f8 = [&](int i, const RawTile& raw) {
 #pragma unroll
-    for (int k = 0; k < COPIES; ++k) {
-      const int s_ = tid + 64 * NW * k;
-      uint4 v;
-      v.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.w[k].x, 1.0f, false));
-      v.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.w[k].x, 1.0f, true));
-      v.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.w[k].y, 1.0f, false));
-      v.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.w[k].y, 1.0f, true));
-      *reinterpret_cast<uint4*>(dst + 16 * s_) = v;
-    }
+    for (int k = 0; k < COPIES; ++k) store_piece_f8(i, raw, k);
   };
   auto restage_first = [&]() {
     if (tbl_base != e_first) {
@@ -895,55 +954,47 @@ void decode_mla_kernel(DecodeArgs a) {
       __syncthreads();
     }
   };
-  // Accumulating pass: tile i+1's loads are issued before tile i's products and written
-  // after them; the softmax is the same as the bf16 path's (reference max fixed by the
-  // first tile with a valid token, a weight beyond 2^64 ends the pass).
+  // Accumulating pass: tile i+1's loads are issued before tile i's products, and its codes
+  // are widened into the buffer tile i-1 left in the shadow of tile i's later output MFMAs
+  // (operands F8_STORE0 ..; in the last iteration that writes unused registers into a
+  // buffer nothing reads again); weights and output as in the bf16 path.
   auto pass_acc_f8 = [&](float& m_ref, bool& have_ref, f32x16_t (&o)[MT], float& lsum) -> bool {
+    constexpr int F8_STORE0 = 4;
+    static_assert(F8_STORE0 + COPIES <= NV, "stores in the output MFMAs' shadow");
     restage_first();
     RawTile raw;
     load_tile_f8(0, tile_entry(0), raw);
     store_tile_f8(0, raw);
     lds_barrier();
     bool ok = true;
+    float mc = have_ref ? m_ref * c : 0.f;
     for (int i = 0; i < n_tiles; ++i) {
-      const bool has_next = i + 1 < n_tiles;
-      if (has_next) load_tile_f8(i + 1, tile_entry(i + 1), raw);
+      if (i + 1 < n_tiles) load_tile_f8(i + 1, tile_entry(i + 1), raw);
       f32x16_t s;
       scores(tile_ptr(i), s, no_filler);
       const int valid = tile_valid(i);
-      float sc[16];
-      if (valid < TT) {
-        masked(s, valid, sc);
-      } else {
+      if (__builtin_expect(valid < TT, 0)) {   // the partition's last tile, or an invalid block
+        const int lim = valid - 4 * c32;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) sc[e] = s[e];
+        for (int e = 0; e < 16; ++e) s[e] = 8 * (e >> 2) + (e & 3) < lim ? s[e] : -INFINITY;
       }
-      if (!have_ref && valid > 0) {   // the first tile with a valid token sets the reference
-        m_ref = row_max(sc);
+      if (__builtin_expect(!have_ref && valid > 0, 0)) {   // the first tile with a valid token sets the reference
+        float mx = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[e]);
+        m_ref = fmaxf(mx, __shfl_xor(mx, 32));
         have_ref = true;
+        mc = m_ref * c;
       }
-      const float mc = have_ref ? m_ref * c : 0.f;
-      float part = 0.f, pe[16];
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        pe[e] = __builtin_amdgcn_exp2f(fmaf(sc[e], c, -mc));
-        part += pe[e];
-      }
-      const bool ovf = __any(part > 0x1p64f);   // a weight above 2^64
-      if (lane == 0) ovf_s[i & 1][wave] = ovf ? 1 : 0;
-      u32x4_t pop[2], plo[2];
-#pragma unroll
-      for (int e = 0; e < 16; e += 2) {
-        const Bf16Pairs w = split_pair(pe[e], pe[e + 1]);
-        pop[e >> 3][(e & 7) >> 1] = w.hi;
-        plo[e >> 3][(e & 7) >> 1] = w.lo;
-      }
-      outputs_all(tile_ptr(i), pop, plo, o);
-      lsum += part;
-      if (has_next) store_tile_f8(i + 1, raw);
+      bf16x8_t vop[VA + 1];
+      const VBase vb = vstart(tile_ptr(i), vop);
+      __builtin_amdgcn_sched_barrier(0);   // the first value reads go out before the weights
+      weigh_and_output(i, s, vb, vop, mc, o, lsum, [&](int n) {
+        if (n >= F8_STORE0 && n < F8_STORE0 + COPIES) store_piece_f8(i + 1, raw, n - F8_STORE0);
+      });
       // tile i+1 written by everyone, everyone done with tile i; the overflow flags seen
       lds_barrier();
-      if (any_overflow(i & 1)) {
+      if (__builtin_expect(any_overflow(i & 1), 0)) {
         ok = false;
         break;
       }
