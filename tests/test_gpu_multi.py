@@ -86,6 +86,55 @@ def test_multi_latent_speculative():
     check_large(w)
 
 
+def test_multi_latent_partners_timing_only():
+    """The latent kernel keeps the units of two new tokens of one partition within a few
+    tiles of each other through a progress array that every launch shares: it changes
+    timing only.  With a full grid (the case where partners are paired), repeated runs of
+    one step are bitwise equal, and two steps launched together on two streams -- sharing
+    that array -- give bitwise what each gives alone."""
+    import decode_attention_paged_kv_amd as P
+
+    say("[multi] latent partners: repeated and concurrent launches")
+    w = wl.small("mq_latent_pairs", [20000, 30000, 12000, 25000], 128, 1, 576, 512, 64, wl.BF16,
+                 partition_tokens=512, latent=True, seed=21, q_lens=[2, 2, 3, 2])
+    dev = torch.device("cuda")
+    T = wl.make_tensors(w, dev)
+
+    def make():
+        return P.MultiDecodeStep(w.n_seqs, w.n_rows, int(w.q_lens.max()), w.n_q_heads, w.n_kv_heads,
+                                 w.dk, w.dv, w.block_size, int(w.context_lens.max()),
+                                 partition_tokens=512, scale=w.scale_f32, device=dev, latent=True)
+
+    a, b = make(), make()
+    a(T["q"], T["query_start"], T["k_new"], T["v_new"], T["k_cache"], T.get("v_cache"),
+      T["block_table"], T["context_lens"])   # the new rows are in the cache from here on
+    args = (T["q"], T["query_start"], T["k_cache"], T.get("v_cache"), T["block_table"], T["context_lens"])
+    torch.cuda.synchronize()
+
+    def written(st):   # partition slots past a sequence's count keep whatever they held
+        used = torch.isfinite(st.part_lse)
+        return st.part_out[used].clone(), st.part_lse.clone()
+
+    ref = written(a)
+    assert ref[0].shape[0] > 0 and torch.isfinite(ref[0]).all()
+    for _ in range(3):
+        a.attend(*args)
+        torch.cuda.synchronize()
+        got = written(a)
+        assert torch.equal(got[0], ref[0]) and torch.equal(got[1], ref[1])
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s1):
+        a.attend(*args)
+    with torch.cuda.stream(s2):
+        b.attend(*args)
+    torch.cuda.synchronize()
+    for st in (a, b):
+        assert int(st.err_flag.item()) == 0
+        got = written(st)
+        assert torch.equal(got[0], ref[0]) and torch.equal(got[1], ref[1])
+
+
 def test_multi_error_flag_on_too_many_new_tokens():
     """A sequence with more new tokens than context tokens is flagged and skipped; the
     others are computed."""
