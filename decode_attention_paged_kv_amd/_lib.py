@@ -344,6 +344,23 @@ def pa_decode_step(q, k_new, v_new, k_cache, v_cache, block_table, context_lens,
     """Append of the new tokens and the attention in one call (``pa_decode_step``): the
     effect of ``pa_kv_append_routed`` then ``pa_decode`` (``pa_decode_fp8`` for a uint8
     cache of E4M3 codes, which takes its scales)."""
+    call_decode_step(decode_step_args(q, k_new, v_new, k_cache, v_cache, block_table, context_lens,
+                                      n_shards, interleave, partition_tokens, max_partitions, scale,
+                                      part_out, part_lse, k_scale, v_scale, slot_mapping, dv,
+                                      err_flag), q)
+
+
+def call_decode_step(args, q):
+    """``pa_decode_step`` on the arguments ``decode_step_args`` built, on ``q``'s device's
+    current stream."""
+    _check(lib.pa_decode_step(*args, _stream(q)))
+
+
+def decode_step_args(q, k_new, v_new, k_cache, v_cache, block_table, context_lens, n_shards,
+                     interleave, partition_tokens, max_partitions, scale, part_out, part_lse,
+                     k_scale=None, v_scale=None, slot_mapping=None, dv=None, err_flag=None):
+    """The checks of ``pa_decode_step`` and its C arguments but the stream, as a list (a
+    caller that passes the same tensors again can reuse it)."""
     _need(q, None, 3, "q")
     _need(k_new, None, 3, "k_new")
     _need(v_new, k_new.dtype, 3, "v_new")
@@ -380,13 +397,11 @@ def pa_decode_step(q, k_new, v_new, k_cache, v_cache, block_table, context_lens,
         ns = _scales(k_scale, v_scale, hkv, v_cache is None)
     elif k_cache.dtype != q.dtype or k_new.dtype != q.dtype:
         raise TypeError("q, k_new and the cache must share an element type (or the cache be uint8 codes)")
-    _check(lib.pa_decode_step(_ptr(q), _ptr(k_new), _ptr(v_new), _dtype_code(k_new), _ptr(k_cache),
-                              _ptr(v_cache), _dtype_code(k_cache, cache=True), _ptr(k_scale),
-                              _ptr(v_scale), ns, _ptr(block_table), _ptr(context_lens), n, hq, hkv,
-                              dk, dv, bs, nb, block_table.shape[2], n_shards, interleave,
-                              partition_tokens, max_partitions, float(scale), _dtype_code(q),
-                              _ptr(slot_mapping), _ptr(part_out), _ptr(part_lse), _ptr(err_flag),
-                              _stream(q)))
+    return [_ptr(q), _ptr(k_new), _ptr(v_new), _dtype_code(k_new), _ptr(k_cache), _ptr(v_cache),
+            _dtype_code(k_cache, cache=True), _ptr(k_scale), _ptr(v_scale), ns, _ptr(block_table),
+            _ptr(context_lens), n, hq, hkv, dk, dv, bs, nb, block_table.shape[2], n_shards, interleave,
+            partition_tokens, max_partitions, float(scale), _dtype_code(q), _ptr(slot_mapping),
+            _ptr(part_out), _ptr(part_lse), _ptr(err_flag)]
 
 
 def pa_slot_mapping_multi(block_table, context_lens, query_start, n_shards, interleave, block_size,

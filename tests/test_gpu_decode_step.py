@@ -191,3 +191,45 @@ def test_decode_step_with_an_invalid_new_token_block(latent):
     if v1 is not None:
         assert torch.equal(_bits(v1), _bits(v2))
     assert torch.equal(_bits(pl1), _bits(pl2)) and torch.equal(_bits(po1), _bits(po2))
+
+
+def test_decode_step_object_reuses_checked_arguments_safely():
+    """DecodeStep keeps the checked argument list of its last call while the same tensors
+    come back.  Calls on tensors A, then B, then A again each equal a fresh step on the
+    same inputs bit for bit; a tensor of another shape in place of one of them is
+    checked (and refused), not run on the old list."""
+    import decode_attention_paged_kv_amd as P
+
+    say("[decode step] argument reuse")
+    dev = torch.device("cuda")
+    w = wl.small("step_reuse", [300, 70, 1, 900], 32, 8, 128, 128, 16, wl.BF16, partition_tokens=128,
+                 seed=12)
+    Lmax = int(w.context_lens.max())
+    mk = lambda: P.DecodeStep(w.n_seqs, 32, 8, 128, 128, 16, Lmax, partition_tokens=128,
+                              scale=float(w.scale_f32), device=dev)
+    sets = [wl.make_tensors(w, dev, seed=s) for s in (1, 2)]
+    caches = [(T["k_cache"].clone(), T["v_cache"].clone()) for T in sets]
+
+    def args(j):
+        T, (kc, vc) = sets[j], caches[j]
+        return (T["q"], T["k_new"], T["v_new"], kc, vc, T["block_table"], T["context_lens"])
+
+    step = mk()
+    for j in (0, 1, 0):
+        kc0, vc0 = caches[j][0].clone(), caches[j][1].clone()
+        out, lse = step(*args(j))
+        out, lse = out.clone(), lse.clone()
+        fresh = mk()
+        T = sets[j]
+        ref_out, ref_lse = fresh(T["q"], T["k_new"], T["v_new"], kc0, vc0, T["block_table"],
+                                 T["context_lens"])
+        torch.cuda.synchronize()
+        assert int(step.err_flag.item()) == 0
+        assert torch.equal(_bits(out), _bits(ref_out)) and torch.equal(_bits(lse), _bits(ref_lse)), \
+            f"call on set {j} differs"
+        # (unused cache slots hold NaN poison: compare the bits)
+        assert torch.equal(_bits(caches[j][0]), _bits(kc0)) and torch.equal(_bits(caches[j][1]), _bits(vc0)), \
+            "appended rows differ"
+    bad_q = sets[0]["q"][:, :16].contiguous()    # 16 query heads where the step has 32
+    with pytest.raises((ValueError, P.PaError)):
+        step(bad_q, *args(0)[1:])
