@@ -191,10 +191,10 @@ __device__ inline uint32_t lds_address(const void* p) {
 // file: the 16 output tiles take the whole AGPR file and the score accumulator lives in
 // VGPRs; the compiler's own choice moves them between the two on every tile.  The
 // compiler does not see inside these statements, so they carry their wait states: three
-// before each MFMA (for an operand just written by a VALU instruction or an accvgpr
-// write), none between MFMAs that accumulate into exactly the same registers, and a
-// drain of 21 after the last score MFMA of a tile and 24 after the last output MFMA,
-// before any VALU instruction reads the result.
+// before an MFMA whose operand may just have been written by a VALU instruction or an
+// accvgpr write (the first score MFMA of a tile, every output MFMA), none before the
+// score chain's others (below), and a drain of 21 after the last score MFMA of a tile
+// and 24 after the last output MFMA, before any VALU instruction reads the result.
 __device__ inline f32x16_t mfma32_vgpr_first(bf16x8_t a, bf16x8_t b) {
   f32x16_t d;
   asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
