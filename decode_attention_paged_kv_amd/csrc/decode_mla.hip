@@ -192,8 +192,8 @@ __device__ inline uint32_t lds_address(const void* p) {
 // VGPRs; the compiler's own choice moves them between the two on every tile.  The
 // compiler does not see inside these statements, so they carry their wait states: three
 // before an MFMA whose operand may just have been written by a VALU instruction or an
-// accvgpr write (the first score MFMA of a tile, every output MFMA), none before the
-// score chain's others (below), and a drain of 21 after the last score MFMA of a tile
+// accvgpr write (the first score MFMA of a tile, the first output MFMAs of each k-step),
+// none before the others (below), and a drain of 21 after the last score MFMA of a tile
 // and 24 after the last output MFMA, before any VALU instruction reads the result.
 __device__ inline f32x16_t mfma32_vgpr_first(bf16x8_t a, bf16x8_t b) {
   f32x16_t d;
@@ -213,6 +213,11 @@ __device__ inline void mfma32_vgpr_last(f32x16_t& d, bf16x8_t a, bf16x8_t b) {
 }
 __device__ inline void mfma32_agpr_acc(f32x16_t& d, bf16x8_t a, bf16x8_t b) {
   asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
+}
+// An output MFMA whose weight operand was formed at least one output MFMA earlier and
+// whose value operand is an LDS read: no wait states.
+__device__ inline void mfma32_agpr_acc_nowait(f32x16_t& d, bf16x8_t a, bf16x8_t b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
 }
 // Pins a value of an output tile to the AGPR file (the compiler copies it in), so that
 // every definition of the loop-carried output tiles is an AGPR one and the loop keeps
@@ -647,18 +652,17 @@ void decode_mla_kernel(DecodeArgs a) {
 #pragma unroll
     for (int n = 0; n < NV; ++n) {
       if (n + VA < NV) vop[(n + VA) % (VA + 1)] = vread(vb, n + VA);
-      mfma32_agpr_acc(o[n % MT], vop[n % (VA + 1)], __builtin_bit_cast(bf16x8_t, pop[n / MT]));
-      mfma32_agpr_acc(o[n % MT], vop[n % (VA + 1)], __builtin_bit_cast(bf16x8_t, plo[n / MT]));
+      if (n % MT == 0) {   // first use of a k-step's weights
+        mfma32_agpr_acc(o[n % MT], vop[n % (VA + 1)], __builtin_bit_cast(bf16x8_t, pop[n / MT]));
+        mfma32_agpr_acc(o[n % MT], vop[n % (VA + 1)], __builtin_bit_cast(bf16x8_t, plo[n / MT]));
+      } else {
+        mfma32_agpr_acc_nowait(o[n % MT], vop[n % (VA + 1)], __builtin_bit_cast(bf16x8_t, pop[n / MT]));
+        mfma32_agpr_acc_nowait(o[n % MT], vop[n % (VA + 1)], __builtin_bit_cast(bf16x8_t, plo[n / MT]));
+      }
       __builtin_amdgcn_sched_barrier(0);
       filler(n);
       __builtin_amdgcn_sched_barrier(0);
     }
-  };
-  auto outputs_all = [&](const lds_char_t* tile, const u32x4_t (&pop)[2], const u32x4_t (&plo)[2],
-                         f32x16_t (&o)[MT]) {
-    bf16x8_t vop[VA + 1];
-    const VBase vb = vstart(tile, vop);
-    outputs(vb, vop, pop, plo, o, no_filler);
   };
   // Weights and output product of tile i from its scores s.  Softmax: lane holds head
   // r32, tokens 8 (e / 4) + 4 c32 + e % 4 of the tile; elements 0..7 are the first

@@ -3,12 +3,14 @@
 The matrix-core kernels issue their MFMAs through inline asm, which the compiler's hazard
 pass does not look into.  A VALU instruction that writes an MFMA's A or B operand needs
 independent instructions (wait states) before the MFMA reads it -- two on gfx950, as many
-as the compiler's own hazard pass places before its MFMAs; the asm statements carry three
-where a weight operand has just been formed, and the score chain of the latent kernel
-carries none because its operands are LDS reads and query registers loaded before the tile
-loop.  This test compiles the kernels to assembly (device code only, on the CPU) and checks
-that no MFMA has a VALU write of its A or B registers within the two instructions before
-it, counting `s_nop N` as N + 1.
+as the compiler's own hazard pass places before its MFMAs; the same holds for a write of
+the accumulator registers (`v_accvgpr_write`).  The asm statements carry three where a
+weight operand has just been formed (the first output MFMA of each k-step) and none
+elsewhere in the latent kernel's tile loop, whose other operands are LDS reads, query
+registers loaded before the loop and weights formed at least one output MFMA earlier.
+This test compiles the kernels to assembly (device code only, on the CPU) and checks that
+no MFMA has a VALU write of its A, B or AGPR accumulator registers within the two
+instructions before it, counting `s_nop N` as N + 1.
 """
 from __future__ import annotations
 
@@ -27,12 +29,16 @@ import build as B  # noqa: E402
 NEEDED = 2
 
 
-def _vregs(tok: str) -> set:
-    m = re.match(r"v\[(\d+):(\d+)\]$", tok)
+def _regs(tok: str, file: str = "v") -> set:
+    m = re.match(file + r"\[(\d+):(\d+)\]$", tok)
     if m:
         return set(range(int(m.group(1)), int(m.group(2)) + 1))
-    m = re.match(r"v(\d+)$", tok)
+    m = re.match(file + r"(\d+)$", tok)
     return {int(m.group(1))} if m else set()
+
+
+def _vregs(tok: str) -> set:
+    return _regs(tok, "v")
 
 
 def hazards(asm: str, needed: int = NEEDED):
@@ -44,6 +50,7 @@ def hazards(asm: str, needed: int = NEEDED):
             continue
         ops = [t.strip() for t in text.split(None, 1)[1].split(",")]
         src = _vregs(ops[1]) | _vregs(ops[2])
+        src_c = _regs(ops[3], "a") if len(ops) > 3 else set()   # accumulator in AGPRs
         ws, j = 0, i - 1
         while j >= 0 and ws < needed:
             prev = ins[j]
@@ -52,7 +59,8 @@ def hazards(asm: str, needed: int = NEEDED):
                 ws += int(prev.split()[1], 0) + 1
             else:
                 if op.startswith("v_") and not op.startswith("v_mfma"):
-                    if _vregs(prev.split(None, 1)[1].split(",")[0].strip()) & src:
+                    dst = prev.split(None, 1)[1].split(",")[0].strip()
+                    if _vregs(dst) & src or _regs(dst, "a") & src_c:
                         found.append((prev, text, ws))
                 ws += 1
             j -= 1
@@ -64,6 +72,8 @@ def test_checker_catches_a_close_write():
     assert len(hazards(asm)) == 1
     asm_ok = "\tv_cvt_pk_bf16_f32 v161, v0, v1\n\ts_nop 1\n\tv_mfma_f32_32x32x16_bf16 a[0:15], v[2:5], v[158:161], a[0:15]\n"
     assert hazards(asm_ok) == []
+    acc = "\tv_accvgpr_write_b32 a7, v0\n\tv_mfma_f32_32x32x16_bf16 a[0:15], v[2:5], v[158:161], a[0:15]\n"
+    assert len(hazards(acc)) == 1
 
 
 @pytest.mark.parametrize("src", ["decode_mla.hip", "decode_gqa.hip"])
