@@ -2,9 +2,11 @@
 //
 // One workgroup computes one (partition, sequence x shard, KV head, chunk of up to 16
 // columns): a column is a query head of that KV head's group, or, with several new
-// tokens per sequence, a (new token, query head) pair with its own causal end.  It walks the partition's local tokens in tiles
-// of 32: scores of the tile (scale * q.k), an online-softmax update of the running max m,
-// sum l and output accumulator, then the weighted values.  At the end it writes
+// tokens per sequence, a (new token, query head) pair with its own causal end.  It walks
+// the partition's local tokens in tiles of up to 32: the tile's keys and values are
+// copied into LDS (as f32) with all of the tile's loads in flight at once, then come the
+// scores of the tile (scale * q.k), an online-softmax update of the running max m, sum l
+// and output accumulator, and the weighted values.  At the end it writes
 // o = acc / l and lse = m + ln l for the partition (DCP page, soroban.highreso.jp,
 // "Why long-context LLMs get slow ...": local attention returns output and LSE, and the
 // LSEs of online softmax are what the merge reweights with).  Keys and values are read
@@ -28,6 +30,9 @@ constexpr int kThreads = 256;
 constexpr int kHeads = 16;  // query heads per workgroup
 constexpr int kTile = 32;   // tokens per tile
 constexpr int kAcc = kHeads * 512 / kThreads;
+constexpr int kStage = 8192;  // floats of LDS staging the tile's keys and values
+constexpr int kDotLanes = 8;  // lanes per score dot product
+static_assert(kTile == 32 && kHeads * 16 == kThreads, "softmax: 16 lanes per head, two tokens each");
 
 template <int QT, int KT>
 __global__ __launch_bounds__(kThreads) void decode_generic_kernel(DecodeArgs a) {
@@ -88,6 +93,7 @@ __global__ __launch_bounds__(kThreads) void decode_generic_kernel(DecodeArgs a) 
   }
 
   __shared__ float q_s[kHeads * kMaxHeadDim];
+  __shared__ float kv_s[kStage];   // the tile's keys, then its values (separate cache)
   __shared__ float s_s[kHeads][kTile];
   __shared__ float m_s[kHeads], l_s[kHeads], alpha_s[kHeads];
   __shared__ int64_t kbase_s[kTile], vbase_s[kTile];
@@ -95,35 +101,68 @@ __global__ __launch_bounds__(kThreads) void decode_generic_kernel(DecodeArgs a) 
   __shared__ int lim_s[kHeads];
   if (tid < kHeads) lim_s[tid] = tid < nh ? min(t_end, visible(tid)) : 0;
 
+  // Tiles of up to kTile tokens whose keys (rows padded by one word) and values (ditto)
+  // fit the staging buffer.
+  const int kstride = dk + 1, vstride = dv + 1;
+  const int tile_n = min(kTile, kStage / (kstride + (vc ? vstride : 0)));
+  float* k_s = kv_s;
+  float* v_s = kv_s + tile_n * kstride;
+
   float score_mul = a.scale, out_mul = 1.f;
   if (KT == kFP8) {
     const int si = a.n_scales > 1 ? kvh : 0;
     score_mul = a.scale * a.k_scale[si];
     out_mul = vc ? a.v_scale[si] : a.k_scale[si];
   }
+  const int32_t* row = a.block_table + (int64_t(b) * a.n_shards + r) * a.max_blocks;
+  // Table entry of token t0 + tid of a tile (threads below its length), read ahead of
+  // its use; the entry's checks (those of table_entry) come where it is used, so that
+  // the read stays in flight meanwhile.
+  auto entry_read = [&](int t0, int n_t) -> int {
+    const int j = (t0 + tid) / bs;
+    return tid < n_t && j < a.max_blocks ? row[j] : 0;
+  };
+  auto entry_check = [&](int t0, int v) -> int {
+    if ((t0 + tid) / bs >= a.max_blocks) return kPastRow;
+    return (v < 0 || int64_t(v) >= a.n_blocks) ? kBadId : v;
+  };
+  int ent = entry_read(t_begin, min(tile_n, t_end - t_begin));   // in flight with the query loads
+#pragma unroll 8
   for (int i = tid; i < nh * dk; i += kThreads) q_s[i] = EQ::load(q, col_row(i / dk) * dk + i % dk);
   if (tid < kHeads) {
     m_s[tid] = -INFINITY;
     l_s[tid] = 0.f;
   }
+  // Accumulator k of this thread is element tid + k * kThreads of the (head, column)
+  // array: head acc_h0 + ..., column acc_d0 + ..., stepped along (no division per k).
   float acc[kAcc];
 #pragma unroll
   for (int k = 0; k < kAcc; ++k) acc[k] = 0.f;
+  const int acc_h0 = tid / dv, acc_d0 = tid - acc_h0 * dv;
+  const int h_step = kThreads / dv, d_step = kThreads - h_step * dv;
+  auto next_acc = [&](int& hh, int& d) {
+    hh += h_step;
+    d += d_step;
+    if (d >= dv) {
+      d -= dv;
+      ++hh;
+    }
+  };
 
-  const int32_t* row = a.block_table + (int64_t(b) * a.n_shards + r) * a.max_blocks;
-  for (int t0 = t_begin; t0 < t_end; t0 += kTile) {
-    const int n_t = min(kTile, t_end - t0);
+  for (int t0 = t_begin; t0 < t_end; t0 += tile_n) {
+    const int n_t = min(tile_n, t_end - t0);
     if (tid < kTile) {
       int ok = 0;
       int64_t kb = 0, vb = 0;
       if (tid < n_t) {
-        const int t = t0 + tid;
-        const int64_t phys = table_block(row, t / bs, a.max_blocks, a.n_blocks, a.flag);
-        if (phys >= 0) {
+        ent = entry_check(t0, ent);
+        if (ent >= 0) {
           ok = 1;
-          const int off = t % bs;
-          kb = key_row(phys, kvh, a.hkv, bs, off, dk);
-          vb = vc ? value_tile(phys, kvh, a.hkv, bs, dv) + off : kb;
+          const int off = (t0 + tid) % bs;
+          kb = key_row(ent, kvh, a.hkv, bs, off, dk);
+          vb = vc ? value_tile(ent, kvh, a.hkv, bs, dv) + off : kb;
+        } else {
+          raise_flag(a.flag, entry_error(ent));
         }
       }
       ok_s[tid] = ok;
@@ -131,57 +170,91 @@ __global__ __launch_bounds__(kThreads) void decode_generic_kernel(DecodeArgs a) 
       vbase_s[tid] = vb;
     }
     __syncthreads();
-    // scores
-    for (int idx = tid; idx < kHeads * kTile; idx += kThreads) {
-      const int hh = idx / kTile, tt = idx % kTile;
-      float s = -INFINITY;
-      if (hh < nh && tt < n_t && ok_s[tt] && t0 + tt < lim_s[hh]) {
-        const int64_t kb = kbase_s[tt];
-        float dot = 0.f;
-        for (int d = 0; d < dk; ++d) dot = fmaf(q_s[hh * dk + d], E::load(kc, kb + d), dot);
-        s = dot * score_mul;
+    // the next tile's entries, in flight with this tile's loads
+    if (t0 + tile_n < t_end) ent = entry_read(t0 + tile_n, min(tile_n, t_end - t0 - tile_n));
+    // every load of the tile issued before any is waited for: keys row by row, values
+    // token-fastest (a block's tokens are adjacent in the value tile)
+#pragma unroll 8
+    for (int i = tid; i < n_t * dk; i += kThreads) {
+      const int tt = i / dk, d = i - tt * dk;
+      k_s[tt * kstride + d] = ok_s[tt] ? E::load(kc, kbase_s[tt] + d) : 0.f;
+    }
+    if (vc) {
+#pragma unroll 8
+      for (int i = tid; i < n_t * dv; i += kThreads) {
+        const int d = i / n_t, tt = i - d * n_t;
+        v_s[tt * vstride + d] = ok_s[tt] ? E::load(vc, vbase_s[tt] + int64_t(d) * bs) : 0.f;
       }
-      s_s[hh][tt] = s;
     }
     __syncthreads();
-    // online softmax update, one thread per head
-    if (tid < nh) {
-      float mt = m_s[tid];
-      for (int tt = 0; tt < n_t; ++tt) mt = fmaxf(mt, s_s[tid][tt]);
-      const float alpha = (mt == -INFINITY) ? 1.f : expf(m_s[tid] - mt);
-      float sum = 0.f;
-      for (int tt = 0; tt < kTile; ++tt) {
-        const float e = (tt < n_t && s_s[tid][tt] != -INFINITY) ? expf(s_s[tid][tt] - mt) : 0.f;
-        s_s[tid][tt] = e;
-        sum += e;
+    // scores of the (head, token) pairs of the tile: kDotLanes lanes per pair, each a
+    // strided share of the dot product, summed across the lanes
+    const int n_pairs = nh * n_t;
+    for (int base = 0; base < n_pairs * kDotLanes; base += kThreads) {
+      const int pi = (base + tid) / kDotLanes, part = tid % kDotLanes;
+      const bool valid = pi < n_pairs;
+      const int hh = valid ? pi / n_t : 0, tt = valid ? pi - hh * n_t : 0;
+      float dot = 0.f;
+      if (valid) {
+        const float* kr = k_s + tt * kstride;
+        const float* qr = q_s + hh * dk;
+        for (int d = part; d < dk; d += kDotLanes) dot = fmaf(qr[d], kr[d], dot);
       }
-      l_s[tid] = l_s[tid] * alpha + sum;
-      m_s[tid] = mt;
-      alpha_s[tid] = alpha;
-    }
-    __syncthreads();
-    // weighted values
 #pragma unroll
-    for (int k = 0; k < kAcc; ++k) {
-      const int idx = tid + k * kThreads;
-      const int hh = idx / dv, d = idx % dv;
-      if (hh < nh) {
-        float v = acc[k] * alpha_s[hh];
-        for (int tt = 0; tt < n_t; ++tt) {
-          if (!ok_s[tt]) continue;
-          const float x = vc ? E::load(vc, vbase_s[tt] + int64_t(d) * bs) : E::load(kc, vbase_s[tt] + d);
-          v = fmaf(s_s[hh][tt], x, v);
+      for (int x = 1; x < kDotLanes; x <<= 1) dot += __shfl_xor(dot, x);
+      if (valid && part == 0) s_s[hh][tt] = ok_s[tt] && t0 + tt < lim_s[hh] ? dot * score_mul : -INFINITY;
+    }
+    __syncthreads();
+    // online softmax update: 16 lanes per head, two tokens each
+    {
+      const int hh = tid >> 4, part = tid & 15;
+      const bool hv = hh < nh;
+      const float s0 = hv && part < n_t ? s_s[hh][part] : -INFINITY;
+      const float s1 = hv && part + 16 < n_t ? s_s[hh][part + 16] : -INFINITY;
+      const float m_old = hv ? m_s[hh] : -INFINITY;
+      float mt = fmaxf(s0, s1);
+#pragma unroll
+      for (int x = 1; x < 16; x <<= 1) mt = fmaxf(mt, __shfl_xor(mt, x));
+      mt = fmaxf(mt, m_old);
+      const float alpha = (mt == -INFINITY) ? 1.f : expf(m_old - mt);
+      const float e0 = s0 != -INFINITY ? expf(s0 - mt) : 0.f;
+      const float e1 = s1 != -INFINITY ? expf(s1 - mt) : 0.f;
+      float sum = e0 + e1;
+#pragma unroll
+      for (int x = 1; x < 16; x <<= 1) sum += __shfl_xor(sum, x);
+      if (hv) {
+        if (part < n_t) s_s[hh][part] = e0;
+        if (part + 16 < n_t) s_s[hh][part + 16] = e1;
+        if (part == 0) {
+          l_s[hh] = l_s[hh] * alpha + sum;
+          m_s[hh] = mt;
+          alpha_s[hh] = alpha;
         }
-        acc[k] = v;
       }
+    }
+    __syncthreads();
+    // weighted values (values of a latent cache: the first dv entries of the key rows)
+    const float* vt = vc ? v_s : k_s;
+    const int vs = vc ? vstride : kstride;
+#pragma unroll
+    for (int k = 0, hh = acc_h0, d = acc_d0; k < kAcc; ++k) {
+      if (hh >= nh) break;
+      float v = acc[k] * alpha_s[hh];
+#pragma unroll 4
+      for (int tt = 0; tt < n_t; ++tt) {
+        if (!ok_s[tt]) continue;
+        v = fmaf(s_s[hh][tt], vt[tt * vs + d], v);
+      }
+      acc[k] = v;
+      next_acc(hh, d);
     }
     __syncthreads();
   }
 #pragma unroll
-  for (int k = 0; k < kAcc; ++k) {
-    const int idx = tid + k * kThreads;
-    const int hh = idx / dv, d = idx % dv;
-    if (hh < nh) a.part_out[out_row(hh) * dv + d] = l_s[hh] > 0.f ? acc[k] / l_s[hh] * out_mul : 0.f;
+  for (int k = 0, hh = acc_h0, d = acc_d0; k < kAcc; ++k) {
+    if (hh >= nh) break;
+    a.part_out[out_row(hh) * dv + d] = l_s[hh] > 0.f ? acc[k] / l_s[hh] * out_mul : 0.f;
+    next_acc(hh, d);
   }
   // a column may see none of this partition's tokens: lse -inf
   if (tid < nh) a.part_lse[out_row(tid)] = l_s[tid] > 0.f ? m_s[tid] + logf(l_s[tid]) : -INFINITY;
