@@ -225,12 +225,26 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(KT == k
   const int c0 = (blockIdx.y % chunks) * 16;
   const int ncol = min(16, nq * g - c0);         // valid columns here
   const int bs = a.bs;
-  // the step's append, when this launch performs it: before any read of the cache
-  if (c0 == 0) fused_append(a, b, r, p, kvh);
-
-  const int L = a.context_lens[b];
-  const int Lr = L > 0 ? shard_len(L, a.n_shards, a.interleave, r) : 0;
   const int T = a.part_tokens;
+  // The step's append, when this launch performs it: the new rows are read first, then
+  // the context length and the table window below arrive together with them, and the
+  // rows are stored (append_store) before any read of the cache.
+  NewRowShare new_rows;
+  if (c0 == 0) new_rows = append_fetch(a, b, kvh);
+  const int L = a.context_lens[b];
+  // Table window: entries tbl_base .. tbl_base + 63 of the shard's row, one per lane,
+  // starting at the partition's first block.  Read raw here, so that no wait follows the
+  // read, and checked as table_entry checks before the first lookup.
+  const int32_t* row = a.block_table + (int64_t(b) * a.n_shards + r) * a.max_blocks;
+  auto raw_entry = [&](int j) -> int { return j < a.max_blocks ? row[j] : 0; };
+  int tbl_base = p * T / bs;
+  int tbl = raw_entry(tbl_base + lane);
+  if (c0 == 0)
+    append_store(a, new_rows, b, r, p, kvh, L, [&](int j) {
+      return j >= tbl_base && j - tbl_base < 64 ? __builtin_amdgcn_readlane(tbl, j - tbl_base) : row[j];
+    });
+
+  const int Lr = L > 0 ? shard_len(L, a.n_shards, a.interleave, r) : 0;
   // several new tokens: more than the context holds, or rows outside the arrays, is an
   // error (flagged, rows left unwritten); one per sequence: an empty context is allowed
   const bool bad = a.query_start && (nq > L || nq > a.max_q || row0 < 0 || row0 + nq > a.n_rows);
@@ -281,10 +295,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(KT == k
   const int s_hi = s_lo + per + (wave < extra ? 1 : 0);
 
   const int spb = bs >> 4;  // sub-tiles per block
-  const int32_t* row = a.block_table + (int64_t(b) * a.n_shards + r) * a.max_blocks;
-  int tbl_base = -(1 << 30);
-  int tbl = -1;
 
+  tbl = tbl_base + lane >= a.max_blocks ? kPastRow : (tbl < 0 || int64_t(tbl) >= a.n_blocks ? kBadId : tbl);
   auto block_of = [&](int e) -> int {            // e: logical block entry (wave-uniform)
     if (e - tbl_base >= 64 || e < tbl_base) {
       tbl_base = e;

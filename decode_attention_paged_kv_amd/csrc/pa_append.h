@@ -124,4 +124,77 @@ __device__ inline void fused_append(const DecodeArgs& a, int b, int r, int p, in
   __syncthreads();
 }
 
+// The same append in two halves, for a decode kernel that issues its own first loads in
+// between.  append_fetch reads this thread's share of sequence b's new rows for KV head h
+// -- key element threadIdx.x and value element threadIdx.x, so dk and dv must not exceed
+// the workgroup size -- before anything is known about the sequence.  append_store then
+// does what fused_append does after its reads: it decides from the context length L
+// whether this workgroup's partition holds the new token, takes the token's block from
+// entry(j), the raw table value of entry j (j < max_blocks), stores the rows (quantised
+// for an E4M3 cache), waits for the stores and meets the workgroup.  Both are called by
+// every thread of the workgroup with the same arguments.
+struct NewRowShare {
+  uint32_t k = 0, v = 0;   // raw bits of one key and one value element
+};
+
+__device__ inline NewRowShare append_fetch(const DecodeArgs& a, int b, int h) {
+  NewRowShare s;
+  if (a.k_new == nullptr) return s;
+  const int t = threadIdx.x;
+  const int nd = a.kv_dtype == kFP8 ? a.new_dtype : a.kv_dtype;   // element type of the new rows
+  const int64_t kr = (int64_t(b) * a.hkv + h) * a.dk, vr = (int64_t(b) * a.hkv + h) * a.dv;
+  if (nd == kF32) {
+    if (t < a.dk) s.k = static_cast<const uint32_t*>(a.k_new)[kr + t];
+    if (a.v_cache != nullptr && t < a.dv) s.v = static_cast<const uint32_t*>(a.v_new)[vr + t];
+  } else {
+    if (t < a.dk) s.k = static_cast<const uint16_t*>(a.k_new)[kr + t];
+    if (a.v_cache != nullptr && t < a.dv) s.v = static_cast<const uint16_t*>(a.v_new)[vr + t];
+  }
+  return s;
+}
+
+template <typename Entry>
+__device__ inline void append_store(const DecodeArgs& a, const NewRowShare& s, int b, int r, int p,
+                                    int h, int L, Entry&& entry) {
+  if (a.k_new == nullptr) return;
+  if (L <= 0) {   // no new token: slot -1, recorded once
+    if (a.slots_out && p == 0 && r == 0 && h == 0 && threadIdx.x == 0) a.slots_out[b] = -1;
+    return;
+  }
+  const int pos = L - 1;
+  const int t = local_index(pos, a.n_shards, a.interleave);
+  if (shard_of(pos, a.n_shards, a.interleave) != r || t / a.part_tokens != p) return;
+  // table errors are reported by the decode's own reads of this entry
+  const int j = t / a.bs;
+  const int e = j < a.max_blocks ? entry(j) : -1;
+  const int64_t slot = (e >= 0 && int64_t(e) < a.n_blocks) ? int64_t(e) * a.bs + t % a.bs : -1;
+  if (a.slots_out && h == 0 && threadIdx.x == 0) a.slots_out[b] = slot;
+  if (slot >= 0) {
+    const int off = t % a.bs, tid = threadIdx.x;
+    const bool vals = a.v_cache != nullptr && tid < a.dv;
+    if (a.kv_dtype == kFP8) {
+      const int si = a.n_scales > 1 ? h : 0;
+      auto widen = [&](uint32_t x) { return a.new_dtype == kF32 ? __uint_as_float(x) : bf16_bits_to_f32(uint16_t(x)); };
+      uint8_t* kc = static_cast<uint8_t*>(const_cast<void*>(a.k_cache));
+      uint8_t* vc = static_cast<uint8_t*>(const_cast<void*>(a.v_cache));
+      if (tid < a.dk) kc[key_row(e, h, a.hkv, a.bs, off, a.dk) + tid] = f32_to_e4m3(__fdiv_rn(widen(s.k), a.k_scale[si]));
+      if (vals)
+        vc[value_tile(e, h, a.hkv, a.bs, a.dv) + int64_t(tid) * a.bs + off] = f32_to_e4m3(__fdiv_rn(widen(s.v), a.v_scale[si]));
+    } else if (a.kv_dtype == kF32) {
+      uint32_t* kc = static_cast<uint32_t*>(const_cast<void*>(a.k_cache));
+      uint32_t* vc = static_cast<uint32_t*>(const_cast<void*>(a.v_cache));
+      if (tid < a.dk) kc[key_row(e, h, a.hkv, a.bs, off, a.dk) + tid] = s.k;
+      if (vals) vc[value_tile(e, h, a.hkv, a.bs, a.dv) + int64_t(tid) * a.bs + off] = s.v;
+    } else {
+      uint16_t* kc = static_cast<uint16_t*>(const_cast<void*>(a.k_cache));
+      uint16_t* vc = static_cast<uint16_t*>(const_cast<void*>(a.v_cache));
+      if (tid < a.dk) kc[key_row(e, h, a.hkv, a.bs, off, a.dk) + tid] = uint16_t(s.k);
+      if (vals) vc[value_tile(e, h, a.hkv, a.bs, a.dv) + int64_t(tid) * a.bs + off] = uint16_t(s.v);
+    }
+  }
+  // as in fused_append: the stores complete in L2, then the waves meet
+  __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0); expcnt and lgkmcnt not waited for
+  __syncthreads();
+}
+
 }  // namespace pa
