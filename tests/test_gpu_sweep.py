@@ -76,3 +76,29 @@ def test_random_shape(i):
                  n_shards=c["S"], interleave=c["I"], partition_tokens=c["T"], latent=c["latent"],
                  seed=100 + i, kv_dtype=c["kv"], scale_per_head=c["per_head"], q_lens=c["q_lens"])
     check_small(w)
+
+
+# The VALU kernel stages each tile's keys and values through a fixed LDS buffer, so its
+# tile holds fewer than 32 tokens when rows are long: 7 tokens at fp32 576/512 with a
+# separate value cache, 14 for an fp32 latent cache of 576, 31 at fp32 128/128.  These
+# cases put several such tiles (and a ragged last one) in each partition.
+GENERIC_CASES = [
+    dict(name="gen_f32_576_512", lens=[0, 1, 100, 333], hq=16, hkv=1, dk=576, dv=512, bs=16,
+         dt=wl.F32, kv="", S=1, I=1, T=64, latent=False, q_lens=None),
+    dict(name="gen_f32_latent576", lens=[700, 5, 64], hq=16, hkv=1, dk=576, dv=512, bs=64,
+         dt=wl.F32, kv="", S=1, I=1, T=128, latent=True, q_lens=None),
+    dict(name="gen_f32_128_multi", lens=[150, 40, 97], hq=8, hkv=2, dk=128, dv=128, bs=8,
+         dt=wl.F32, kv="", S=2, I=16, T=96, latent=False, q_lens=[3, 1, 5]),
+    dict(name="gen_bf16_96_g20", lens=[260, 1, 33], hq=40, hkv=2, dk=96, dv=96, bs=16,
+         dt=wl.BF16, kv="", S=1, I=1, T=128, latent=False, q_lens=[2, 1, 4]),
+    dict(name="gen_fp8_f32q_128", lens=[300, 77], hq=8, hkv=2, dk=128, dv=128, bs=16,
+         dt=wl.F32, kv=wl.FP8, S=2, I=16, T=256, latent=False, q_lens=None),
+]
+
+
+@pytest.mark.parametrize("c", GENERIC_CASES, ids=[c["name"] for c in GENERIC_CASES])
+def test_generic_tile_sizes(c):
+    w = wl.small(c["name"], c["lens"], c["hq"], c["hkv"], c["dk"], c["dv"], c["bs"], c["dt"],
+                 n_shards=c["S"], interleave=c["I"], partition_tokens=c["T"], latent=c["latent"],
+                 seed=7, kv_dtype=c["kv"], q_lens=c["q_lens"])
+    check_small(w)
