@@ -125,6 +125,25 @@ def measured_traffic(config, launches_bytes):
     return d.get("hbm_bytes_per_launch")
 
 
+_SPIN_RATE = []
+
+
+def spin_cycles(ms):
+    """The argument of torch.cuda._sleep that spins the GPU for about ``ms``
+    milliseconds (its rate measured once per process)."""
+    import torch
+
+    if not _SPIN_RATE:
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(1000)
+        a.record()
+        torch.cuda._sleep(1_000_000)
+        b.record()
+        torch.cuda.synchronize()
+        _SPIN_RATE.append(1_000_000 / max(a.elapsed_time(b), 1e-3))   # argument units per ms
+    return int(ms * _SPIN_RATE[0])
+
+
 def time_gpu(w, T, step, steps, warmup, settle_s=SETTLE_S):
     import torch
 
@@ -157,22 +176,39 @@ def time_gpu(w, T, step, steps, warmup, settle_s=SETTLE_S):
             step(*args)
         settle += 10
         torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
+    # The timed region holds exactly the K steps.  The decode launch's own duration comes
+    # from the next K steps, identical, with an event pair recorded on the launch stream
+    # around each decode launch: an event record costs the host ~4.5 us, which inside the
+    # timed loop would make the host, not the GPU, set the pace of short steps.
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t0.record()
     for i in range(steps):
         prepare()
-        ev[i][0].record()
         attend()
-        ev[i][1].record()
         step.merge()
     t1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = t0.elapsed_time(t1)
+    # Short steps (the host's enqueue time, ~20 us a step with the events, then exceeds the
+    # GPU's): a bounded spin of ~50 us per step is queued first, so that the host has
+    # enqueued these steps before the GPU reaches them and each event interval holds the
+    # decode launch, not the host's time to enqueue it.  Long steps keep the GPU ahead of
+    # the host by themselves (and a spin would let the clocks of power-limited kernels
+    # drop before the measured launches).
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    if total_ms / steps < 0.1:
+        torch.cuda._sleep(spin_cycles(50e-3 * steps))
+    for i in range(steps):
+        prepare()
+        ev[i][0].record()
+        attend()
+        ev[i][1].record()
+        step.merge()
+    torch.cuda.synchronize()
     dec = sorted(a.elapsed_time(b) for a, b in ev)
     res = dict(total_ms=total_ms, wall_s=wall, decode_ms_mean=sum(dec) / len(dec),
                decode_ms_median=dec[len(dec) // 2], decode_ms_min=dec[0], settle_steps=settle)
