@@ -464,6 +464,12 @@ def pa_decode_multi(q, query_start, max_q_len, k_cache, v_cache, block_table, co
 
 def pa_merge_lse(part_out, part_lse, out, lse=None):
     """``part_out [N][P...][Hq][dv]`` (any number of part axes), ``out [N][Hq][dv]``."""
+    call_merge_lse(merge_lse_args(part_out, part_lse, out, lse), out)
+
+
+def merge_lse_args(part_out, part_lse, out, lse=None):
+    """The checks of ``pa_merge_lse`` and its C arguments but the stream, as a tuple (a
+    caller that merges into the same tensors again can reuse it)."""
     _need(part_out, torch.float32, None, "part_out")
     _need(part_lse, torch.float32, None, "part_lse")
     _need(out, None, 3, "out")
@@ -472,8 +478,13 @@ def pa_merge_lse(part_out, part_lse, out, lse=None):
     n_parts = part_lse.numel() // max(n * hq, 1)
     if part_lse.numel() != n * n_parts * hq or part_out.numel() != n * n_parts * hq * dv:
         raise ValueError("part_out / part_lse / out sizes disagree")
-    _check(lib.pa_merge_lse(_ptr(part_out), _ptr(part_lse), n, n_parts, hq, dv, _ptr(out),
-                            _dtype_code(out), _ptr(lse), _stream(out)))
+    return (_ptr(part_out), _ptr(part_lse), n, n_parts, hq, dv, _ptr(out), _dtype_code(out), _ptr(lse))
+
+
+def call_merge_lse(args, out):
+    """``pa_merge_lse`` on the arguments ``merge_lse_args`` built, on ``out``'s device's
+    current stream."""
+    _check(lib.pa_merge_lse(*args, _stream(out)))
 
 
 def pa_gather_kv(k_cache, v_cache, block_table, seq, shard, context_len, n_shards, interleave,

@@ -239,6 +239,26 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(KT == k
   auto raw_entry = [&](int j) -> int { return j < a.max_blocks ? row[j] : 0; };
   int tbl_base = p * T / bs;
   int tbl = raw_entry(tbl_base + lane);
+
+  // query operand: lane (column col, group grp) holds q[row][head][32j + 8grp .. +7]
+  // (bf16 cache) or [grp*D/4 + 8j .. +7] (E4M3 cache), the order of the key operand.
+  // Issued with the reads above, so that the append's wait for its stores also covers
+  // them; the rows are inside the array whenever query_start is (checked again below).
+  bf16x8_t qop[KJ];
+  {
+    const bool rows_ok = !a.query_start || (row0 >= 0 && nq >= 0 && row0 + nq <= a.n_rows);
+    const int qi = (c0 + col) / g, h = (c0 + col) - qi * g;
+    const uint16_t* qrow = q + (int64_t(row0 + qi) * a.hq + kvh * g + h) * D +
+                           (F8 ? grp * (D / 4) : 8 * grp);
+#pragma unroll
+    for (int j = 0; j < KJ; ++j) {
+      if (col < ncol && rows_ok)
+        qop[j] = *reinterpret_cast<const bf16x8_t*>(qrow + (F8 ? 8 * j : 32 * j));
+      else
+        qop[j] = bf16x8_t{};
+    }
+  }
+
   if (c0 == 0)
     append_store(a, new_rows, b, r, p, kvh, L, [&](int j) {
       return j >= tbl_base && j - tbl_base < 64 ? __builtin_amdgcn_readlane(tbl, j - tbl_base) : row[j];
@@ -269,22 +289,6 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(KT == k
     return;
   }
   const int lim = min(t_end, visible(min(col, ncol - 1)));   // this lane's column's end
-
-  // query operand: lane (column col, group grp) holds q[row][head][32j + 8grp .. +7]
-  // (bf16 cache) or [grp*D/4 + 8j .. +7] (E4M3 cache), the order of the key operand
-  bf16x8_t qop[KJ];
-  {
-    const int qi = (c0 + col) / g, h = (c0 + col) - qi * g;
-    const uint16_t* qrow = q + (int64_t(row0 + qi) * a.hq + kvh * g + h) * D +
-                           (F8 ? grp * (D / 4) : 8 * grp);
-#pragma unroll
-    for (int j = 0; j < KJ; ++j) {
-      if (col < ncol)
-        qop[j] = *reinterpret_cast<const bf16x8_t*>(qrow + (F8 ? 8 * j : 32 * j));
-      else
-        qop[j] = bf16x8_t{};
-    }
-  }
 
   // this wave's contiguous range of steps of SUBS 16-token sub-tiles
   const int u0 = t_begin >> 4;                   // first sub-tile (T and bs are multiples of 16)

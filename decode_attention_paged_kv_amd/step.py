@@ -43,6 +43,9 @@ class DecodeStep:
                                                    n_shards, P, out_dtype, dev)
         self.err_flag = torch.zeros(1, dtype=torch.int32, device=dev)
         self._step_key, self._step_args = None, None   # see append_attend
+        # the merge always reads and writes this object's own buffers: checked once
+        self._merge_args = None if self.direct else L.merge_lse_args(self.part_out, self.part_lse,
+                                                                      self.out, self.lse)
 
     def route(self, block_table, context_lens, n_blocks):
         L.pa_slot_mapping(block_table, context_lens, self.n_shards, self.interleave,
@@ -76,7 +79,7 @@ class DecodeStep:
 
     def merge(self):
         if not self.direct:
-            L.pa_merge_lse(self.part_out, self.part_lse, self.out, self.lse)
+            L.call_merge_lse(self._merge_args, self.out)
 
     def append_attend(self, q, k_new, v_new, k_cache, v_cache, block_table, context_lens,
                       k_scale=None, v_scale=None):
@@ -86,15 +89,13 @@ class DecodeStep:
         # objects, storage and shapes): the checks cost more host time than a small
         # step's launch.  The library checks every call again.
         ts = (q, k_new, v_new, k_cache, v_cache, block_table, context_lens, k_scale, v_scale)
-        key = self._step_key
-        if key is None or not all(t is k[0] and (t is None or (t.data_ptr() == k[1] and t.shape == k[2]))
-                                  for t, k in zip(ts, key)):
+        if not _same_tensors(ts, self._step_key):
             self._step_args = L.decode_step_args(q, k_new, v_new, k_cache, v_cache, block_table,
                                                  context_lens, self.n_shards, self.interleave,
                                                  self.partition_tokens, self.max_partitions,
                                                  self.scale, self.part_out, self.part_lse, k_scale,
                                                  v_scale, self.slot_mapping, self.dv, self.err_flag)
-            self._step_key = tuple((t, None, None) if t is None else (t, t.data_ptr(), t.shape) for t in ts)
+            self._step_key = _tensor_key(ts)
         L.call_decode_step(self._step_args, q)
 
     def __call__(self, q, k_new, v_new, k_cache, v_cache, block_table, context_lens, k_scale=None,
@@ -112,6 +113,22 @@ class DecodeStep:
         tensors hold at that time.  The library allocates nothing and issues no memset,
         so the recorded launches are the step itself."""
         return capture_graph(lambda: self(*args, **kwargs))
+
+
+def _tensor_key(ts):
+    """What ``_same_tensors`` compares: each argument, its data address and shape."""
+    return tuple((t, None, None) if t is None else (t, t.data_ptr(), t.shape) for t in ts)
+
+
+def _same_tensors(ts, key):
+    """True when ``ts`` are the very tensors ``key`` was taken of, still at the same
+    addresses and shapes (a plain loop: this runs on every step)."""
+    if key is None:
+        return False
+    for t, (t0, p0, s0) in zip(ts, key):
+        if t is not t0 or (t is not None and (t.data_ptr() != p0 or t.shape != s0)):
+            return False
+    return True
 
 
 def _outputs(part_out, part_lse, n_rows, hq, dv, n_shards, max_partitions, out_dtype, dev):
@@ -173,6 +190,8 @@ class MultiDecodeStep:
         self.out, self.lse, self.direct = _outputs(self.part_out, self.part_lse, n_rows, n_q_heads, dv,
                                                    n_shards, P, out_dtype, dev)
         self.err_flag = torch.zeros(1, dtype=torch.int32, device=dev)
+        self._merge_args = None if self.direct else L.merge_lse_args(self.part_out, self.part_lse,
+                                                                      self.out, self.lse)
 
     def route(self, block_table, context_lens, query_start, n_blocks):
         L.pa_slot_mapping_multi(block_table, context_lens, query_start, self.n_shards,
@@ -195,7 +214,7 @@ class MultiDecodeStep:
 
     def merge(self):
         if not self.direct:
-            L.pa_merge_lse(self.part_out, self.part_lse, self.out, self.lse)
+            L.call_merge_lse(self._merge_args, self.out)
 
     def __call__(self, q, query_start, k_new, v_new, k_cache, v_cache, block_table, context_lens,
                  k_scale=None, v_scale=None):
