@@ -5,7 +5,8 @@ pa_decode_fp8): every byte of both caches, the slots, and every partial output a
 (the decode reads the same cache, so the results must be identical, not merely close).
 The two-call path is itself held to the oracle by the routed-append and decode parity
 tests.  Cases cover each decode kernel with the append fused (GQA bf16, the generic
-kernel in fp32, E4M3, DCP shards with interleave, the latent kernel) and the shapes that
+kernel in fp32 and with an E4M3 cache or a latent view, E4M3, DCP shards with interleave,
+the latent kernel) and the shapes that
 keep the append a launch of its own (more than 16 query heads per KV head; more than 128
 on the latent kernel), with empty, one-token and multi-partition sequences."""
 import numpy as np
@@ -30,6 +31,8 @@ CASES = [
     ("gqa_bf16", [1, 17, 300, 0, 1000], 32, 8, 128, 128, 16, wl.BF16, 1, 1, False, "", 64),
     ("gqa_g32_unfused", [5, 260, 0, 77], 64, 2, 128, 128, 16, wl.BF16, 1, 1, False, "", 128),
     ("generic_f32_dcp", [0, 1, 5, 130, 77], 6, 3, 40, 24, 8, wl.F32, 3, 2, False, "", 16),
+    ("generic_e4m3", [0, 3, 40, 77, 130], 8, 2, 40, 24, 8, wl.BF16, 2, 4, False, wl.FP8, 32),
+    ("generic_latent_f32", [1, 9, 66, 0, 200], 4, 1, 64, 48, 4, wl.F32, 1, 1, True, "", 16),
     ("gqa_dcp16", [900, 31, 16, 0], 64, 8, 128, 128, 16, wl.BF16, 4, 16, False, "", 96),
     ("gqa_e4m3", [33, 520, 0, 1], 32, 8, 128, 128, 16, wl.BF16, 1, 1, False, wl.FP8, 128),
     ("latent", [65, 300, 1, 0, 2000], 16, 1, 576, 512, 64, wl.BF16, 1, 1, True, "", 256),
