@@ -21,8 +21,8 @@ workloads.
 K and V element of every sequence read once per step; one byte per element for the
 ``_fp8`` configurations, whose cache holds E4M3 codes).  ``roofline`` prices the
 decode kernel alone (with the append it performs): the same algorithmic bytes over
-its average launch time, measured with HIP events around each launch inside the
-timed region.
+its average launch time, measured with HIP events on its stream around K launches of
+it, back to back, right after the timed region.
 """
 from __future__ import annotations
 
@@ -177,9 +177,8 @@ def time_gpu(w, T, step, steps, warmup, settle_s=SETTLE_S):
         settle += 10
         torch.cuda.synchronize()
     # The timed region holds exactly the K steps.  The decode launch's own duration comes
-    # from the next K steps, identical, with an event pair recorded on the launch stream
-    # around each decode launch: an event record costs the host ~4.5 us, which inside the
-    # timed loop would make the host, not the GPU, set the pace of short steps.
+    # from launches after it (below): an event record costs the host ~4.5 us, which inside
+    # the timed loop would make the host, not the GPU, set the pace of short steps.
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
@@ -210,8 +209,21 @@ def time_gpu(w, T, step, steps, warmup, settle_s=SETTLE_S):
         step.merge()
     torch.cuda.synchronize()
     dec = sorted(a.elapsed_time(b) for a, b in ev)
-    res = dict(total_ms=total_ms, wall_s=wall, decode_ms_mean=sum(dec) / len(dec),
-               decode_ms_median=dec[len(dec) // 2], decode_ms_min=dec[0], settle_steps=settle)
+    # The decode launch's average duration (what the roofline prices): K more decode
+    # launches alone, back to back, between one event pair on the launch stream, behind
+    # the same spin when launches are short.  The pairs above give the spread from launch
+    # to launch, but each pair's markers add a few microseconds to a short launch.
+    b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    if total_ms / steps < 0.1:
+        torch.cuda._sleep(spin_cycles(50e-3 * steps))
+    b0.record()
+    for i in range(steps):
+        attend()
+    b1.record()
+    torch.cuda.synchronize()
+    res = dict(total_ms=total_ms, wall_s=wall, decode_ms_mean=b0.elapsed_time(b1) / steps,
+               decode_ms_pairs_mean=sum(dec) / len(dec), decode_ms_median=dec[len(dec) // 2],
+               decode_ms_min=dec[0], settle_steps=settle)
     # After the timed region: the same step recorded once as a HIP graph and replayed
     # K times (reported separately; it removes the host's per-launch cost).
     graph = step.capture(*args)
@@ -254,11 +266,21 @@ def time_gpu(w, T, step, steps, warmup, settle_s=SETTLE_S):
     return res
 
 
+def mfma_roofline(r):
+    """The latent decode against the dense bf16 matrix-core peak: the attention's products
+    counted once (``mfma_frac``), and the MFMA work the kernel issues for them
+    (``mfma_frac_executed``: the value product twice, for the weights' bf16 pair)."""
+    return {"mfma_tflops": round(r["tflops"], 2), "mfma_frac": round(r["tflops"] / MFMA_BF16_TFLOPS, 4),
+            "mfma_tflops_executed": round(r["tflops_executed"], 2),
+            "mfma_frac_executed": round(r["tflops_executed"] / MFMA_BF16_TFLOPS, 4)}
+
+
 def timing_fields(t):
-    """The per-iteration spread of the hot (cache-warm, back-to-back) decode launch and
-    the cold (caches flushed before each step) step and decode launch, in ms."""
-    keys = ("decode_ms_median", "decode_ms_min", "cold_ms_per_step_median", "cold_decode_ms_median",
-            "cold_decode_ms_min")
+    """The per-iteration spread of the hot (cache-warm, back-to-back) decode launch, each
+    between its own event pair (mean, median, min), and the cold (caches flushed before
+    each step) step and decode launch, in ms."""
+    keys = ("decode_ms_pairs_mean", "decode_ms_median", "decode_ms_min", "cold_ms_per_step_median",
+            "cold_decode_ms_median", "cold_decode_ms_min")
     out = {k: round(t[k], 5) for k in keys}
     out["settle_steps"] = t["settle_steps"]
     out["cold_iterations"] = t["cold_iterations"]
@@ -409,8 +431,13 @@ def run_config(name, steps, warmup, with_cpu, partition_tokens=0, settle_s=SETTL
                value=kv_bytes / (ms * 1e-3) / 1e9, seq_steps=w.n_seqs / (ms * 1e-3),
                achieved=achieved, timing=t, cpu=cpu)
     if w.latent:
+        # the attention's own products (scores and weighted values, each counted once),
+        # and the matrix-core work the kernel issues for them: the weights enter the value
+        # product as a bf16 pair, two MFMAs per value operand
         flops = int(np.sum(w.context_lens.astype(np.int64))) * w.n_q_heads * 2 * (w.dk + w.dv)
+        executed = int(np.sum(w.context_lens.astype(np.int64))) * w.n_q_heads * 2 * (w.dk + 2 * w.dv)
         res["tflops"] = flops / (dec_ms * 1e-3) / 1e12
+        res["tflops_executed"] = executed / (dec_ms * 1e-3) / 1e12
     return res
 
 
@@ -503,8 +530,7 @@ def main():
         "cpu_baseline": r["cpu"],
     }
     if "tflops" in r:
-        line["roofline"]["mfma_tflops"] = round(r["tflops"], 2)
-        line["roofline"]["mfma_frac"] = round(r["tflops"] / MFMA_BF16_TFLOPS, 4)
+        line["roofline"].update(mfma_roofline(r))
     if not a.no_secondary:
         import torch
 
@@ -538,8 +564,7 @@ def main():
                 "cpu_baseline": s["cpu"],
             }
             if "tflops" in s:
-                sec[name]["roofline"]["mfma_tflops"] = round(s["tflops"], 2)
-                sec[name]["roofline"]["mfma_frac"] = round(s["tflops"] / MFMA_BF16_TFLOPS, 4)
+                sec[name]["roofline"].update(mfma_roofline(s))
             del s
             torch.cuda.empty_cache()
             print(f"bench.py: {name} done", file=sys.stderr, flush=True)
