@@ -496,7 +496,7 @@ def main():
     w = r["w"]
     traffic = measured_traffic(a.config, r["kv_bytes"])
     line = {
-        "metric": "paged decode-attention KV-read GB/s (and % of MI355X HBM peak; seq-steps/s)",
+        "metric": "paged decode-attention KV-read GB/s and % of MI355X HBM peak; seq-steps/s",
         "value": round(r["value"], 2),
         "unit": "GB/s",
         "n_gpus": 1,
