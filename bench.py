@@ -16,7 +16,7 @@ around 142K tokens), the configuration the HBM-roofline target is stated for.
 The other synthetic workloads (tiny, batch, DCP I=1 and I=16, the same 200K
 sequence unsharded, latent) follow under ``secondary``, each with its own rates,
 decode roofline and oracle baseline; ``--next`` adds the E4M3 and multi-token
-workloads.
+workloads, the same way.
 ``value`` is KV-read GB/s over the whole step (algorithmic bytes: every stored
 K and V element of every sequence read once per step; one byte per element for the
 ``_fp8`` configurations, whose cache holds E4M3 codes).  ``roofline`` prices the
@@ -541,7 +541,7 @@ def main():
         for name in names:
             if name == a.config:
                 continue
-            with_cpu = not a.no_cpu_baseline and name in SECONDARY
+            with_cpu = not a.no_cpu_baseline
             s = run_config(name, a.steps, a.warmup, with_cpu, settle_s=a.settle, cpu_budget=a.cpu_budget / 2)
             sw = s["w"]
             sec[name] = {
