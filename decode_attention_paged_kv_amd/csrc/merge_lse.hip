@@ -11,6 +11,8 @@
 // per (sequence, head) and block of columns.
 #include <math.h>
 
+#include <type_traits>
+
 #include "pa_common.h"
 #include "pa_launch.h"
 
@@ -148,7 +150,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const float* __restrict
 // VEC columns: in a round, lane (pg, cg) reads parts p0 + pg + PG k, k < 8 (issued
 // together) of its columns, so a round covers 8 PG parts; the part groups' sums meet by
 // xor exchanges.  PG = 8: one round for up to 64 parts, narrow blocks (many waves when
-// rows are few); PG = 1: wide blocks, every lane's loads useful (many rows).
+// rows are few); smaller PG: wider blocks, fewer waves (many rows).
 constexpr int kWaveParts = 64;
 
 __device__ inline float wave_max(float v) {
@@ -249,15 +251,26 @@ hipError_t launch_merge(const float* part_out, const float* part_lse, int n_seqs
   // groups per workgroup), so each workgroup has enough work.
   const int vec = dv % 4 == 0 ? 4 : 1;
   if (n_parts <= kWaveParts) {
-    // narrow blocks (8 part groups) while they give fewer than ~16K waves, else wide ones
+    // As many part groups (8, 4, 2 or 1; more groups: narrower column blocks, more waves,
+    // more parts read at once) as keep the launch within ~16K waves.  Measured, merge
+    // alone: latent (4,096 rows, 16 parts) 14.5 / 12.2 / 20.5 / 34.9 us with 1 / 2 / 4 / 8
+    // groups; long (256 rows, ~50 parts) 6.8 / 5.0 / 4.0 / 3.5 us.
     const int rows = n_seqs * hq;
-    const bool narrow = int64_t(rows) * ((dv + 8 * vec - 1) / (8 * vec)) <= 16384;
-    if (vec == 4)
-      narrow ? launch_wave<4, 8>(part_out, part_lse, rows, n_parts, hq, dv, out, out_dtype, lse, st)
-             : launch_wave<4, 1>(part_out, part_lse, rows, n_parts, hq, dv, out, out_dtype, lse, st);
-    else
-      narrow ? launch_wave<1, 8>(part_out, part_lse, rows, n_parts, hq, dv, out, out_dtype, lse, st)
-             : launch_wave<1, 1>(part_out, part_lse, rows, n_parts, hq, dv, out, out_dtype, lse, st);
+    int pg = 8;
+    while (pg > 1 && int64_t(rows) * ((dv + (64 / pg) * vec - 1) / ((64 / pg) * vec)) > 16384) pg /= 2;
+    auto go = [&](auto v, auto g) {
+      launch_wave<decltype(v)::value, decltype(g)::value>(part_out, part_lse, rows, n_parts, hq, dv, out,
+                                                          out_dtype, lse, st);
+    };
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I4 = std::integral_constant<int, 4>;
+    using I8 = std::integral_constant<int, 8>;
+    if (vec == 4) {
+      if (pg == 8) go(I4{}, I8{}); else if (pg == 4) go(I4{}, I4{}); else if (pg == 2) go(I4{}, I2{}); else go(I4{}, I1{});
+    } else {
+      if (pg == 8) go(I1{}, I8{}); else if (pg == 4) go(I1{}, I4{}); else if (pg == 2) go(I1{}, I2{}); else go(I1{}, I1{});
+    }
     return hipGetLastError();
   }
   int cb = 128 * vec;
