@@ -82,6 +82,7 @@ SMALL = [
     # 128 query heads on the latent cache: the matrix-core latent kernel
     ("f8_latent128", [129, 200, 700, 1500], 128, 1, 576, 512, 64, wl.BF16, 1, 1, 256, True, True),
     ("f8_latent128_edges", [0, 1, 65, 64], 128, 1, 576, 512, 64, wl.BF16, 1, 1, 64, True, False),
+    ("f8_latent128_bs128", [65, 1000], 128, 1, 576, 512, 128, wl.BF16, 1, 1, 384, True, True),
 ]
 
 
