@@ -223,6 +223,7 @@ SWEEP = [
     ("empty_seqs", [0, 1, 0, 20], 8, 4, 64, 64, 16, wl.BF16, 2, 16, 16, False, None),
     ("latent_small", [129, 200, 700, 1500], 128, 1, 576, 512, 64, wl.BF16, 1, 1, 256, True, (4, 128)),
     ("latent_f32", [65, 300], 16, 1, 576, 512, 64, wl.F32, 1, 1, 128, True, None),
+    ("gqa128_bs64_dcp", [1, 63, 64, 65, 640, 2000], 32, 8, 128, 128, 64, wl.BF16, 3, 4, 192, False, None),
     # the latent kernel with one tile per block, and with eight, on shards
     ("latent_bs32_dcp", [129, 700, 1500, 0], 128, 1, 576, 512, 32, wl.BF16, 2, 16, 256, True, None),
     ("latent_bs256", [300, 1500, 2100], 128, 1, 576, 512, 256, wl.BF16, 1, 1, 512, True, None),
